@@ -1,0 +1,163 @@
+"""Python front end of the fp64 CPU oracle (ssm_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.
+
+`build()` compiles ssm_oracle.c with gcc; the wrappers take numpy arrays of
+any float dtype, widen them to fp64 (exact for fp32 and for bf16 already
+decoded to fp32/fp64), and call the C code, optionally on several threads
+over disjoint ranges of (b, d) chains.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libssm_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+# strict IEEE fp64: no fast-math, no contraction into fma
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off"]
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle C source into a shared library; returns its path."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_L = ctypes.c_long
+
+
+def _bind(lib):
+    lib.oracle_selective_scan.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp, _dp,
+                                          _dp, _dp, _dp, _L, _L, _L, _L, _L, _L]
+    lib.oracle_selective_scan.restype = None
+    lib.oracle_state_update.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp,
+                                        _dp, _dp, _L, _L, _L, _L, _L]
+    lib.oracle_state_update.restype = None
+    lib.oracle_sm1_scan.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
+                                    _dp, _dp, _L, _L, _L, _L, _L]
+    lib.oracle_sm1_scan.restype = None
+    return lib
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if needed) the oracle library."""
+    global _lib
+    with _lock:
+        if path is not None:
+            return _bind(ctypes.CDLL(path))
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB_PATH))
+        return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.cast(None, _dp)
+    return a.ctypes.data_as(_dp)
+
+
+def _run_chains(fn, n_chains: int, threads: int):
+    threads = max(1, min(int(threads), n_chains if n_chains > 0 else 1))
+    if threads == 1:
+        fn(0, n_chains)
+        return
+    step = (n_chains + threads - 1) // threads
+    ts = [threading.Thread(target=fn, args=(i, min(i + step, n_chains)))
+          for i in range(0, n_chains, step)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+
+
+def selective_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                   h0=None, threads: int = 1, lib=None):
+    """Sequential fp64 scan.  x, delta, z: (Bt, T, Dd); B, C: (Bt, T, N); A: (Dd, N);
+    D, delta_bias: (Dd,); h0: (Bt, Dd, N).  Returns (y, last_state) in fp64."""
+    lib = lib or load()
+    x, delta, A, B, C = _f64(x), _f64(delta), _f64(A), _f64(B), _f64(C)
+    D, z, delta_bias, h0 = _f64(D), _f64(z), _f64(delta_bias), _f64(h0)
+    Bt, T, Dd = x.shape
+    N = A.shape[1]
+    assert delta.shape == x.shape and A.shape == (Dd, N)
+    assert B.shape == (Bt, T, N) and C.shape == (Bt, T, N)
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (Bt, Dd, N)
+    y = np.zeros((Bt, T, Dd), dtype=np.float64)
+    last = np.zeros((Bt, Dd, N), dtype=np.float64)
+
+    def go(c0, c1):
+        lib.oracle_selective_scan(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                  _ptr(y), _ptr(last), Bt, T, Dd, N, c0, c1)
+
+    _run_chains(go, Bt * Dd, threads)
+    return y, last
+
+
+def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=True, threads: int = 1, lib=None):
+    """One decode step.  state: (Bt, Dd, N) (not modified; the new state is
+    returned); x, delta, z: (Bt, Dd); B, C: (Bt, N).  Returns (y, new_state)."""
+    lib = lib or load()
+    st = _f64(state).copy()
+    x, delta, A, B, C = _f64(x), _f64(delta), _f64(A), _f64(B), _f64(C)
+    D, z, delta_bias = _f64(D), _f64(z), _f64(delta_bias)
+    Bt, Dd = x.shape
+    N = A.shape[1]
+    assert st.shape == (Bt, Dd, N) and B.shape == (Bt, N) and C.shape == (Bt, N)
+    y = np.zeros((Bt, Dd), dtype=np.float64)
+
+    def go(c0, c1):
+        lib.oracle_state_update(_ptr(st), _ptr(x), _ptr(delta), _ptr(delta_bias),
+                                int(bool(delta_softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(z), _ptr(y), Bt, Dd, N, c0, c1)
+
+    _run_chains(go, Bt * Dd, threads)
+    return y, st
+
+
+def sm1_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, threads: int = 1, lib=None):
+    """d_state = 1 scan.  A: (Dd,); B, C: (Bt, T); h0: (Bt, Dd).  Returns
+    (y (Bt,T,Dd), last_state (Bt,Dd))."""
+    lib = lib or load()
+    x, delta, A, B, C = _f64(x), _f64(delta), _f64(A), _f64(B), _f64(C)
+    D, z, delta_bias, h0 = _f64(D), _f64(z), _f64(delta_bias), _f64(h0)
+    Bt, T, Dd = x.shape
+    assert A.shape == (Dd,) and B.shape == (Bt, T) and C.shape == (Bt, T)
+    assert h0 is None or h0.shape == (Bt, Dd)
+    y = np.zeros((Bt, T, Dd), dtype=np.float64)
+    last = np.zeros((Bt, Dd), dtype=np.float64)
+
+    def go(c0, c1):
+        lib.oracle_sm1_scan(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                            _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+                            _ptr(last), Bt, T, Dd, c0, c1)
+
+    _run_chains(go, Bt * Dd, threads)
+    return y, last

@@ -1,0 +1,136 @@
+/*
+ * Selective-scan ORACLE: plain, slow, sequential fp64 CPU code.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, includes or calls it, and it shares no code with the GPU path.
+ *
+ * What it computes is the textbook definition of the Mamba-1 selective scan,
+ * written out with no blocking, fusion or reordering:
+ *
+ *   Delta discretisation  -- "Mamba State Space Models complete guide"
+ *       (youngju.dev), section 5, "core innovation: selective mechanism":
+ *       Delta is made positive by a softplus of its projection; here the
+ *       projection output is `delta` plus an optional per-channel bias.
+ *   Per-state decay       -- same page, section 2 "Discretization" (ZOH):
+ *       Abar = exp(Delta * A).  A is diagonal, so this is one scalar exp per
+ *       (channel d, state n).
+ *   Input term            -- same page, section 5, the pure-PyTorch
+ *       selective_scan of the "complete Mamba implementation": the input is
+ *       injected as Delta * B * x (the simplified Bbar, not the ZOH one).
+ *   Recurrence, readout   -- same page, section 2: x[t] = Abar x[t-1] + Bbar u[t],
+ *       y[t] = C x[t]; plus the D skip term of the continuous SSM (section 2,
+ *       "continuous-time SSM") and of the selective_scan listing.
+ *   Gate                  -- same page, section 5 MambaBlock.forward: the SSM
+ *       output is multiplied by SiLU(z).
+ *   Initial / final state -- the state enters as h0 (as in the SM1 closed
+ *       form, "Windows SM1 (Scalar Mamba1)" page, detailed-sections part) and
+ *       the state after the last step is returned for continuation.
+ *
+ * Layouts (row-major, all fp64 here):
+ *   x, delta, z, y : (B, T, D)      B, C : (B, T, N)      A : (D, N)
+ *   D, delta_bias  : (D)            h0, last_state : (B, D, N)
+ * Optional pointers may be NULL: delta_bias (no bias), D (no skip), z (no
+ * gate), h0 (zero state), last_state (not written).  h0 and last_state may be
+ * the same array: each chain reads its h0 before it writes its last_state.
+ *
+ * Chains (b, d) are independent; [chain_begin, chain_end) selects a range of
+ * chain index c = b * D + d so a caller may run disjoint ranges on several
+ * threads.  Nothing is shared between chains.
+ *
+ * The three entry points used by the tests:
+ *   oracle_selective_scan  -- the general scan (any N >= 1)
+ *   oracle_state_update    -- one decode step: the scan with T = 1, state in/out
+ *   oracle_sm1_scan        -- the d_state = 1 special case (same definition)
+ */
+#include <math.h>
+#include <stddef.h>
+
+/* softplus(v) = log(1 + exp(v)), evaluated without overflow:
+ * for v > 0, log(1 + e^v) = v + log(1 + e^-v). */
+static double softplus(double v)
+{
+    if (v > 0.0)
+        return v + log1p(exp(-v));
+    return log1p(exp(v));
+}
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)). */
+static double silu(double v)
+{
+    return v / (1.0 + exp(-v));
+}
+
+void oracle_selective_scan(const double *x, const double *delta, const double *delta_bias,
+                           int delta_softplus, const double *A, const double *Bm,
+                           const double *Cm, const double *Dv, const double *z,
+                           const double *h0, double *y, double *last_state,
+                           long nbatch, long seqlen, long dim, long dstate,
+                           long chain_begin, long chain_end)
+{
+    if (dstate < 1)
+        return;
+    double h[dstate];
+    for (long c = chain_begin; c < chain_end && c < nbatch * dim; ++c) {
+        const long b = c / dim;
+        const long d = c % dim;
+
+        for (long n = 0; n < dstate; ++n)
+            h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
+
+        for (long t = 0; t < seqlen; ++t) {
+            const long bt = b * seqlen + t;     /* row of the (B, T, .) tensors */
+            const double xv = x[bt * dim + d];
+
+            double v = delta[bt * dim + d];
+            if (delta_bias)
+                v += delta_bias[d];
+            const double dt = delta_softplus ? softplus(v) : v;
+
+            /* h[n] <- exp(dt * A[d,n]) * h[n] + dt * B[b,t,n] * x[b,t,d] */
+            for (long n = 0; n < dstate; ++n) {
+                const double decay = exp(dt * A[d * dstate + n]);
+                h[n] = decay * h[n] + dt * Bm[bt * dstate + n] * xv;
+            }
+
+            /* y = sum_n C[b,t,n] h[n]  (+ D[d] x)  (* SiLU(z)) */
+            double out = 0.0;
+            for (long n = 0; n < dstate; ++n)
+                out += Cm[bt * dstate + n] * h[n];
+            if (Dv)
+                out += Dv[d] * xv;
+            if (z)
+                out *= silu(z[bt * dim + d]);
+            y[bt * dim + d] = out;
+        }
+
+        if (last_state)
+            for (long n = 0; n < dstate; ++n)
+                last_state[(b * dim + d) * dstate + n] = h[n];
+    }
+}
+
+/* One recurrent decode step: the scan above with T = 1, the state read from
+ * and written back to `state` (B, D, N).  x, delta, z, y are (B, D); B, C are
+ * (B, N). */
+void oracle_state_update(double *state, const double *x, const double *delta,
+                         const double *delta_bias, int delta_softplus, const double *A,
+                         const double *Bm, const double *Cm, const double *Dv, const double *z,
+                         double *y, long nbatch, long dim, long dstate,
+                         long chain_begin, long chain_end)
+{
+    oracle_selective_scan(x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dv, z,
+                          state, y, state, nbatch, 1, dim, dstate, chain_begin, chain_end);
+}
+
+/* SM1: the d_state = 1 case.  A is (D); B, C are (B, T); h0, last_state are
+ * (B, D) -- the general layouts with N = 1. */
+void oracle_sm1_scan(const double *x, const double *delta, const double *delta_bias,
+                     int delta_softplus, const double *A, const double *Bm, const double *Cm,
+                     const double *Dv, const double *z, const double *h0, double *y,
+                     double *last_state, long nbatch, long seqlen, long dim,
+                     long chain_begin, long chain_end)
+{
+    oracle_selective_scan(x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dv, z, h0, y,
+                          last_state, nbatch, seqlen, dim, 1, chain_begin, chain_end);
+}
