@@ -1,0 +1,139 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ *               (libssmscan.so).
+ *
+ * What the library computes (the Mamba-1 selective scan; definitions from
+ * "Mamba State Space Models complete guide", youngju.dev, sections 2 and 5,
+ * and the "Windows SM1 (Scalar Mamba1)" page for the d_state = 1 case):
+ *
+ *   for every batch b, channel d (independently) and step t = 0 .. T-1:
+ *     v        = delta[b,t,d] + delta_bias[d]            (bias optional)
+ *     Delta    = softplus(v) if delta_softplus else v    (section 5, selection)
+ *     h[n]     = exp(Delta * A[d,n]) * h[n]              (section 2, ZOH Abar)
+ *              + Delta * B[b,t,n] * x[b,t,d]             (section 5, Delta*B*x)
+ *     out      = sum_n C[b,t,n] * h[n] + D[d] * x[b,t,d] (section 2 readout, D skip)
+ *     y[b,t,d] = out * SiLU(z[b,t,d])                    (section 5 block gate; optional)
+ *   with h starting at h0[b,d,:] (or 0) and last_state[b,d,:] = h after step T-1
+ *   (h0 when T = 0).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major, contiguous:
+ *       x, delta, z, y : (batch, seqlen, d_inner)      -- io dtype
+ *       B, C           : (batch, seqlen, d_state)      -- io dtype, shared by all d
+ *       A              : (d_inner, d_state)            -- fp32
+ *       D, delta_bias  : (d_inner)                     -- fp32
+ *       h0, last_state, state : (batch, d_inner, d_state) -- fp32
+ *     io dtype is SSM_F32 (float) or SSM_BF16 (bfloat16, stored as 16-bit
+ *     words).  Internal arithmetic is fp32; y is rounded to the io dtype with
+ *     round-to-nearest-even.
+ *   - Ownership: every buffer is owned by the caller; the library never
+ *     allocates or frees device memory, and keeps no pointer after a call
+ *     returns.  The optional workspace is caller-provided scratch of at least
+ *     the size the matching *_workspace_bytes() reports (NULL is allowed when
+ *     that size is 0); its contents need not be initialised and are garbage
+ *     after the call.
+ *   - Aliasing: no output may overlap any input (y, last_state vs x, delta,
+ *     z, B, C, h0 ...), except `state` of ssm_state_update, which is updated
+ *     in place by design.
+ *   - Streams: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns without waiting.  The caller synchronises.
+ *   - Errors: arguments are validated before anything is enqueued; on a
+ *     negative status nothing was launched and no output was touched.
+ *     SSM_ERR_HIP means a HIP launch error was reported (nothing more is
+ *     enqueued by that call).  A fault inside a kernel surfaces at the
+ *     caller's next synchronisation, as for any HIP kernel.
+ *   - Edge cases: batch == 0 or d_inner == 0 is a no-op returning SSM_OK.
+ *     seqlen == 0 writes last_state := h0 (or zeros) and leaves y untouched.
+ *   - Alignment: every pointer must be aligned to its element size (4 bytes
+ *     for fp32 tensors, 2 bytes for bf16 tensors), else SSM_ERR_ALIGN.
+ *   - Thread safety: the entry points keep no mutable global state and may be
+ *     called concurrently on different streams.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+#define SSM_MAX_D_STATE 16
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = -1,      /* a required pointer is NULL                      */
+    SSM_ERR_SHAPE = -2,     /* negative size, d_state outside [1, 16], overflow */
+    SSM_ERR_DTYPE = -3,     /* io_dtype is not SSM_F32 / SSM_BF16              */
+    SSM_ERR_ALIGN = -4,     /* a pointer is not aligned to its element size    */
+    SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required         */
+    SSM_ERR_HIP = -6,       /* the HIP runtime reported a launch error          */
+    SSM_ERR_ALIAS = -7      /* an output overlaps an input                      */
+} ssm_status_t;
+
+/*
+ * ssm_scan_fwd -- the forward selective scan over a whole sequence.
+ * Passage: youngju.dev guide, section 5 ("complete Mamba implementation",
+ * selective_scan; MambaBlock.forward for the gate), section 2 (ZOH and the
+ * discrete recurrence).
+ *   x, delta, B, C, A, y  required.
+ *   delta_bias, D, z, h0  optional (NULL: no bias / no skip / no gate / h0 = 0).
+ *   last_state            optional output (NULL: not written).
+ *   d_state in [1, 16].
+ */
+int ssm_scan_fwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int64_t d_state, int io_dtype, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ssm_scan_fwd needs for this shape (0 = none). Returns
+ * (size_t)-1 for invalid arguments. */
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                int io_dtype);
+
+/*
+ * sm1_scan_fwd -- the d_state = 1 scan ("Windows SM1 (Scalar Mamba1)" page,
+ * detailed sections: the scalar-state recurrence whose closed form is a
+ * cumulative product and a cumulative sum).  Same definition as ssm_scan_fwd
+ * with d_state = 1; the shapes drop the state axis:
+ *   A: (d_inner)   B, C: (batch, seqlen)   h0, last_state: (batch, d_inner).
+ * The kernel splits time into chunks scanned in parallel and combines them
+ * with the associative (decay, offset) operator, so it needs a workspace.
+ */
+int sm1_scan_fwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int io_dtype, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+size_t sm1_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int io_dtype);
+
+/*
+ * ssm_state_update -- one recurrent decode step (the recurrence with T = 1;
+ * the constant-size state replaces any cache: "Windows SM1" page, detailed
+ * sections, and the youngju.dev guide, section 2 duality note).
+ *   state : (batch, d_inner, d_state) fp32, read and overwritten in place.
+ *   x, delta, z, y : (batch, d_inner)   B, C : (batch, d_state).
+ *   delta_bias, D, z optional.  d_state in [1, 16].
+ */
+int ssm_state_update(float *state, const void *x, const void *delta, const float *delta_bias,
+                     int delta_softplus, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, void *y, int64_t batch, int64_t d_inner,
+                     int64_t d_state, int io_dtype, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *ssm_status_string(int status);
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,90 @@
+"""ctypes loader of libssmscan.so (the gfx950 kernels behind include/ssm_scan.h).
+
+The library is built in-tree by selective_scan_ssm_amd/build.py.  Loading it
+after torch makes it bind to the HIP runtime torch already mapped, so torch's
+device pointers and stream handles are valid inside the library; `load()`
+checks that exactly one HIP runtime is mapped when torch is imported.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import sys
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",
+           "ssm_state_update", "ssm_status_string", "ssm_abi_version")
+ABI_VERSION = 1
+
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def _bind(lib):
+    lib.ssm_scan_fwd.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.ssm_scan_fwd.restype = _int
+    lib.ssm_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _int]
+    lib.ssm_scan_workspace_bytes.restype = _sz
+    lib.sm1_scan_fwd.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.sm1_scan_fwd.restype = _int
+    lib.sm1_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _int]
+    lib.sm1_scan_workspace_bytes.restype = _sz
+    lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _i64, _i64, _i64, _int, _vp]
+    lib.ssm_state_update.restype = _int
+    lib.ssm_status_string.argtypes = [_int]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_abi_version.restype = _int
+    return lib
+
+
+def hip_runtimes_mapped() -> set:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    out = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and os.path.basename(parts[-1]).startswith("libamdhip64"):
+                out.add(parts[-1])
+    return out
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once).  Raises LibraryMissing if it was not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise LibraryMissing(
+                f"{path} is not built; run `python -m selective_scan_ssm_amd.build` "
+                "(or __graft_entry__.build()) first")
+        lib = _bind(ctypes.CDLL(path))
+        if lib.ssm_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libssmscan ABI {lib.ssm_abi_version()} != {ABI_VERSION}")
+        if "torch" in sys.modules:
+            rts = hip_runtimes_mapped()
+            if len(rts) > 1:
+                raise RuntimeError(f"more than one HIP runtime mapped: {sorted(rts)}")
+        _lib = lib
+        return lib
+
+
+def status_string(code: int) -> str:
+    return load().ssm_status_string(int(code)).decode()

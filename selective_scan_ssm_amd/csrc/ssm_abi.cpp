@@ -1,0 +1,209 @@
+// C ABI of libssmscan.so (declared in include/ssm_scan.h): argument
+// validation, then one launch on the caller's stream.  Validation never
+// touches the HIP runtime, so every error path returns before anything is
+// enqueued.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <limits>
+
+#include "ssm_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxGridY = 65535;   // batch rides on gridDim.y in the scan kernels
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// byte range [p, p + bytes) of one tensor, for overlap checks
+struct Range {
+    uintptr_t lo, hi;
+};
+Range range(const void *p, int64_t elems, size_t esize) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + static_cast<uintptr_t>(elems) * esize};
+}
+bool overlap(Range a, Range b) {
+    if (a.lo == 0 || b.lo == 0 || a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// a*b*c without int64 overflow; -1 on overflow
+int64_t mul3(int64_t a, int64_t b, int64_t c) {
+    const int64_t big = std::numeric_limits<int64_t>::max() / 16;
+    if (a < 0 || b < 0 || c < 0) return -1;
+    if (a && b > big / a) return -1;
+    const int64_t ab = a * b;
+    if (ab && c > big / ab) return -1;
+    return ab * c;
+}
+
+int check_dtype(int io) { return (io == SSM_F32 || io == SSM_BF16) ? SSM_OK : SSM_ERR_DTYPE; }
+size_t io_size(int io) { return io == SSM_BF16 ? 2 : 4; }
+
+// Validation shared by the two whole-sequence scans.
+int validate_scan(const void *x, const void *delta, const float *delta_bias, const float *A,
+                  const void *B, const void *C, const float *D, const void *z, const float *h0,
+                  const void *y, const float *last_state, int64_t batch, int64_t seqlen,
+                  int64_t dim, int64_t dstate, int io) {
+    if (int r = check_dtype(io)) return r;
+    if (batch < 0 || seqlen < 0 || dim < 0) return SSM_ERR_SHAPE;
+    if (dstate < 1 || dstate > SSM_MAX_D_STATE) return SSM_ERR_SHAPE;
+    if (batch > kMaxGridY) return SSM_ERR_SHAPE;
+    const int64_t n_btd = mul3(batch, seqlen, dim);
+    const int64_t n_btn = mul3(batch, seqlen, dstate);
+    const int64_t n_bdn = mul3(batch, dim, dstate);
+    if (n_btd < 0 || n_btn < 0 || n_bdn < 0 || mul3(dim, dstate, 1) < 0) return SSM_ERR_SHAPE;
+    if (batch == 0 || dim == 0) return SSM_OK;   // nothing to read or write
+    if (!A) return SSM_ERR_NULL;
+    if (seqlen > 0 && (!x || !delta || !B || !C || !y)) return SSM_ERR_NULL;
+    const size_t es = io_size(io);
+    const void *io_ptrs[] = {x, delta, B, C, z, y};
+    for (const void *p : io_ptrs)
+        if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+    const void *f_ptrs[] = {delta_bias, A, D, h0, last_state};
+    for (const void *p : f_ptrs)
+        if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+    const Range outs[] = {range(y, seqlen > 0 ? n_btd : 0, es), range(last_state, n_bdn, 4)};
+    const Range ins[] = {range(x, n_btd, es),        range(delta, n_btd, es),
+                         range(z, n_btd, es),        range(B, n_btn, es),
+                         range(C, n_btn, es),        range(A, dim * dstate, 4),
+                         range(D, dim, 4),           range(delta_bias, dim, 4),
+                         range(h0, n_bdn, 4)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    return SSM_OK;
+}
+
+ssm::ScanArgs make_args(const void *x, const void *delta, const float *delta_bias, int softplus,
+                        const float *A, const void *B, const void *C, const float *D,
+                        const void *z, const float *h0, void *y, float *last_state,
+                        int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io,
+                        void *ws, size_t ws_bytes) {
+    ssm::ScanArgs a;
+    a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.delta_bias = delta_bias; a.A = A; a.D = D; a.h0 = h0;
+    a.y = y; a.last_state = last_state;
+    a.batch = batch; a.seqlen = seqlen; a.dim = dim; a.dstate = dstate;
+    a.softplus = softplus ? 1 : 0;
+    a.bf16 = io == SSM_BF16 ? 1 : 0;
+    a.workspace = ws; a.workspace_bytes = ws_bytes;
+    return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char *ssm_status_string(int status) {
+    switch (status) {
+    case SSM_OK: return "SSM_OK: success";
+    case SSM_ERR_NULL: return "SSM_ERR_NULL: a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "SSM_ERR_SHAPE: invalid sizes (negative, d_state outside [1,16], batch > 65535 or overflow)";
+    case SSM_ERR_DTYPE: return "SSM_ERR_DTYPE: io dtype must be SSM_F32 or SSM_BF16";
+    case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: a pointer is not aligned to its element size";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported a launch error";
+    case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
+    default: return "unknown ssm status";
+    }
+}
+
+size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                int io_dtype) {
+    if (check_dtype(io_dtype) || batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 ||
+        d_state > SSM_MAX_D_STATE)
+        return static_cast<size_t>(-1);
+    ssm::ScanArgs a = make_args(nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr, batch, seqlen, d_inner,
+                                d_state, io_dtype, nullptr, 0);
+    return ssm::scan_fwd_workspace(a);
+}
+
+int ssm_scan_fwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int64_t d_state, int io_dtype, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, seqlen,
+                          d_inner, d_state, io_dtype);
+    if (r) return r;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, seqlen, d_inner, d_state, io_dtype, workspace,
+                                workspace_bytes);
+    const size_t need = ssm::scan_fwd_workspace(a);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t sm1_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int io_dtype) {
+    if (check_dtype(io_dtype) || batch < 0 || seqlen < 0 || d_inner < 0)
+        return static_cast<size_t>(-1);
+    return ssm::sm1_workspace(batch, seqlen, d_inner, io_dtype == SSM_BF16);
+}
+
+int sm1_scan_fwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                 int64_t d_inner, int io_dtype, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, seqlen,
+                          d_inner, 1, io_dtype);
+    if (r) return r;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    const size_t need = ssm::sm1_workspace(batch, seqlen, d_inner, io_dtype == SSM_BF16);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, seqlen, d_inner, 1, io_dtype, workspace,
+                                workspace_bytes);
+    return hip_status(ssm::launch_sm1_scan(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_state_update(float *state, const void *x, const void *delta, const float *delta_bias,
+                     int delta_softplus, const float *A, const void *B, const void *C,
+                     const float *D, const void *z, void *y, int64_t batch, int64_t d_inner,
+                     int64_t d_state, int io_dtype, void *stream) {
+    if (int r = check_dtype(io_dtype)) return r;
+    if (batch < 0 || d_inner < 0 || d_state < 1 || d_state > SSM_MAX_D_STATE) return SSM_ERR_SHAPE;
+    const int64_t n_bd = mul3(batch, d_inner, 1), n_bdn = mul3(batch, d_inner, d_state);
+    if (n_bd < 0 || n_bdn < 0 || mul3(batch, d_inner, 4) < 0 || mul3(batch, d_inner, 4) > INT32_MAX * 64LL)
+        return SSM_ERR_SHAPE;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    if (!state || !x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+    const size_t es = io_size(io_dtype);
+    const void *io_ptrs[] = {x, delta, B, C, z, y};
+    for (const void *p : io_ptrs)
+        if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+    const void *f_ptrs[] = {state, delta_bias, A, D};
+    for (const void *p : f_ptrs)
+        if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+    const int64_t n_bn = batch * d_state;
+    const Range outs[] = {range(y, n_bd, es), range(state, n_bdn, 4)};
+    const Range ins[] = {range(x, n_bd, es),       range(delta, n_bd, es), range(z, n_bd, es),
+                         range(B, n_bn, es),       range(C, n_bn, es),     range(A, d_inner * d_state, 4),
+                         range(D, d_inner, 4),     range(delta_bias, d_inner, 4)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    ssm::StepArgs a;
+    a.state = state; a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.delta_bias = delta_bias; a.A = A; a.D = D; a.y = y;
+    a.batch = batch; a.dim = d_inner; a.dstate = d_state;
+    a.softplus = delta_softplus ? 1 : 0;
+    a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    return hip_status(ssm::launch_state_update(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

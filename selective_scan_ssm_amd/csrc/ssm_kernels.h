@@ -1,0 +1,44 @@
+// Internal interface between the C ABI (ssm_abi.cpp) and the kernel
+// launchers (*.hip).  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct ScanArgs {
+    const void *x, *delta, *z, *B, *C;   // io dtype
+    const float *delta_bias, *A, *D, *h0;
+    void *y;
+    float *last_state;
+    int64_t batch, seqlen, dim, dstate;
+    int softplus;
+    int bf16;                            // io dtype: 1 = bf16, 0 = fp32
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+struct StepArgs {
+    float *state;
+    const void *x, *delta, *z, *B, *C;
+    const float *delta_bias, *A, *D;
+    void *y;
+    int64_t batch, dim, dstate;
+    int softplus;
+    int bf16;
+};
+
+// General forward scan, 1 <= dstate <= 16.
+size_t scan_fwd_workspace(const ScanArgs &a);
+hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t s);
+
+// d_state = 1 time-chunked scan.
+size_t sm1_workspace(int64_t batch, int64_t seqlen, int64_t dim, int bf16);
+hipError_t launch_sm1_scan(const ScanArgs &a, hipStream_t s);
+
+// One decode step.
+hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
+
+}  // namespace ssm

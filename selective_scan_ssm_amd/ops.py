@@ -1,0 +1,152 @@
+"""Thin torch-facing wrappers of the C ABI (include/ssm_scan.h).
+
+They only marshal arguments: check devices, dtypes, shapes and contiguity,
+allocate outputs (and the workspace) with torch, pass raw device pointers and
+torch's current HIP stream to libssmscan.so, and turn a nonzero status into
+RuntimeError.  Every step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_IO = {torch.float32: _lib.SSM_F32, torch.bfloat16: _lib.SSM_BF16}
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {_lib.status_string(rc)}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
+             return_last_state=False, out=None, last_state_out=None, workspace=None):
+    """Selective scan.  x, delta, z: (batch, seqlen, d_inner) fp32 or bf16;
+    B, C: (batch, seqlen, d_state) same dtype; A: (d_inner, d_state) fp32;
+    D, delta_bias: (d_inner,) fp32; h0: (batch, d_inner, d_state) fp32.
+    Returns y (same dtype as x) or (y, last_state fp32)."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, Dd = x.shape
+    N = A.shape[-1]
+    _dev(x, "x", io)
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(B, "B", io, (Bt, T, N))
+    _dev(C, "C", io, (Bt, T, N))
+    _dev(A, "A", torch.float32, (Dd, N))
+    _dev(D, "D", torch.float32, (Dd,))
+    _dev(delta_bias, "delta_bias", torch.float32, (Dd,))
+    _dev(h0, "h0", torch.float32, (Bt, Dd, N))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    last = None
+    if return_last_state:
+        last = last_state_out if last_state_out is not None else torch.empty(
+            (Bt, Dd, N), dtype=torch.float32, device=x.device)
+        _dev(last, "last_state_out", torch.float32, (Bt, Dd, N))
+    need = lib.ssm_scan_workspace_bytes(Bt, T, Dd, N, _IO[io])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("ssm_scan_workspace_bytes: invalid arguments")
+    ws = None
+    if need:
+        ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
+            need, dtype=torch.uint8, device=x.device)
+    rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
+                          Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(x.device))
+    _check(rc, "ssm_scan_fwd")
+    return (y, last) if return_last_state else y
+
+
+def sm1_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
+                 return_last_state=False, out=None, last_state_out=None, workspace=None):
+    """d_state = 1 scan.  x, delta, z: (batch, seqlen, d_inner); B, C: (batch, seqlen);
+    A, D, delta_bias: (d_inner,); h0, last_state: (batch, d_inner)."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, Dd = x.shape
+    _dev(x, "x", io)
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(B, "B", io, (Bt, T))
+    _dev(C, "C", io, (Bt, T))
+    _dev(A, "A", torch.float32, (Dd,))
+    _dev(D, "D", torch.float32, (Dd,))
+    _dev(delta_bias, "delta_bias", torch.float32, (Dd,))
+    _dev(h0, "h0", torch.float32, (Bt, Dd))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    last = None
+    if return_last_state:
+        last = last_state_out if last_state_out is not None else torch.empty(
+            (Bt, Dd), dtype=torch.float32, device=x.device)
+        _dev(last, "last_state_out", torch.float32, (Bt, Dd))
+    need = lib.sm1_scan_workspace_bytes(Bt, T, Dd, _IO[io])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("sm1_scan_workspace_bytes: invalid arguments")
+    ws = None
+    if need:
+        ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
+            need, dtype=torch.uint8, device=x.device)
+    rc = lib.sm1_scan_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
+                          Bt, T, Dd, _IO[io], _ptr(ws), need, _stream(x.device))
+    _check(rc, "sm1_scan_fwd")
+    return (y, last) if return_last_state else y
+
+
+def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 out=None):
+    """One decode step; `state` (batch, d_inner, d_state) fp32 is updated in place.
+    x, delta, z: (batch, d_inner); B, C: (batch, d_state).  Returns y."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, Dd = x.shape
+    N = A.shape[-1]
+    _dev(state, "state", torch.float32, (Bt, Dd, N))
+    _dev(x, "x", io)
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(B, "B", io, (Bt, N))
+    _dev(C, "C", io, (Bt, N))
+    _dev(A, "A", torch.float32, (Dd, N))
+    _dev(D, "D", torch.float32, (Dd,))
+    _dev(delta_bias, "delta_bias", torch.float32, (Dd,))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    rc = lib.ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(delta_bias),
+                              int(bool(delta_softplus)), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(y), Bt, Dd, N, _IO[io], _stream(x.device))
+    _check(rc, "ssm_state_update")
+    return y

@@ -1,0 +1,108 @@
+"""Helpers of the GPU parity tests: move seeded inputs to the device, run the
+HIP path through the C ABI wrappers, run the fp64 oracle on the same values,
+and measure the error the way the tolerances are stated."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+import oracle
+from selective_scan_ssm_amd import inputs as gen
+
+IO_KEYS = ("x", "delta", "z", "B", "C")
+F32_KEYS = ("A", "D", "delta_bias", "h0")
+TOL = {gen.F32: 1e-5, gen.BF16: 2e-2}
+ORACLE_THREADS = min(16, os.cpu_count() or 1)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_torch(arr, io, device="cuda"):
+    import torch
+    if arr is None:
+        return None
+    if io == gen.BF16 and arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def from_torch(t):
+    import torch
+    if t is None:
+        return None
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return gen.f32_from_bf16(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def device_inputs(inp, device="cuda"):
+    io = inp["io"]
+    out = {k: to_torch(inp[k], io, device) for k in IO_KEYS}
+    out.update({k: to_torch(inp[k], gen.F32, device) for k in F32_KEYS})
+    return out
+
+
+def decoded(inp):
+    """fp64 copies of the inputs, exactly as the GPU reads them."""
+    io = inp["io"]
+    d = {k: (None if inp[k] is None else gen.to_f64(inp[k], io)) for k in IO_KEYS}
+    d.update({k: (None if inp[k] is None else np.asarray(inp[k], np.float64)) for k in F32_KEYS})
+    return d
+
+
+def run_scan(inp, softplus=True, sm1=False, last=True, device="cuda"):
+    import torch
+    from selective_scan_ssm_amd import ops
+    t = device_inputs(inp, device)
+    if sm1:
+        r = ops.sm1_scan_fwd(t["x"], t["delta"], t["A"][:, 0].contiguous(), t["B"][..., 0].contiguous(),
+                             t["C"][..., 0].contiguous(), D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                             delta_softplus=softplus,
+                             h0=None if t["h0"] is None else t["h0"][..., 0].contiguous(),
+                             return_last_state=last)
+    else:
+        r = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                         delta_bias=t["delta_bias"], delta_softplus=softplus, h0=t["h0"],
+                         return_last_state=last)
+    torch.cuda.synchronize()
+    if last:
+        y, ls = r
+        ls = from_torch(ls)
+        if sm1:
+            ls = ls[..., None]
+        return from_torch(y), ls
+    return from_torch(r), None
+
+
+def run_oracle(inp, softplus=True, d_index=None):
+    """Oracle on all chains, or only on channels d_index (all batches)."""
+    d = decoded(inp)
+    if d_index is not None:
+        di = np.asarray(d_index)
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :, di])
+        d = dict(d, x=sl(d["x"]), delta=sl(d["delta"]), z=sl(d["z"]),
+                 A=d["A"][di], D=None if d["D"] is None else d["D"][di],
+                 delta_bias=None if d["delta_bias"] is None else d["delta_bias"][di],
+                 h0=None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, di]))
+    return oracle.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                                 delta_bias=d["delta_bias"], delta_softplus=softplus, h0=d["h0"],
+                                 threads=ORACLE_THREADS)
+
+
+def err(g, o):
+    """max_i |g_i - o_i| / max(|o_i|, rms(o)): relative error with an rms floor
+    (outputs where C.h + D.x cancels to ~0 carry only absolute rounding)."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    if o.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    rms = float(np.sqrt(np.mean(o * o)))
+    den = np.maximum(np.abs(o), rms if rms > 0 else 1e-300)
+    return float(np.max(np.abs(g - o) / den))

@@ -1,0 +1,157 @@
+"""C ABI contract, checked on the CPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments before touching the HIP
+runtime (so these calls never launch anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_scan_ssm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16 = 0, 1
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from selective_scan_ssm_amd import build
+        build.build()
+    return _lib.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    assert set(fns) == set(_lib.EXPORTS), fns
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.ssm_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EALIAS):
+        s = lib.ssm_status_string(code).decode()
+        assert s.startswith("SSM_"), s
+    assert "unknown" in lib.ssm_status_string(12345).decode()
+
+
+class FakeDev:
+    """Distinct, well-aligned fake device addresses: never dereferenced
+    because every call below fails validation (or is a documented no-op)."""
+
+    def __init__(self):
+        self.base = 0x7f0000000000
+        self.off = 0
+
+    def __call__(self, nbytes=64 * MB):
+        p = self.base + self.off
+        self.off += (nbytes + 4095) & ~4095
+        return p
+
+
+def scan_args(batch=2, seqlen=16, dim=8, dstate=4, io=F32, **over):
+    f = FakeDev()
+    a = dict(x=f(), delta=f(), delta_bias=f(), softplus=1, A=f(), B=f(), C=f(), D=f(), z=f(),
+             h0=f(), y=f(), last=f(), batch=batch, seqlen=seqlen, dim=dim, dstate=dstate, io=io,
+             ws=f(), ws_bytes=64 * MB, stream=None)
+    a.update(over)
+    return a
+
+
+def call_scan(lib, a):
+    return lib.ssm_scan_fwd(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"],
+                            a["C"], a["D"], a["z"], a["h0"], a["y"], a["last"], a["batch"],
+                            a["seqlen"], a["dim"], a["dstate"], a["io"], a["ws"], a["ws_bytes"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), ENULL), (dict(delta=None), ENULL), (dict(A=None), ENULL),
+    (dict(B=None), ENULL), (dict(C=None), ENULL), (dict(y=None), ENULL),
+    (dict(dstate=0), ESHAPE), (dict(dstate=17), ESHAPE), (dict(batch=-1), ESHAPE),
+    (dict(seqlen=-3), ESHAPE), (dict(dim=-1), ESHAPE), (dict(batch=70000), ESHAPE),
+    (dict(batch=1 << 40, seqlen=1 << 40), ESHAPE),
+    (dict(io=2), EDTYPE), (dict(io=-1), EDTYPE),
+    (dict(x=0x7f0000000002), EALIGN), (dict(io=BF16, x=0x7f0000000001), EALIGN),
+    (dict(A=0x7f0000000002), EALIGN), (dict(h0=0x7f000000000e), EALIGN),
+    (dict(io=BF16, ws=None, ws_bytes=0), EWS), (dict(io=BF16, ws_bytes=16), EWS),
+])
+def test_scan_validation(lib, over, code):
+    assert call_scan(lib, scan_args(**over)) == code
+
+
+def test_scan_alias_detection(lib):
+    a = scan_args()
+    a["y"] = a["x"] + 64           # inside x
+    assert call_scan(lib, a) == EALIAS
+    a = scan_args()
+    a["last"] = a["h0"]            # last_state may not alias h0
+    assert call_scan(lib, a) == EALIAS
+    a = scan_args()
+    a["y"] = a["last"]
+    assert call_scan(lib, a) == EALIAS
+
+
+def test_scan_empty_is_noop(lib):
+    # batch == 0 or d_inner == 0: nothing to read or write; returns before any launch
+    assert call_scan(lib, scan_args(batch=0)) == OK
+    assert call_scan(lib, scan_args(dim=0)) == OK
+    assert call_scan(lib, scan_args(batch=0, x=None, delta=None, y=None)) == OK
+
+
+def test_workspace_sizes(lib):
+    assert lib.ssm_scan_workspace_bytes(2, 16, 8, 4, F32) == 0
+    assert lib.ssm_scan_workspace_bytes(2, 16, 8, 4, BF16) >= 2 * 2 * 16 * 4 * 4
+    assert lib.ssm_scan_workspace_bytes(2, 16, 8, 0, F32) == (1 << 64) - 1
+    assert lib.ssm_scan_workspace_bytes(2, 16, 8, 4, 7) == (1 << 64) - 1
+    assert lib.sm1_scan_workspace_bytes(2, 16, 8, 9) == (1 << 64) - 1
+    assert lib.sm1_scan_workspace_bytes(8, 4096, 1536, F32) < (1 << 40)
+
+
+def call_sm1(lib, a):
+    return lib.sm1_scan_fwd(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"],
+                            a["C"], a["D"], a["z"], a["h0"], a["y"], a["last"], a["batch"],
+                            a["seqlen"], a["dim"], a["io"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), ENULL), (dict(io=5), EDTYPE), (dict(batch=-2), ESHAPE),
+    (dict(y=0x7f0000000003), EALIGN), (dict(batch=0), OK),
+])
+def test_sm1_validation(lib, over, code):
+    assert call_sm1(lib, scan_args(dstate=1, **over)) == code
+
+
+def call_step(lib, a):
+    return lib.ssm_state_update(a["h0"], a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"],
+                                a["B"], a["C"], a["D"], a["z"], a["y"], a["batch"], a["dim"],
+                                a["dstate"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(h0=None), ENULL), (dict(x=None), ENULL), (dict(y=None), ENULL),
+    (dict(dstate=17), ESHAPE), (dict(dstate=0), ESHAPE), (dict(io=3), EDTYPE),
+    (dict(h0=0x7f0000000002), EALIGN), (dict(batch=0), OK), (dict(dim=0), OK),
+])
+def test_state_update_validation(lib, over, code):
+    assert call_step(lib, scan_args(**over)) == code
+
+
+def test_state_update_alias(lib):
+    a = scan_args()
+    a["y"] = a["x"]
+    assert call_step(lib, a) == EALIAS

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Tolerance (max relative error with an rms floor, see
+gpu_util.err): 1e-5 for fp32 io, 2e-2 for bf16 io with fp32 state."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import gpu_util as G
+from selective_scan_ssm_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_scan_ssm_amd import _lib
+    _lib.load()
+    assert len(_lib.hip_runtimes_mapped()) == 1
+
+
+def check(inp, softplus=True, sm1=False, d_index=None, tol=None, tag=""):
+    tol = tol or G.TOL[inp["io"]]
+    G.say(f"[parity] {tag} B={inp['batch']} T={inp['seqlen']} D={inp['d_inner']} N={inp['d_state']} "
+          f"io={inp['io']} sm1={sm1} sampled={d_index is not None}")
+    y, last = G.run_scan(inp, softplus=softplus, sm1=sm1)
+    yo, lo = G.run_oracle(inp, softplus=softplus, d_index=d_index)
+    if d_index is not None:
+        assert np.all(np.isfinite(y)) and np.all(np.isfinite(last))
+        y, last = y[:, :, d_index], last[:, d_index]
+    ey, el = G.err(y, yo), G.err(last, lo)
+    G.say(f"[parity] {tag} err_y={ey:.3e} err_last={el:.3e} tol={tol:g}")
+    assert ey <= tol and el <= tol, (ey, el)
+    return ey, el
+
+
+# ------------------------------------------------------------ the five workloads
+def test_workload0_tiny_fp32():
+    check(gen.workload_inputs(0), tag="w0")
+
+
+def test_workload1_sm1_fp32_full():
+    check(gen.workload_inputs(1), sm1=True, tag="w1-sm1")
+
+
+def test_workload2_mamba130m_bf16_sampled():
+    d_index = np.r_[0:32, 700:716, 1520:1536]
+    check(gen.workload_inputs(2), d_index=d_index, tag="w2")
+
+
+def test_workload3_mamba2p8b_bf16_sampled():
+    d_index = np.r_[0:16, 2500:2516, 5104:5120]
+    check(gen.workload_inputs(3), d_index=d_index, tag="w3")
+
+
+def test_workload4_decode_bf16_two_layers():
+    from selective_scan_ssm_amd import ops
+    for layer in range(2):
+        inp = gen.workload_inputs(4, layer=layer)
+        G.say(f"[parity] w4 decode layer {layer}")
+        t = G.device_inputs(inp)
+        state = t["h0"].clone()
+        y = ops.state_update(state, t["x"][:, 0].contiguous(), t["delta"][:, 0].contiguous(), t["A"],
+                             t["B"][:, 0].contiguous(), t["C"][:, 0].contiguous(), D=t["D"],
+                             z=t["z"][:, 0].contiguous(), delta_bias=t["delta_bias"])
+        torch.cuda.synchronize()
+        yo, so = G.run_oracle(inp)
+        ey, es = G.err(G.from_torch(y), yo[:, 0]), G.err(G.from_torch(state), so)
+        G.say(f"[parity] w4 layer {layer} err_y={ey:.3e} err_state={es:.3e}")
+        assert ey <= 2e-2 and es <= 2e-2
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+def test_all_state_sizes_fp32(N):
+    check(gen.make_inputs(2, 37, 70, N, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=100 + N),
+          tag=f"N{N}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 63, 130])
+def test_ragged_lengths_bf16(T):
+    check(gen.make_inputs(3, T, 129, 16, io=gen.BF16, h0_kind="normal", seed=200 + T), tag=f"T{T}")
+
+
+@pytest.mark.parametrize("flags", [
+    dict(with_z=False), dict(with_D=False), dict(with_bias=False),
+    dict(with_z=False, with_D=False, with_bias=False)])
+def test_optional_inputs(flags):
+    check(gen.make_inputs(2, 50, 96, 16, io=gen.F32, h0_kind="normal", seed=300, **flags),
+          tag=str(flags))
+
+
+def test_softplus_off():
+    inp = gen.make_inputs(2, 40, 64, 8, io=gen.F32, seed=301)
+    inp["delta"] = np.abs(inp["delta"]) * np.float32(0.05)
+    check(inp, softplus=False, tag="softplus-off")
+
+
+def test_empty_sequence_returns_h0():
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(2, 0, 70, 16, io=gen.BF16, h0_kind="normal", seed=302)
+    t = G.device_inputs(inp)
+    y, last = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           delta_bias=t["delta_bias"], h0=t["h0"], return_last_state=True)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 70)
+    assert torch.equal(last, t["h0"])
+
+
+def test_sm1_entry_matches_general_entry():
+    inp = gen.make_inputs(2, 300, 130, 1, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=303)
+    ya, la = G.run_scan(inp, sm1=True)
+    yb, lb = G.run_scan(inp, sm1=False)
+    assert G.err(ya, yb) <= 1e-5 and G.err(la, lb) <= 1e-5
+    check(inp, sm1=True, tag="sm1-small")
+
+
+def test_sm1_bf16():
+    check(gen.make_inputs(2, 500, 96, 1, io=gen.BF16, a_kind="sm1", h0_kind="normal", seed=304),
+          sm1=True, tag="sm1-bf16")
+
+
+def test_softplus_accuracy_sweep():
+    """T = 1, N = 1, A = 0, B = C = x = 1, h0 = 0: y = Delta = softplus(delta)."""
+    from selective_scan_ssm_amd import ops
+    v = np.concatenate([np.linspace(-30, 30, 4001), -np.logspace(-6, 1.5, 200), np.logspace(-6, 1.5, 200)])
+    v = v.astype(np.float32)
+    Dd = v.size
+    dev = "cuda"
+    x = torch.ones((1, 1, Dd), device=dev)
+    y = ops.scan_fwd(x, torch.from_numpy(v).view(1, 1, Dd).to(dev), torch.zeros((Dd, 1), device=dev),
+                     torch.ones((1, 1, 1), device=dev), torch.ones((1, 1, 1), device=dev))
+    torch.cuda.synchronize()
+    ref = np.logaddexp(0.0, v.astype(np.float64))
+    rel = np.abs(y.cpu().numpy().ravel().astype(np.float64) - ref) / ref
+    G.say(f"[parity] softplus max rel err {rel.max():.3e}")
+    # fp32 rounding of the exp argument costs about |v| * 6e-8 * ln2 of relative error
+    assert rel.max() < 4e-6 and rel[np.abs(v) <= 10].max() < 2e-6
+
+
+def test_gate_accuracy_sweep():
+    """y = x * SiLU(z) with C = 0, D = 1, A = 0."""
+    from selective_scan_ssm_amd import ops
+    zv = np.linspace(-80, 80, 8001).astype(np.float32)
+    Dd = zv.size
+    dev = "cuda"
+    x = torch.ones((1, 1, Dd), device=dev)
+    z = torch.from_numpy(zv).view(1, 1, Dd).to(dev)
+    y = ops.scan_fwd(x, torch.zeros_like(x), torch.zeros((Dd, 1), device=dev),
+                     torch.ones((1, 1, 1), device=dev), torch.zeros((1, 1, 1), device=dev),
+                     D=torch.ones(Dd, device=dev), z=z)
+    torch.cuda.synchronize()
+    z64 = zv.astype(np.float64)
+    ref = z64 / (1.0 + np.exp(-z64))
+    den = np.maximum(np.abs(ref), 1e-30)
+    rel = np.abs(y.cpu().numpy().ravel() - ref) / den
+    big = np.abs(ref) > 1e-30
+    G.say(f"[parity] silu max rel err {rel[big].max():.3e}")
+    assert rel[big].max() < 1e-5 and rel[big & (np.abs(z64) <= 10)].max() < 2e-6
+
+
+def test_continuation_from_last_state():
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(2, 96, 128, 16, io=gen.F32, h0_kind="normal", seed=305)
+    t = G.device_inputs(inp)
+    kw = dict(D=t["D"], delta_bias=t["delta_bias"])
+    y, last = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], z=t["z"], h0=t["h0"],
+                           return_last_state=True, **kw)
+    t1 = 41
+    sl = lambda a, s: a[:, s].contiguous()
+    ya, la = ops.scan_fwd(sl(t["x"], slice(0, t1)), sl(t["delta"], slice(0, t1)), t["A"],
+                          sl(t["B"], slice(0, t1)), sl(t["C"], slice(0, t1)), z=sl(t["z"], slice(0, t1)),
+                          h0=t["h0"], return_last_state=True, **kw)
+    yb, lb = ops.scan_fwd(sl(t["x"], slice(t1, None)), sl(t["delta"], slice(t1, None)), t["A"],
+                          sl(t["B"], slice(t1, None)), sl(t["C"], slice(t1, None)),
+                          z=sl(t["z"], slice(t1, None)), h0=la, return_last_state=True, **kw)
+    torch.cuda.synchronize()
+    assert G.err(G.from_torch(torch.cat([ya, yb], 1)), G.from_torch(y)) <= 1e-5
+    assert G.err(G.from_torch(lb), G.from_torch(last)) <= 1e-5
+
+
+def test_decode_steps_equal_scan():
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(3, 20, 100, 16, io=gen.F32, h0_kind="normal", seed=306)
+    t = G.device_inputs(inp)
+    y, last = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           delta_bias=t["delta_bias"], h0=t["h0"], return_last_state=True)
+    st = t["h0"].clone()
+    ys = []
+    for s in range(20):
+        ys.append(ops.state_update(st, t["x"][:, s].contiguous(), t["delta"][:, s].contiguous(), t["A"],
+                                   t["B"][:, s].contiguous(), t["C"][:, s].contiguous(), D=t["D"],
+                                   z=t["z"][:, s].contiguous(), delta_bias=t["delta_bias"]))
+    torch.cuda.synchronize()
+    assert G.err(G.from_torch(torch.stack(ys, 1)), G.from_torch(y)) <= 1e-5
+    assert G.err(G.from_torch(st), G.from_torch(last)) <= 1e-5
+    yo, lo = G.run_oracle(inp)
+    assert G.err(G.from_torch(torch.stack(ys, 1)), yo) <= 1e-5 and G.err(G.from_torch(st), lo) <= 1e-5
+
+
+@pytest.mark.parametrize("N", [1, 3, 16])
+def test_decode_small_shapes(N):
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(5, 1, 37, N, io=gen.BF16, a_kind="sm1", h0_kind="normal", seed=307 + N)
+    t = G.device_inputs(inp)
+    st = t["h0"].clone()
+    y = ops.state_update(st, t["x"][:, 0].contiguous(), t["delta"][:, 0].contiguous(), t["A"],
+                         t["B"][:, 0].contiguous(), t["C"][:, 0].contiguous(), D=t["D"],
+                         z=t["z"][:, 0].contiguous(), delta_bias=t["delta_bias"])
+    torch.cuda.synchronize()
+    yo, so = G.run_oracle(inp)
+    assert G.err(G.from_torch(y), yo[:, 0]) <= 2e-2 and G.err(G.from_torch(st), so) <= 1e-5
+
+
+def test_deterministic_and_guard_bands():
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(2, 77, 200, 16, io=gen.BF16, h0_kind="normal", seed=308)
+    t = G.device_inputs(inp)
+    n = 2 * 77 * 200
+    canary = torch.full((n + 2048,), 3.5, device="cuda").to(torch.bfloat16)
+    out = canary[1024:1024 + n].view(2, 77, 200)
+    lcan = torch.full((2 * 200 * 16 + 2048,), -7.0, device="cuda")
+    lout = lcan[1024:1024 + 2 * 200 * 16].view(2, 200, 16)
+    r = []
+    for _ in range(2):
+        y, last = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               delta_bias=t["delta_bias"], h0=t["h0"], return_last_state=True,
+                               out=out, last_state_out=lout)
+        torch.cuda.synchronize()
+        r.append((y.clone(), last.clone()))
+    assert torch.equal(r[0][0].view(torch.int16), r[1][0].view(torch.int16))
+    assert torch.equal(r[0][1], r[1][1])
+    assert torch.all(canary[:1024] == 3.5) and torch.all(canary[1024 + n:] == 3.5)
+    assert torch.all(lcan[:1024] == -7.0) and torch.all(lcan[1024 + 2 * 200 * 16:] == -7.0)
