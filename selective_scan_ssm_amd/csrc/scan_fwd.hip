@@ -7,8 +7,8 @@
 //     y     = (sum_n C[b,t,n] h[n] + D[d] x) * SiLU(z)
 //
 // Mapping: one lane owns one (b, d) chain and keeps all N states in VGPRs for
-// the whole sequence, so each (t, d, n) item costs one v_exp_f32 and three
-// VALU ops plus one FMA of the readout, and the per-element work (softplus,
+// the whole sequence, so each (t, d, n) item costs (bf16 io) one v_exp_f32 and
+// three VALU ops plus one FMA of the readout, and the per-element work (softplus,
 // Delta*x, D*x, SiLU, bf16 conversion) is paid once per N items.  A wave
 // covers 64 consecutive channels of one batch row, so B[b,t,:] and C[b,t,:]
 // are wave-uniform and come in through scalar loads; x, delta, z are read
@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_chain_kernel(
     const float *__restrict__ Bf, const float *__restrict__ Cf, const float *__restrict__ A_in,
     const float *__restrict__ D_in, const float *__restrict__ bias_in, const float *__restrict__ h0_in,
     T *__restrict__ y_out, float *__restrict__ last_out, int64_t seqlen, int64_t dim, int softplus_flag) {
+    using M = typename MathFor<T>::type;
     const int64_t b = blockIdx.y;
     const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
     const bool active = d_raw < dim;
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kWave) void scan_fwd_chain_kernel(
     float A2[N], h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        A2[n] = A_in[d * N + n] * kLog2e;
+        A2[n] = M::prep_A(A_in[d * N + n]);
         h[n] = h0_in ? h0_in[(b * dim + d) * N + n] : 0.0f;
     }
     const float bias = bias_in ? bias_in[d] : 0.0f;
@@ -97,15 +98,14 @@ __global__ __launch_bounds__(kWave) void scan_fwd_chain_kernel(
             if (t < seqlen) {
                 const float xv = to_f32(xs[k]);
                 const float v = to_f32(ds[k]) + bias;
-                const float dt = softplus_on ? softplus(v) : v;
+                const float dt = softplus_on ? M::softplus(v) : v;
                 const float dtx = dt * xv;
                 float acc = 0.0f;
 #pragma unroll
                 for (int n = 0; n < N; ++n) {
                     const float Bn = Bp[t * N + n];
                     const float Cn = Cp[t * N + n];
-                    const float dA = fast_exp2(dt * A2[n]);
-                    h[n] = fmaf(dA, h[n], dtx * Bn);
+                    h[n] = M::step(dt * A2[n], h[n], dtx * Bn);
                     acc = fmaf(Cn, h[n], acc);
                 }
                 float out = fmaf(Dd, xv, acc);
@@ -135,6 +135,7 @@ template <int N, typename T> hipError_t launch_chain(const ScanArgs &a, hipStrea
     const float *Bf = static_cast<const float *>(a.B);
     const float *Cf = static_cast<const float *>(a.C);
     if (a.bf16 && a.seqlen > 0) {
+        if (a.workspace == nullptr || a.workspace_bytes < 2 * bc_bytes(a)) return hipErrorInvalidValue;
         float *wb = static_cast<float *>(a.workspace);
         float *wc = reinterpret_cast<float *>(static_cast<char *>(a.workspace) + bc_bytes(a));
         const int64_t cnt = static_cast<int64_t>(bc_count(a));

@@ -1,6 +1,22 @@
 // Device helpers shared by the gfx950 selective-scan kernels: io-dtype
-// loads/stores, the fp32 elementwise pieces of the discretisation (softplus,
-// SiLU) and the hardware transcendental wrappers.
+// conversions, the fp32 elementwise pieces of the discretisation (softplus,
+// the per-state decay, SiLU) in two precisions, and hardware transcendental
+// wrappers.
+//
+// Two math policies:
+//   FastMath    -- v_exp_f32 / v_log_f32 / v_rcp_f32 straight from the
+//                  hardware.  Used for bf16 io, whose output rounding (2^-9)
+//                  is orders of magnitude above their error.
+//   PreciseMath -- used for fp32 io.  Two hardware shortcuts are not good
+//                  enough there:
+//                  * v_exp_f32 is about 0.1 ulp biased below 1 for small
+//                    arguments, and a decay close to 1 is multiplied into the
+//                    state thousands of times, so the bias compounds
+//                    (~T * 0.1 ulp).  The decay is instead applied as
+//                    h + expm1(Delta*A) * h with an accurate expm1, so no
+//                    near-1 factor is ever rounded.
+//                  * log1p in softplus is taken from a series instead of
+//                    v_log_f32 near 1.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,6 +26,8 @@ namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLn2Hi = 0.693147182464599609375f;   // float(ln 2)
+constexpr float kLn2Lo = -1.904654323148236e-09f;    // ln 2 - kLn2Hi
 
 // ---------------------------------------------------------------- io dtypes
 struct bf16_t {
@@ -32,31 +50,98 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 }
 
 // ------------------------------------------------------ hardware transcendentals
-// v_exp_f32 computes 2^x, v_log_f32 log2(x), v_rcp_f32 1/x (about 1 ulp).
+// v_exp_f32 computes 2^x, v_log_f32 log2(x), v_rcp_f32 1/x (within 1 ulp).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log(1 + e) for e in [0, 1], accurate for tiny e: with u = 1 + e rounded,
-// log1p(e) = log(u) * e / (u - 1) (Goldberg, "What every computer scientist
-// should know about floating-point arithmetic", Theorem 4); u == 1 means
-// log1p(e) = e to working precision.
-__device__ __forceinline__ float log1p_small(float e) {
-    const float u = 1.0f + e;
-    const float um1 = u - 1.0f;
-    const float r = fast_log2(u) * kLn2 * e * fast_rcp(um1);
-    return um1 == 0.0f ? e : r;
-}
-
-// softplus(v) = log(1 + exp(v)) = max(v, 0) + log(1 + exp(-|v|)).
-__device__ __forceinline__ float softplus(float v) {
-    const float e = fast_exp2(-fabsf(v) * kLog2e);
-    return fmaxf(v, 0.0f) + log1p_small(e);
-}
-
 // SiLU(z) = z / (1 + exp(-z)); exp overflow to +inf gives the correct -0 limit.
+// Its error does not accumulate anywhere, so one form serves both policies.
 __device__ __forceinline__ float silu(float z) {
     return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
 }
+
+// ----------------------------------------------------------- accurate pieces
+// expm1(x) to a few ulp for any x (overflow above ~88): x = k ln2 + r with
+// |r| <= ln2/2 (two-part ln2), expm1(r) by its Taylor series through r^7
+// (truncation < 1.5e-8 relative), then expm1(x) = 2^k expm1(r) + (2^k - 1).
+__device__ __forceinline__ float expm1_accurate(float x) {
+    const float k = rintf(x * kLog2e);
+    float r = fmaf(-k, kLn2Hi, x);
+    r = fmaf(-k, kLn2Lo, r);
+    float q = fmaf(r, 1.0f / 5040.0f, 1.0f / 720.0f);
+    q = fmaf(r, q, 1.0f / 120.0f);
+    q = fmaf(r, q, 1.0f / 24.0f);
+    q = fmaf(r, q, 1.0f / 6.0f);
+    q = fmaf(r, q, 0.5f);
+    q = fmaf(r, q, 1.0f);
+    const float p = r * q;                                   // expm1(r)
+    const float scale = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(k));
+    return fmaf(scale, p, scale - 1.0f);
+}
+
+// log(1 + e) for e in [0, 1]: with s = e / (2 + e) <= 1/3,
+// log1p(e) = 2 atanh(s) = 2 s (1 + s^2/3 + s^4/5 + ... + s^12/13)
+// (truncation < 1.4e-8 relative).
+__device__ __forceinline__ float log1p_unit(float e) {
+    const float s = e * fast_rcp(2.0f + e);
+    const float w = s * s;
+    float q = fmaf(w, 1.0f / 13.0f, 1.0f / 11.0f);
+    q = fmaf(w, q, 1.0f / 9.0f);
+    q = fmaf(w, q, 1.0f / 7.0f);
+    q = fmaf(w, q, 1.0f / 5.0f);
+    q = fmaf(w, q, 1.0f / 3.0f);
+    q = fmaf(w, q, 1.0f);
+    return 2.0f * s * q;
+}
+
+// ------------------------------------------------------------- math policies
+struct FastMath {
+    // log(1 + e), e in [0, 1]: log(u) * e / (u - 1) with u = 1 + e rounded
+    // (Goldberg's compensation for the rounding of u).
+    static __device__ __forceinline__ float log1p_unit(float e) {
+        const float u = 1.0f + e;
+        const float um1 = u - 1.0f;
+        const float r = fast_log2(u) * kLn2 * e * fast_rcp(um1);
+        return um1 == 0.0f ? e : r;
+    }
+    // softplus(v) = max(v, 0) + log(1 + exp(-|v|))
+    static __device__ __forceinline__ float softplus(float v) {
+        return fmaxf(v, 0.0f) + log1p_unit(fast_exp2(-fabsf(v) * kLog2e));
+    }
+    // the per-state decay factor exp(Delta * A), with A pre-scaled by log2(e)
+    static constexpr bool kScaledA = true;
+    static __device__ __forceinline__ float prep_A(float a) { return a * kLog2e; }
+    // one recurrence step h <- exp(Delta A) h + u, arg = Delta * prep_A(A)
+    static __device__ __forceinline__ float step(float arg, float h, float u) {
+        return fmaf(fast_exp2(arg), h, u);
+    }
+    // exp(A * S) as a plain factor (aggregates of several steps)
+    static __device__ __forceinline__ float decay(float arg) { return fast_exp2(arg); }
+    // the same step split in two, for kernels that keep the factor between passes
+    static __device__ __forceinline__ float factor(float arg) { return fast_exp2(arg); }
+    static __device__ __forceinline__ float apply(float f, float h, float u) { return fmaf(f, h, u); }
+};
+
+struct PreciseMath {
+    static __device__ __forceinline__ float softplus(float v) {
+        return fmaxf(v, 0.0f) + ssm::log1p_unit(fast_exp2(-fabsf(v) * kLog2e));
+    }
+    static constexpr bool kScaledA = false;
+    static __device__ __forceinline__ float prep_A(float a) { return a; }
+    // (h + expm1(Delta A) h) + u: the near-1 factor exp(Delta A) is never
+    // rounded, and exp(Delta A) h comes out of one fma (no h + u - h
+    // cancellation when the decay is fast)
+    static __device__ __forceinline__ float step(float arg, float h, float u) {
+        return fmaf(expm1_accurate(arg), h, h) + u;
+    }
+    static __device__ __forceinline__ float decay(float arg) { return expm1_accurate(arg) + 1.0f; }
+    static __device__ __forceinline__ float factor(float arg) { return expm1_accurate(arg); }
+    static __device__ __forceinline__ float apply(float f, float h, float u) { return fmaf(f, h, h) + u; }
+};
+
+template <typename T> struct MathFor;
+template <> struct MathFor<float> { using type = PreciseMath; };
+template <> struct MathFor<bf16_t> { using type = FastMath; };
 
 }  // namespace ssm

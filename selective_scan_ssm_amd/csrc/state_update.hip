@@ -32,6 +32,7 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 template <int N, typename T>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a) {
+    using M = typename MathFor<T>::type;
     constexpr int NPL = (N + kQuad - 1) / kQuad;   // states per lane
     const int64_t chains = a.batch * a.dim;
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a) {
 
     const float xv = to_f32(x[c]);
     const float v = to_f32(dl[c]) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
-    const float dt = a.softplus ? softplus(v) : v;
+    const float dt = a.softplus ? M::softplus(v) : v;
     const float dtx = dt * xv;
 
     float part = 0.0f;
@@ -62,8 +63,7 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a) {
     for (int i = 0; i < NPL; ++i) {
         const int n = q * NPL + i;
         if (n < N) {
-            const float dA = fast_exp2(dt * a.A[d * N + n] * kLog2e);
-            const float hn = fmaf(dA, hs[i], dtx * to_f32(Bm[b * N + n]));
+            const float hn = M::step(dt * M::prep_A(a.A[d * N + n]), hs[i], dtx * to_f32(Bm[b * N + n]));
             hs[i] = hn;
             part = fmaf(to_f32(Cm[b * N + n]), hn, part);
         }

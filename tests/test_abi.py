@@ -113,6 +113,13 @@ def test_scan_empty_is_noop(lib):
     assert call_scan(lib, scan_args(batch=0, x=None, delta=None, y=None)) == OK
 
 
+def test_sm1_bf16_needs_its_workspace(lib):
+    need = lib.sm1_scan_workspace_bytes(2, 16, 8, BF16)
+    assert need > 0
+    assert call_sm1(lib, scan_args(dstate=1, io=BF16, ws=None, ws_bytes=0)) == EWS
+    assert call_sm1(lib, scan_args(dstate=1, io=BF16, ws_bytes=need - 1)) == EWS
+
+
 def test_workspace_sizes(lib):
     assert lib.ssm_scan_workspace_bytes(2, 16, 8, 4, F32) == 0
     assert lib.ssm_scan_workspace_bytes(2, 16, 8, 4, BF16) >= 2 * 2 * 16 * 4 * 4

@@ -93,8 +93,8 @@ def test_optional_inputs(flags):
 
 
 def test_softplus_off():
-    inp = gen.make_inputs(2, 40, 64, 8, io=gen.F32, seed=301)
-    inp["delta"] = np.abs(inp["delta"]) * np.float32(0.05)
+    inp = gen.make_inputs(2, 40, 64, 8, io=gen.F32, seed=301, with_bias=False)
+    inp["delta"] = np.abs(inp["delta"]) * np.float32(0.05)   # positive Delta without softplus
     check(inp, softplus=False, tag="softplus-off")
 
 
@@ -115,6 +115,21 @@ def test_sm1_entry_matches_general_entry():
     yb, lb = G.run_scan(inp, sm1=False)
     assert G.err(ya, yb) <= 1e-5 and G.err(la, lb) <= 1e-5
     check(inp, sm1=True, tag="sm1-small")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64), (2, 127, 64), (2, 129, 100), (3, 1000, 36),
+                                   (1, 5000, 8), (2, 257, 70), (1, 300, 3)])
+def test_sm1_shapes_fp32(shape):
+    Bt, T, Dd = shape   # ragged sequence tails, partial channel tiles, d_inner % 4 != 0 (fallback)
+    check(gen.make_inputs(Bt, T, Dd, 1, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=400 + T),
+          sm1=True, tag=f"sm1{shape}")
+
+
+def test_sm1_no_optional_inputs():
+    inp = gen.make_inputs(2, 700, 64, 1, io=gen.F32, a_kind="sm1", h0_kind="none", seed=401,
+                          with_z=False, with_D=False, with_bias=False)
+    inp["delta"] = np.abs(inp["delta"]) * np.float32(0.02)
+    check(inp, softplus=False, sm1=True, tag="sm1-plain")
 
 
 def test_sm1_bf16():
