@@ -6,156 +6,428 @@
 //     h[n] <- exp(Delta_t A[d,n]) h[n] + Delta_t B[b,t,n] x[b,t,d]
 //     y     = (sum_n C[b,t,n] h[n] + D[d] x) * SiLU(z)
 //
-// Mapping: one lane owns one (b, d) chain and keeps all N states in VGPRs for
-// the whole sequence, so each (t, d, n) item costs (bf16 io) one v_exp_f32 and
-// three VALU ops plus one FMA of the readout, and the per-element work (softplus,
-// Delta*x, D*x, SiLU, bf16 conversion) is paid once per N items.  A wave
-// covers 64 consecutive channels of one batch row, so B[b,t,:] and C[b,t,:]
-// are wave-uniform and come in through scalar loads; x, delta, z are read
-// along d (128 contiguous bytes per wave for bf16) and prefetched one chunk
-// of kChunk steps ahead so the memory latency hides behind the recurrence.
+// At d_state 16 the scan is bound by VALU issue, not by HBM: every (t, d, n)
+// item needs one v_exp_f32 (half rate on gfx950) and four full-rate ops, while
+// it moves only half a byte of HBM traffic.  The kernel is laid out to spend
+// VALU cycles on little but those items:
+//
+//   * A workgroup owns a tile of 64 consecutive channels of one batch row
+//     (lane = channel, so every global access of a wave is one contiguous
+//     128-byte (bf16) / 256-byte (fp32) row).  Its NW waves split the d_state
+//     axis: wave w keeps states [w*NPW, (w+1)*NPW) of all 64 chains in VGPRs.
+//     NW = 4 at d_state 16 gives 4x more waves than one lane per chain, with
+//     no cross-lane arithmetic.
+//   * Per block of TB steps the per-element work (softplus of delta + bias,
+//     Delta*x) is done once per (t, d), split over the waves, and shared
+//     through LDS; B and C of the block are widened to fp32 once into LDS and
+//     read back as wave-uniform broadcasts.  Each wave's partial readout
+//     sum_{n in its slice} C h goes to LDS, and the epilogue (sum of the NW
+//     partials, D skip, SiLU gate, rounding, store) is split over the waves
+//     again.  The three phases form a software pipeline over blocks (produce
+//     block j, finish block j-2, scan block j-1) with double-buffered LDS and
+//     one barrier per block; global loads are issued two blocks ahead of
+//     their use, which hides the HBM latency behind two scan phases.
+//   * Long sequences are cut into segments.  Each (tile, segment) is one
+//     workgroup; segments are taken in order from an atomic ticket and hand
+//     the 64 x d_state state to the next segment of the same tile through
+//     global memory (release / acquire at agent scope).  A workgroup only
+//     waits on a segment that started before it, and the dispatcher places
+//     each next segment wherever a CU frees up, which evens out the load when
+//     the tile count is not a multiple of the CU count.
+#include <utility>
+
 #include "ssm_device.h"
 #include "ssm_kernels.h"
+
+#ifndef SSM_SCAN_TB
+#define SSM_SCAN_TB 16            // steps per pipeline block
+#endif
+#ifndef SSM_SCAN_NW16
+#define SSM_SCAN_NW16 4           // waves splitting d_state = 16
+#endif
+#ifndef SSM_SCAN_MAX_SEGS
+#define SSM_SCAN_MAX_SEGS 8       // most segments per tile
+#endif
+#ifndef SSM_SCAN_MIN_SEG_STEPS
+#define SSM_SCAN_MIN_SEG_STEPS 512
+#endif
 
 namespace ssm {
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kChunk = 8;
+constexpr int kTB = SSM_SCAN_TB;
+constexpr int kTile = 64;                    // channels per workgroup (one per lane)
+constexpr uint32_t kSpinLimit = 1u << 22;    // bounded wait on the previous segment
 
-// Widen B and C to fp32 once (they are tiny: batch * seqlen * d_state values)
-// so the scan can take them straight from scalar loads with no unpacking.
-template <typename T>
-__global__ __launch_bounds__(256) void widen_bc_kernel(const T *__restrict__ B, const T *__restrict__ C,
-                                                      float *__restrict__ Bf, float *__restrict__ Cf,
-                                                      int64_t count) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i < count) {
-        Bf[i] = to_f32(B[i]);
-        Cf[i] = to_f32(C[i]);
-    }
+template <int N> constexpr int waves_for() {
+    return N == 16 ? SSM_SCAN_NW16 : (N % 4 == 0 ? 4 : (N % 2 == 0 ? 2 : 1));
 }
 
-// Pointers come in as separate __restrict__ kernel parameters: that is what
-// lets the compiler prove B/C are never written and read them with scalar
-// loads into SGPRs.
-template <int N, typename T>
-__global__ __launch_bounds__(kWave) void scan_fwd_chain_kernel(
-    const T *__restrict__ x_in, const T *__restrict__ delta_in, const T *__restrict__ z_in,
-    const float *__restrict__ Bf, const float *__restrict__ Cf, const float *__restrict__ A_in,
-    const float *__restrict__ D_in, const float *__restrict__ bias_in, const float *__restrict__ h0_in,
-    T *__restrict__ y_out, float *__restrict__ last_out, int64_t seqlen, int64_t dim, int softplus_flag) {
+struct Params {
+    const void *x, *delta, *z, *B, *C;
+    const float *A, *D, *bias, *h0;
+    void *y;
+    float *last;
+    uint32_t *words;     // [0] ticket, [1] error flag, [64 ..) per-tile progress
+    float *hbuf;         // per tile: d_state x 64 carried states
+    int64_t seqlen, dim;
+    int n_dt, n_tiles, seg_len, n_segs, softplus;
+};
+
+struct Layout {
+    int n_dt, n_tiles, seg_len, n_segs;
+    size_t hbuf_off, total;
+};
+
+Layout make_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t esize) {
+    Layout l{};
+    l.n_dt = static_cast<int>((dim + kTile - 1) / kTile);
+    l.n_tiles = static_cast<int>(batch * l.n_dt);
+    const int64_t blocks = (seqlen + kTB - 1) / kTB;
+    int64_t segs = seqlen / SSM_SCAN_MIN_SEG_STEPS;
+    segs = segs < 1 ? 1 : (segs > SSM_SCAN_MAX_SEGS ? SSM_SCAN_MAX_SEGS : segs);
+    // row offsets inside a segment are 32-bit buffer offsets: keep a segment
+    // of (seqlen, d_inner) below 1 GiB
+    const int64_t max_rows = (int64_t(1) << 30) / (dim * esize > 0 ? dim * esize : 1);
+    const int64_t need = max_rows > kTB ? (seqlen + max_rows - kTB - 1) / (max_rows - kTB) : seqlen;
+    segs = segs > need ? segs : need;
+    const int64_t seg_blocks = blocks > 0 ? (blocks + segs - 1) / segs : 1;
+    l.seg_len = static_cast<int>(seg_blocks * kTB);
+    l.n_segs = static_cast<int>(seqlen > 0 ? (seqlen + l.seg_len - 1) / l.seg_len : 1);
+    auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+    // [0, 256): ticket + error word; [256, hbuf_off): per-tile progress
+    l.hbuf_off = 256 + up(static_cast<size_t>(l.n_tiles) * sizeof(uint32_t));
+    l.total = l.hbuf_off + up(static_cast<size_t>(l.n_tiles) * dstate * kTile * sizeof(float));
+    return l;
+}
+
+// ---- DPP row broadcasts: lane K of every 16-lane row feeds the whole row
+constexpr int kRowNewBcast = 0x150;   // DPP control row_newbcast:0
+
+template <int K> __device__ __forceinline__ float row_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kRowNewBcast + K, 0xF, 0xF, true));
+}
+
+// acc += (lane K of each row of c) * h as a single v_fmac_f32 with a DPP
+// source (the compiler folds DPP into v_mul but not into v_fmac).  c must
+// come from a load, not from a VALU write just before (DPP read hazard).
+template <int K> __device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(acc) : "v"(c), "v"(h), "n"(K));
+    return acc;
+}
+
+// One step of the wave's NPW states: breg holds B of the step in row lanes
+// [0, NPW), creg holds C in row lanes [CB, CB + NPW).  Returns sum_i C_i h_i.
+template <typename M, int NPW, int CB, int... I>
+__device__ __forceinline__ float scan_step(std::integer_sequence<int, I...>, float (&h)[NPW],
+                                           const float (&A2)[NPW], float dt, float dtx, float breg,
+                                           float creg) {
+    ((h[I] = M::step(dt * A2[I], h[I], dtx * row_bcast<I>(breg))), ...);
+    float acc = h[0] * row_bcast<CB>(creg);
+    ((acc = I > 0 ? fmac_row_bcast<CB + I>(acc, creg, h[I]) : acc), ...);
+    return acc;
+}
+
+// ---- buffer loads / stores.  A wave-uniform descriptor (base and size in
+// SGPRs) plus a per-lane byte offset and a scalar row offset is how gfx950
+// addresses memory without per-lane 64-bit arithmetic.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, kRsrcWord3);
+}
+
+template <typename T> struct Io;
+template <> struct Io<bf16_t> {
+    using raw = uint16_t;
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, voff, soff, 0);
+    }
+};
+template <> struct Io<float> {
+    using raw = uint32_t;
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(v); }
+    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+};
+
+#ifndef SSM_SCAN_WAVES_PER_EU
+#define SSM_SCAN_WAVES_PER_EU 2   // occupancy the register allocator may assume
+#endif
+
+template <int N, int NW, typename T>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, SSM_SCAN_WAVES_PER_EU)))
+void scan_fwd_kernel(Params p) {
     using M = typename MathFor<T>::type;
-    const int64_t b = blockIdx.y;
-    const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
-    const bool active = d_raw < dim;
-    const int64_t d = active ? d_raw : dim - 1;   // inactive lanes shadow the last channel
+    static_assert(N % NW == 0 && kTB % NW == 0, "waves must split d_state and the block evenly");
+    constexpr int NPW = N / NW;      // states per wave
+    constexpr int PB = kTB / NW;     // steps per wave in the produce / finish phases
+    constexpr int NT = NW * 64;
+    constexpr int kBCV = 2 * NPW <= 16 ? 1 : 2;        // VGPRs holding one step's B and C
+    constexpr int NBC = 2 * kTB * N;                   // B and C values of one block
+    constexpr int BC_PER = (NBC + NT - 1) / NT;        // of them staged per thread
 
-    float A2[N], h[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        A2[n] = M::prep_A(A_in[d * N + n]);
-        h[n] = h0_in ? h0_in[(b * dim + d) * N + n] : 0.0f;
-    }
-    const float bias = bias_in ? bias_in[d] : 0.0f;
-    const float Dd = D_in ? D_in[d] : 0.0f;
-    const bool has_z = z_in != nullptr;
-    const bool softplus_on = softplus_flag != 0;
+    __shared__ float2 sDX[2][kTB][kTile];       // (Delta, Delta*x)
+    __shared__ float sP[2][NW][kTB][kTile];     // partial readouts per wave
+    __shared__ float sBC[2][2][kTB][N];         // [buf][B|C][t][n] in fp32
+    __shared__ uint32_t s_ticket;
 
-    const int64_t row0 = b * seqlen;   // first (b, t) row
-    const T *xp = x_in + row0 * dim + d;
-    const T *dp = delta_in + row0 * dim + d;
-    const T *zp = has_z ? z_in + row0 * dim + d : xp;
-    const float *Bp = Bf + row0 * N;
-    const float *Cp = Cf + row0 * N;
-    T *yp = y_out + row0 * dim + d;
+    using raw = typename Io<T>::raw;
+    const int64_t seqlen = p.seqlen, dim = p.dim;
 
-    T xs[kChunk], ds[kChunk], zs[kChunk];
-    if (seqlen > 0) {
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-            const int64_t t = k < seqlen ? k : seqlen - 1;
-            xs[k] = xp[t * dim];
-            ds[k] = dp[t * dim];
-            zs[k] = has_z ? zp[t * dim] : xs[k];
-        }
-    }
+    const int tid = threadIdx.x, lane = tid % 64;
+    // the wave index is uniform across the wave; saying so keeps every step,
+    // row and state index derived from it in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    if (tid == 0) s_ticket = atomicAdd(&p.words[0], 1u);
+    __syncthreads();
+    const uint32_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);   // uniform: keeps tile math scalar
+    const int seg = static_cast<int>(ticket / static_cast<uint32_t>(p.n_tiles));
+    const int tile = static_cast<int>(ticket % static_cast<uint32_t>(p.n_tiles));
+    const int64_t b = tile / p.n_dt;
+    const int64_t d0 = static_cast<int64_t>(tile % p.n_dt) * kTile;   // first channel of the tile
+    const bool active = d0 + lane < dim;
+    // column of this lane inside the tile; inactive lanes shadow the last channel
+    const uint32_t col = active ? static_cast<uint32_t>(lane) : static_cast<uint32_t>(dim - 1 - d0);
+    const int64_t d = d0 + col;
+    const int n0 = w * NPW;
+    const int64_t t_begin = static_cast<int64_t>(seg) * p.seg_len;
+    const int64_t t_end = (t_begin + p.seg_len < seqlen) ? t_begin + p.seg_len : seqlen;
+    const int steps = static_cast<int>(t_end - t_begin);   // steps of this segment (32-bit compares stay scalar)
+    const int nb = (steps + kTB - 1) / kTB;
+    const bool softplus_on = p.softplus != 0;
+    const bool has_z = p.z != nullptr;
+    uint32_t *progress = p.words + 64;
 
-    for (int64_t t0 = 0; t0 < seqlen; t0 += kChunk) {
-        // prefetch the next chunk (clamped to a valid row; unused past the end)
-        T xn[kChunk], dn[kChunk], zn[kChunk];
+    // descriptors start at this segment's first row (and, for the (t, d)
+    // tensors, at the tile's first channel); rows are scalar byte offsets
+    const int64_t row0 = b * seqlen + t_begin;
+    const int64_t e0 = (row0 * dim + d0) * static_cast<int64_t>(sizeof(T));
+    const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + e0);
+    const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + e0);
+    const rsrc_t rz = make_rsrc(static_cast<const char *>(has_z ? p.z : p.x) + e0);
+    const rsrc_t ry = make_rsrc(static_cast<char *>(p.y) + e0);
+    const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * static_cast<int64_t>(sizeof(T)));
+    const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * static_cast<int64_t>(sizeof(T)));
+    const uint32_t voff = col * static_cast<uint32_t>(sizeof(T));
+    const uint32_t row_bytes = static_cast<uint32_t>(dim * static_cast<int64_t>(sizeof(T)));
+    float *hslot = p.hbuf + static_cast<int64_t>(tile) * N * kTile;
+
+    float A2[NPW], h[NPW];
 #pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-            int64_t t = t0 + kChunk + k;
-            t = t < seqlen ? t : seqlen - 1;
-            xn[k] = xp[t * dim];
-            dn[k] = dp[t * dim];
-            zn[k] = has_z ? zp[t * dim] : xn[k];
-        }
+    for (int i = 0; i < NPW; ++i) A2[i] = M::prep_A(p.A[d * N + n0 + i]);
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float Dd = p.D ? p.D[d] : 0.0f;
+
+    // ---- state entering this segment
+    if (seg == 0) {
 #pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-            const int64_t t = t0 + k;
-            if (t < seqlen) {
-                const float xv = to_f32(xs[k]);
-                const float v = to_f32(ds[k]) + bias;
-                const float dt = softplus_on ? M::softplus(v) : v;
-                const float dtx = dt * xv;
-                float acc = 0.0f;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float Bn = Bp[t * N + n];
-                    const float Cn = Cp[t * N + n];
-                    h[n] = M::step(dt * A2[n], h[n], dtx * Bn);
-                    acc = fmaf(Cn, h[n], acc);
+        for (int i = 0; i < NPW; ++i) h[i] = p.h0 ? p.h0[(b * dim + d) * N + n0 + i] : 0.0f;
+    } else {
+        // Poll with relaxed coherent loads (an acquire per poll would
+        // invalidate the L2 every time) and acquire once when the flag is seen.
+        if (tid == 0) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(&progress[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                   static_cast<uint32_t>(seg)) {
+                if (++spins > kSpinLimit) {       // never wait unboundedly
+                    p.words[1] = 1u;
+                    break;
                 }
-                float out = fmaf(Dd, xv, acc);
-                if (has_z) out *= silu(to_f32(zs[k]));
-                if (active) yp[t * dim] = from_f32<T>(out);
+                __builtin_amdgcn_s_sleep(2);
             }
         }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-            xs[k] = xn[k];
-            ds[k] = dn[k];
-            zs[k] = zn[k];
-        }
+        for (int i = 0; i < NPW; ++i) h[i] = hslot[(n0 + i) * kTile + lane];
     }
 
-    if (last_out && active) {
+    // ---- prefetch registers.  Loads are issued right after the data they
+    // replace was consumed and two blocks ahead of their use.  Every load is
+    // unconditional (rows clamped into the segment) so the loop body is
+    // straight-line code.
+    struct Pre {
+        raw dP[PB], xP[PB];    // produce phase: delta, x
+        raw xE[PB], zE[PB];    // finish phase: x, z
+        raw bc[BC_PER];        // B/C values this thread stages
+    };
+    auto clamp_step = [&](int j, int k) -> uint32_t {   // segment step of step k of block j, clamped
+        const int s = j * kTB + k;
+        return static_cast<uint32_t>(s < 0 ? 0 : (s < steps ? s : steps - 1));
+    };
+    auto load_pre = [&](Pre &r, int jp, int je) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) last_out[(b * dim + d) * N + n] = h[n];
+        for (int kk = 0; kk < PB; ++kk) {
+            const uint32_t sp = clamp_step(jp, w + kk * NW) * row_bytes;
+            r.dP[kk] = Io<T>::load(rd, voff, sp);
+            r.xP[kk] = Io<T>::load(rx, voff, sp);
+            const uint32_t se = clamp_step(je, w + kk * NW) * row_bytes;
+            r.xE[kk] = Io<T>::load(rx, voff, se);
+            r.zE[kk] = Io<T>::load(rz, voff, se);
+        }
+#pragma unroll
+        for (int m = 0; m < BC_PER; ++m) {
+            int i = tid + m * NT;
+            i = i < NBC ? i : NBC - 1;
+            const int which = i / (kTB * N), rem = i % (kTB * N);
+            const uint32_t off = (clamp_step(jp, rem / N) * N + rem % N) * static_cast<uint32_t>(sizeof(T));
+            r.bc[m] = Io<T>::load(which == 0 ? rB : rC, off, 0);
+        }
+    };
+
+    // produce block j into LDS buffer j%2
+    auto produce = [&](const Pre &r, int j) {
+        const int buf = j & 1;
+#pragma unroll
+        for (int kk = 0; kk < PB; ++kk) {
+            const int k = w + kk * NW;
+            const bool tv = j * kTB + k < steps;     // wave-uniform
+            const float v = Io<T>::f32(r.dP[kk]) + bias;
+            float dt = softplus_on ? M::softplus(v) : v;
+            dt = tv ? dt : 0.0f;                     // past the end: identity step
+            sDX[buf][k][lane] = make_float2(dt, dt * Io<T>::f32(r.xP[kk]));
+        }
+#pragma unroll
+        for (int m = 0; m < BC_PER; ++m) {
+            const int i = tid + m * NT;
+            if (i < NBC) (&sBC[buf][0][0][0])[i] = Io<T>::f32(r.bc[m]);
+        }
+    };
+
+    // Scan operands of block j (LDS buffer j%2), read in one go: Delta and
+    // Delta*x per step, and B, C of the wave's states laid out so that lane q
+    // of every 16-lane row holds value q of the step (B in lanes [0, NPW), C
+    // after them).  The steps then run on registers only; B and C reach the
+    // arithmetic through DPP row broadcasts.
+    struct ScanOps {
+        float2 dx[kTB];
+        float bcr[kTB][kBCV];
+    };
+    auto scan_read = [&](ScanOps &o, int j) {
+        const int buf = j & 1;
+        const int q = lane & 15;
+#pragma unroll
+        for (int k = 0; k < kTB; ++k) {
+            o.dx[k] = sDX[buf][k][lane];
+            if constexpr (kBCV == 1) {
+                const int qq = q < 2 * NPW ? q : 0;
+                o.bcr[k][0] = sBC[buf][qq < NPW ? 0 : 1][k][n0 + (qq < NPW ? qq : qq - NPW)];
+            } else {
+                const int qq = q < NPW ? q : 0;
+                o.bcr[k][0] = sBC[buf][0][k][n0 + qq];
+                o.bcr[k][1] = sBC[buf][1][k][n0 + qq];
+            }
+        }
+    };
+    auto scan = [&](const ScanOps &o, int j) {
+        const int buf = j & 1;
+#pragma unroll
+        for (int k = 0; k < kTB; ++k)
+            sP[buf][w][k][lane] = scan_step<M, NPW, (kBCV == 1 ? NPW : 0)>(
+                std::make_integer_sequence<int, NPW>{}, h, A2, o.dx[k].x, o.dx[k].y, o.bcr[k][0],
+                o.bcr[k][kBCV - 1]);
+    };
+
+    // finish block j: sum the partials, D skip, gate, store
+    auto finish = [&](const Pre &r, int j) {
+        const int buf = j & 1;
+#pragma unroll
+        for (int kk = 0; kk < PB; ++kk) {
+            const int k = w + kk * NW;
+            const int sl = j * kTB + k;
+            float acc = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) acc += sP[buf][ww][k][lane];
+            float out = fmaf(Dd, Io<T>::f32(r.xE[kk]), acc);
+            if (has_z) out *= silu(Io<T>::f32(r.zE[kk]));
+            if (sl < steps && active) Io<T>::store(out, ry, voff, static_cast<uint32_t>(sl) * row_bytes);
+        }
+    };
+
+    // ---- the pipeline: iteration j reads the scan operands of block j-1,
+    // produces block j, finishes block j-2, issues the global loads of two
+    // iterations ahead and scans block j-1.  Two prefetch register sets
+    // alternate, so every global load has two scan phases to arrive.
+    ScanOps so;
+    auto iteration = [&](Pre &r, int j) {
+        const bool do_scan = j >= 1 && j - 1 < nb;
+        if (do_scan) scan_read(so, j - 1);
+        if (j < nb) produce(r, j);
+        if (j >= 2) finish(r, j - 2);
+        load_pre(r, j + 2, j);
+        if (do_scan) scan(so, j - 1);
+        __syncthreads();
+    };
+    Pre r0, r1;
+    load_pre(r0, 0, 0);
+    load_pre(r1, 1, 0);
+    for (int j = 0; j < nb + 2; j += 2) {
+        iteration(r0, j);
+        if (j + 1 < nb + 2) iteration(r1, j + 1);
+    }
+
+    // ---- hand the state on, or write last_state
+    if (seg + 1 < p.n_segs) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) hslot[(n0 + i) * kTile + lane] = h[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // every wave's stores, then the flag
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(&progress[tile], static_cast<uint32_t>(seg + 1), __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if (p.last && active) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) p.last[(b * dim + d) * N + n0 + i] = h[i];
     }
 }
 
-// fp32 copies of B and C live in the workspace when the io dtype is bf16.
-size_t bc_count(const ScanArgs &a) { return static_cast<size_t>(a.batch * a.seqlen * a.dstate); }
-size_t bc_bytes(const ScanArgs &a) { return (bc_count(a) * sizeof(float) + 255) & ~size_t(255); }
+// seqlen == 0: last_state = h0 (or 0)
+__global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float *last, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) last[i] = h0 ? h0[i] : 0.0f;
+}
 
-template <int N, typename T> hipError_t launch_chain(const ScanArgs &a, hipStream_t s) {
-    const float *Bf = static_cast<const float *>(a.B);
-    const float *Cf = static_cast<const float *>(a.C);
-    if (a.bf16 && a.seqlen > 0) {
-        if (a.workspace == nullptr || a.workspace_bytes < 2 * bc_bytes(a)) return hipErrorInvalidValue;
-        float *wb = static_cast<float *>(a.workspace);
-        float *wc = reinterpret_cast<float *>(static_cast<char *>(a.workspace) + bc_bytes(a));
-        const int64_t cnt = static_cast<int64_t>(bc_count(a));
-        hipLaunchKernelGGL((widen_bc_kernel<T>), dim3(static_cast<unsigned>((cnt + 255) / 256)), dim3(256),
-                           0, s, static_cast<const T *>(a.B), static_cast<const T *>(a.C), wb, wc, cnt);
-        Bf = wb;
-        Cf = wc;
-    }
-    const dim3 grid(static_cast<unsigned>((a.dim + kWave - 1) / kWave), static_cast<unsigned>(a.batch));
-    hipLaunchKernelGGL((scan_fwd_chain_kernel<N, T>), grid, dim3(kWave), 0, s,
-                       static_cast<const T *>(a.x), static_cast<const T *>(a.delta),
-                       static_cast<const T *>(a.z), Bf, Cf, a.A, a.D, a.delta_bias, a.h0,
-                       static_cast<T *>(a.y), a.last_state, a.seqlen, a.dim, a.softplus);
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *w, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) w[i] = 0u;
+}
+
+template <int N, typename T> hipError_t launch(const ScanArgs &a, hipStream_t s) {
+    constexpr int NW = waves_for<N>();
+    const Layout l = make_layout(a.batch, a.seqlen, a.dim, N, sizeof(T));
+    char *ws = static_cast<char *>(a.workspace);
+    Params p;
+    p.x = a.x; p.delta = a.delta; p.z = a.z; p.B = a.B; p.C = a.C;
+    p.A = a.A; p.D = a.D; p.bias = a.delta_bias; p.h0 = a.h0;
+    p.y = a.y; p.last = a.last_state;
+    p.words = reinterpret_cast<uint32_t *>(ws);
+    p.hbuf = reinterpret_cast<float *>(ws + l.hbuf_off);
+    p.seqlen = a.seqlen; p.dim = a.dim;
+    p.n_dt = l.n_dt; p.n_tiles = l.n_tiles; p.seg_len = l.seg_len; p.n_segs = l.n_segs;
+    p.softplus = a.softplus;
+    const int64_t nclear = static_cast<int64_t>(l.hbuf_off / sizeof(uint32_t));   // ticket + progress
+    hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
+                       p.words, nclear);
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(l.n_tiles) * l.n_segs);
+    hipLaunchKernelGGL((scan_fwd_kernel<N, NW, T>), dim3(grid), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     switch (a.dstate) {
 #define SSM_CASE(NN) \
-    case NN: return launch_chain<NN, T>(a, s);
+    case NN: return launch<NN, T>(a, s);
         SSM_CASE(1) SSM_CASE(2) SSM_CASE(3) SSM_CASE(4) SSM_CASE(5) SSM_CASE(6) SSM_CASE(7)
         SSM_CASE(8) SSM_CASE(9) SSM_CASE(10) SSM_CASE(11) SSM_CASE(12) SSM_CASE(13)
         SSM_CASE(14) SSM_CASE(15) SSM_CASE(16)
@@ -166,10 +438,21 @@ template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
 
 }  // namespace
 
-size_t scan_fwd_workspace(const ScanArgs &a) { return a.bf16 && a.seqlen > 0 ? 2 * bc_bytes(a) : 0; }
+size_t scan_fwd_workspace(const ScanArgs &a) {
+    if (a.batch == 0 || a.dim == 0 || a.seqlen == 0) return 0;
+    return make_layout(a.batch, a.seqlen, a.dim, a.dstate, a.bf16 ? 2 : 4).total;
+}
 
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t s) {
     if (a.batch == 0 || a.dim == 0) return hipSuccess;
+    if (a.seqlen == 0) {
+        if (!a.last_state) return hipSuccess;
+        const int64_t n = a.batch * a.dim * a.dstate;
+        hipLaunchKernelGGL(copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                           a.h0, a.last_state, n);
+        return hipGetLastError();
+    }
+    if (a.workspace == nullptr || a.workspace_bytes < scan_fwd_workspace(a)) return hipErrorInvalidValue;
     if (a.bf16) return dispatch_n<bf16_t>(a, s);
     return dispatch_n<float>(a, s);
 }

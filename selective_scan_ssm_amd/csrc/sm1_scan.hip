@@ -217,7 +217,9 @@ __global__ __launch_bounds__(kThreads) void sm1_chunked_kernel(
             h_in = 0.0f;
             while (true) {
                 const int64_t ks = static_cast<int64_t>(tile) * n_chunks + k;
-                const uint32_t fl = __hip_atomic_load(&flags[ks], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                // relaxed coherent poll; one acquire fence once a flag is seen
+                const uint32_t fl = __hip_atomic_load(&flags[ks], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (fl != kFlagEmpty) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 if (fl == kFlagPrefix) {
                     h_in = fmaf(Pa, pre[ks * kTileC + ch], Ha);
                     break;

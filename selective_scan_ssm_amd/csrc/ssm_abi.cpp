@@ -56,6 +56,8 @@ int validate_scan(const void *x, const void *delta, const float *delta_bias, con
     const int64_t n_btn = mul3(batch, seqlen, dstate);
     const int64_t n_bdn = mul3(batch, dim, dstate);
     if (n_btd < 0 || n_btn < 0 || n_bdn < 0 || mul3(dim, dstate, 1) < 0) return SSM_ERR_SHAPE;
+    // workgroups are numbered by a 32-bit ticket: (batch x 64-channel tiles) x up to 8 time segments
+    if (mul3(batch, (dim + 63) / 64, 8) > (int64_t(1) << 31)) return SSM_ERR_SHAPE;
     if (batch == 0 || dim == 0) return SSM_OK;   // nothing to read or write
     if (!A) return SSM_ERR_NULL;
     if (seqlen > 0 && (!x || !delta || !B || !C || !y)) return SSM_ERR_NULL;

@@ -97,17 +97,13 @@ __device__ __forceinline__ float log1p_unit(float e) {
 
 // ------------------------------------------------------------- math policies
 struct FastMath {
-    // log(1 + e), e in [0, 1]: log(u) * e / (u - 1) with u = 1 + e rounded
-    // (Goldberg's compensation for the rounding of u).
-    static __device__ __forceinline__ float log1p_unit(float e) {
-        const float u = 1.0f + e;
-        const float um1 = u - 1.0f;
-        const float r = fast_log2(u) * kLn2 * e * fast_rcp(um1);
-        return um1 == 0.0f ? e : r;
-    }
-    // softplus(v) = max(v, 0) + log(1 + exp(-|v|))
+    // softplus(v) = max(v, 0) + log(1 + e), e = exp(-|v|) in (0, 1].
+    // log1p(e) is log2(1 + e) ln 2 for e >= 1/1024 (the rounding of 1 + e costs
+    // at most ~1e-4 relative there) and e - e^2/2 below (truncation < e^2/3).
     static __device__ __forceinline__ float softplus(float v) {
-        return fmaxf(v, 0.0f) + log1p_unit(fast_exp2(-fabsf(v) * kLog2e));
+        const float e = fast_exp2(-fabsf(v) * kLog2e);
+        const float l = e >= (1.0f / 1024.0f) ? fast_log2(1.0f + e) * kLn2 : fmaf(-0.5f * e, e, e);
+        return fmaxf(v, 0.0f) + l;
     }
     // the per-state decay factor exp(Delta * A), with A pre-scaled by log2(e)
     static constexpr bool kScaledA = true;
