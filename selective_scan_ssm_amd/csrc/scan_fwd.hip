@@ -34,6 +34,7 @@
 //     waits on a segment that started before it, and the dispatcher places
 //     each next segment wherever a CU frees up, which evens out the load when
 //     the tile count is not a multiple of the CU count.
+#include <type_traits>
 #include <utility>
 
 #include "ssm_device.h"
@@ -174,8 +175,8 @@ void scan_fwd_kernel(Params p) {
     constexpr int PB = kTB / NW;     // steps per wave in the produce / finish phases
     constexpr int NT = NW * 64;
     constexpr int kBCV = 2 * NPW <= 16 ? 1 : 2;        // VGPRs holding one step's B and C
-    constexpr int NBC = 2 * kTB * N;                   // B and C values of one block
-    constexpr int BC_PER = (NBC + NT - 1) / NT;        // of them staged per thread
+    constexpr int BC_HALF = (kTB * N + NT - 1) / NT;   // B (or C) values of a block staged per thread
+    constexpr int BC_PER = 2 * BC_HALF;
 
     __shared__ float2 sDX[2][kTB][kTile];       // (Delta, Delta*x)
     __shared__ float sP[2][NW][kTB][kTile];     // partial readouts per wave
@@ -220,6 +221,9 @@ void scan_fwd_kernel(Params p) {
     const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * static_cast<int64_t>(sizeof(T)));
     const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * static_cast<int64_t>(sizeof(T)));
     const uint32_t voff = col * static_cast<uint32_t>(sizeof(T));
+    // stores of lanes past d_inner use an offset beyond the descriptor's
+    // range, which the buffer unit drops (no branch around the store)
+    const uint32_t voff_store = active ? voff : 0x80000000u;
     const uint32_t row_bytes = static_cast<uint32_t>(dim * static_cast<int64_t>(sizeof(T)));
     float *hslot = p.hbuf + static_cast<int64_t>(tile) * N * kTile;
 
@@ -276,13 +280,13 @@ void scan_fwd_kernel(Params p) {
             r.xE[kk] = Io<T>::load(rx, voff, se);
             r.zE[kk] = Io<T>::load(rz, voff, se);
         }
+        // B then C of the block; each loop has a uniform descriptor
 #pragma unroll
         for (int m = 0; m < BC_PER; ++m) {
-            int i = tid + m * NT;
-            i = i < NBC ? i : NBC - 1;
-            const int which = i / (kTB * N), rem = i % (kTB * N);
-            const uint32_t off = (clamp_step(jp, rem / N) * N + rem % N) * static_cast<uint32_t>(sizeof(T));
-            r.bc[m] = Io<T>::load(which == 0 ? rB : rC, off, 0);
+            int e = tid + (m % BC_HALF) * NT;
+            e = e < kTB * N ? e : kTB * N - 1;
+            const uint32_t off = (clamp_step(jp, e / N) * N + e % N) * static_cast<uint32_t>(sizeof(T));
+            r.bc[m] = Io<T>::load(m < BC_HALF ? rB : rC, off, 0);
         }
     };
 
@@ -300,8 +304,8 @@ void scan_fwd_kernel(Params p) {
         }
 #pragma unroll
         for (int m = 0; m < BC_PER; ++m) {
-            const int i = tid + m * NT;
-            if (i < NBC) (&sBC[buf][0][0][0])[i] = Io<T>::f32(r.bc[m]);
+            const int e = tid + (m % BC_HALF) * NT;
+            if (e < kTB * N) sBC[buf][m < BC_HALF ? 0 : 1][e / N][e % N] = Io<T>::f32(r.bc[m]);
         }
     };
 
@@ -351,30 +355,59 @@ void scan_fwd_kernel(Params p) {
             for (int ww = 0; ww < NW; ++ww) acc += sP[buf][ww][k][lane];
             float out = fmaf(Dd, Io<T>::f32(r.xE[kk]), acc);
             if (has_z) out *= silu(Io<T>::f32(r.zE[kk]));
-            if (sl < steps && active) Io<T>::store(out, ry, voff, static_cast<uint32_t>(sl) * row_bytes);
+            if (sl < steps) Io<T>::store(out, ry, voff_store, static_cast<uint32_t>(sl) * row_bytes);
         }
     };
 
     // ---- the pipeline: iteration j reads the scan operands of block j-1,
     // produces block j, finishes block j-2, issues the global loads of two
     // iterations ahead and scans block j-1.  Two prefetch register sets
-    // alternate, so every global load has two scan phases to arrive.
+    // alternate, so every global load has two scan phases to arrive.  The
+    // phases of an iteration are compile-time flags: the steady-state
+    // iterations are straight-line code, which lets the compiler count
+    // outstanding loads exactly instead of draining them at every branch.
     ScanOps so;
-    auto iteration = [&](Pre &r, int j) {
-        const bool do_scan = j >= 1 && j - 1 < nb;
-        if (do_scan) scan_read(so, j - 1);
-        if (j < nb) produce(r, j);
-        if (j >= 2) finish(r, j - 2);
+    auto iteration = [&](auto produce_on, auto finish_on, auto scan_on, Pre &r, int j) {
+        if constexpr (decltype(scan_on)::value) scan_read(so, j - 1);
+        if constexpr (decltype(produce_on)::value) produce(r, j);
+        if constexpr (decltype(finish_on)::value) finish(r, j - 2);
         load_pre(r, j + 2, j);
-        if (do_scan) scan(so, j - 1);
+        if constexpr (decltype(scan_on)::value) scan(so, j - 1);
         __syncthreads();
     };
+    using on = std::true_type;
+    using off = std::false_type;
     Pre r0, r1;
     load_pre(r0, 0, 0);
     load_pre(r1, 1, 0);
-    for (int j = 0; j < nb + 2; j += 2) {
-        iteration(r0, j);
-        if (j + 1 < nb + 2) iteration(r1, j + 1);
+    if (nb >= 3) {
+        iteration(on{}, off{}, off{}, r0, 0);
+        iteration(on{}, off{}, on{}, r1, 1);
+        int j = 2;
+        for (; j + 1 < nb; j += 2) {
+            iteration(on{}, on{}, on{}, r0, j);
+            iteration(on{}, on{}, on{}, r1, j + 1);
+        }
+        if (j < nb) {          // one steady iteration left (even j): drain ends on set r1
+            iteration(on{}, on{}, on{}, r0, j);
+            iteration(off{}, on{}, on{}, r1, nb);
+            iteration(off{}, on{}, off{}, r0, nb + 1);
+        } else {               // j == nb (even): drain ends on set r0
+            iteration(off{}, on{}, on{}, r0, nb);
+            iteration(off{}, on{}, off{}, r1, nb + 1);
+        }
+    } else {
+        // short segments: the same phases with run-time conditions
+        for (int j = 0; j < nb + 2; ++j) {
+            Pre &r = (j & 1) ? r1 : r0;
+            const bool do_scan = j >= 1 && j - 1 < nb;
+            if (do_scan) scan_read(so, j - 1);
+            if (j < nb) produce(r, j);
+            if (j >= 2) finish(r, j - 2);
+            load_pre(r, j + 2, j);
+            if (do_scan) scan(so, j - 1);
+            __syncthreads();
+        }
     }
 
     // ---- hand the state on, or write last_state
