@@ -1,23 +1,35 @@
 #!/usr/bin/env python3
-"""Benchmark of the gfx950 selective scan (one GPU).
+"""Benchmark of the gfx950 selective-scan kernels on one GPU.
 
-One step = one forward selective scan (ssm_scan_fwd: discretisation, scan,
-readout, D skip, SiLU gate, last_state) over a mamba-2.8b-shaped layer:
+Default step: one forward selective scan (ssm_scan_fwd: Delta discretisation,
+scan, readout, D skip, SiLU gate, last_state) over a mamba-2.8b-shaped layer:
 batch 4, seqlen 8192, d_inner 5120, d_state 16, bf16 x/delta/z/B/C, fp32
 A/D/bias/state.  Inputs are seeded synthetic tensors already resident in HBM.
+Other workloads (--workload): 0 tiny fp32, 1 SM1 (d_state 1) fp32 through
+sm1_scan_fwd, 2 mamba-130m-shaped layer, 4 decode (ssm_state_update over 64
+independent layer states, one launch per layer).
 
-Prints one JSON line:  value = B*T*D elements per second (wall clock over the
-timed steps), plus the roofline of the scan kernel (HIP events on the stream
-the kernel runs on) and the fp64 CPU oracle timed on a bounded sample of the
-same workload.
+Prints one JSON line:  value = elements (B*T*D; decode B*D per layer) per
+second over the timed steps, the roofline of the dominant kernel (timed with
+HIP events on the stream it is launched on) and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 0..4] [--extra]
+    python bench.py [--steps K] [--warmup W] [--workload 0..4]
+
+Profiling helpers (no GPU work of their own beyond what they state):
+    python bench.py --copy-calibration       1 GiB device copy, for the
+                                             FETCH_SIZE / WRITE_SIZE scale
+    python bench.py --summarize-stats DIR    rocprofv3 kernel_stats.csv -> text
+    python bench.py --summarize-traffic ...  two --pmc runs + copy runs -> text
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -25,26 +37,49 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-N_CU, CLOCK_HZ, LANES_PER_CU = 256, 2.4e9, 64   # 4 SIMD x 16 lanes, plain fp32 VALU
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
+# fp32 VALU issue slots of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+# (157.3 TFLOP/s = this x 2 for packed-fp32 x 2 for FMA; packed fp32 is not used.)
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Minimal fp32 VALU lane-slots of the fast (bf16 io) arithmetic:
+#  per (t, d, n) item: Delta*A mul, exp2 (half rate: 2 slots), Delta*x*B mul,
+#  decay*h + u fma, C*h fma  -> 6
+#  per (t, d) element: 3 widening converts, softplus (add bias, scale, exp2 (2),
+#  add, log2 (2), scale, max, add = 10), Delta*x, SiLU (scale, exp2 (2), add,
+#  rcp (2), mul = 7), D*x fma, gate mul, rounding convert -> 24
+SLOTS_PER_ITEM, SLOTS_PER_ELEM = 6, 24
+COPY_CAL_BYTES = 1 << 30
+
+SOURCES = {
+    "scan": ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "sm1": ["selective_scan_ssm_amd/csrc/sm1_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+}
+KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "sm1": "sm1_chunked_kernel", "decode": "state_update_kernel"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, io_bytes, with_last=True):
-    """Bytes the method must move once: x, delta, z read + y written per
-    element; B, C per (b, t, n); A, D, bias per channel; h0 / last_state."""
+def algorithmic_bytes(w, io_bytes):
+    """Bytes the method must move once per launch: x, delta, z read and y
+    written per element; B, C per (b, t, n); A, D, delta_bias per channel;
+    h0 read (if given) and last_state written.  Decode: the state is read and
+    written in place; T = 1."""
     Bt, T, Dd, N = w.batch, w.seqlen, w.d_inner, w.d_state
-    b = 4 * Bt * T * Dd * io_bytes            # x, delta, z, y
-    b += 2 * Bt * T * N * io_bytes            # B, C
-    b += (Dd * N + 2 * Dd) * 4                # A, D, delta_bias
+    b = 4 * Bt * T * Dd * io_bytes
+    b += 2 * Bt * T * N * io_bytes
+    b += (Dd * N + 2 * Dd) * 4
     if w.h0_kind != "none":
         b += Bt * Dd * N * 4
-    if with_last:
-        b += Bt * Dd * N * 4
+    b += Bt * Dd * N * 4
     return b
+
+
+def valu_slots(w):
+    items = w.batch * w.seqlen * w.d_inner * w.d_state
+    return items * SLOTS_PER_ITEM + w.batch * w.seqlen * w.d_inner * SLOTS_PER_ELEM
 
 
 def source_hash(files):
@@ -55,42 +90,55 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-SCAN_SOURCES = ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"]
+def traffic_file(kind, wname):
+    return os.path.join(ROOT, "profiles", f"{KERNEL_PREFIX[kind]}_{wname}_traffic.txt")
 
 
-def traffic_from_profile(kernel_files, name):
+def read_kv(path):
+    out = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip()
+    return out
+
+
+def traffic_from_profile(kind, wname):
     """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE,
-    scaled by the copy-kernel factor), if the stored measurement was taken on
-    the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    each scaled by the copy-kernel factor), if the stored measurement was taken
+    on the current kernel source; else None."""
+    path = traffic_file(kind, wname)
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    if rec.get("source_hash") != source_hash(kernel_files):
+    rec = read_kv(path)
+    if rec.get("source_hash") != source_hash(SOURCES[kind]):
         return None
-    return rec.get("bytes_per_launch")
+    return int(float(rec["bytes_per_launch"]))
 
 
 def cpu_baseline(inp, w, seconds_target):
-    """The fp64 oracle on a bounded sample of the workload: all batches and the
-    first `nd` channels over the full sequence."""
+    """The fp64 oracle on a bounded sample of the workload: all batches over
+    the full sequence and the first `nd` channels (decode: one layer)."""
     import numpy as np
     import oracle
     from selective_scan_ssm_amd import inputs as gen
     io = inp["io"]
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     threads = max(1, min(16, threads))
-    # oracle speed is about 7e6 elements/s per core at d_state 16: size the
-    # sample to roughly `seconds_target` core-seconds of work
+    # about 7e6 elements/s per core at d_state 16: size the sample to about
+    # `seconds_target` core-seconds
     per_core = 7e6 * 16 / max(1, w.d_state)
     nd = int(min(w.d_inner, max(64, seconds_target * per_core / (w.batch * w.seqlen))))
-    sl = lambda a: np.ascontiguousarray(gen.to_f64(a[:, :, :nd], io))
+    sl = lambda a: None if a is None else np.ascontiguousarray(gen.to_f64(a[:, :, :nd], io))
     x, dl, z = sl(inp["x"]), sl(inp["delta"]), sl(inp["z"])
     B, C = gen.to_f64(inp["B"], io), gen.to_f64(inp["C"], io)
-    h0 = None if inp["h0"] is None else inp["h0"][:, :nd]
+    h0 = None if inp["h0"] is None else np.ascontiguousarray(inp["h0"][:, :nd])
+    bias = None if inp["delta_bias"] is None else inp["delta_bias"][:nd]
+    D = None if inp["D"] is None else inp["D"][:nd]
     t0 = time.perf_counter()
-    oracle.selective_scan(x, dl, inp["A"][:nd], B, C, D=inp["D"][:nd], z=z,
-                          delta_bias=inp["delta_bias"][:nd], h0=h0, threads=threads)
+    oracle.selective_scan(x, dl, np.ascontiguousarray(inp["A"][:nd]), B, C, D=D, z=z,
+                          delta_bias=bias, h0=h0, threads=threads)
     dt = time.perf_counter() - t0
     elems = w.batch * w.seqlen * nd
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
@@ -98,64 +146,118 @@ def cpu_baseline(inp, w, seconds_target):
                       f"({elems} elements, d_state {w.d_state}), fp64, {dt:.2f} s wall"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
+def upload(a, io, dev):
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import inputs as gen
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if io == gen.BF16 and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the selective scan here runs on a single MI355X "
-              "and has no multi-GPU path (sharding is described in DESIGN.md); use --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
 
+def device_set(inp, dev, decode=False, sm1=False):
+    """One device-resident input/output set (decode: T axis dropped; SM1: N axis dropped)."""
+    import torch
+    from selective_scan_ssm_amd import inputs as gen
+    io = inp["io"]
+    t = {}
+    for k in ("x", "delta", "z"):
+        a = inp[k]
+        if a is not None and decode:
+            a = a[:, 0, :]
+        t[k] = upload(a, io, dev)
+    for k in ("B", "C"):
+        a = inp[k]
+        if decode:
+            a = a[:, 0, :]
+        elif sm1:
+            a = a[:, :, 0]
+        t[k] = upload(a, io, dev)
+    for k in ("A", "D", "delta_bias", "h0"):
+        a = inp[k]
+        if a is not None and sm1 and k in ("A", "h0"):
+            a = a[..., 0]
+        t[k] = upload(a, gen.F32, dev)
+    t["y"] = torch.empty_like(t["x"])
+    return t
+
+
+def bench_workload(args, dev):
     import numpy as np
     import torch
     from selective_scan_ssm_amd import _lib, ops
     from selective_scan_ssm_amd import inputs as gen
 
-    _lib.load()
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    dev = torch.device("cuda:0")
+    lib = _lib.load()
     w = gen.WORKLOADS[args.workload]
-    if w.kind != "scan":
-        raise SystemExit("the bench step is the forward scan; pick workload 0, 2 or 3")
-    log(f"[bench] generating workload {args.workload} ({w.name})")
-    inp = gen.workload_inputs(args.workload)
+    kind = {"scan": "scan", "sm1": "sm1", "decode": "decode"}[w.kind]
+    io = w.io
+    io_code = _lib.SSM_BF16 if io == gen.BF16 else _lib.SSM_F32
+    log(f"[bench] workload {args.workload} ({w.name}): generating inputs")
+    inp0 = gen.workload_inputs(args.workload)
+    stream = torch.cuda.current_stream(dev)      # the stream ops.* launch on
 
-    def up(a, io):
-        if a is None:
-            return None
-        if io == gen.BF16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    if kind == "decode":
+        sets = [device_set(inp0, dev, decode=True)]
+        for layer in range(1, w.layers):
+            sets.append(device_set(gen.workload_inputs(args.workload, layer=layer), dev, decode=True))
+        # the state is updated in place: keep it in the set
+        for s in sets:
+            s["state"] = s["h0"]
+        launches = w.layers
 
-    io = inp["io"]
-    t = {k: up(inp[k], io) for k in ("x", "delta", "z", "B", "C")}
-    t.update({k: up(inp[k], gen.F32) for k in ("A", "D", "delta_bias", "h0")})
-    y = torch.empty_like(t["x"])
-    last = torch.empty((w.batch, w.d_inner, w.d_state), dtype=torch.float32, device=dev)
-    need = _lib.load().ssm_scan_workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state,
-                                                 _lib.SSM_BF16 if io == gen.BF16 else _lib.SSM_F32)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        # validate every layer's tensors once through the wrapper, then queue the
+        # 64 launches straight through the C ABI so host overhead stays below a
+        # launch's duration
+        for s in sets:
+            ops.state_update(s["state"], s["x"], s["delta"], s["A"], s["B"], s["C"], D=s["D"],
+                             z=s["z"], delta_bias=s["delta_bias"], out=s["y"])
+        sid = stream.cuda_stream
+        p = lambda t: None if t is None else t.data_ptr()
+        calls = [(p(s["state"]), p(s["x"]), p(s["delta"]), p(s["delta_bias"]), 1, p(s["A"]), p(s["B"]),
+                  p(s["C"]), p(s["D"]), p(s["z"]), p(s["y"]), w.batch, w.d_inner, w.d_state, io_code, sid)
+                 for s in sets]
+        fn = lib.ssm_state_update
 
-    def step():
-        ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                     delta_bias=t["delta_bias"], h0=t["h0"], return_last_state=True, out=y,
-                     last_state_out=last, workspace=ws)
+        def step():
+            for c in calls:
+                rc = fn(*c)
+                if rc:
+                    raise RuntimeError(lib.ssm_status_string(rc).decode())
+    else:
+        # rotate input sets until their footprint exceeds the 256 MB last-level
+        # cache, so no launch reads inputs a previous launch left cached
+        io_b = 2 if io == gen.BF16 else 4
+        foot = algorithmic_bytes(w, io_b)
+        nset = max(1, math.ceil(600e6 / foot)) if args.rotate is None else args.rotate
+        sets = [device_set(inp0, dev, sm1=(kind == "sm1")) for _ in range(nset)]
+        N = w.d_state
+        for s in sets:
+            shape = (w.batch, w.d_inner) if kind == "sm1" else (w.batch, w.d_inner, N)
+            s["last"] = torch.empty(shape, dtype=torch.float32, device=dev)
+        if kind == "sm1":
+            need = lib.sm1_scan_workspace_bytes(w.batch, w.seqlen, w.d_inner, io_code)
+        else:
+            need = lib.ssm_scan_workspace_bytes(w.batch, w.seqlen, w.d_inner, N, io_code)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        launches = 1
+        cur = [0]
+
+        def step():
+            s = sets[cur[0] % len(sets)]
+            cur[0] += 1
+            fn = ops.sm1_scan_fwd if kind == "sm1" else ops.scan_fwd
+            fn(s["x"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+               delta_bias=s["delta_bias"], h0=s["h0"], return_last_state=True, out=s["y"],
+               last_state_out=s["last"], workspace=ws)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)   # the stream ops launch on
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
@@ -167,35 +269,189 @@ def main():
         e.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    step_ms = [s.elapsed_time(e) for s, e in ev]
     ms_per_step = wall * 1e3 / args.steps
-    kern_ms = float(np.mean(launch_ms))
+    launch_ms = float(np.mean(step_ms)) / launches     # mean launch duration, events on `stream`
 
-    elems = w.batch * w.seqlen * w.d_inner
-    io_bytes = 2 if io == gen.BF16 else 4
-    alg = algorithmic_bytes(w, io_bytes)
-    achieved = alg / (kern_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(SCAN_SOURCES, f"scan_fwd_w{args.workload}")
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "ssm_scan_fwd (bf16->fp32 B/C widen + scan)",
-            "launch_ms_mean": round(kern_ms, 4), "launch_ms_min": round(min(launch_ms), 4),
-            "algorithmic_bytes_per_launch": alg}
+    elems = w.batch * w.seqlen * w.d_inner * launches
+    io_b = 2 if io == gen.BF16 else 4
+    alg = algorithmic_bytes(w, io_b)
+    hbm_gbs = alg / (launch_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(kind, w.name)
+    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "sm1": "sm1_scan_fwd (sm1_chunked_kernel)",
+             "decode": "ssm_state_update (state_update_kernel)"}[kind]
+    if kind == "scan" and w.d_state > 1:
+        slots = valu_slots(w)
+        ach = slots / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                "unit": "T fp32 VALU lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
+                "traffic": traffic, "kernel": kname,
+                "algorithmic_slots_per_launch": slots,
+                "hbm_achieved_GBs": round(hbm_gbs, 1), "hbm_peak_GBs": HBM_PEAK_GBS,
+                "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname}
+    roof.update({"launch_ms_mean": round(launch_ms, 5),
+                 "launch_ms_min": round(min(step_ms) / launches, 5),
+                 "algorithmic_bytes_per_launch": alg})
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a sample)")
-        cpu = cpu_baseline(inp, w, args.cpu_seconds)
+        cpu = cpu_baseline(inp0, w, args.cpu_seconds)
 
-    rec = {"metric": "selective-scan fwd elements/s (B*T*D) and achieved HBM GB/s as % of peak",
-           "value": elems / (ms_per_step * 1e-3), "unit": "elements/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
-           "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
-                      "d_inner": w.d_inner, "d_state": w.d_state, "io": io,
-                      "state": "fp32", "seed": args.workload},
-           "roofline": roof, "cpu_baseline": cpu}
+    cfg = {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.d_inner,
+           "d_state": w.d_state, "io": io, "state": "fp32", "seed": args.workload}
+    if kind == "decode":
+        cfg["layers"] = w.layers
+    elif len(sets) > 1:
+        cfg["rotated_input_sets"] = len(sets)
+    return {"metric": "selective-scan fwd elements/s (B*T*D) and achieved HBM GB/s as % of peak",
+            "value": elems / (ms_per_step * 1e-3), "unit": "elements/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
+def copy_calibration():
+    """A plain device copy of COPY_CAL_BYTES, three times: under rocprofv3
+    --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the counter scale."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_CAL_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_CAL_BYTES}), flush=True)
+
+
+# ---------------------------------------------------------------- summaries
+
+def _rows(d, name):
+    paths = glob.glob(os.path.join(d, "**", name), recursive=True)
+    if not paths:
+        raise SystemExit(f"no {name} under {d}")
+    with open(sorted(paths)[-1], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_stats(d, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run (kernel_stats.csv)."""
+    rows = _rows(d, "*kernel_stats.csv")
+    lines = [f"command: {command}", "", "| kernel | calls | total ms | avg us | min us | max us | % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        if name.startswith("void "):
+            name = name[5:]
+        short = name.split("(")[0][:110]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['TotalDurationNs'])/1e6:.3f} | "
+                     f"{float(r['AverageNs'])/1e3:.2f} | {float(r['MinNs'])/1e3:.2f} | "
+                     f"{float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def _counter_per_dispatch(d, counter, kernel_prefix):
+    vals = {}
+    for r in _rows(d, "*counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        kn = r["Kernel_Name"]
+        if kernel_prefix not in kn:
+            continue
+        key = r["Dispatch_Id"]
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_prefix} in {d}")
+    v = sorted(vals.values())
+    return v[len(v) // 2], len(v)
+
+
+def summarize_traffic(kind, wname, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands,
+                      alg_bytes):
+    pre = KERNEL_PREFIX[kind]
+    cf, _ = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "")
+    cw, _ = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "")
+    kib = COPY_CAL_BYTES / 1024
+    f_fac, w_fac = kib / cf, kib / cw
+    kf, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", pre)
+    kw, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", pre)
+    fb, wb = kf * f_fac * 1024, kw * w_fac * 1024
+    total = fb + wb
+    lines = [
+        f"# HBM traffic of {pre} on {wname}, from rocprofv3 --pmc (median over dispatches)",
+        *[f"# command: {c}" for c in commands],
+        f"kernel: {pre}",
+        f"workload: {wname}",
+        f"source_hash: {source_hash(SOURCES[kind])}",
+        f"copy_calibration_bytes: {COPY_CAL_BYTES}",
+        f"copy_FETCH_SIZE_KiB: {cf:.1f}",
+        f"copy_WRITE_SIZE_KiB: {cw:.1f}",
+        f"fetch_scale: {f_fac:.4f}",
+        f"write_scale: {w_fac:.4f}",
+        f"kernel_FETCH_SIZE_KiB: {kf:.1f}  ({nf} dispatches)",
+        f"kernel_WRITE_SIZE_KiB: {kw:.1f}  ({nw} dispatches)",
+        f"fetch_bytes: {fb:.0f}",
+        f"write_bytes: {wb:.0f}",
+        f"bytes_per_launch: {total:.0f}",
+        f"algorithmic_bytes_per_launch: {alg_bytes}",
+        f"traffic_over_algorithmic: {total / alg_bytes:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--rotate", type=int, default=None, help="input sets to rotate (default: enough to exceed 600 MB)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample size in core-seconds")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "COMMAND"))
+    ap.add_argument("--summarize-traffic", nargs=7,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
+                             "KERNEL_COMMAND", "COPY_COMMAND"))
+    args = ap.parse_args()
+
+    if args.summarize_stats:
+        sys.stdout.write(summarize_stats(*args.summarize_stats))
+        return
+    if args.summarize_traffic:
+        from selective_scan_ssm_amd import inputs as gen
+        wl, fd, wd, cfd, cwd, kcmd, ccmd = args.summarize_traffic
+        w = gen.WORKLOADS[int(wl)]
+        kind = {"scan": "scan", "sm1": "sm1", "decode": "decode"}[w.kind]
+        alg = algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
+        cmds = [kcmd.replace("{COUNTER}", c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        cmds += [ccmd.replace("{COUNTER}", c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        text = summarize_traffic(kind, w.name, fd, wd, cfd, cwd, cmds, alg)
+        with open(traffic_file(kind, w.name), "w") as f:
+            f.write(text)
+        sys.stdout.write(text)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the selective scan here runs on a single MI355X "
+              "and has no multi-GPU path; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from selective_scan_ssm_amd import _lib
+    _lib.load()
+    rec = bench_workload(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)
 
 
