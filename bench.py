@@ -55,7 +55,7 @@ SOURCES = {
     "sm1": ["selective_scan_ssm_amd/csrc/sm1_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
-KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "sm1": "sm1_chunked_kernel", "decode": "state_update_kernel"}
+KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "sm1": "sm1_scan_kernel", "decode": "state_update_kernel"}
 
 
 def log(*a):
@@ -278,7 +278,7 @@ def bench_workload(args, dev):
     alg = algorithmic_bytes(w, io_b)
     hbm_gbs = alg / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(kind, w.name)
-    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "sm1": "sm1_scan_fwd (sm1_chunked_kernel)",
+    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
              "decode": "ssm_state_update (state_update_kernel)"}[kind]
     if kind == "scan" and w.d_state > 1:
         slots = valu_slots(w)

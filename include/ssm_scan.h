@@ -102,8 +102,11 @@ size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, 
  * cumulative product and a cumulative sum).  Same definition as ssm_scan_fwd
  * with d_state = 1; the shapes drop the state axis:
  *   A: (d_inner)   B, C: (batch, seqlen)   h0, last_state: (batch, d_inner).
- * The kernel splits time into chunks scanned in parallel and combines them
- * with the associative (decay, offset) operator, so it needs a workspace.
+ * The kernel splits time into sub-chunks scanned in parallel inside one
+ * workgroup and combines them with the associative (decay, offset) operator.
+ * It needs no workspace (sm1_scan_workspace_bytes returns 0) except for
+ * shapes it hands to the general kernel: seqlen == 0, or 256 rows of d_inner
+ * spanning 2 GiB or more.
  */
 int sm1_scan_fwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
                  const float *A, const void *B, const void *C, const float *D, const void *z,

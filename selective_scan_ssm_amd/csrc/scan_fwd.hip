@@ -133,34 +133,6 @@ __device__ __forceinline__ float scan_step(std::integer_sequence<int, I...>, flo
 // ---- buffer loads / stores.  A wave-uniform descriptor (base and size in
 // SGPRs) plus a per-lane byte offset and a scalar row offset is how gfx950
 // addresses memory without per-lane 64-bit arithmetic.
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, kRsrcWord3);
-}
-
-template <typename T> struct Io;
-template <> struct Io<bf16_t> {
-    using raw = uint16_t;
-    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-    }
-    static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, voff, soff, 0);
-    }
-};
-template <> struct Io<float> {
-    using raw = uint32_t;
-    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-    }
-    static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(v); }
-    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
-    }
-};
 
 #ifndef SSM_SCAN_WAVES_PER_EU
 #define SSM_SCAN_WAVES_PER_EU 2   // occupancy the register allocator may assume
@@ -223,7 +195,7 @@ void scan_fwd_kernel(Params p) {
     const uint32_t voff = col * static_cast<uint32_t>(sizeof(T));
     // stores of lanes past d_inner use an offset beyond the descriptor's
     // range, which the buffer unit drops (no branch around the store)
-    const uint32_t voff_store = active ? voff : 0x80000000u;
+    const uint32_t voff_store = active ? voff : kOffNone;
     const uint32_t row_bytes = static_cast<uint32_t>(dim * static_cast<int64_t>(sizeof(T)));
     float *hslot = p.hbuf + static_cast<int64_t>(tile) * N * kTile;
 

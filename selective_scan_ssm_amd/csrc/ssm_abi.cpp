@@ -179,8 +179,10 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
     if (int r = check_dtype(io_dtype)) return r;
     if (batch < 0 || d_inner < 0 || d_state < 1 || d_state > SSM_MAX_D_STATE) return SSM_ERR_SHAPE;
     const int64_t n_bd = mul3(batch, d_inner, 1), n_bdn = mul3(batch, d_inner, d_state);
-    if (n_bd < 0 || n_bdn < 0 || mul3(batch, d_inner, 4) < 0 || mul3(batch, d_inner, 4) > INT32_MAX * 64LL)
-        return SSM_ERR_SHAPE;
+    // one quad of lanes per chain, 64 chains per workgroup: the grid's lane
+    // count (batch x d_inner rounded up to 64, x 4) must stay below 2^32
+    const int64_t lanes = mul3(batch, (d_inner + 63) / 64 * 64, 4);
+    if (n_bd < 0 || n_bdn < 0 || lanes < 0 || lanes >= (int64_t(1) << 32)) return SSM_ERR_SHAPE;
     if (batch == 0 || d_inner == 0) return SSM_OK;
     if (!state || !x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
     const size_t es = io_size(io_dtype);

@@ -49,6 +49,40 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
     return r;
 }
 
+// ------------------------------------------------------------ buffer access
+// Raw buffer descriptors: 32-bit byte offsets from a per-wave base, and the
+// buffer unit's range check (offset >= num_records) makes loads return 0 and
+// drops stores, so tails and inactive lanes need no branch.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr uint32_t kOffNone = 0x80000000u; // an offset beyond every descriptor's range
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes = 0x7fffffffu) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename T> struct Io;
+template <> struct Io<bf16_t> {
+    using raw = uint16_t;
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, voff, soff, 0);
+    }
+};
+template <> struct Io<float> {
+    using raw = uint32_t;
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(v); }
+    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+};
+
 // ------------------------------------------------------ hardware transcendentals
 // v_exp_f32 computes 2^x, v_log_f32 log2(x), v_rcp_f32 1/x (within 1 ulp).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -117,6 +151,9 @@ struct FastMath {
     // the same step split in two, for kernels that keep the factor between passes
     static __device__ __forceinline__ float factor(float arg) { return fast_exp2(arg); }
     static __device__ __forceinline__ float apply(float f, float h, float u) { return fmaf(f, h, u); }
+    // factor of two runs of steps in sequence (decay product)
+    static __device__ __forceinline__ float compose(float f1, float f2) { return f1 * f2; }
+    static constexpr float kIdentity = 1.0f;
 };
 
 struct PreciseMath {
@@ -134,6 +171,9 @@ struct PreciseMath {
     static __device__ __forceinline__ float decay(float arg) { return expm1_accurate(arg) + 1.0f; }
     static __device__ __forceinline__ float factor(float arg) { return expm1_accurate(arg); }
     static __device__ __forceinline__ float apply(float f, float h, float u) { return fmaf(f, h, h) + u; }
+    // (1 + f1)(1 + f2) - 1 without forming the near-1 products
+    static __device__ __forceinline__ float compose(float f1, float f2) { return fmaf(f1, f2, f1 + f2); }
+    static constexpr float kIdentity = 0.0f;
 };
 
 template <typename T> struct MathFor;

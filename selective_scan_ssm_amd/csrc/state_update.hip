@@ -30,48 +30,84 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
-template <int N, typename T>
-__global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a) {
+// 4 consecutive B or C values of one batch row, widened (VEC path)
+__device__ __forceinline__ void load4_io(const float *p, float (&v)[4]) {
+    const float4 q = *reinterpret_cast<const float4 *>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void load4_io(const bf16_t *p, float (&v)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(p);
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
+// One workgroup = 64 chains (channels cb*64 .. cb*64+63) of one batch row;
+// block index = b * n_cblk + cb.  VEC: d_state 16 with 16-byte aligned state
+// and A rows, so each lane moves its 4 states as one 16-byte access and a
+// wave covers 1 KiB of contiguous state.
+template <int N, typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a, int n_cblk) {
     using M = typename MathFor<T>::type;
     constexpr int NPL = (N + kQuad - 1) / kQuad;   // states per lane
-    const int64_t chains = a.batch * a.dim;
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const int64_t c_raw = gid / kQuad;
-    const int q = static_cast<int>(gid % kQuad);
-    const bool active = c_raw < chains;
-    const int64_t c = active ? c_raw : chains - 1;   // keep the quad's DPP partners valid
-    const int64_t b = c / a.dim, d = c % a.dim;
+    static_assert(!VEC || N == 16, "vector path is for d_state 16");
+    const int b = static_cast<int>(blockIdx.x) / n_cblk;
+    const int cb = static_cast<int>(blockIdx.x) - b * n_cblk;
+    const int tid = threadIdx.x, q = tid % kQuad;
+    const int d_raw = cb * (kThreads / kQuad) + tid / kQuad;
+    const bool active = d_raw < a.dim;
+    const int d = active ? d_raw : static_cast<int>(a.dim) - 1;   // keep the quad's DPP partners valid
+    const int64_t c = static_cast<int64_t>(b) * a.dim + d;          // chain (b, d)
 
     const T *x = static_cast<const T *>(a.x);
     const T *dl = static_cast<const T *>(a.delta);
-    const T *Bm = static_cast<const T *>(a.B);
-    const T *Cm = static_cast<const T *>(a.C);
+    const T *Bm = static_cast<const T *>(a.B) + static_cast<int64_t>(b) * N;
+    const T *Cm = static_cast<const T *>(a.C) + static_cast<int64_t>(b) * N;
+    float *st = a.state + c * N;
+    const float *Ad = a.A + static_cast<int64_t>(d) * N;
 
+    float hs[NPL], Av[NPL], Bv[NPL], Cv[NPL];
+    if constexpr (VEC) {
+        const float4 s4 = *reinterpret_cast<const float4 *>(st + q * 4);
+        const float4 a4 = *reinterpret_cast<const float4 *>(Ad + q * 4);
+        hs[0] = s4.x; hs[1] = s4.y; hs[2] = s4.z; hs[3] = s4.w;
+        Av[0] = a4.x; Av[1] = a4.y; Av[2] = a4.z; Av[3] = a4.w;
+        load4_io(Bm + q * 4, Bv);
+        load4_io(Cm + q * 4, Cv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int n = q * NPL + i;
+            const int nn = n < N ? n : N - 1;
+            hs[i] = st[nn];
+            Av[i] = Ad[nn];
+            Bv[i] = to_f32(Bm[nn]);
+            Cv[i] = to_f32(Cm[nn]);
+        }
+    }
     const float xv = to_f32(x[c]);
     const float v = to_f32(dl[c]) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
     const float dt = a.softplus ? M::softplus(v) : v;
     const float dtx = dt * xv;
 
     float part = 0.0f;
-    float hs[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int n = q * NPL + i;
-        if (n < N) hs[i] = a.state[c * N + n];
-    }
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int n = q * NPL + i;
         if (n < N) {
-            const float hn = M::step(dt * M::prep_A(a.A[d * N + n]), hs[i], dtx * to_f32(Bm[b * N + n]));
-            hs[i] = hn;
-            part = fmaf(to_f32(Cm[b * N + n]), hn, part);
+            hs[i] = M::step(dt * M::prep_A(Av[i]), hs[i], dtx * Bv[i]);
+            part = fmaf(Cv[i], hs[i], part);
         }
     }
+    if (active) {
+        if constexpr (VEC) {
+            *reinterpret_cast<float4 *>(st + q * 4) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+        } else {
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int n = q * NPL + i;
-        if (n < N && active) a.state[c * N + n] = hs[i];
+            for (int i = 0; i < NPL; ++i) {
+                const int n = q * NPL + i;
+                if (n < N) st[n] = hs[i];
+            }
+        }
     }
     const float acc = quad_sum(part);
     if (q == 0 && active) {
@@ -81,10 +117,19 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a) {
     }
 }
 
+bool aligned_to(const void *p, size_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
+
 template <int N, typename T> hipError_t launch(const StepArgs &a, hipStream_t s) {
-    const int64_t threads = a.batch * a.dim * kQuad;
-    const dim3 grid(static_cast<unsigned>((threads + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL((state_update_kernel<N, T>), grid, dim3(kThreads), 0, s, a);
+    const int n_cblk = static_cast<int>((a.dim + kThreads / kQuad - 1) / (kThreads / kQuad));
+    const dim3 grid(static_cast<unsigned>(a.batch * n_cblk));
+    if constexpr (N == 16) {
+        const size_t bc = sizeof(T) * 4;
+        if (aligned_to(a.state, 16) && aligned_to(a.A, 16) && aligned_to(a.B, bc) && aligned_to(a.C, bc)) {
+            hipLaunchKernelGGL((state_update_kernel<N, T, true>), grid, dim3(kThreads), 0, s, a, n_cblk);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((state_update_kernel<N, T, false>), grid, dim3(kThreads), 0, s, a, n_cblk);
     return hipGetLastError();
 }
 

@@ -114,11 +114,14 @@ def test_scan_empty_is_noop(lib):
     assert call_scan(lib, scan_args(batch=0, x=None, delta=None, y=None)) == OK
 
 
-def test_sm1_bf16_needs_its_workspace(lib):
-    need = lib.sm1_scan_workspace_bytes(2, 16, 8, BF16)
+def test_sm1_workspace(lib):
+    # the tiled SM1 kernel keeps every carry inside one workgroup: no workspace
+    assert lib.sm1_scan_workspace_bytes(8, 4096, 1536, F32) == 0
+    assert lib.sm1_scan_workspace_bytes(2, 16, 8, BF16) == 0
+    # d_inner too wide for its 32-bit round offsets: handed to the general kernel
+    need = lib.sm1_scan_workspace_bytes(1, 1, 1 << 22, F32)
     assert need > 0
-    assert call_sm1(lib, scan_args(dstate=1, io=BF16, ws=None, ws_bytes=0)) == EWS
-    assert call_sm1(lib, scan_args(dstate=1, io=BF16, ws_bytes=need - 1)) == EWS
+    assert call_sm1(lib, scan_args(batch=1, seqlen=1, dstate=1, dim=1 << 22, ws=None, ws_bytes=0)) == EWS
 
 
 def test_workspace_sizes(lib):
@@ -155,6 +158,8 @@ def call_step(lib, a):
     (dict(h0=None), ENULL), (dict(x=None), ENULL), (dict(y=None), ENULL),
     (dict(dstate=17), ESHAPE), (dict(dstate=0), ESHAPE), (dict(io=3), EDTYPE),
     (dict(h0=0x7f0000000002), EALIGN), (dict(batch=0), OK), (dict(dim=0), OK),
+    # grid of one lane quad per chain, 64 chains per workgroup: below 2^32 lanes
+    (dict(batch=1 << 16, dim=1 << 14), ESHAPE), (dict(batch=1, dim=1 << 30), ESHAPE),
 ])
 def test_state_update_validation(lib, over, code):
     assert call_step(lib, scan_args(**over)) == code

@@ -132,6 +132,16 @@ def test_sm1_no_optional_inputs():
     check(inp, softplus=False, sm1=True, tag="sm1-plain")
 
 
+@pytest.mark.parametrize("softplus,with_z", [(True, False), (False, True)])
+def test_sm1_flag_variants(softplus, with_z):
+    # the SM1 kernel is specialised on (softplus, gate): cover the two mixed cases
+    inp = gen.make_inputs(2, 600, 48, 1, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=405,
+                          with_z=with_z, with_bias=softplus)
+    if not softplus:
+        inp["delta"] = np.abs(inp["delta"]) * np.float32(0.02)
+    check(inp, softplus=softplus, sm1=True, tag=f"sm1-sp{int(softplus)}-z{int(with_z)}")
+
+
 def test_sm1_bf16():
     check(gen.make_inputs(2, 500, 96, 1, io=gen.BF16, a_kind="sm1", h0_kind="normal", seed=304),
           sm1=True, tag="sm1-bf16")
