@@ -138,7 +138,9 @@ __device__ __forceinline__ float scan_step(std::integer_sequence<int, I...>, flo
 #define SSM_SCAN_WAVES_PER_EU 2   // occupancy the register allocator may assume
 #endif
 
-template <int N, int NW, typename T>
+// FL = 1: softplus and gate known to be on at compile time (the common
+// Mamba call); FL = 0 reads both flags at run time.
+template <int N, int NW, typename T, int FL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, SSM_SCAN_WAVES_PER_EU)))
 void scan_fwd_kernel(Params p) {
     using M = typename MathFor<T>::type;
@@ -178,8 +180,8 @@ void scan_fwd_kernel(Params p) {
     const int64_t t_end = (t_begin + p.seg_len < seqlen) ? t_begin + p.seg_len : seqlen;
     const int steps = static_cast<int>(t_end - t_begin);   // steps of this segment (32-bit compares stay scalar)
     const int nb = (steps + kTB - 1) / kTB;
-    const bool softplus_on = p.softplus != 0;
-    const bool has_z = p.z != nullptr;
+    const bool softplus_on = FL ? true : p.softplus != 0;
+    const bool has_z = FL ? true : p.z != nullptr;
     uint32_t *progress = p.words + 64;
 
     // descriptors start at this segment's first row (and, for the (t, d)
@@ -242,33 +244,38 @@ void scan_fwd_kernel(Params p) {
         const int s = j * kTB + k;
         return static_cast<uint32_t>(s < 0 ? 0 : (s < steps ? s : steps - 1));
     };
-    auto load_pre = [&](Pre &r, int jp, int je) {
+    // full: blocks jp and je lie wholly inside the segment (no clamping)
+    auto load_pre = [&](Pre &r, int jp, int je, auto full) {
+        constexpr bool F = decltype(full)::value;
+        auto step_of = [&](int j, int k) -> uint32_t {
+            return F ? static_cast<uint32_t>(j * kTB + k) : clamp_step(j, k);
+        };
 #pragma unroll
         for (int kk = 0; kk < PB; ++kk) {
-            const uint32_t sp = clamp_step(jp, w + kk * NW) * row_bytes;
+            const uint32_t sp = step_of(jp, w + kk * NW) * row_bytes;
             r.dP[kk] = Io<T>::load(rd, voff, sp);
             r.xP[kk] = Io<T>::load(rx, voff, sp);
-            const uint32_t se = clamp_step(je, w + kk * NW) * row_bytes;
+            const uint32_t se = step_of(je, w + kk * NW) * row_bytes;
             r.xE[kk] = Io<T>::load(rx, voff, se);
-            r.zE[kk] = Io<T>::load(rz, voff, se);
+            if (has_z) r.zE[kk] = Io<T>::load(rz, voff, se);
         }
         // B then C of the block; each loop has a uniform descriptor
 #pragma unroll
         for (int m = 0; m < BC_PER; ++m) {
             int e = tid + (m % BC_HALF) * NT;
             e = e < kTB * N ? e : kTB * N - 1;
-            const uint32_t off = (clamp_step(jp, e / N) * N + e % N) * static_cast<uint32_t>(sizeof(T));
+            const uint32_t off = (step_of(jp, e / N) * N + e % N) * static_cast<uint32_t>(sizeof(T));
             r.bc[m] = Io<T>::load(m < BC_HALF ? rB : rC, off, 0);
         }
     };
 
     // produce block j into LDS buffer j%2
-    auto produce = [&](const Pre &r, int j) {
+    auto produce = [&](const Pre &r, int j, auto full) {
         const int buf = j & 1;
 #pragma unroll
         for (int kk = 0; kk < PB; ++kk) {
             const int k = w + kk * NW;
-            const bool tv = j * kTB + k < steps;     // wave-uniform
+            const bool tv = decltype(full)::value || j * kTB + k < steps;     // wave-uniform
             const float v = Io<T>::f32(r.dP[kk]) + bias;
             float dt = softplus_on ? M::softplus(v) : v;
             dt = tv ? dt : 0.0f;                     // past the end: identity step
@@ -315,19 +322,31 @@ void scan_fwd_kernel(Params p) {
                 o.bcr[k][kBCV - 1]);
     };
 
-    // finish block j: sum the partials, D skip, gate, store
-    auto finish = [&](const Pre &r, int j) {
+    // finish block j: sum the partials (read early, at the top of the
+    // iteration, so their LDS latency hides behind the produce phase), D skip,
+    // gate, store
+    struct Partials {
+        float v[PB][NW];
+    };
+    auto finish_read = [&](Partials &pv, int j) {
         const int buf = j & 1;
+#pragma unroll
+        for (int kk = 0; kk < PB; ++kk)
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) pv.v[kk][ww] = sP[buf][ww][w + kk * NW][lane];
+    };
+    auto finish = [&](const Pre &r, const Partials &pv, int j, auto full) {
 #pragma unroll
         for (int kk = 0; kk < PB; ++kk) {
             const int k = w + kk * NW;
             const int sl = j * kTB + k;
             float acc = 0.0f;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) acc += sP[buf][ww][k][lane];
+            for (int ww = 0; ww < NW; ++ww) acc += pv.v[kk][ww];
             float out = fmaf(Dd, Io<T>::f32(r.xE[kk]), acc);
             if (has_z) out *= silu(Io<T>::f32(r.zE[kk]));
-            if (sl < steps) Io<T>::store(out, ry, voff_store, static_cast<uint32_t>(sl) * row_bytes);
+            if (decltype(full)::value || sl < steps)
+                Io<T>::store(out, ry, voff_store, static_cast<uint32_t>(sl) * row_bytes);
         }
     };
 
@@ -339,44 +358,54 @@ void scan_fwd_kernel(Params p) {
     // iterations are straight-line code, which lets the compiler count
     // outstanding loads exactly instead of draining them at every branch.
     ScanOps so;
-    auto iteration = [&](auto produce_on, auto finish_on, auto scan_on, Pre &r, int j) {
+    auto iteration = [&](auto produce_on, auto finish_on, auto scan_on, auto full, Pre &r, int j) {
+        Partials pv;
         if constexpr (decltype(scan_on)::value) scan_read(so, j - 1);
-        if constexpr (decltype(produce_on)::value) produce(r, j);
-        if constexpr (decltype(finish_on)::value) finish(r, j - 2);
-        load_pre(r, j + 2, j);
+        if constexpr (decltype(finish_on)::value) finish_read(pv, j - 2);
+        if constexpr (decltype(produce_on)::value) produce(r, j, full);
+        if constexpr (decltype(finish_on)::value) finish(r, pv, j - 2, full);
+        load_pre(r, j + 2, j, full);
         if constexpr (decltype(scan_on)::value) scan(so, j - 1);
         __syncthreads();
     };
     using on = std::true_type;
     using off = std::false_type;
+    const int nfull = steps / kTB;               // blocks with no step past the segment
     Pre r0, r1;
-    load_pre(r0, 0, 0);
-    load_pre(r1, 1, 0);
+    load_pre(r0, 0, 0, off{});
+    load_pre(r1, 1, 0, off{});
     if (nb >= 3) {
-        iteration(on{}, off{}, off{}, r0, 0);
-        iteration(on{}, off{}, on{}, r1, 1);
+        iteration(on{}, off{}, off{}, off{}, r0, 0);
+        iteration(on{}, off{}, on{}, off{}, r1, 1);
         int j = 2;
+        // steady state over whole blocks: no clamping, no store guards
+        for (; j + 3 < nfull; j += 2) {
+            iteration(on{}, on{}, on{}, on{}, r0, j);
+            iteration(on{}, on{}, on{}, on{}, r1, j + 1);
+        }
         for (; j + 1 < nb; j += 2) {
-            iteration(on{}, on{}, on{}, r0, j);
-            iteration(on{}, on{}, on{}, r1, j + 1);
+            iteration(on{}, on{}, on{}, off{}, r0, j);
+            iteration(on{}, on{}, on{}, off{}, r1, j + 1);
         }
         if (j < nb) {          // one steady iteration left (even j): drain ends on set r1
-            iteration(on{}, on{}, on{}, r0, j);
-            iteration(off{}, on{}, on{}, r1, nb);
-            iteration(off{}, on{}, off{}, r0, nb + 1);
+            iteration(on{}, on{}, on{}, off{}, r0, j);
+            iteration(off{}, on{}, on{}, off{}, r1, nb);
+            iteration(off{}, on{}, off{}, off{}, r0, nb + 1);
         } else {               // j == nb (even): drain ends on set r0
-            iteration(off{}, on{}, on{}, r0, nb);
-            iteration(off{}, on{}, off{}, r1, nb + 1);
+            iteration(off{}, on{}, on{}, off{}, r0, nb);
+            iteration(off{}, on{}, off{}, off{}, r1, nb + 1);
         }
     } else {
         // short segments: the same phases with run-time conditions
         for (int j = 0; j < nb + 2; ++j) {
             Pre &r = (j & 1) ? r1 : r0;
             const bool do_scan = j >= 1 && j - 1 < nb;
+            Partials pv;
             if (do_scan) scan_read(so, j - 1);
-            if (j < nb) produce(r, j);
-            if (j >= 2) finish(r, j - 2);
-            load_pre(r, j + 2, j);
+            if (j >= 2) finish_read(pv, j - 2);
+            if (j < nb) produce(r, j, off{});
+            if (j >= 2) finish(r, pv, j - 2, off{});
+            load_pre(r, j + 2, j, off{});
             if (do_scan) scan(so, j - 1);
             __syncthreads();
         }
@@ -408,7 +437,7 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *w, int64_t n
     if (i < n) w[i] = 0u;
 }
 
-template <int N, typename T> hipError_t launch(const ScanArgs &a, hipStream_t s) {
+template <int N, typename T, int FL> hipError_t launch(const ScanArgs &a, hipStream_t s) {
     constexpr int NW = waves_for<N>();
     const Layout l = make_layout(a.batch, a.seqlen, a.dim, N, sizeof(T));
     char *ws = static_cast<char *>(a.workspace);
@@ -425,14 +454,17 @@ template <int N, typename T> hipError_t launch(const ScanArgs &a, hipStream_t s)
     hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
                        p.words, nclear);
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(l.n_tiles) * l.n_segs);
-    hipLaunchKernelGGL((scan_fwd_kernel<N, NW, T>), dim3(grid), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((scan_fwd_kernel<N, NW, T, FL>), dim3(grid), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
+    // d_state 16 with softplus and gate (the Mamba layer) gets the kernel
+    // with both flags fixed at compile time
+    if (a.dstate == 16 && a.softplus && a.z) return launch<16, T, 1>(a, s);
     switch (a.dstate) {
 #define SSM_CASE(NN) \
-    case NN: return launch<NN, T>(a, s);
+    case NN: return launch<NN, T, 0>(a, s);
         SSM_CASE(1) SSM_CASE(2) SSM_CASE(3) SSM_CASE(4) SSM_CASE(5) SSM_CASE(6) SSM_CASE(7)
         SSM_CASE(8) SSM_CASE(9) SSM_CASE(10) SSM_CASE(11) SSM_CASE(12) SSM_CASE(13)
         SSM_CASE(14) SSM_CASE(15) SSM_CASE(16)

@@ -136,7 +136,11 @@ struct FastMath {
     // at most ~1e-4 relative there) and e - e^2/2 below (truncation < e^2/3).
     static __device__ __forceinline__ float softplus(float v) {
         const float e = fast_exp2(-fabsf(v) * kLog2e);
-        const float l = e >= (1.0f / 1024.0f) ? fast_log2(1.0f + e) * kLn2 : fmaf(-0.5f * e, e, e);
+        float lg = fast_log2(1.0f + e) * kLn2;
+        // both candidates are computed and one is selected: without this the
+        // compiler branches around the log, which costs more than the log
+        asm volatile("" : "+v"(lg));
+        const float l = e >= (1.0f / 1024.0f) ? lg : fmaf(-0.5f * e, e, e);
         return fmaxf(v, 0.0f) + l;
     }
     // the per-state decay factor exp(Delta * A), with A pre-scaled by log2(e)
