@@ -52,6 +52,12 @@
 #ifndef SSM_SCAN_MIN_SEG_STEPS
 #define SSM_SCAN_MIN_SEG_STEPS 512
 #endif
+#ifndef SSM_SCAN_SMALL_TILES
+// Below this many channel tiles (the CU count of an MI355X) every tile has a
+// CU to itself: d_state 16 is then split over 8 waves for more waves per
+// SIMD, and sequences are not cut into segments (nothing to balance).
+#define SSM_SCAN_SMALL_TILES 256
+#endif
 
 namespace ssm {
 namespace {
@@ -85,7 +91,7 @@ Layout make_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
     l.n_dt = static_cast<int>((dim + kTile - 1) / kTile);
     l.n_tiles = static_cast<int>(batch * l.n_dt);
     const int64_t blocks = (seqlen + kTB - 1) / kTB;
-    int64_t segs = seqlen / SSM_SCAN_MIN_SEG_STEPS;
+    int64_t segs = l.n_tiles < SSM_SCAN_SMALL_TILES ? 1 : seqlen / SSM_SCAN_MIN_SEG_STEPS;
     segs = segs < 1 ? 1 : (segs > SSM_SCAN_MAX_SEGS ? SSM_SCAN_MAX_SEGS : segs);
     // row offsets inside a segment are 32-bit buffer offsets: keep a segment
     // of (seqlen, d_inner) below 1 GiB
@@ -437,8 +443,7 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *w, int64_t n
     if (i < n) w[i] = 0u;
 }
 
-template <int N, typename T, int FL> hipError_t launch(const ScanArgs &a, hipStream_t s) {
-    constexpr int NW = waves_for<N>();
+template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a, hipStream_t s) {
     const Layout l = make_layout(a.batch, a.seqlen, a.dim, N, sizeof(T));
     char *ws = static_cast<char *>(a.workspace);
     Params p;
@@ -461,10 +466,14 @@ template <int N, typename T, int FL> hipError_t launch(const ScanArgs &a, hipStr
 template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     // d_state 16 with softplus and gate (the Mamba layer) gets the kernel
     // with both flags fixed at compile time
-    if (a.dstate == 16 && a.softplus && a.z) return launch<16, T, 1>(a, s);
+    if (a.dstate == 16 && a.softplus && a.z) {
+        const int64_t tiles = a.batch * ((a.dim + kTile - 1) / kTile);
+        if (tiles < SSM_SCAN_SMALL_TILES) return launch<16, 8, T, 1>(a, s);
+        return launch<16, waves_for<16>(), T, 1>(a, s);
+    }
     switch (a.dstate) {
 #define SSM_CASE(NN) \
-    case NN: return launch<NN, T, 0>(a, s);
+    case NN: return launch<NN, waves_for<NN>(), T, 0>(a, s);
         SSM_CASE(1) SSM_CASE(2) SSM_CASE(3) SSM_CASE(4) SSM_CASE(5) SSM_CASE(6) SSM_CASE(7)
         SSM_CASE(8) SSM_CASE(9) SSM_CASE(10) SSM_CASE(11) SSM_CASE(12) SSM_CASE(13)
         SSM_CASE(14) SSM_CASE(15) SSM_CASE(16)

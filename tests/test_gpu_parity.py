@@ -55,6 +55,15 @@ def test_workload3_mamba2p8b_bf16_sampled():
     check(gen.workload_inputs(3), d_index=d_index, tag="w3")
 
 
+@pytest.mark.parametrize("io,tol", [(gen.BF16, None), (gen.F32, None)])
+def test_segments_ragged_many_tiles(io, tol):
+    # 256 channel tiles and a ragged 1500-step sequence: the 4-wave kernel with
+    # the sequence cut into chained segments, the last block partial
+    inp = gen.make_inputs(2, 1500, 8192, 16, io=io, h0_kind="normal", seed=309)
+    d_index = np.r_[0:8, 4000:4008, 8184:8192]
+    check(inp, d_index=d_index, tol=tol, tag=f"segments-{io}")
+
+
 def test_workload4_decode_bf16_two_layers():
     from selective_scan_ssm_amd import ops
     for layer in range(2):
