@@ -158,9 +158,15 @@ void scan_fwd_kernel(Params p) {
     constexpr int BC_HALF = (kTB * N + NT - 1) / NT;   // B (or C) values of a block staged per thread
     constexpr int BC_PER = 2 * BC_HALF;
 
-    __shared__ float2 sDX[2][kTB][kTile];       // (Delta, Delta*x)
-    __shared__ float sP[2][NW][kTB][kTile];     // partial readouts per wave
-    __shared__ float sBC[2][2][kTB][N];         // [buf][B|C][t][n] in fp32
+    // LDS layouts are chosen for 128-bit reads: (Delta, Delta*x) of two
+    // consecutive steps per lane and slot, partial readouts of four
+    // consecutive steps, and B / C transposed to [state][step] (row stride
+    // kTB + 4 floats keeps the 2*NPW rows a wave reads in distinct banks).
+    static_assert(kTB % 4 == 0, "steps per block must be a multiple of 4");
+    constexpr int kBCS = kTB + 4;
+    __shared__ float4 sDX[2][kTB / 2][kTile];   // (Delta, Delta*x) of steps 2i, 2i+1
+    __shared__ float4 sP[2][NW][kTB / 4][kTile];// partial readouts of steps 4i .. 4i+3
+    __shared__ float sBC[2][2 * N][kBCS];       // [buf][n (B) | N + n (C)][step], fp32
     __shared__ uint32_t s_ticket;
 
     using raw = typename Io<T>::raw;
@@ -246,22 +252,22 @@ void scan_fwd_kernel(Params p) {
         raw xE[PB], zE[PB];    // finish phase: x, z
         raw bc[BC_PER];        // B/C values this thread stages
     };
-    auto clamp_step = [&](int j, int k) -> uint32_t {   // segment step of step k of block j, clamped
+    auto clamp_step = [&](int j, int k) -> uint32_t __attribute__((always_inline)) {   // segment step of step k of block j, clamped
         const int s = j * kTB + k;
         return static_cast<uint32_t>(s < 0 ? 0 : (s < steps ? s : steps - 1));
     };
     // full: blocks jp and je lie wholly inside the segment (no clamping)
-    auto load_pre = [&](Pre &r, int jp, int je, auto full) {
+    auto load_pre = [&](Pre &r, int jp, int je, auto full) __attribute__((always_inline)) {
         constexpr bool F = decltype(full)::value;
-        auto step_of = [&](int j, int k) -> uint32_t {
+        auto step_of = [&](int j, int k) -> uint32_t __attribute__((always_inline)) {
             return F ? static_cast<uint32_t>(j * kTB + k) : clamp_step(j, k);
         };
 #pragma unroll
         for (int kk = 0; kk < PB; ++kk) {
-            const uint32_t sp = step_of(jp, w + kk * NW) * row_bytes;
+            const uint32_t sp = step_of(jp, w * PB + kk) * row_bytes;
             r.dP[kk] = Io<T>::load(rd, voff, sp);
             r.xP[kk] = Io<T>::load(rx, voff, sp);
-            const uint32_t se = step_of(je, w + kk * NW) * row_bytes;
+            const uint32_t se = step_of(je, w * PB + kk) * row_bytes;
             r.xE[kk] = Io<T>::load(rx, voff, se);
             if (has_z) r.zE[kk] = Io<T>::load(rz, voff, se);
         }
@@ -276,21 +282,21 @@ void scan_fwd_kernel(Params p) {
     };
 
     // produce block j into LDS buffer j%2
-    auto produce = [&](const Pre &r, int j, auto full) {
+    auto produce = [&](const Pre &r, int j, auto full) __attribute__((always_inline)) {
         const int buf = j & 1;
 #pragma unroll
         for (int kk = 0; kk < PB; ++kk) {
-            const int k = w + kk * NW;
+            const int k = w * PB + kk;
             const bool tv = decltype(full)::value || j * kTB + k < steps;     // wave-uniform
             const float v = Io<T>::f32(r.dP[kk]) + bias;
             float dt = softplus_on ? M::softplus(v) : v;
             dt = tv ? dt : 0.0f;                     // past the end: identity step
-            sDX[buf][k][lane] = make_float2(dt, dt * Io<T>::f32(r.xP[kk]));
+            reinterpret_cast<float2 *>(&sDX[buf][k / 2][lane])[k % 2] = make_float2(dt, dt * Io<T>::f32(r.xP[kk]));
         }
 #pragma unroll
         for (int m = 0; m < BC_PER; ++m) {
             const int e = tid + (m % BC_HALF) * NT;
-            if (e < kTB * N) sBC[buf][m < BC_HALF ? 0 : 1][e / N][e % N] = Io<T>::f32(r.bc[m]);
+            if (e < kTB * N) sBC[buf][(m < BC_HALF ? 0 : N) + e % N][e / N] = Io<T>::f32(r.bc[m]);
         }
     };
 
@@ -298,34 +304,56 @@ void scan_fwd_kernel(Params p) {
     // Delta*x per step, and B, C of the wave's states laid out so that lane q
     // of every 16-lane row holds value q of the step (B in lanes [0, NPW), C
     // after them).  The steps then run on registers only; B and C reach the
-    // arithmetic through DPP row broadcasts.
+    // arithmetic through DPP row broadcasts.  Every read is 128 bits.
     struct ScanOps {
         float2 dx[kTB];
         float bcr[kTB][kBCV];
     };
-    auto scan_read = [&](ScanOps &o, int j) {
+    auto scan_read = [&](ScanOps &o, int j) __attribute__((always_inline)) {
         const int buf = j & 1;
         const int q = lane & 15;
 #pragma unroll
-        for (int k = 0; k < kTB; ++k) {
-            o.dx[k] = sDX[buf][k][lane];
-            if constexpr (kBCV == 1) {
-                const int qq = q < 2 * NPW ? q : 0;
-                o.bcr[k][0] = sBC[buf][qq < NPW ? 0 : 1][k][n0 + (qq < NPW ? qq : qq - NPW)];
-            } else {
-                const int qq = q < NPW ? q : 0;
-                o.bcr[k][0] = sBC[buf][0][k][n0 + qq];
-                o.bcr[k][1] = sBC[buf][1][k][n0 + qq];
-            }
+        for (int k2 = 0; k2 < kTB / 2; ++k2) {
+            const float4 v = sDX[buf][k2][lane];
+            o.dx[2 * k2] = make_float2(v.x, v.y);
+            o.dx[2 * k2 + 1] = make_float2(v.z, v.w);
         }
+        // the state row each lane reads: B rows for lanes [0, NPW), C rows
+        // after them (kBCV == 1); kBCV == 2 keeps B and C in two registers
+        int mrow[kBCV];
+        if constexpr (kBCV == 1) {
+            const int qq = q < 2 * NPW ? q : 0;
+            mrow[0] = qq < NPW ? n0 + qq : N + n0 + qq - NPW;
+        } else {
+            const int qq = q < NPW ? q : 0;
+            mrow[0] = n0 + qq;
+            mrow[1] = N + n0 + qq;
+        }
+#pragma unroll
+        for (int v = 0; v < kBCV; ++v)
+#pragma unroll
+            for (int k4 = 0; k4 < kTB / 4; ++k4) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(&sBC[buf][mrow[v]][4 * k4]);
+                o.bcr[4 * k4][v] = c4.x;
+                o.bcr[4 * k4 + 1][v] = c4.y;
+                o.bcr[4 * k4 + 2][v] = c4.z;
+                o.bcr[4 * k4 + 3][v] = c4.w;
+            }
     };
-    auto scan = [&](const ScanOps &o, int j) {
+    auto scan = [&](const ScanOps &o, int j) __attribute__((always_inline)) {
         const int buf = j & 1;
 #pragma unroll
-        for (int k = 0; k < kTB; ++k)
-            sP[buf][w][k][lane] = scan_step<M, NPW, (kBCV == 1 ? NPW : 0)>(
-                std::make_integer_sequence<int, NPW>{}, h, A2, o.dx[k].x, o.dx[k].y, o.bcr[k][0],
-                o.bcr[k][kBCV - 1]);
+        for (int k4 = 0; k4 < kTB / 4; ++k4) {
+            float part[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 4 * k4 + i;
+                part[i] = scan_step<M, NPW, (kBCV == 1 ? NPW : 0)>(
+                    std::make_integer_sequence<int, NPW>{}, h, A2, o.dx[k].x, o.dx[k].y, o.bcr[k][0],
+                    o.bcr[k][kBCV - 1]);
+            }
+            sP[buf][w][k4][lane] = make_float4(part[0], part[1], part[2], part[3]);
+        }
     };
 
     // finish block j: sum the partials (read early, at the top of the
@@ -334,17 +362,21 @@ void scan_fwd_kernel(Params p) {
     struct Partials {
         float v[PB][NW];
     };
-    auto finish_read = [&](Partials &pv, int j) {
+    auto finish_read = [&](Partials &pv, int j) __attribute__((always_inline)) {
         const int buf = j & 1;
-#pragma unroll
-        for (int kk = 0; kk < PB; ++kk)
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) pv.v[kk][ww] = sP[buf][ww][w + kk * NW][lane];
-    };
-    auto finish = [&](const Pre &r, const Partials &pv, int j, auto full) {
+        const float *base = reinterpret_cast<const float *>(&sP[buf][0][0][0]);
 #pragma unroll
         for (int kk = 0; kk < PB; ++kk) {
-            const int k = w + kk * NW;
+            const int k = w * PB + kk;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww)
+                pv.v[kk][ww] = base[((ww * (kTB / 4) + k / 4) * kTile + lane) * 4 + k % 4];
+        }
+    };
+    auto finish = [&](const Pre &r, const Partials &pv, int j, auto full) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < PB; ++kk) {
+            const int k = w * PB + kk;
             const int sl = j * kTB + k;
             float acc = 0.0f;
 #pragma unroll
@@ -364,7 +396,7 @@ void scan_fwd_kernel(Params p) {
     // iterations are straight-line code, which lets the compiler count
     // outstanding loads exactly instead of draining them at every branch.
     ScanOps so;
-    auto iteration = [&](auto produce_on, auto finish_on, auto scan_on, auto full, Pre &r, int j) {
+    auto iteration = [&](auto produce_on, auto finish_on, auto scan_on, auto full, Pre &r, int j) __attribute__((always_inline)) {
         Partials pv;
         if constexpr (decltype(scan_on)::value) scan_read(so, j - 1);
         if constexpr (decltype(finish_on)::value) finish_read(pv, j - 2);
