@@ -141,7 +141,7 @@ __device__ __forceinline__ float scan_step(std::integer_sequence<int, I...>, flo
 // addresses memory without per-lane 64-bit arithmetic.
 
 #ifndef SSM_SCAN_WAVES_PER_EU
-#define SSM_SCAN_WAVES_PER_EU 2   // occupancy the register allocator may assume
+#define SSM_SCAN_WAVES_PER_EU 1   // occupancy the register allocator may assume
 #endif
 
 // FL = 1: softplus and gate known to be on at compile time (the common
