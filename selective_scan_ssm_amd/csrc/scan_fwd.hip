@@ -52,6 +52,9 @@
 #ifndef SSM_SCAN_MIN_SEG_STEPS
 #define SSM_SCAN_MIN_SEG_STEPS 512
 #endif
+#ifndef SSM_ROWS_MAX_SEGS
+#define SSM_ROWS_MAX_SEGS 4
+#endif
 #ifndef SSM_SCAN_SMALL_TILES
 // Below this many channel tiles (the CU count of an MI355X) every tile has a
 // CU to itself: d_state 16 is then split over 8 waves for more waves per
@@ -86,13 +89,21 @@ struct Layout {
     size_t hbuf_off, total;
 };
 
+// the row kernel (d_state 16, at least SSM_SCAN_SMALL_TILES tiles) takes
+// the sequence in at most SSM_ROWS_MAX_SEGS segments; the other kernel in at
+// most SSM_SCAN_MAX_SEGS
+bool rows_path(int64_t batch, int64_t dim, int64_t dstate) {
+    return dstate == 16 && batch * ((dim + kTile - 1) / kTile) >= SSM_SCAN_SMALL_TILES;
+}
+
 Layout make_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t esize) {
     Layout l{};
+    const int64_t max_segs = rows_path(batch, dim, dstate) ? SSM_ROWS_MAX_SEGS : SSM_SCAN_MAX_SEGS;
     l.n_dt = static_cast<int>((dim + kTile - 1) / kTile);
     l.n_tiles = static_cast<int>(batch * l.n_dt);
     const int64_t blocks = (seqlen + kTB - 1) / kTB;
     int64_t segs = l.n_tiles < SSM_SCAN_SMALL_TILES ? 1 : seqlen / SSM_SCAN_MIN_SEG_STEPS;
-    segs = segs < 1 ? 1 : (segs > SSM_SCAN_MAX_SEGS ? SSM_SCAN_MAX_SEGS : segs);
+    segs = segs < 1 ? 1 : (segs > max_segs ? max_segs : segs);
     // row offsets inside a segment are 32-bit buffer offsets: keep a segment
     // of (seqlen, d_inner) below 1 GiB
     const int64_t max_rows = (int64_t(1) << 30) / (dim * esize > 0 ? dim * esize : 1);
@@ -104,7 +115,9 @@ Layout make_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
     auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
     // [0, 256): ticket + error word; [256, hbuf_off): per-tile progress
     l.hbuf_off = 256 + up(static_cast<size_t>(l.n_tiles) * sizeof(uint32_t));
-    l.total = l.hbuf_off + up(static_cast<size_t>(l.n_tiles) * dstate * kTile * sizeof(float));
+    // carried states: 8 bytes each (the row kernel tags every value with its
+    // segment; the other kernel uses the first half of the slab as floats)
+    l.total = l.hbuf_off + up(static_cast<size_t>(l.n_tiles) * dstate * kTile * sizeof(uint64_t));
     return l;
 }
 
@@ -464,6 +477,328 @@ void scan_fwd_kernel(Params p) {
     }
 }
 
+// ===========================================================================
+// d_state 16: the row kernel.
+//
+// A wave owns 16 channels and all 16 states of each: lane = 16 * r + c holds
+// states [4r, 4r + 4) of channel c, so a 16-lane DPP row is one state group
+// and a lane column is one channel.  Waves share nothing and never wait on
+// each other; within a wave, the per-(t, d) work and the readout sum over
+// states cross the four rows with the gfx950 lane-swap instructions
+// (v_permlane16_swap / v_permlane32_swap), not with LDS:
+//   * per group of 4 steps, row r discretises step kRowStep[r] of the group
+//     (softplus of delta + bias, Delta*x) and an all-gather of the four rows
+//     gives every lane the four steps (3 swaps per value);
+//   * B and C of the block, staged in this wave's own LDS slice, reach the
+//     arithmetic through DPP row broadcasts (lane q < 4 of row r holds
+//     B[4r + q], lanes 4..7 hold C[4r + q - 4]);
+//   * the four steps' partial readouts are summed across rows by a
+//     reduce-scatter (3 swaps, 3 adds) that leaves the total of step
+//     kRowStep[r] in row r, which then applies the D skip and the gate and
+//     stores it.
+// x, delta and z of a group are loaded two blocks ahead.  Long sequences are
+// cut into segments handed on through the workspace, as in the kernel above.
+constexpr int kRowTB = 16;                   // steps per block (four groups of four)
+#ifndef SSM_ROWS_WG_PER_CU
+// persistent workgroups (4 waves each) per CU.  One: no more workgroups than
+// the 320 tiles of the 2.8b layer can keep busy, so a job never waits on a
+// predecessor that has not finished
+#define SSM_ROWS_WG_PER_CU 1
+#endif
+constexpr int kRowBCS = kRowTB + 4;          // LDS row stride of the staged B / C (floats)
+constexpr int kRowCOff = 16 * kRowBCS + 16;  // C rows start 16 banks after the B rows
+constexpr int kRowBCWords = kRowCOff + 16 * kRowBCS;
+
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// out[k] = the value row k holds, in every lane of its column
+__device__ __forceinline__ void row_allgather(float v, float (&out)[4]) {
+    float a = v, b = v;
+    swap16(a, b);          // a: rows (0, 0, 2, 2)   b: rows (1, 1, 3, 3)
+    float a2 = a, b2 = b;
+    swap32(a, a2);         // a: row 0 everywhere    a2: row 2 everywhere
+    swap32(b, b2);         // b: row 1 everywhere    b2: row 3 everywhere
+    out[0] = a; out[1] = b; out[2] = a2; out[3] = b2;
+}
+// sum over the four rows of p[0..3]; row r receives the total of p[kRowStep[r]]
+__device__ __forceinline__ float row_reduce_scatter(const float (&p)[4]) {
+    float a = p[0], b = p[1];
+    swap32(a, b);          // a + b: rows (0+2, 1+3) of p0 in rows 0-1, of p1 in rows 2-3
+    const float u = a + b;
+    float c = p[2], e = p[3];
+    swap32(c, e);
+    const float v = c + e; // the same for p2, p3
+    float s0 = u, s1 = v;
+    swap16(s0, s1);        // rows: (u0, v0, u2, v2) and (u1, v1, u3, v3)
+    return s0 + s1;        // totals of p0, p2, p1, p3 in rows 0, 1, 2, 3
+}
+
+template <typename T> struct Wide4;          // four consecutive io elements as one load
+template <> struct Wide4<bf16_t> {
+    typedef uint32_t raw __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    }
+    static __device__ __forceinline__ float get(const raw &v, int i) {
+        const uint32_t wd = v[i / 2];
+        return __uint_as_float(i % 2 ? (wd & 0xffff0000u) : (wd << 16));
+    }
+};
+template <> struct Wide4<float> {
+    typedef uint32_t raw __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    }
+    static __device__ __forceinline__ float get(const raw &v, int i) { return __uint_as_float(v[i]); }
+};
+
+template <typename T, int FL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void scan_rows_kernel(Params p) {
+    using M = typename MathFor<T>::type;
+    using raw = typename Io<T>::raw;
+    using W4 = Wide4<T>;
+    constexpr int N = 16, NPL = 4, NG = kRowTB / 4;
+    constexpr uint32_t es = sizeof(T);
+    __shared__ __attribute__((aligned(16))) float sBC[4][2][kRowBCWords];   // per wave, double-buffered B / C
+    __shared__ uint32_t s_ticket;
+
+    const int64_t seqlen = p.seqlen, dim = p.dim;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int r = lane / 16, c = lane % 16;
+    const int rstep = r == 1 ? 2 : (r == 2 ? 1 : r);   // the step of a group this row discretises / finishes
+    const uint32_t n_jobs = static_cast<uint32_t>(p.n_tiles) * static_cast<uint32_t>(p.n_segs);
+    // Persistent workgroups take (segment, tile) jobs in ticket order, all
+    // tiles' segment s before any segment s + 1: a job's predecessor was
+    // taken by a running workgroup long before, so waits are rare and short,
+    // and every workgroup does the same number of jobs to within one.
+    for (;;) {
+    if (tid == 0) s_ticket = atomicAdd(&p.words[0], 1u);
+    __syncthreads();
+    const uint32_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    if (ticket >= n_jobs) break;
+    const int seg = static_cast<int>(ticket / static_cast<uint32_t>(p.n_tiles));
+    const int tile = static_cast<int>(ticket % static_cast<uint32_t>(p.n_tiles));
+    const int64_t b = tile / p.n_dt;
+    const int64_t d0 = static_cast<int64_t>(tile % p.n_dt) * kTile;
+    const int tcol = w * 16 + c;                        // channel inside the 64-channel tile
+    const bool active = d0 + tcol < dim;
+    const uint32_t col = active ? static_cast<uint32_t>(tcol) : static_cast<uint32_t>(dim - 1 - d0);
+    const int64_t d = d0 + col;
+    const int n0 = r * NPL;
+    const int64_t t_begin = static_cast<int64_t>(seg) * p.seg_len;
+    const int64_t t_end = (t_begin + p.seg_len < seqlen) ? t_begin + p.seg_len : seqlen;
+    const int steps = static_cast<int>(t_end - t_begin);
+    const int nb = (steps + kRowTB - 1) / kRowTB;
+    const int nfull = steps / kRowTB;
+    const bool softplus_on = FL ? true : p.softplus != 0;
+    const bool has_z = FL ? true : p.z != nullptr;
+
+    const int64_t row0 = b * seqlen + t_begin;
+    const int64_t e0 = (row0 * dim + d0) * static_cast<int64_t>(es);
+    const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + e0);
+    const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + e0);
+    const rsrc_t rz = make_rsrc(static_cast<const char *>(has_z ? p.z : p.x) + e0);
+    const rsrc_t ry = make_rsrc(static_cast<char *>(p.y) + e0);
+    // B / C of the segment; rows past its end read 0
+    const uint32_t bc_bytes = static_cast<uint32_t>(steps) * N * es;
+    const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * static_cast<int64_t>(es), bc_bytes);
+    const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * static_cast<int64_t>(es), bc_bytes);
+    const uint32_t row_bytes = static_cast<uint32_t>(dim * static_cast<int64_t>(es));
+    const uint32_t vcol = col * es;
+    const uint32_t voff_full = vcol + static_cast<uint32_t>(rstep) * row_bytes;   // + group row in the scalar offset
+    // carried states of this tile: one 64-bit word per state, the value in
+    // the low half and (segment + 1) of its writer in the high half
+    uint64_t *hslot = reinterpret_cast<uint64_t *>(p.hbuf) + static_cast<int64_t>(tile) * N * kTile;
+    float *bc_lds = sBC[w][0];
+
+    float A2[NPL], h[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) A2[i] = M::prep_A(p.A[d * N + n0 + i]);
+    const float bias = p.bias ? p.bias[d] : 0.0f;
+    const float Dd = p.D ? p.D[d] : 0.0f;
+
+    if (seg == 0) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) h[i] = p.h0 ? p.h0[(b * dim + d) * N + n0 + i] : 0.0f;
+    } else {
+        // Each lane waits for its own four words to carry the previous
+        // segment's tag: value and tag arrive together in one 64-bit atomic,
+        // so no fence (and no cache-wide invalidate or write-back) is needed,
+        // and the waves of the workgroup do not wait for one another.
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            uint64_t *slot = &hslot[(n0 + i) * kTile + tcol];
+            uint64_t v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t spins = 0;
+            while (static_cast<uint32_t>(v >> 32) != static_cast<uint32_t>(seg)) {
+                if (++spins > kSpinLimit) {          // never wait unboundedly
+                    p.words[1] = 1u;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            h[i] = __uint_as_float(static_cast<uint32_t>(v));
+        }
+    }
+
+    // ---- per-lane raw inputs of one block: delta, x, z of step kRowStep[r]
+    // of each group
+    struct Pre {
+        raw d[NG], x[NG], z[NG];
+    };
+    // the segment step this lane touches in group g of block j (clamped when
+    // the block is not whole)
+    auto lane_step = [&](int j, int g) __attribute__((always_inline)) {
+        const int s = j * kRowTB + 4 * g + rstep;
+        return s < steps ? s : steps - 1;
+    };
+    auto load_group = [&](Pre &pr, int j, int g, auto full) __attribute__((always_inline)) {
+        if constexpr (decltype(full)::value) {
+            const uint32_t so = static_cast<uint32_t>(j * kRowTB + 4 * g) * row_bytes;
+            pr.d[g] = Io<T>::load(rd, voff_full, so);
+            pr.x[g] = Io<T>::load(rx, voff_full, so);
+            if (has_z) pr.z[g] = Io<T>::load(rz, voff_full, so);
+        } else {
+            const uint32_t vo = vcol + static_cast<uint32_t>(lane_step(j, g)) * row_bytes;
+            pr.d[g] = Io<T>::load(rd, vo, 0);
+            pr.x[g] = Io<T>::load(rx, vo, 0);
+            if (has_z) pr.z[g] = Io<T>::load(rz, vo, 0);
+        }
+    };
+    // B / C of block j: lane l fetches elements [4l, 4l + 4) of each (16 steps x 16 states)
+    struct BCRaw {
+        typename W4::raw b, c;
+    };
+    auto load_bc = [&](BCRaw &v, int j) __attribute__((always_inline)) {
+        const uint32_t off = (static_cast<uint32_t>(j) * kRowTB * N + 4 * lane) * es;
+        v.b = W4::load(rB, off);
+        v.c = W4::load(rC, off);
+    };
+    auto stash_bc = [&](BCRaw &v, int j) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(v.b), "+v"(v.c));     // widen here, not next to the load
+        float *buf = bc_lds + (j & 1) * kRowBCWords;
+        const int t = (4 * lane) / N, n = (4 * lane) % N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            buf[(n + i) * kRowBCS + t] = W4::get(v.b, i);
+            buf[kRowCOff + (n + i) * kRowBCS + t] = W4::get(v.c, i);
+        }
+    };
+    // the staged row this lane reads: B rows for lanes q < 4 of its DPP row,
+    // C rows for q in [4, 8)
+    const int q = c < 2 * NPL ? c : 0;
+    const int bc_row = q < NPL ? (n0 + q) * kRowBCS : kRowCOff + (n0 + q - NPL) * kRowBCS;
+
+    // one block: four groups; the raw inputs of block j + 2 are loaded into
+    // the same registers right after each group consumed its own
+    auto block = [&](Pre &pr, BCRaw &bcn, int j, auto full) __attribute__((always_inline)) {
+        constexpr bool F = decltype(full)::value;
+        stash_bc(bcn, j + 1);                       // loaded one block ago
+        load_bc(bcn, j + 2);
+        const float *buf = bc_lds + (j & 1) * kRowBCWords + bc_row;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            // pin the first use of this group's raw inputs here: otherwise the
+            // scheduler hoists their widening next to the loads two blocks
+            // ahead and the wave waits for memory it does not need yet
+            if constexpr (sizeof(raw) == 4) {
+                asm volatile("" : "+v"(pr.d[g]), "+v"(pr.x[g]), "+v"(pr.z[g]));
+            } else {
+                uint32_t dd = pr.d[g], xx = pr.x[g], zz = pr.z[g];
+                asm volatile("" : "+v"(dd), "+v"(xx), "+v"(zz));
+                pr.d[g] = static_cast<raw>(dd); pr.x[g] = static_cast<raw>(xx); pr.z[g] = static_cast<raw>(zz);
+            }
+            const int sl = j * kRowTB + 4 * g + rstep;
+            const bool valid = F || sl < steps;
+            const float v = Io<T>::f32(pr.d[g]) + bias;
+            float dt = softplus_on ? M::softplus(v) : v;
+            dt = valid ? dt : 0.0f;                  // past the end: identity step
+            const float xv = Io<T>::f32(pr.x[g]);
+            float dts[4], dtxs[4];
+            row_allgather(dt, dts);
+            row_allgather(dt * xv, dtxs);
+            const float4 bc4 = *reinterpret_cast<const float4 *>(buf + 4 * g);
+            const float bcs[4] = {bc4.x, bc4.y, bc4.z, bc4.w};
+            // group step k lives in row kRowStep^-1(k): 0 -> 0, 1 -> 2, 2 -> 1, 3 -> 3
+            constexpr int src_row[4] = {0, 2, 1, 3};
+            float part[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                part[k] = scan_step<M, NPL, NPL>(std::make_integer_sequence<int, NPL>{}, h, A2,
+                                                 dts[src_row[k]], dtxs[src_row[k]], bcs[k], bcs[k]);
+            float out = fmaf(Dd, xv, row_reduce_scatter(part));
+            if (has_z) out *= silu(Io<T>::f32(pr.z[g]));
+            if constexpr (F) {
+                Io<T>::store(out, ry, active ? voff_full : kOffNone, static_cast<uint32_t>(j * kRowTB + 4 * g) * row_bytes);
+            } else {
+                const uint32_t vo = (active && sl < steps) ? vcol + static_cast<uint32_t>(sl) * row_bytes : kOffNone;
+                Io<T>::store(out, ry, vo, 0);
+            }
+            load_group(pr, j + 2, g, std::integral_constant<bool, F>{});
+            asm volatile("" ::: "memory");
+        }
+    };
+
+    Pre p0, p1;
+    BCRaw bca, bcb;
+    {
+        // Start the job with nothing in flight and issue in the steady
+        // state's order (B/C of block 1 before the inputs of blocks 0 and 1):
+        // the wait counts the compiler derives at the loop head then stay as
+        // partial as inside the loop.
+        __builtin_amdgcn_s_waitcnt(0);
+        using off = std::false_type;
+        load_bc(bca, 0);
+        load_bc(bcb, 1);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            load_group(p0, 0, g, off{});
+            asm volatile("" ::: "memory");           // keep the per-group issue order
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            load_group(p1, 1, g, off{});
+            asm volatile("" ::: "memory");
+        }
+        stash_bc(bca, 0);
+    }
+    // bcb carries block j + 1 into block j (stashed there), then block j + 2
+    int j = 0;
+    for (; j + 1 < nb && j + 3 < nfull; j += 2) {
+        block(p0, bcb, j, std::true_type{});
+        block(p1, bcb, j + 1, std::true_type{});
+    }
+    for (; j + 1 < nb; j += 2) {
+        block(p0, bcb, j, std::false_type{});
+        block(p1, bcb, j + 1, std::false_type{});
+    }
+    if (j < nb) block(p0, bcb, j, std::false_type{});
+
+    if (seg + 1 < p.n_segs) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            __hip_atomic_store(&hslot[(n0 + i) * kTile + tcol],
+                               (static_cast<uint64_t>(seg + 1) << 32) | __float_as_uint(h[i]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if (p.last && active) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) p.last[(b * dim + d) * N + n0 + i] = h[i];
+    }
+    __syncthreads();                                 // every wave is done with s_ticket
+    }
+}
+
 // seqlen == 0: last_state = h0 (or 0)
 __global__ __launch_bounds__(256) void copy_state_kernel(const float *h0, float *last, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -495,13 +830,40 @@ template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a
     return hipGetLastError();
 }
 
+template <typename T, int FL> hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
+    const Layout l = make_layout(a.batch, a.seqlen, a.dim, 16, sizeof(T));
+    char *ws = static_cast<char *>(a.workspace);
+    Params p;
+    p.x = a.x; p.delta = a.delta; p.z = a.z; p.B = a.B; p.C = a.C;
+    p.A = a.A; p.D = a.D; p.bias = a.delta_bias; p.h0 = a.h0;
+    p.y = a.y; p.last = a.last_state;
+    p.words = reinterpret_cast<uint32_t *>(ws);
+    p.hbuf = reinterpret_cast<float *>(ws + l.hbuf_off);
+    p.seqlen = a.seqlen; p.dim = a.dim;
+    p.n_dt = l.n_dt; p.n_tiles = l.n_tiles; p.seg_len = l.seg_len; p.n_segs = l.n_segs;
+    p.softplus = a.softplus;
+    // ticket, error word and the tagged carried states (tag 0 = not written)
+    const int64_t nclear = static_cast<int64_t>(l.total / sizeof(uint32_t));
+    hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
+                       p.words, nclear);
+    // persistent: SSM_ROWS_WG_PER_CU workgroups per CU, never more than jobs
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const int64_t jobs = static_cast<int64_t>(l.n_tiles) * l.n_segs;
+    const int64_t workers = static_cast<int64_t>(cus) * SSM_ROWS_WG_PER_CU;
+    const unsigned grid = static_cast<unsigned>(jobs < workers ? jobs : workers);
+    hipLaunchKernelGGL((scan_rows_kernel<T, FL>), dim3(grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     // d_state 16 with softplus and gate (the Mamba layer) gets the kernel
     // with both flags fixed at compile time
-    if (a.dstate == 16 && a.softplus && a.z) {
-        const int64_t tiles = a.batch * ((a.dim + kTile - 1) / kTile);
-        if (tiles < SSM_SCAN_SMALL_TILES) return launch<16, 8, T, 1>(a, s);
-        return launch<16, waves_for<16>(), T, 1>(a, s);
+    if (a.dstate == 16) {
+        const bool fl = a.softplus && a.z;
+        if (rows_path(a.batch, a.dim, a.dstate)) return fl ? launch_rows<T, 1>(a, s) : launch_rows<T, 0>(a, s);
+        return fl ? launch<16, 8, T, 1>(a, s) : launch<16, 8, T, 0>(a, s);
     }
     switch (a.dstate) {
 #define SSM_CASE(NN) \
