@@ -8,15 +8,18 @@
 //
 // At d_state 16 the scan is bound by VALU issue, not by HBM: every (t, d, n)
 // item needs one v_exp_f32 (half rate on gfx950) and four full-rate ops, while
-// it moves only half a byte of HBM traffic.  The kernel is laid out to spend
-// VALU cycles on little but those items:
+// it moves only half a byte of HBM traffic.  Two kernels live here.
 //
+// scan_rows_kernel (d_state 16, the Mamba layer) is described above its
+// definition: a wave owns 16 channels and all their states, rows of lanes
+// exchange through lane-swap instructions, waves never synchronise, and
+// persistent workgroups take (segment, tile) jobs from a queue.
+//
+// scan_fwd_kernel (every other d_state):
 //   * A workgroup owns a tile of 64 consecutive channels of one batch row
 //     (lane = channel, so every global access of a wave is one contiguous
 //     128-byte (bf16) / 256-byte (fp32) row).  Its NW waves split the d_state
 //     axis: wave w keeps states [w*NPW, (w+1)*NPW) of all 64 chains in VGPRs.
-//     NW = 4 at d_state 16 gives 4x more waves than one lane per chain, with
-//     no cross-lane arithmetic.
 //   * Per block of TB steps the per-element work (softplus of delta + bias,
 //     Delta*x) is done once per (t, d), split over the waves, and shared
 //     through LDS; B and C of the block are widened to fp32 once into LDS and
@@ -43,9 +46,6 @@
 #ifndef SSM_SCAN_TB
 #define SSM_SCAN_TB 16            // steps per pipeline block
 #endif
-#ifndef SSM_SCAN_NW16
-#define SSM_SCAN_NW16 4           // waves splitting d_state = 16
-#endif
 #ifndef SSM_SCAN_MAX_SEGS
 #define SSM_SCAN_MAX_SEGS 8       // most segments per tile
 #endif
@@ -53,12 +53,12 @@
 #define SSM_SCAN_MIN_SEG_STEPS 512
 #endif
 #ifndef SSM_ROWS_MAX_SEGS
-#define SSM_ROWS_MAX_SEGS 4
+#define SSM_ROWS_MAX_SEGS 4       // most segments per tile in the row kernel
 #endif
 #ifndef SSM_SCAN_SMALL_TILES
-// Below this many channel tiles (the CU count of an MI355X) every tile has a
-// CU to itself: d_state 16 is then split over 8 waves for more waves per
-// SIMD, and sequences are not cut into segments (nothing to balance).
+// Below this many channel tiles (the CU count of an MI355X) every tile of
+// scan_fwd_kernel has a CU to itself: sequences are then not cut into
+// segments (nothing to balance).
 #define SSM_SCAN_SMALL_TILES 256
 #endif
 
@@ -70,7 +70,7 @@ constexpr int kTile = 64;                    // channels per workgroup (one per 
 constexpr uint32_t kSpinLimit = 1u << 22;    // bounded wait on the previous segment
 
 template <int N> constexpr int waves_for() {
-    return N == 16 ? SSM_SCAN_NW16 : (N % 4 == 0 ? 4 : (N % 2 == 0 ? 2 : 1));
+    return N % 4 == 0 ? 4 : (N % 2 == 0 ? 2 : 1);
 }
 
 struct Params {
@@ -89,20 +89,20 @@ struct Layout {
     size_t hbuf_off, total;
 };
 
-// the row kernel (d_state 16, at least SSM_SCAN_SMALL_TILES tiles) takes
-// the sequence in at most SSM_ROWS_MAX_SEGS segments; the other kernel in at
-// most SSM_SCAN_MAX_SEGS
-bool rows_path(int64_t batch, int64_t dim, int64_t dstate) {
-    return dstate == 16 && batch * ((dim + kTile - 1) / kTile) >= SSM_SCAN_SMALL_TILES;
-}
+// d_state 16 runs on the row kernel, whose persistent workgroups balance
+// any number of tiles, in at most SSM_ROWS_MAX_SEGS segments; the other
+// kernel takes at most SSM_SCAN_MAX_SEGS, and none when the tiles do not
+// fill the CUs
+bool rows_path(int64_t dstate) { return dstate == 16; }
 
 Layout make_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t esize) {
     Layout l{};
-    const int64_t max_segs = rows_path(batch, dim, dstate) ? SSM_ROWS_MAX_SEGS : SSM_SCAN_MAX_SEGS;
+    const bool rows = rows_path(dstate);
+    const int64_t max_segs = rows ? SSM_ROWS_MAX_SEGS : SSM_SCAN_MAX_SEGS;
     l.n_dt = static_cast<int>((dim + kTile - 1) / kTile);
     l.n_tiles = static_cast<int>(batch * l.n_dt);
     const int64_t blocks = (seqlen + kTB - 1) / kTB;
-    int64_t segs = l.n_tiles < SSM_SCAN_SMALL_TILES ? 1 : seqlen / SSM_SCAN_MIN_SEG_STEPS;
+    int64_t segs = (!rows && l.n_tiles < SSM_SCAN_SMALL_TILES) ? 1 : seqlen / SSM_SCAN_MIN_SEG_STEPS;
     segs = segs < 1 ? 1 : (segs > max_segs ? max_segs : segs);
     // row offsets inside a segment are 32-bit buffer offsets: keep a segment
     // of (seqlen, d_inner) below 1 GiB
@@ -860,17 +860,13 @@ template <typename T, int FL> hipError_t launch_rows(const ScanArgs &a, hipStrea
 template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     // d_state 16 with softplus and gate (the Mamba layer) gets the kernel
     // with both flags fixed at compile time
-    if (a.dstate == 16) {
-        const bool fl = a.softplus && a.z;
-        if (rows_path(a.batch, a.dim, a.dstate)) return fl ? launch_rows<T, 1>(a, s) : launch_rows<T, 0>(a, s);
-        return fl ? launch<16, 8, T, 1>(a, s) : launch<16, 8, T, 0>(a, s);
-    }
+    if (rows_path(a.dstate)) return (a.softplus && a.z) ? launch_rows<T, 1>(a, s) : launch_rows<T, 0>(a, s);
     switch (a.dstate) {
 #define SSM_CASE(NN) \
     case NN: return launch<NN, waves_for<NN>(), T, 0>(a, s);
         SSM_CASE(1) SSM_CASE(2) SSM_CASE(3) SSM_CASE(4) SSM_CASE(5) SSM_CASE(6) SSM_CASE(7)
         SSM_CASE(8) SSM_CASE(9) SSM_CASE(10) SSM_CASE(11) SSM_CASE(12) SSM_CASE(13)
-        SSM_CASE(14) SSM_CASE(15) SSM_CASE(16)
+        SSM_CASE(14) SSM_CASE(15)
 #undef SSM_CASE
     default: return hipErrorInvalidValue;
     }
