@@ -52,10 +52,19 @@ COPY_CAL_BYTES = 1 << 30
 
 SOURCES = {
     "scan": ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "rows": ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "sm1": ["selective_scan_ssm_amd/csrc/sm1_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
-KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "sm1": "sm1_scan_kernel", "decode": "state_update_kernel"}
+# the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
+KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
+                 "decode": "state_update_kernel"}
+
+
+def kind_of(w):
+    if w.kind == "scan":
+        return "rows" if w.d_state == 16 else "scan"
+    return w.kind
 
 
 def log(*a):
@@ -193,7 +202,7 @@ def bench_workload(args, dev):
 
     lib = _lib.load()
     w = gen.WORKLOADS[args.workload]
-    kind = {"scan": "scan", "sm1": "sm1", "decode": "decode"}[w.kind]
+    kind = kind_of(w)
     io = w.io
     io_code = _lib.SSM_BF16 if io == gen.BF16 else _lib.SSM_F32
     log(f"[bench] workload {args.workload} ({w.name}): generating inputs")
@@ -278,9 +287,10 @@ def bench_workload(args, dev):
     alg = algorithmic_bytes(w, io_b)
     hbm_gbs = alg / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(kind, w.name)
-    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
+    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "rows": "ssm_scan_fwd (scan_rows_kernel)",
+             "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
              "decode": "ssm_state_update (state_update_kernel)"}[kind]
-    if kind == "scan" and w.d_state > 1:
+    if kind in ("scan", "rows") and w.d_state > 1:
         slots = valu_slots(w)
         ach = slots / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
@@ -375,8 +385,8 @@ def _counter_per_dispatch(d, counter, kernel_prefix):
 def summarize_traffic(kind, wname, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands,
                       alg_bytes):
     pre = KERNEL_PREFIX[kind]
-    cf, _ = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "")
-    cw, _ = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "")
+    cf, _ = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     kib = COPY_CAL_BYTES / 1024
     f_fac, w_fac = kib / cf, kib / cw
     kf, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", pre)
@@ -428,7 +438,7 @@ def main():
         from selective_scan_ssm_amd import inputs as gen
         wl, fd, wd, cfd, cwd, kcmd, ccmd = args.summarize_traffic
         w = gen.WORKLOADS[int(wl)]
-        kind = {"scan": "scan", "sm1": "sm1", "decode": "decode"}[w.kind]
+        kind = kind_of(w)
         alg = algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
         cmds = [kcmd.replace("{COUNTER}", c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
         cmds += [ccmd.replace("{COUNTER}", c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
