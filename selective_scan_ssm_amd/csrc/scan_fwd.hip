@@ -654,8 +654,8 @@ void scan_rows_kernel(Params p) {
 
     // ---- per-lane raw inputs of one block: delta, x, z of step kRowStep[r]
     // of each group
-    struct Pre {
-        raw d[NG], x[NG], z[NG];
+    struct Pre {                                     // raw words, zero-extended at the load
+        uint32_t d[NG], x[NG], z[NG];
     };
     // the segment step this lane touches in group g of block j (clamped when
     // the block is not whole)
@@ -711,20 +711,18 @@ void scan_rows_kernel(Params p) {
         for (int g = 0; g < NG; ++g) {
             // pin the first use of this group's raw inputs here: otherwise the
             // scheduler hoists their widening next to the loads two blocks
-            // ahead and the wave waits for memory it does not need yet
-            if constexpr (sizeof(raw) == 4) {
-                asm volatile("" : "+v"(pr.d[g]), "+v"(pr.x[g]), "+v"(pr.z[g]));
-            } else {
-                uint32_t dd = pr.d[g], xx = pr.x[g], zz = pr.z[g];
-                asm volatile("" : "+v"(dd), "+v"(xx), "+v"(zz));
-                pr.d[g] = static_cast<raw>(dd); pr.x[g] = static_cast<raw>(xx); pr.z[g] = static_cast<raw>(zz);
-            }
+            // ahead and the wave waits for memory it does not need yet.  The
+            // pinned words are widened straight from 32 bits (a bf16 load
+            // zero-extends, and the shift drops the upper half anyway).
+            uint32_t dw = pr.d[g], xw = pr.x[g], zw = pr.z[g];   // (raw words)
+            asm volatile("" : "+v"(dw), "+v"(xw), "+v"(zw));
+            auto widen = [](uint32_t wd) { return sizeof(raw) == 4 ? __uint_as_float(wd) : __uint_as_float(wd << 16); };
             const int sl = j * kRowTB + 4 * g + rstep;
             const bool valid = F || sl < steps;
-            const float v = Io<T>::f32(pr.d[g]) + bias;
+            const float v = widen(dw) + bias;
             float dt = softplus_on ? M::softplus(v) : v;
             dt = valid ? dt : 0.0f;                  // past the end: identity step
-            const float xv = Io<T>::f32(pr.x[g]);
+            const float xv = widen(xw);
             float dts[4], dtxs[4];
             row_allgather(dt, dts);
             row_allgather(dt * xv, dtxs);
@@ -738,7 +736,7 @@ void scan_rows_kernel(Params p) {
                 part[k] = scan_step<M, NPL, NPL>(std::make_integer_sequence<int, NPL>{}, h, A2,
                                                  dts[src_row[k]], dtxs[src_row[k]], bcs[k], bcs[k]);
             float out = fmaf(Dd, xv, row_reduce_scatter(part));
-            if (has_z) out *= silu(Io<T>::f32(pr.z[g]));
+            if (has_z) out *= silu(widen(zw));
             if constexpr (F) {
                 Io<T>::store(out, ry, active ? voff_full : kOffNone, static_cast<uint32_t>(j * kRowTB + 4 * g) * row_bytes);
             } else {
