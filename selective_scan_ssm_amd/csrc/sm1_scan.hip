@@ -117,12 +117,12 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
         const rsrc_t rs = io_rsrc(base, r);
         if (r < n_full) {
 #pragma unroll
-            for (int i = 0; i < kL; ++i) dst[i] = Io<T>::load(rs, voff, static_cast<uint32_t>(i) * row_bytes);
+            for (int i = 0; i < kL; ++i) dst[i] = Io<T>::template load<kStream>(rs, voff, static_cast<uint32_t>(i) * row_bytes);
         } else {
             uint32_t vt = voff;
             asm volatile("" : "+v"(vt));             // keep the tail offsets local to this branch
 #pragma unroll
-            for (int i = 0; i < kL; ++i) dst[i] = Io<T>::load(rs, vt + static_cast<uint32_t>(i) * row_bytes, 0);
+            for (int i = 0; i < kL; ++i) dst[i] = Io<T>::template load<kStream>(rs, vt + static_cast<uint32_t>(i) * row_bytes, 0);
         }
     };
     // B and C of a round: the first kRound threads fetch step tid of B, the
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
                 float o = fmaf(cv[k], h, Dc * Io<T>::f32(cur.x[i]));
                 if constexpr (GATE) o *= silu(Io<T>::f32(zr[i]));
                 const uint32_t step = static_cast<uint32_t>(i) * row_bytes;
-                if (full) Io<T>::store(o, ry, vt, step);
-                else Io<T>::store(o, ry, vt + step, 0);
+                if (full) Io<T>::template store<kStream>(o, ry, vt, step);
+                else Io<T>::template store<kStream>(o, ry, vt + step, 0);
             }
         }
     };

@@ -61,28 +61,36 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes = 0
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
+// Cache policy bits of a buffer access: kStream marks data read or written
+// once (non-temporal), which an HBM-bound kernel streams past the caches.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
 template <typename T> struct Io;
 template <> struct Io<bf16_t> {
     using raw = uint16_t;
+    template <int CP = kCached>
     static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, CP);
     }
     static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+    template <int CP = kCached>
     static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, voff, soff, CP);
     }
 };
 template <> struct Io<float> {
     using raw = uint32_t;
+    template <int CP = kCached>
     static __device__ __forceinline__ raw load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, CP);
     }
     static __device__ __forceinline__ float f32(raw v) { return __uint_as_float(v); }
+    template <int CP = kCached>
     static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, CP);
     }
 };
-
 // ------------------------------------------------------ hardware transcendentals
 // v_exp_f32 computes 2^x, v_log_f32 log2(x), v_rcp_f32 1/x (within 1 ulp).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -66,10 +66,12 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a, int 
     const float *Ad = a.A + static_cast<int64_t>(d) * N;
 
     float hs[NPL], Av[NPL], Bv[NPL], Cv[NPL];
+    // the state is read once and written once: non-temporal accesses
+    typedef float f4v __attribute__((ext_vector_type(4)));
     if constexpr (VEC) {
-        const float4 s4 = *reinterpret_cast<const float4 *>(st + q * 4);
+        const f4v s4 = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(st + q * 4));
         const float4 a4 = *reinterpret_cast<const float4 *>(Ad + q * 4);
-        hs[0] = s4.x; hs[1] = s4.y; hs[2] = s4.z; hs[3] = s4.w;
+        hs[0] = s4[0]; hs[1] = s4[1]; hs[2] = s4[2]; hs[3] = s4[3];
         Av[0] = a4.x; Av[1] = a4.y; Av[2] = a4.z; Av[3] = a4.w;
         load4_io(Bm + q * 4, Bv);
         load4_io(Cm + q * 4, Cv);
@@ -100,7 +102,8 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(StepArgs a, int 
     }
     if (active) {
         if constexpr (VEC) {
-            *reinterpret_cast<float4 *>(st + q * 4) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+            const f4v ov = {hs[0], hs[1], hs[2], hs[3]};
+            __builtin_nontemporal_store(ov, reinterpret_cast<f4v *>(st + q * 4));
         } else {
 #pragma unroll
             for (int i = 0; i < NPL; ++i) {

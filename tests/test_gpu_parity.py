@@ -57,8 +57,9 @@ def test_workload3_mamba2p8b_bf16_sampled():
 
 @pytest.mark.parametrize("io,tol", [(gen.BF16, None), (gen.F32, None)])
 def test_segments_ragged_many_tiles(io, tol):
-    # 256 channel tiles and a ragged 1500-step sequence: the 4-wave kernel with
-    # the sequence cut into chained segments, the last block partial
+    # 256 channel tiles and a ragged 1500-step sequence: the d_state-16 kernel
+    # with the sequence cut into segments handed from job to job, the last
+    # block partial
     inp = gen.make_inputs(2, 1500, 8192, 16, io=io, h0_kind="normal", seed=309)
     d_index = np.r_[0:8, 4000:4008, 8184:8192]
     check(inp, d_index=d_index, tol=tol, tag=f"segments-{io}")
@@ -99,6 +100,19 @@ def test_ragged_lengths_bf16(T):
 def test_optional_inputs(flags):
     check(gen.make_inputs(2, 50, 96, 16, io=gen.F32, h0_kind="normal", seed=300, **flags),
           tag=str(flags))
+
+
+@pytest.mark.parametrize("io", [gen.BF16, gen.F32])
+def test_segments_ragged_channels(io):
+    # d_inner 1000 (a partial 64-channel tile and a partial 16-channel wave)
+    # and 2100 steps (4 segments, the last block partial), every output checked
+    check(gen.make_inputs(1, 2100, 1000, 16, io=io, h0_kind="normal", seed=310), tag=f"seg-ragged-{io}")
+
+
+def test_softplus_off_dstate16():
+    inp = gen.make_inputs(2, 300, 80, 16, io=gen.BF16, seed=311, with_bias=False)
+    inp["delta"] = gen.bf16_from_f32(np.abs(gen.f32_from_bf16(inp["delta"])) * np.float32(0.05))
+    check(inp, softplus=False, tag="softplus-off-16")
 
 
 def test_softplus_off():
