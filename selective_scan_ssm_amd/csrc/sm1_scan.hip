@@ -85,27 +85,35 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
     const int64_t bd = static_cast<int64_t>(b) * p.dim;
     float h_in = p.h0 ? p.h0[bd + chc] : 0.0f;
 
-    // Addressing inside a round: row (s*kL + i), column ch.  Lanes past
-    // d_inner use an offset beyond every descriptor's range (loads read 0,
-    // stores are dropped).  Full rounds put the step stride i*row_bytes in the
-    // scalar offset; the last, partial round puts it in the vector offset,
-    // which the buffer unit checks against a descriptor that ends at the last
-    // valid row, so the tail past the sequence reads 0 and stores nothing.
+    // Addressing inside a round: row (s*kL + i), column ch, as a vector offset
+    // from a descriptor that starts at the round's first row and ends at its
+    // last valid one.  The buffer unit checks the vector offset against that
+    // range, so steps past the sequence read 0 and store nothing, and lanes
+    // past d_inner, whose offsets start at 2 GiB, do the same.  The kL offsets
+    // are computed once and kept in registers; every round, full or partial,
+    // uses the same instructions.
     const uint32_t row_bytes = static_cast<uint32_t>(p.dim) * es;
     const uint32_t voff = cvalid ? static_cast<uint32_t>(s * kL) * row_bytes + static_cast<uint32_t>(ch) * es
                                  : kOffNone;
+    uint32_t vo[kL];
+#pragma unroll
+    for (int i = 0; i < kL; ++i) {
+        vo[i] = voff + static_cast<uint32_t>(i) * row_bytes;
+        asm volatile("" : "+v"(vo[i]));              // keep, do not recompute per access
+    }
     const char *xb = static_cast<const char *>(p.x);
     const char *db = static_cast<const char *>(p.delta);
     const char *zb = static_cast<const char *>(GATE ? p.z : p.x);
     char *yb = static_cast<char *>(p.y);
     const char *Bb = static_cast<const char *>(p.B);
     const char *Cb = static_cast<const char *>(p.C);
-    const int n_full = static_cast<int>(p.seqlen / kRound);
     const int n_rounds = static_cast<int>((p.seqlen + kRound - 1) / kRound);
 
+    // steps of round r; 0 past the last round, whose loads then go through an
+    // empty descriptor and return zeros without touching memory
     auto steps_in = [&](int r) {
         const int64_t rem = p.seqlen - static_cast<int64_t>(r) * kRound;
-        return static_cast<int>(rem < kRound ? rem : kRound);
+        return static_cast<int>(rem < kRound ? (rem > 0 ? rem : 0) : kRound);
     };
     auto row_of = [&](int r) { return static_cast<int64_t>(b) * p.seqlen + static_cast<int64_t>(r) * kRound; };
     auto io_rsrc = [&](const char *base, int r) {
@@ -115,19 +123,14 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
     // load kL steps of one tensor for round r
     auto load_steps = [&](R (&dst)[kL], const char *base, int r) {
         const rsrc_t rs = io_rsrc(base, r);
-        if (r < n_full) {
 #pragma unroll
-            for (int i = 0; i < kL; ++i) dst[i] = Io<T>::template load<kStream>(rs, voff, static_cast<uint32_t>(i) * row_bytes);
-        } else {
-            uint32_t vt = voff;
-            asm volatile("" : "+v"(vt));             // keep the tail offsets local to this branch
-#pragma unroll
-            for (int i = 0; i < kL; ++i) dst[i] = Io<T>::template load<kStream>(rs, vt + static_cast<uint32_t>(i) * row_bytes, 0);
-        }
+        for (int i = 0; i < kL; ++i) dst[i] = Io<T>::template load<kStream>(rs, vo[i], 0);
     };
     // B and C of a round: the first kRound threads fetch step tid of B, the
-    // next kRound step tid - kRound of C (the choice is uniform per wave)
-    const bool bc_c = tid >= kRound;
+    // next kRound step tid - kRound of C.  The choice is taken from the wave
+    // index so that the descriptor stays in scalar registers.
+    static_assert(kRound % 64 == 0, "B/C loads split at a wave boundary");
+    const bool bc_c = w >= kRound / 64;
     const int bc_k = bc_c ? tid - kRound : tid;
     auto load_bc = [&](R &v, int r) {
         const uint32_t n = static_cast<uint32_t>(steps_in(r)) * es;
@@ -135,23 +138,23 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
         v = Io<T>::load(make_rsrc((bc_c ? Cb : Bb) + e0, n), static_cast<uint32_t>(bc_k) * es, 0);
     };
     auto stash_bc = [&](R v, int r) {
-        if (tid < 2 * kRound) reinterpret_cast<float *>(sBC[r % 3][bc_c ? 1 : 0])[bc_k] = Io<T>::f32(v);
+        if (w < 2 * kRound / 64) reinterpret_cast<float *>(sBC[r % 3][bc_c ? 1 : 0])[bc_k] = Io<T>::f32(v);
     };
 
-    struct Raw { R d[kL], x[kL]; };
+    struct Raw { R d[kL], x[kL], z[kL]; };
     R bcnext;
     auto round = [&](Raw &cur, Raw &next, int r) {
         const int left = steps_in(r);
-        // this round's gate input, then the next round's delta and x and the
-        // B, C two rounds ahead: all in flight while this round computes
-        R zr[kL];
-        if constexpr (GATE) load_steps(zr, zb, r);
-        if (r + 1 < n_rounds) {
-            load_steps(next.d, db, r + 1);
-            load_steps(next.x, xb, r + 1);
-            stash_bc(bcnext, r + 1);
-            if (r + 2 < n_rounds) load_bc(bcnext, r + 2);
-        }
+        // the next round's delta, x and gate input and the B, C two rounds
+        // ahead go in flight while this round computes.  They are issued on
+        // every round, past the end through empty descriptors, so that the
+        // number of accesses in flight is the same on every path through the
+        // loop and the compiler's wait counts stay exact.
+        load_steps(next.d, db, r + 1);
+        load_steps(next.x, xb, r + 1);
+        if constexpr (GATE) load_steps(next.z, zb, r + 1);
+        if (r + 1 < n_rounds) stash_bc(bcnext, r + 1);
+        load_bc(bcnext, r + 2);
         // ---- pass 1: discretise, keep (f, u), fold into the aggregate
         float f[kL], u[kL];
         float S = 0.0f, H = 0.0f;
@@ -193,9 +196,6 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
         // ---- pass 2: replay from the incoming state, write y
         const rsrc_t ry = make_rsrc(yb + row_of(r) * static_cast<int64_t>(row_bytes),
                                     static_cast<uint32_t>(left) * row_bytes);
-        const bool full = r < n_full;
-        uint32_t vt = voff;
-        asm volatile("" : "+v"(vt));
         float h = hs;
 #pragma unroll
         for (int j = 0; j < kL / 4; ++j) {
@@ -206,24 +206,27 @@ __global__ __launch_bounds__(kThreads) void sm1_scan_kernel(Sm1Params p) {
                 const int i = 4 * j + k;
                 h = M::apply(f[i], h, u[i]);
                 float o = fmaf(cv[k], h, Dc * Io<T>::f32(cur.x[i]));
-                if constexpr (GATE) o *= silu(Io<T>::f32(zr[i]));
-                const uint32_t step = static_cast<uint32_t>(i) * row_bytes;
-                if (full) Io<T>::template store<kStream>(o, ry, vt, step);
-                else Io<T>::template store<kStream>(o, ry, vt + step, 0);
+                if constexpr (GATE) o *= silu(Io<T>::f32(cur.z[i]));
+                Io<T>::template store<kStream>(o, ry, vo[i], 0);
             }
         }
     };
 
-    // prologue: round 0's delta and x, B/C of round 0 in LDS, B/C of round 1 in flight
+    // prologue: round 0's delta, x and z, B/C of round 0 in LDS, B/C of round 1
     Raw ra, rb;
     load_steps(ra.d, db, 0);
     load_steps(ra.x, xb, 0);
+    if constexpr (GATE) load_steps(ra.z, zb, 0);
     {
         R bc0;
         load_bc(bc0, 0);
         stash_bc(bc0, 0);
     }
-    if (n_rounds > 1) load_bc(bcnext, 1);
+    load_bc(bcnext, 1);
+    // Drain the prologue's loads: the loop then starts with nothing in
+    // flight, as after a steady-state round, so the compiler's wait counts
+    // inside the loop stay those of the steady state.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // rounds alternate between the two register sets (no copies)
     for (int r = 0; r < n_rounds; r += 2) {
