@@ -45,9 +45,9 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 #  per (t, d, n) item: Delta*A mul, exp2 (half rate: 2 slots), Delta*x*B mul,
 #  decay*h + u fma, C*h fma  -> 6
 #  per (t, d) element: 3 widening converts, softplus (add bias, scale, exp2 (2),
-#  add, log2 (2), scale, max, add = 10), Delta*x, SiLU (scale, exp2 (2), add,
-#  rcp (2), mul = 7), D*x fma, gate mul, rounding convert -> 24
-SLOTS_PER_ITEM, SLOTS_PER_ELEM = 6, 24
+#  add, log2 (2), max, fma = 9), Delta*x, SiLU (scale, exp2 (2), add,
+#  rcp (2), mul = 7), D*x fma, gate mul, rounding convert -> 23
+SLOTS_PER_ITEM, SLOTS_PER_ELEM = 6, 23
 COPY_CAL_BYTES = 1 << 30
 
 SOURCES = {

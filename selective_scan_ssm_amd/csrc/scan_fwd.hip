@@ -265,14 +265,14 @@ void scan_fwd_kernel(Params p) {
         raw xE[PB], zE[PB];    // finish phase: x, z
         raw bc[BC_PER];        // B/C values this thread stages
     };
-    auto clamp_step = [&](int j, int k) -> uint32_t __attribute__((always_inline)) {   // segment step of step k of block j, clamped
+    auto clamp_step = [&](int j, int k) __attribute__((always_inline)) -> uint32_t {   // segment step of step k of block j, clamped
         const int s = j * kTB + k;
         return static_cast<uint32_t>(s < 0 ? 0 : (s < steps ? s : steps - 1));
     };
     // full: blocks jp and je lie wholly inside the segment (no clamping)
     auto load_pre = [&](Pre &r, int jp, int je, auto full) __attribute__((always_inline)) {
         constexpr bool F = decltype(full)::value;
-        auto step_of = [&](int j, int k) -> uint32_t __attribute__((always_inline)) {
+        auto step_of = [&](int j, int k) __attribute__((always_inline)) -> uint32_t {
             return F ? static_cast<uint32_t>(j * kTB + k) : clamp_step(j, k);
         };
 #pragma unroll
@@ -702,13 +702,20 @@ void scan_rows_kernel(Params p) {
 
     // one block: four groups; the raw inputs of block j + 2 are loaded into
     // the same registers right after each group consumed its own
-    auto block = [&](Pre &pr, BCRaw &bcn, int j, auto full) __attribute__((always_inline)) {
+    // bcq holds the staged B / C of the group about to run: each group reads
+    // the next group's (the first of block j + 1 comes from the other buffer,
+    // stashed at the start of block j) so the LDS latency is covered by a
+    // whole group of arithmetic.
+    auto block = [&](Pre &pr, BCRaw &bcn, float4 &bcq, int j, auto full) __attribute__((always_inline)) {
         constexpr bool F = decltype(full)::value;
         stash_bc(bcn, j + 1);                       // loaded one block ago
         load_bc(bcn, j + 2);
         const float *buf = bc_lds + (j & 1) * kRowBCWords + bc_row;
+        const float *nbuf = bc_lds + ((j + 1) & 1) * kRowBCWords + bc_row;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
+            const float4 bc4 = bcq;
+            bcq = *reinterpret_cast<const float4 *>(g + 1 < NG ? buf + 4 * (g + 1) : nbuf);
             // pin the first use of this group's raw inputs here: otherwise the
             // scheduler hoists their widening next to the loads two blocks
             // ahead and the wave waits for memory it does not need yet.  The
@@ -726,7 +733,6 @@ void scan_rows_kernel(Params p) {
             float dts[4], dtxs[4];
             row_allgather(dt, dts);
             row_allgather(dt * xv, dtxs);
-            const float4 bc4 = *reinterpret_cast<const float4 *>(buf + 4 * g);
             const float bcs[4] = {bc4.x, bc4.y, bc4.z, bc4.w};
             // group step k lives in row kRowStep^-1(k): 0 -> 0, 1 -> 2, 2 -> 1, 3 -> 3
             constexpr int src_row[4] = {0, 2, 1, 3};
@@ -771,17 +777,18 @@ void scan_rows_kernel(Params p) {
         }
         stash_bc(bca, 0);
     }
+    float4 bcq = *reinterpret_cast<const float4 *>(bc_lds + bc_row);   // block 0, group 0
     // bcb carries block j + 1 into block j (stashed there), then block j + 2
     int j = 0;
     for (; j + 1 < nb && j + 3 < nfull; j += 2) {
-        block(p0, bcb, j, std::true_type{});
-        block(p1, bcb, j + 1, std::true_type{});
+        block(p0, bcb, bcq, j, std::true_type{});
+        block(p1, bcb, bcq, j + 1, std::true_type{});
     }
     for (; j + 1 < nb; j += 2) {
-        block(p0, bcb, j, std::false_type{});
-        block(p1, bcb, j + 1, std::false_type{});
+        block(p0, bcb, bcq, j, std::false_type{});
+        block(p1, bcb, bcq, j + 1, std::false_type{});
     }
-    if (j < nb) block(p0, bcb, j, std::false_type{});
+    if (j < nb) block(p0, bcb, bcq, j, std::false_type{});
 
     if (seg + 1 < p.n_segs) {
 #pragma unroll
