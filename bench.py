@@ -58,7 +58,7 @@ SOURCES = {
 }
 # the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
-                 "decode": "state_update_kernel"}
+                 "decode": "state_update_rows_kernel"}
 
 
 def kind_of(w):
@@ -289,7 +289,7 @@ def bench_workload(args, dev):
     traffic = traffic_from_profile(kind, w.name)
     kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "rows": "ssm_scan_fwd (scan_rows_kernel)",
              "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
-             "decode": "ssm_state_update (state_update_kernel)"}[kind]
+             "decode": "ssm_state_update (state_update_rows_kernel)"}[kind]
     if kind in ("scan", "rows") and w.d_state > 1:
         slots = valu_slots(w)
         ach = slots / (launch_ms * 1e-3) / 1e12
@@ -346,7 +346,7 @@ def _rows(d, name):
     paths = glob.glob(os.path.join(d, "**", name), recursive=True)
     if not paths:
         raise SystemExit(f"no {name} under {d}")
-    with open(sorted(paths)[-1], newline="") as f:
+    with open(max(paths, key=os.path.getmtime), newline="") as f:   # the latest run in d
         return list(csv.DictReader(f))
 
 

@@ -25,7 +25,7 @@
 //     carry, kept in a register: no workgroup ever waits on another);
 //   * pass 2 replays the 8 steps from the incoming state and writes
 //     y = (C h + D x) SiLU(z).
-// The next round's delta and x are loaded while the current one computes;
+// The next round's delta, x and z are loaded while the current one computes;
 // B and C of a round are widened once into LDS two rounds ahead.  Every input
 // byte is read once and every output byte written once; one barrier per round.
 // Full-row accesses matter more here than filling every CU: at the SM1
