@@ -52,6 +52,10 @@ def _bind(lib):
     lib.oracle_sm1_scan.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
                                     _dp, _dp, _L, _L, _L, _L, _L]
     lib.oracle_sm1_scan.restype = None
+    lib.oracle_selective_scan_bwd.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp, _dp,
+                                              _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                              _dp, _dp, _L, _L, _L, _L, _L, _L]
+    lib.oracle_selective_scan_bwd.restype = None
     return lib
 
 
@@ -161,3 +165,55 @@ def sm1_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
 
     _run_chains(go, Bt * Dd, threads)
     return y, last
+
+
+def selective_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, dlast=None, threads: int = 1, lib=None):
+    """fp64 gradient of `selective_scan` (ssm_oracle.c, oracle_selective_scan_bwd).
+    dout: (Bt, T, Dd) = dL/dy; dlast: (Bt, Dd, N) = dL/dlast_state or None.
+    Returns a dict with dx, ddelta (Bt,T,Dd), dA (Dd,N), dB, dC (Bt,T,N),
+    dh0 (Bt,Dd,N), and dD, ddelta_bias (Dd,), dz (Bt,T,Dd) when the forward
+    had D, delta_bias, z (else None).  Threads accumulate the summed gradients
+    into separate arrays, added in thread order."""
+    lib = lib or load()
+    x, delta, A, B, C, dout = _f64(x), _f64(delta), _f64(A), _f64(B), _f64(C), _f64(dout)
+    D, z, delta_bias, h0, dlast = _f64(D), _f64(z), _f64(delta_bias), _f64(h0), _f64(dlast)
+    Bt, T, Dd = x.shape
+    N = A.shape[1]
+    assert delta.shape == x.shape and dout.shape == x.shape and A.shape == (Dd, N)
+    assert B.shape == (Bt, T, N) and C.shape == (Bt, T, N)
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (Bt, Dd, N)
+    assert dlast is None or dlast.shape == (Bt, Dd, N)
+    dx = np.zeros_like(x)
+    ddelta = np.zeros_like(x)
+    dz = np.zeros_like(x) if z is not None else None
+    dh0 = np.zeros((Bt, Dd, N))
+    n_chains = Bt * Dd
+    nthr = max(1, min(int(threads), n_chains if n_chains > 0 else 1))
+    step = (n_chains + nthr - 1) // nthr if n_chains > 0 else 1
+    ranges = [(c0, min(c0 + step, n_chains)) for c0 in range(0, max(n_chains, 1), step)]
+    acc = [dict(dA=np.zeros((Dd, N)), dB=np.zeros((Bt, T, N)), dC=np.zeros((Bt, T, N)),
+                dD=np.zeros(Dd), dbias=np.zeros(Dd)) for _ in ranges]
+
+    def go(i):
+        c0, c1 = ranges[i]
+        a = acc[i]
+        lib.oracle_selective_scan_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                      _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(dout), _ptr(dlast), _ptr(dx), _ptr(ddelta),
+                                      _ptr(a["dbias"]), _ptr(a["dA"]), _ptr(a["dB"]), _ptr(a["dC"]),
+                                      _ptr(a["dD"]), _ptr(dz), _ptr(dh0), Bt, T, Dd, N, c0, c1)
+
+    if len(ranges) == 1:
+        go(0)
+    else:
+        ts = [threading.Thread(target=go, args=(i,)) for i in range(len(ranges))]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    tot = {k: sum(a[k] for a in acc) for k in acc[0]}
+    return dict(dx=dx, ddelta=ddelta, dA=tot["dA"], dB=tot["dB"], dC=tot["dC"], dh0=dh0,
+                dD=tot["dD"] if D is not None else None,
+                ddelta_bias=tot["dbias"] if delta_bias is not None else None, dz=dz)

@@ -38,13 +38,15 @@
  * chain index c = b * D + d so a caller may run disjoint ranges on several
  * threads.  Nothing is shared between chains.
  *
- * The three entry points used by the tests:
- *   oracle_selective_scan  -- the general scan (any N >= 1)
- *   oracle_state_update    -- one decode step: the scan with T = 1, state in/out
- *   oracle_sm1_scan        -- the d_state = 1 special case (same definition)
+ * The entry points used by the tests:
+ *   oracle_selective_scan      -- the general scan (any N >= 1)
+ *   oracle_state_update        -- one decode step: the scan with T = 1, state in/out
+ *   oracle_sm1_scan            -- the d_state = 1 special case (same definition)
+ *   oracle_selective_scan_bwd  -- the gradient of the general scan (below)
  */
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 /* softplus(v) = log(1 + exp(v)), evaluated without overflow:
  * for v > 0, log(1 + e^v) = v + log(1 + e^-v). */
@@ -133,4 +135,148 @@ void oracle_sm1_scan(const double *x, const double *delta, const double *delta_b
 {
     oracle_selective_scan(x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dv, z, h0, y,
                           last_state, nbatch, seqlen, dim, 1, chain_begin, chain_end);
+}
+
+/* ---------------------------------------------------------------------------
+ * The gradient of the scan above.
+ *
+ * Training a Mamba model differentiates the loss through the selective scan
+ * (youngju.dev guide, the training loop of its practical section calls
+ * loss.backward(); the "Windows SM1" page trains its scalar-state model the
+ * same way through native PyTorch autograd).  The pages give no backward
+ * formulas: what is computed here is the exact derivative of the forward
+ * definition, by the chain rule applied to each statement of the forward
+ * body in reverse order (reverse-mode differentiation), with the states of
+ * the forward pass kept for every step.
+ *
+ * Given dout = dL/dout (B, T, D) and, optionally, dlast = dL/dlast_state
+ * (B, D, N), it produces
+ *   per element  : dx, ddelta, dz (B, T, D)      (dz only when z is given)
+ *   per chain    : dh0 (B, D, N)                 (optional)
+ *   accumulated  : dA (D, N), dB, dC (B, T, N), dD (D), ddelta_bias (D)
+ * The accumulated ones are ADDED to what the arrays hold (the caller zeroes
+ * them; several threads use separate arrays and sum them).  Any output
+ * pointer may be NULL (not computed); dD / ddelta_bias / dz are skipped when
+ * the forward had no D / bias / z.
+ *
+ * Per chain (b, d), with a_t[n] = exp(dt_t A[d,n]) and h_{-1} = h0:
+ *   forward   h_t[n] = a_t[n] h_{t-1}[n] + dt_t B[t,n] x_t
+ *             yv_t   = sum_n C[t,n] h_t[n] + D x_t ;  out_t = yv_t SiLU(z_t)
+ *   backward  g[n]   = dlast[n]                        (dL/dh after the last step)
+ *             for t = T-1 .. 0:
+ *               dyv   = dout_t SiLU(z_t)
+ *               dz_t  = dout_t yv_t SiLU'(z_t),  SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *               dD   += dyv x_t ;  dx_t = dyv D
+ *               dC[t,n] += dyv h_t[n] ;  g[n] += dyv C[t,n]        (g = dL/dh_t)
+ *               ddt   = sum_n g[n] (A[d,n] a_t[n] h_{t-1}[n] + B[t,n] x_t)
+ *               dA[d,n] += g[n] dt_t a_t[n] h_{t-1}[n]
+ *               dB[t,n] += g[n] dt_t x_t ;  dx_t += sum_n g[n] dt_t B[t,n]
+ *               g[n]  = g[n] a_t[n]                                (now dL/dh_{t-1})
+ *               ddelta_t = ddt sigmoid(v_t) with softplus (its derivative), else ddt
+ *               dbias += ddelta_t
+ *             dh0[n] = g[n]
+ */
+static double sigmoid(double v)
+{
+    return 1.0 / (1.0 + exp(-v));
+}
+
+void oracle_selective_scan_bwd(const double *x, const double *delta, const double *delta_bias,
+                               int delta_softplus, const double *A, const double *Bm,
+                               const double *Cm, const double *Dv, const double *z,
+                               const double *h0, const double *dout, const double *dlast,
+                               double *dx, double *ddelta, double *ddelta_bias, double *dA,
+                               double *dB, double *dC, double *dD, double *dz, double *dh0,
+                               long nbatch, long seqlen, long dim, long dstate,
+                               long chain_begin, long chain_end)
+{
+    if (dstate < 1)
+        return;
+    /* hs[(t + 1) * N + n] = h_t[n], hs[n] = h0 ; dts[t] = Delta_t ; vs[t] = v_t */
+    double *hs = malloc(sizeof(double) * (size_t)(seqlen + 1) * (size_t)dstate);
+    double *dts = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+    double *vs = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+    double g[dstate];
+    if (!hs || !dts || !vs) {
+        free(hs); free(dts); free(vs);
+        return;
+    }
+    for (long c = chain_begin; c < chain_end && c < nbatch * dim; ++c) {
+        const long b = c / dim;
+        const long d = c % dim;
+
+        /* forward, keeping every state */
+        for (long n = 0; n < dstate; ++n)
+            hs[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
+        for (long t = 0; t < seqlen; ++t) {
+            const long bt = b * seqlen + t;
+            const double xv = x[bt * dim + d];
+            double v = delta[bt * dim + d];
+            if (delta_bias)
+                v += delta_bias[d];
+            const double dt = delta_softplus ? softplus(v) : v;
+            vs[t] = v;
+            dts[t] = dt;
+            for (long n = 0; n < dstate; ++n) {
+                const double decay = exp(dt * A[d * dstate + n]);
+                hs[(t + 1) * dstate + n] = decay * hs[t * dstate + n] + dt * Bm[bt * dstate + n] * xv;
+            }
+        }
+
+        /* backward */
+        for (long n = 0; n < dstate; ++n)
+            g[n] = dlast ? dlast[(b * dim + d) * dstate + n] : 0.0;
+        for (long t = seqlen - 1; t >= 0; --t) {
+            const long bt = b * seqlen + t;
+            const double xv = x[bt * dim + d];
+            const double dt = dts[t];
+            const double *h_now = &hs[(t + 1) * dstate];
+            const double *h_prev = &hs[t * dstate];
+            const double go = dout[bt * dim + d];
+
+            double dyv = go;
+            if (z) {
+                const double zv = z[bt * dim + d];
+                const double s = sigmoid(zv);
+                double yv = 0.0;
+                for (long n = 0; n < dstate; ++n)
+                    yv += Cm[bt * dstate + n] * h_now[n];
+                if (Dv)
+                    yv += Dv[d] * xv;
+                dyv = go * zv * s;
+                if (dz)
+                    dz[bt * dim + d] = go * yv * s * (1.0 + zv * (1.0 - s));
+            }
+            double dxv = Dv ? dyv * Dv[d] : 0.0;
+            if (Dv && dD)
+                dD[d] += dyv * xv;
+            double ddt = 0.0;
+            for (long n = 0; n < dstate; ++n) {
+                const double a = exp(dt * A[d * dstate + n]);
+                if (dC)
+                    dC[bt * dstate + n] += dyv * h_now[n];
+                g[n] += dyv * Cm[bt * dstate + n];
+                ddt += g[n] * (A[d * dstate + n] * a * h_prev[n] + Bm[bt * dstate + n] * xv);
+                if (dA)
+                    dA[d * dstate + n] += g[n] * dt * a * h_prev[n];
+                if (dB)
+                    dB[bt * dstate + n] += g[n] * dt * xv;
+                dxv += g[n] * dt * Bm[bt * dstate + n];
+                g[n] *= a;
+            }
+            const double dv = delta_softplus ? ddt * sigmoid(vs[t]) : ddt;
+            if (dx)
+                dx[bt * dim + d] = dxv;
+            if (ddelta)
+                ddelta[bt * dim + d] = dv;
+            if (delta_bias && ddelta_bias)
+                ddelta_bias[d] += dv;
+        }
+        if (dh0)
+            for (long n = 0; n < dstate; ++n)
+                dh0[(b * dim + d) * dstate + n] = g[n];
+    }
+    free(hs);
+    free(dts);
+    free(vs);
 }

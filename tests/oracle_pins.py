@@ -307,4 +307,108 @@ def pin_empty_sequence(lib):
     assert y.shape[1] == 0 and _rel(last, i["h0"]) == 0.0
 
 
+# ------------------------------------------------------------ backward pins
+# The gradient of the scan (oracle_selective_scan_bwd) is pinned to the
+# forward oracle (itself pinned above) by central finite differences, to the
+# adjoint identity of the linear part, and to closed forms at A = 0.
+
+_GRAD_OF = {"x": "dx", "delta": "ddelta", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "D": "dD",
+            "delta_bias": "ddelta_bias", "h0": "dh0"}
+
+
+def _bwd(lib, i, dout, dlast, softplus=True, **over):
+    kw = dict(D=i["D"], z=i["z"], delta_bias=i["delta_bias"], delta_softplus=softplus, h0=i["h0"],
+              dlast=dlast)
+    kw.update(over)
+    return oracle.selective_scan_bwd(i["x"], i["delta"], i["A"], i["B"], i["C"], dout, lib=lib, **kw)
+
+
+def fd_gradients(lib, i, W, Wl, softplus, names, eps=1e-6):
+    """Central differences of L = sum(W * y) + sum(Wl * last_state) through
+    the forward oracle, one input element at a time."""
+    def loss(ii):
+        y, last = oracle.selective_scan(ii["x"], ii["delta"], ii["A"], ii["B"], ii["C"], D=ii["D"],
+                                        z=ii["z"], delta_bias=ii["delta_bias"],
+                                        delta_softplus=softplus, h0=ii["h0"], lib=lib)
+        return float((W * y).sum() + (Wl * last).sum())
+
+    out = {}
+    for name in names:
+        base = i[name]
+        g = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            v0 = base[idx]
+            h = eps * max(1.0, abs(v0))
+            hi, lo = dict(i), dict(i)
+            hi[name], lo[name] = base.copy(), base.copy()
+            hi[name][idx], lo[name][idx] = v0 + h, v0 - h
+            g[idx] = (loss(hi) - loss(lo)) / (2.0 * h)
+        out[name] = g
+    return out
+
+
+def pin_bwd_finite_differences(lib):
+    """Every gradient against central differences of the forward, with every
+    optional input on (softplus, bias, D, gate, h0, dL/dlast_state), and with
+    softplus, bias and gate off."""
+    rng = np.random.default_rng(31)
+    i = _small(seed=21, Bt=2, T=6, Dd=3, N=3)
+    i["A"] = -np.exp(rng.uniform(-1.5, 0.5, size=i["A"].shape))
+    W, Wl = rng.standard_normal(i["x"].shape), rng.standard_normal(i["h0"].shape)
+    g = _bwd(lib, i, W, Wl)
+    fd = fd_gradients(lib, i, W, Wl, True, list(_GRAD_OF))
+    for name, key in _GRAD_OF.items():
+        assert _rel(g[key], fd[name]) < 1e-7, (name, _rel(g[key], fd[name]))
+
+    j = _small(seed=22, Bt=1, T=7, Dd=2, N=2)
+    j["delta"] = np.abs(j["delta"]) * 0.5 + 0.05     # positive Delta without softplus
+    j["z"], j["delta_bias"] = None, None
+    W, Wl = rng.standard_normal(j["x"].shape), rng.standard_normal(j["h0"].shape)
+    g = _bwd(lib, j, W, Wl, softplus=False)
+    assert g["dz"] is None and g["ddelta_bias"] is None
+    names = [n for n in _GRAD_OF if n not in ("z", "delta_bias")]
+    fd = fd_gradients(lib, j, W, Wl, False, names)
+    for name in names:
+        assert _rel(g[_GRAD_OF[name]], fd[name]) < 1e-7, (name, _rel(g[_GRAD_OF[name]], fd[name]))
+
+
+def pin_bwd_adjoint_identity(lib):
+    """For fixed Delta and no gate, (x, h0) -> (y, last_state) is linear, and
+    the backward applies its transpose: <dy, y> + <dl, last> = <dx, x> + <dh0, h0>."""
+    rng = np.random.default_rng(32)
+    i = _small(seed=23, Bt=2, T=20, Dd=4, N=3)
+    y, last = _scan(lib, i, z=None)
+    dy, dl = rng.standard_normal(y.shape), rng.standard_normal(last.shape)
+    g = _bwd(lib, i, dy, dl, z=None)
+    lhs = (dy * y).sum() + (dl * last).sum()
+    rhs = (g["dx"] * i["x"]).sum() + (g["dh0"] * i["h0"]).sum()
+    # x also enters through nothing else here (Delta does not depend on x)
+    assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1.0), (lhs, rhs)
+
+
+def pin_bwd_A_zero_closed_form(lib):
+    """A = 0: no decay, so dL/dh_t = dlast + sum_{s >= t} C_s dy_s (a reverse
+    cumulative sum), and every gradient has a closed form in it."""
+    rng = np.random.default_rng(33)
+    i = _small(seed=24, Bt=2, T=15, Dd=3, N=3)
+    i["A"] = np.zeros_like(i["A"])
+    dy, dl = rng.standard_normal(i["x"].shape), rng.standard_normal(i["h0"].shape)
+    g = _bwd(lib, i, dy, dl, D=None, z=None)
+    dt = ref_delta(i["delta"], i["delta_bias"], True)                          # (Bt,T,Dd)
+    v = i["delta"] + i["delta_bias"][None, None]
+    u = dt[..., None] * i["B"][:, :, None, :] * i["x"][..., None]             # (Bt,T,Dd,N)
+    h = i["h0"][:, None] + np.cumsum(u, axis=1)                              # h_t
+    h_prev = np.concatenate([i["h0"][:, None], h[:, :-1]], axis=1)          # h_{t-1}
+    cdy = i["C"][:, :, None, :] * dy[..., None]                              # (Bt,T,Dd,N)
+    G = dl[:, None] + np.flip(np.cumsum(np.flip(cdy, 1), axis=1), 1)         # dL/dh_t
+    assert _rel(g["dh0"], G[:, 0]) < 1e-12
+    assert _rel(g["dC"], np.einsum("btd,btdn->btn", dy, h)) < 1e-12
+    assert _rel(g["dB"], np.einsum("btdn,btd->btn", G, dt * i["x"])) < 1e-12
+    assert _rel(g["dx"], np.einsum("btdn,btn->btd", G, i["B"]) * dt) < 1e-12
+    assert _rel(g["dA"], np.einsum("btdn,btd,btdn->dn", G, dt, h_prev)) < 1e-12
+    ddt = np.einsum("btdn,btn->btd", G, i["B"]) * i["x"]
+    assert _rel(g["ddelta"], ddt * expit(v)) < 1e-12
+    assert _rel(g["ddelta_bias"], (ddt * expit(v)).sum(axis=(0, 1))) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
