@@ -129,6 +129,47 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
                      const float *D, const void *z, void *y, int64_t batch, int64_t d_inner,
                      int64_t d_state, int io_dtype, void *stream);
 
+/*
+ * ssm_scan_bwd -- the gradient of ssm_scan_fwd (any d_state in [1, 16]; the
+ * SM1 shapes are the d_state = 1 case with B, C of shape (batch, seqlen, 1)).
+ * The pages train through the scan (youngju.dev guide, practical section: the
+ * training loop's loss.backward(); "Windows SM1" page: the scalar-state model
+ * is trained through autograd) without printing a backward: this is the exact
+ * reverse-mode derivative of the definition above.
+ *   Inputs: the forward's inputs (same layouts and conventions), plus
+ *     dout  : (batch, seqlen, d_inner) io dtype  -- dL/dy
+ *     dlast : (batch, d_inner, d_state) fp32     -- dL/dlast_state, optional
+ *   Outputs (overwritten, never accumulated into):
+ *     dx, ddelta     : (batch, seqlen, d_inner) io dtype, required
+ *     dz             : same, required when z is given (not touched otherwise)
+ *     dB, dC         : (batch, seqlen, d_state) io dtype, required
+ *     dA             : (d_inner, d_state) fp32, required
+ *     dD, ddelta_bias: (d_inner) fp32, optional (written only when D / delta_bias
+ *                      are given and the pointer is not NULL)
+ *     dh0            : (batch, d_inner, d_state) fp32, optional (written even
+ *                      when h0 is NULL: it is dL/d(initial state))
+ *   The gradient of delta is taken through softplus when delta_softplus is set.
+ *   Workspace: ssm_scan_bwd_workspace_bytes() (state checkpoints every 16
+ *   steps and per-tile partial sums; 256-byte aligned).  Sums over channels
+ *   and over the batch are added in a fixed order: results are deterministic.
+ *   Limits: seqlen * d_inner and seqlen * d_state elements of one batch row
+ *   must span less than 2 GiB, else SSM_ERR_SHAPE.
+ *   Edge cases: seqlen == 0 gives dh0 = dlast (or 0) and zero dA, dD,
+ *   ddelta_bias; batch == 0 gives zero dA, dD, ddelta_bias; d_inner == 0
+ *   gives zero dB, dC.
+ */
+int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, const void *dout, const float *dlast, void *dx, void *ddelta,
+                 float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
+                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ssm_scan_bwd needs for this shape.  Returns (size_t)-1 for
+ * invalid arguments. */
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                    int64_t d_state, int io_dtype);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ssm_status_string(int status);
 

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",
-           "ssm_state_update", "ssm_status_string", "ssm_abi_version")
+           "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_status_string",
+           "ssm_abi_version")
 ABI_VERSION = 1
 
 _lib = None
@@ -47,6 +48,12 @@ def _bind(lib):
     lib.ssm_state_update.argtypes = [_vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _i64, _i64, _i64, _int, _vp]
     lib.ssm_state_update.restype = _int
+    lib.ssm_scan_bwd.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.ssm_scan_bwd.restype = _int
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _int]
+    lib.ssm_scan_bwd_workspace_bytes.restype = _sz
     lib.ssm_status_string.argtypes = [_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []

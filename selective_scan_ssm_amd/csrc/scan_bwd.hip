@@ -1,0 +1,560 @@
+// Backward of the selective scan: the gradient of
+//   h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_t,  y_t = (C_t . h_t + D x_t) SiLU(z_t),
+//   Delta_t = softplus(delta_t + bias)
+// with respect to every input, given dL/dy and dL/dlast_state.  The pages
+// train through this scan (the youngju.dev guide's training loop calls
+// loss.backward(); the "Windows SM1" page trains its scalar-state model with
+// autograd) but print no backward: the kernels compute the exact reverse-mode
+// derivative of the forward definition, statement by statement.
+//
+// Three launches:
+//   1. ckpt_kernel   -- the forward recurrence again, writing the state that
+//                       enters every block of kBT steps (no output).
+//   2. bwd_kernel    -- walks the blocks from last to first.  For a block it
+//                       recomputes the kBT states from the checkpoint (kept in
+//                       registers), then runs the adjoint g = dL/dh backwards
+//                       through them:  g += dy C ;  contributions ;  g *= a.
+//   3. bwd_reduce    -- sums the per-tile partials of dB, dC (over channel
+//                       tiles) and of dA, dD, dbias (over the batch).
+//
+// Work split of 1 and 2 (the forward general kernel's split): a workgroup of
+// four waves owns 64 channels of one batch row (lane = channel) for the whole
+// sequence; wave w owns states [w NPW, w NPW + NPW).  Per-(t, d) work (softplus,
+// gate, their derivatives) is split over the waves by step and shared through
+// LDS; the per-state partial sums (d Delta, dx and the readout needed by dz)
+// meet in LDS and are added in a fixed order.  dB and dC sum over channels,
+// i.e. over the 64 lanes: a butterfly reduce-scatter (v_permlane32_swap,
+// v_permlane16_swap, then DPP row rotations and mirrors) leaves each lane one
+// channel-sum, written as a per-tile partial.  Results are deterministic.
+#include "ssm_device.h"
+#include "ssm_kernels.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kBT = 16;        // steps per block
+constexpr int kBWaves = 4;     // waves per workgroup
+constexpr int kBTile = 64;     // channels per workgroup
+constexpr int kBThreads = kBWaves * 64;
+
+struct BwdParams {
+    const void *x, *delta, *z, *B, *C, *dout;
+    const float *A, *D, *bias, *h0, *dlast;
+    void *dx, *ddelta, *dz;
+    float *ckpt;        // (batch, nblk, dim, N): the state entering each block
+    float *dBp, *dCp;   // (n_dt, batch, seqlen, N): per-tile channel sums
+    float *dAp;         // (batch, dim, N)
+    float *dDp, *dbp;   // (batch, dim)
+    float *dh0;         // (batch, dim, N) or null
+    int64_t seqlen, dim;
+    int n_dt, nblk, N, softplus;
+};
+
+__device__ __forceinline__ float sigmoid_f(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
+
+// ---- lane exchange
+__device__ __forceinline__ void bswap32(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void bswap16(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+constexpr int kDppRor8 = 0x128;        // row_ror:8   (lane i <-> i ^ 8 within a row)
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror (i <-> 7 - i within 8 lanes)
+constexpr int kDppQuad2301 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppQuad1032 = 0xB1;     // quad_perm [1,0,3,2]
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// One butterfly stage inside a 16-lane row: lanes whose `bit` is 0 keep the
+// lower half of the R values, the others the upper half, and each adds the
+// matching half of its partner (the lane the DPP pattern pairs it with, which
+// differs in `bit`).  With one value left the stage sums both lanes.
+template <int R, int CTRL>
+__device__ __forceinline__ void dpp_stage(float (&v)[R], float (&out)[R > 1 ? R / 2 : 1], bool upper) {
+    if constexpr (R == 1) {
+        out[0] = v[0] + dpp<CTRL>(v[0]);
+    } else {
+#pragma unroll
+        for (int m = 0; m < R / 2; ++m) {
+            const float keep = upper ? v[m + R / 2] : v[m];
+            const float send = upper ? v[m] : v[m + R / 2];
+            out[m] = keep + dpp<CTRL>(send);
+        }
+    }
+}
+
+// Sum over the 64 lanes of each of V values (V = 4, 8 or 16); lane l returns
+// the total of value  l >> (6 - log2 V).
+template <int V> __device__ __forceinline__ float wave_reduce_scatter(float (&v)[V]) {
+    static_assert(V == 4 || V == 8 || V == 16, "V values per lane");
+    const int lane = threadIdx.x & 63;
+    float s32[V / 2];
+#pragma unroll
+    for (int m = 0; m < V / 2; ++m) {          // lanes 0-31 keep m, 32-63 keep m + V/2
+        float a = v[m], b = v[m + V / 2];
+        bswap32(a, b);
+        s32[m] = a + b;
+    }
+    float s16[V / 4];
+#pragma unroll
+    for (int m = 0; m < V / 4; ++m) {          // rows 0, 2 keep m, rows 1, 3 keep m + V/4
+        float a = s32[m], b = s32[m + V / 4];
+        bswap16(a, b);
+        s16[m] = a + b;
+    }
+    constexpr int R3 = V / 4;
+    float s8[R3 > 1 ? R3 / 2 : 1];
+    dpp_stage<R3, kDppRor8>(s16, s8, (lane >> 3) & 1);
+    constexpr int R4 = R3 > 1 ? R3 / 2 : 1;
+    float s4[R4 > 1 ? R4 / 2 : 1];
+    dpp_stage<R4, kDppHalfMirror>(s8, s4, (lane >> 2) & 1);
+    constexpr int R5 = R4 > 1 ? R4 / 2 : 1;
+    float s2[1];
+    static_assert(R5 == 1, "at most 16 values");
+    dpp_stage<1, kDppQuad2301>(s4, s2, false);
+    float s1[1];
+    dpp_stage<1, kDppQuad1032>(s2, s1, false);
+    return s1[0];
+}
+
+template <int NPW> struct PowV { static constexpr int v = (4 * NPW <= 4) ? 4 : (4 * NPW <= 8 ? 8 : 16); };
+
+// ===========================================================================
+// 1. checkpoints: the state entering each block
+template <typename IO, int NPW>
+__global__ __launch_bounds__(kBThreads) void ckpt_kernel(BwdParams p) {
+    using M = typename MathFor<IO>::type;
+    constexpr uint32_t es = sizeof(IO);
+    __shared__ float2 sDX[2][kBT][kBTile];            // (Delta, Delta x)
+    __shared__ float sB[2][kBT][16];
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int b = blockIdx.y;
+    const int64_t T = p.seqlen, dim = p.dim;
+    const int N = p.N;
+    const int64_t ch = static_cast<int64_t>(blockIdx.x) * kBTile + lane;
+    const bool active = ch < dim;
+    const int64_t chc = active ? ch : dim - 1;
+
+    float A2[NPW], h[NPW];
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+        const int n = w * NPW + i;
+        A2[i] = n < N ? M::prep_A(p.A[chc * N + n]) : 0.0f;
+        h[i] = (n < N && p.h0 && active) ? p.h0[(b * dim + chc) * N + n] : 0.0f;
+    }
+    const float bias = p.bias ? p.bias[chc] : 0.0f;
+
+    const int64_t row0 = static_cast<int64_t>(b) * T;
+    const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + row0 * dim * es, static_cast<uint32_t>(T * dim * es));
+    const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + row0 * dim * es, static_cast<uint32_t>(T * dim * es));
+    const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * es, static_cast<uint32_t>(T * N * es));
+
+    // wave w discretises steps 4w .. 4w+3 of a block; thread tid stages B of
+    // step tid / 16, state tid % 16 (zero past N or past the sequence)
+    auto produce = [&](int blk, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kk = 4 * w + k;
+            const int64_t t = static_cast<int64_t>(blk) * kBT + kk;
+            const bool in = active && t < T;
+            const uint32_t vo = in ? static_cast<uint32_t>((t * dim + ch) * es) : kOffNone;
+            const float xv = Io<IO>::f32(Io<IO>::load(rx, vo, 0));
+            const float v = Io<IO>::f32(Io<IO>::load(rd, vo, 0)) + bias;
+            float dt = p.softplus ? M::softplus(v) : v;
+            dt = in ? dt : 0.0f;
+            sDX[buf][kk][lane] = make_float2(dt, dt * xv);
+        }
+        const int k = tid / 16, n = tid % 16;
+        const int64_t t = static_cast<int64_t>(blk) * kBT + k;
+        const uint32_t bo = (n < N && t < T) ? static_cast<uint32_t>((t * N + n) * es) : kOffNone;
+        sB[buf][k][n] = Io<IO>::f32(Io<IO>::load(rB, bo, 0));
+    };
+
+    float *ck = p.ckpt + (static_cast<int64_t>(b) * p.nblk * dim + ch) * N;
+    if (p.nblk > 0) produce(0, 0);
+    __syncthreads();
+    for (int blk = 0; blk < p.nblk; ++blk) {
+        const int cur = blk & 1;
+        if (blk + 1 < p.nblk) produce(blk + 1, cur ^ 1);
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < NPW; ++i)
+                if (w * NPW + i < N) ck[static_cast<int64_t>(blk) * dim * N + w * NPW + i] = h[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kBT; ++k) {
+            const float2 q = sDX[cur][k][lane];
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) h[i] = M::step(q.x * A2[i], h[i], q.y * sB[cur][k][w * NPW + i]);
+        }
+        __syncthreads();
+    }
+}
+
+// ===========================================================================
+// 2. the reverse sweep
+template <typename IO, int NPW>
+__global__ __launch_bounds__(kBThreads) void bwd_kernel(BwdParams p) {
+    using M = typename MathFor<IO>::type;
+    using R = typename Io<IO>::raw;
+    constexpr uint32_t es = sizeof(IO);
+    constexpr int V = PowV<NPW>::v;                   // dB / dC values per 4-step chunk, padded
+    __shared__ float4 sP[kBT][kBTile];                // (Delta, Delta x, dL/d(pre-gate y), x)
+    __shared__ float sB[kBT][16], sC[kBT][16];
+    __shared__ float2 sQ[kBWaves][kBT][kBTile];       // per-wave (dL/dDelta, dx) partials
+    __shared__ float sY[kBWaves][kBT][kBTile];        // per-wave readout partials (for dz)
+    __shared__ float2 sAcc[kBWaves][kBTile];
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int b = blockIdx.y;
+    const int64_t T = p.seqlen, dim = p.dim;
+    const int N = p.N;
+    const bool gate = p.z != nullptr;
+    const int64_t ch = static_cast<int64_t>(blockIdx.x) * kBTile + lane;
+    const bool active = ch < dim;
+    const int64_t chc = active ? ch : dim - 1;
+
+    float A2[NPW], Ar[NPW], g[NPW], dA[NPW];
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+        const int n = w * NPW + i;
+        const bool vn = n < N;
+        Ar[i] = vn ? p.A[chc * N + n] : 0.0f;
+        A2[i] = M::prep_A(Ar[i]);
+        g[i] = (vn && active && p.dlast) ? p.dlast[(b * dim + chc) * N + n] : 0.0f;
+        dA[i] = 0.0f;
+    }
+    const float bias = p.bias ? p.bias[chc] : 0.0f;
+    const float Dd = p.D ? p.D[chc] : 0.0f;
+
+    const int64_t row0 = static_cast<int64_t>(b) * T;
+    const uint32_t io_bytes = static_cast<uint32_t>(T * dim * es);
+    const int64_t ebase = row0 * dim * es;
+    const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + ebase, io_bytes);
+    const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + ebase, io_bytes);
+    const rsrc_t rz = make_rsrc(static_cast<const char *>(gate ? p.z : p.x) + ebase, io_bytes);
+    const rsrc_t rg = make_rsrc(static_cast<const char *>(p.dout) + ebase, io_bytes);
+    const rsrc_t rdx = make_rsrc(static_cast<char *>(p.dx) + ebase, io_bytes);
+    const rsrc_t rdd = make_rsrc(static_cast<char *>(p.ddelta) + ebase, io_bytes);
+    const rsrc_t rdz = make_rsrc(static_cast<char *>(gate ? p.dz : p.dx) + ebase, gate ? io_bytes : 0u);
+    const uint32_t bc_bytes = static_cast<uint32_t>(T * N * es);
+    const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * es, bc_bytes);
+    const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * es, bc_bytes);
+    const float *ckb = p.ckpt + (static_cast<int64_t>(b) * p.nblk * dim + chc) * N;
+
+    // raw inputs of wave w's four steps of a block, B / C of (step tid/16,
+    // state tid%16), and the checkpoint of the block
+    struct Raw {
+        R d[4], x[4], z[4], g[4];
+        R b, c;
+        float ck[NPW];
+    };
+    auto step_off = [&](int blk, int k) __attribute__((always_inline)) -> uint32_t {
+        const int64_t t = static_cast<int64_t>(blk) * kBT + 4 * w + k;
+        return (active && t < T) ? static_cast<uint32_t>((t * dim + ch) * es) : kOffNone;
+    };
+    auto load_raw = [&](Raw &r, int blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t vo = step_off(blk, k);
+            r.d[k] = Io<IO>::load(rd, vo, 0);
+            r.x[k] = Io<IO>::load(rx, vo, 0);
+            r.z[k] = gate ? Io<IO>::load(rz, vo, 0) : R(0);
+            r.g[k] = Io<IO>::load(rg, vo, 0);
+        }
+        const int k = tid / 16, n = tid % 16;
+        const int64_t t = static_cast<int64_t>(blk) * kBT + k;
+        const uint32_t bo = (n < N && t < T) ? static_cast<uint32_t>((t * N + n) * es) : kOffNone;
+        r.b = Io<IO>::load(rB, bo, 0);
+        r.c = Io<IO>::load(rC, bo, 0);
+#pragma unroll
+        for (int i = 0; i < NPW; ++i)
+            r.ck[i] = (w * NPW + i < N && active) ? ckb[static_cast<int64_t>(blk) * dim * N + w * NPW + i] : 0.0f;
+    };
+    // per-(t, d) discretisation of wave w's steps, and B / C staging
+    auto produce = [&](const Raw &r, int blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kk = 4 * w + k;
+            const int64_t t = static_cast<int64_t>(blk) * kBT + kk;
+            const bool in = active && t < T;
+            const float xv = Io<IO>::f32(r.x[k]);
+            const float v = Io<IO>::f32(r.d[k]) + bias;
+            float dt = p.softplus ? M::softplus(v) : v;
+            float dy = Io<IO>::f32(r.g[k]);
+            if (gate) {
+                const float zv = Io<IO>::f32(r.z[k]);
+                dy *= zv * sigmoid_f(zv);
+            }
+            dt = in ? dt : 0.0f;
+            dy = in ? dy : 0.0f;
+            sP[kk][lane] = make_float4(dt, dt * xv, dy, xv);
+        }
+        sB[tid / 16][tid % 16] = Io<IO>::f32(r.b);
+        sC[tid / 16][tid % 16] = Io<IO>::f32(r.c);
+    };
+
+    float dD_acc = 0.0f, db_acc = 0.0f;
+    // the partial sums of dB / dC of one 4-step chunk, reduced over the 64
+    // channels and written as this tile's partial
+    const int64_t part0 = (static_cast<int64_t>(blockIdx.x) * gridDim.y + b) * T * N;
+    auto flush = [&](float (&vals)[V], float *dst, int blk, int kc) __attribute__((always_inline)) {
+        const float s = wave_reduce_scatter<V>(vals);
+        constexpr int shift = V == 16 ? 2 : (V == 8 ? 3 : 4);
+        const int idx = lane >> shift;
+        const int kk = idx / NPW, i = idx % NPW;
+        const int64_t t = static_cast<int64_t>(blk) * kBT + 4 * kc + kk;
+        const int n = w * NPW + i;
+        if ((lane & ((1 << shift) - 1)) == 0 && idx < 4 * NPW && n < N && t < T) dst[part0 + t * N + n] = s;
+    };
+
+    Raw cur, nxt;
+    if (p.nblk > 0) {
+        load_raw(cur, p.nblk - 1);
+        produce(cur, p.nblk - 1);
+    }
+    __syncthreads();
+    for (int blk = p.nblk - 1; blk >= 0; --blk) {
+        if (blk > 0) load_raw(nxt, blk - 1);     // in flight during the sweep
+
+        // ---- recompute the block's states from its checkpoint
+        float hs[kBT + 1][NPW], fk[kBT][NPW];
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) hs[0][i] = cur.ck[i];
+#pragma unroll
+        for (int k = 0; k < kBT; ++k) {
+            const float4 q = sP[k][lane];
+            float yv = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) {
+                fk[k][i] = M::factor(q.x * A2[i]);
+                hs[k + 1][i] = M::apply(fk[k][i], hs[k][i], q.y * sB[k][w * NPW + i]);
+                yv = fmaf(sC[k][w * NPW + i], hs[k + 1][i], yv);
+            }
+            if (gate) sY[w][k][lane] = yv;
+        }
+        // ---- adjoint sweep, last step first
+#pragma unroll
+        for (int kc = kBT / 4 - 1; kc >= 0; --kc) {
+            float vB[V], vC[V];
+#pragma unroll
+            for (int m = 0; m < V; ++m) vB[m] = vC[m] = 0.0f;
+#pragma unroll
+            for (int kk = 3; kk >= 0; --kk) {
+                const int k = 4 * kc + kk;
+                const float4 q = sP[k][lane];            // Delta, Delta x, dy, x
+                float ddt = 0.0f, dxp = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NPW; ++i) {
+                    const float bk = sB[k][w * NPW + i], ck = sC[k][w * NPW + i];
+                    g[i] = fmaf(q.z, ck, g[i]);                      // dL/dh_t
+                    const float ah = M::apply(fk[k][i], hs[k][i], 0.0f);   // a_t h_{t-1}
+                    const float qa = g[i] * ah;
+                    ddt = fmaf(qa, Ar[i], ddt);
+                    dA[i] = fmaf(qa, q.x, dA[i]);
+                    const float gb = g[i] * bk;
+                    ddt = fmaf(gb, q.w, ddt);
+                    dxp = fmaf(gb, q.x, dxp);
+                    vB[kk * NPW + i] = g[i] * q.y;
+                    vC[kk * NPW + i] = q.z * hs[k + 1][i];
+                    g[i] = M::apply(fk[k][i], g[i], 0.0f);           // dL/dh_{t-1}
+                }
+                sQ[w][k][lane] = make_float2(ddt, dxp);
+            }
+            flush(vB, p.dBp, blk, kc);
+            flush(vC, p.dCp, blk, kc);
+        }
+        __syncthreads();
+
+        // ---- finish wave w's steps: sum the four waves' partials in order
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kk = 4 * w + k;
+            const int64_t t = static_cast<int64_t>(blk) * kBT + kk;
+            const bool in = active && t < T;
+            const float4 q = sP[kk][lane];
+            float ddt = 0.0f, dxs = 0.0f, yv = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kBWaves; ++u) {
+                const float2 s = sQ[u][kk][lane];
+                ddt += s.x;
+                dxs += s.y;
+                if (gate) yv += sY[u][kk][lane];
+            }
+            const float v = Io<IO>::f32(cur.d[k]) + bias;
+            const float dv = p.softplus ? ddt * sigmoid_f(v) : ddt;
+            const float dxv = fmaf(q.z, Dd, dxs);
+            const uint32_t vo = step_off(blk, k);
+            Io<IO>::store(dxv, rdx, vo, 0);
+            Io<IO>::store(dv, rdd, vo, 0);
+            if (gate) {
+                const float zv = Io<IO>::f32(cur.z[k]);
+                const float s = sigmoid_f(zv);
+                const float yfull = fmaf(Dd, q.w, yv);
+                const float dzv = Io<IO>::f32(cur.g[k]) * yfull * s * fmaf(zv, 1.0f - s, 1.0f);
+                Io<IO>::store(dzv, rdz, vo, 0);
+            }
+            if (in) {
+                dD_acc = fmaf(q.z, q.w, dD_acc);
+                db_acc += dv;
+            }
+        }
+        if (blk > 0) {
+            produce(nxt, blk - 1);
+            cur = nxt;
+        }
+        __syncthreads();
+    }
+
+    // ---- per-chain and per-(b, d) results
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            const int n = w * NPW + i;
+            if (n < N) {
+                p.dAp[(b * dim + ch) * N + n] = dA[i];
+                if (p.dh0) p.dh0[(b * dim + ch) * N + n] = g[i];
+            }
+        }
+    }
+    sAcc[w][lane] = make_float2(dD_acc, db_acc);
+    __syncthreads();
+    if (w == 0 && active) {
+        float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kBWaves; ++u) {
+            sd += sAcc[u][lane].x;
+            sb += sAcc[u][lane].y;
+        }
+        p.dDp[b * dim + ch] = sd;
+        p.dbp[b * dim + ch] = sb;
+    }
+}
+
+// ===========================================================================
+// 3. reductions: dB, dC over the channel tiles; dA, dD, dbias over the batch
+struct ReduceParams {
+    const float *dBp, *dCp, *dAp, *dDp, *dbp;
+    void *dB, *dC;
+    float *dA, *dD, *dbias;
+    int64_t n_btn, n_dn, dim;
+    int n_dt, batch;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(ReduceParams r) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < r.n_btn; e += stride) {
+        float sb = 0.0f, sc = 0.0f;
+        for (int j = 0; j < r.n_dt; ++j) {
+            sb += r.dBp[j * r.n_btn + e];
+            sc += r.dCp[j * r.n_btn + e];
+        }
+        static_cast<T *>(r.dB)[e] = from_f32<T>(sb);
+        static_cast<T *>(r.dC)[e] = from_f32<T>(sc);
+    }
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < r.n_dn; e += stride) {
+        float s = 0.0f;
+        for (int bb = 0; bb < r.batch; ++bb) s += r.dAp[bb * r.n_dn + e];
+        r.dA[e] = s;
+    }
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < r.dim; e += stride) {
+        float sd = 0.0f, sb = 0.0f;
+        for (int bb = 0; bb < r.batch; ++bb) {
+            sd += r.dDp[bb * r.dim + e];
+            sb += r.dbp[bb * r.dim + e];
+        }
+        if (r.dD) r.dD[e] = sd;
+        if (r.dbias) r.dbias[e] = sb;
+    }
+}
+
+// ---- workspace
+struct BwdLayout {
+    int64_t nblk, n_dt;
+    size_t ckpt_off, dBp_off, dCp_off, dAp_off, dDp_off, dbp_off, total;
+};
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
+    BwdLayout l;
+    l.nblk = (seqlen + kBT - 1) / kBT;
+    l.n_dt = (dim + kBTile - 1) / kBTile;
+    size_t o = 0;
+    l.ckpt_off = o; o = align256(o + sizeof(float) * size_t(batch) * l.nblk * dim * N);
+    l.dBp_off = o;  o = align256(o + sizeof(float) * size_t(l.n_dt) * batch * seqlen * N);
+    l.dCp_off = o;  o = align256(o + sizeof(float) * size_t(l.n_dt) * batch * seqlen * N);
+    l.dAp_off = o;  o = align256(o + sizeof(float) * size_t(batch) * dim * N);
+    l.dDp_off = o;  o = align256(o + sizeof(float) * size_t(batch) * dim);
+    l.dbp_off = o;  o = align256(o + sizeof(float) * size_t(batch) * dim);
+    l.total = o;
+    return l;
+}
+
+template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+    const BwdLayout l = bwd_layout(a.batch, a.seqlen, a.dim, a.dstate);
+    // batch == 0 or d_inner == 0 leaves only the reduction, which writes the
+    // zero sums (dB, dC over no channel, dA, dD, dbias over no batch row)
+    char *ws = static_cast<char *>(a.workspace);
+    BwdParams p;
+    p.x = a.x; p.delta = a.delta; p.z = a.z; p.B = a.B; p.C = a.C; p.dout = a.dout;
+    p.A = a.A; p.D = a.D; p.bias = a.delta_bias; p.h0 = a.h0; p.dlast = a.dlast;
+    p.dx = a.dx; p.ddelta = a.ddelta; p.dz = a.dz;
+    p.ckpt = reinterpret_cast<float *>(ws + l.ckpt_off);
+    p.dBp = reinterpret_cast<float *>(ws + l.dBp_off);
+    p.dCp = reinterpret_cast<float *>(ws + l.dCp_off);
+    p.dAp = reinterpret_cast<float *>(ws + l.dAp_off);
+    p.dDp = reinterpret_cast<float *>(ws + l.dDp_off);
+    p.dbp = reinterpret_cast<float *>(ws + l.dbp_off);
+    p.dh0 = a.dh0;
+    p.seqlen = a.seqlen; p.dim = a.dim;
+    p.n_dt = static_cast<int>(l.n_dt); p.nblk = static_cast<int>(l.nblk);
+    p.N = static_cast<int>(a.dstate); p.softplus = a.softplus;
+    if (l.n_dt > 0 && a.batch > 0) {
+        const dim3 grid(static_cast<unsigned>(l.n_dt), static_cast<unsigned>(a.batch));
+        hipLaunchKernelGGL((ckpt_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
+        hipLaunchKernelGGL((bwd_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
+    }
+    ReduceParams r;
+    r.dBp = p.dBp; r.dCp = p.dCp; r.dAp = p.dAp; r.dDp = p.dDp; r.dbp = p.dbp;
+    r.dB = a.dB; r.dC = a.dC; r.dA = a.dA; r.dD = a.dD; r.dbias = a.ddelta_bias;
+    r.n_btn = a.batch * a.seqlen * a.dstate;
+    r.n_dn = a.dim * a.dstate;
+    r.dim = a.dim;
+    r.n_dt = static_cast<int>(l.n_dt);
+    r.batch = static_cast<int>(a.batch);
+    const int64_t most = r.n_btn > r.n_dn ? r.n_btn : r.n_dn;
+    const int64_t blocks = (most + 255) / 256;
+    hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3(static_cast<unsigned>(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096)),
+                       dim3(256), 0, s, r);
+    return hipGetLastError();
+}
+
+template <typename T> hipError_t launch_bwd_npw(const BwdArgs &a, hipStream_t s) {
+    switch ((a.dstate + 3) / 4) {
+    case 1: return launch_bwd_t<T, 1>(a, s);
+    case 2: return launch_bwd_t<T, 2>(a, s);
+    case 3: return launch_bwd_t<T, 3>(a, s);
+    default: return launch_bwd_t<T, 4>(a, s);
+    }
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+    return bwd_layout(batch, seqlen, dim, dstate).total;
+}
+
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
+    return a.bf16 ? launch_bwd_npw<bf16_t>(a, s) : launch_bwd_npw<float>(a, s);
+}
+
+}  // namespace ssm

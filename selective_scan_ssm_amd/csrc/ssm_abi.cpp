@@ -210,4 +210,79 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
     return hip_status(ssm::launch_state_update(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                    int64_t d_state, int io_dtype) {
+    if (check_dtype(io_dtype) || batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 ||
+        d_state > SSM_MAX_D_STATE)
+        return static_cast<size_t>(-1);
+    return ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state);
+}
+
+int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, const void *dout, const float *dlast, void *dx, void *ddelta,
+                 float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
+                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (int r = check_dtype(io_dtype)) return r;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > SSM_MAX_D_STATE)
+        return SSM_ERR_SHAPE;
+    if (batch > kMaxGridY) return SSM_ERR_SHAPE;
+    const size_t es = io_size(io_dtype);
+    const int64_t n_btd = mul3(batch, seqlen, d_inner), n_btn = mul3(batch, seqlen, d_state);
+    const int64_t n_bdn = mul3(batch, d_inner, d_state), n_dn = mul3(d_inner, d_state, 1);
+    if (n_btd < 0 || n_btn < 0 || n_bdn < 0 || n_dn < 0) return SSM_ERR_SHAPE;
+    // one batch row of x (seqlen x d_inner) and of B (seqlen x d_state) is
+    // addressed with 32-bit byte offsets
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    if (mul3(seqlen, d_inner, static_cast<int64_t>(es)) > lim ||
+        mul3(seqlen, d_state, static_cast<int64_t>(es)) > lim)
+        return SSM_ERR_SHAPE;
+    // required pointers, for whatever this shape reads or writes
+    if (n_dn > 0 && (!A || !dA)) return SSM_ERR_NULL;
+    if (n_btd > 0 && (!x || !delta || !dout || !dx || !ddelta)) return SSM_ERR_NULL;
+    if (n_btd > 0 && z && !dz) return SSM_ERR_NULL;
+    if (n_btn > 0 && (!B || !C || !dB || !dC)) return SSM_ERR_NULL;
+    const void *io_ptrs[] = {x, delta, B, C, z, dout, dx, ddelta, dB, dC, dz};
+    for (const void *p : io_ptrs)
+        if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+    const void *f_ptrs[] = {delta_bias, A, D, h0, dlast, ddelta_bias, dA, dD, dh0};
+    for (const void *p : f_ptrs)
+        if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+    const Range ins[] = {range(x, n_btd, es),         range(delta, n_btd, es),
+                         range(z, n_btd, es),         range(dout, n_btd, es),
+                         range(B, n_btn, es),         range(C, n_btn, es),
+                         range(A, n_dn, 4),           range(D, d_inner, 4),
+                         range(delta_bias, d_inner, 4), range(h0, n_bdn, 4),
+                         range(dlast, n_bdn, 4)};
+    const Range outs[] = {range(dx, n_btd, es),        range(ddelta, n_btd, es),
+                          range(z ? dz : nullptr, n_btd, es), range(dB, n_btn, es),
+                          range(dC, n_btn, es),        range(dA, n_dn, 4),
+                          range(D ? dD : nullptr, d_inner, 4),
+                          range(delta_bias ? ddelta_bias : nullptr, d_inner, 4),
+                          range(dh0, n_bdn, 4)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    constexpr int n_out = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < n_out; ++i)
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
+    if (batch == 0 && d_inner == 0) return SSM_OK;
+    const size_t need = ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    ssm::BwdArgs a;
+    a.x = x; a.delta = delta; a.z = z; a.B = B; a.C = C; a.dout = dout;
+    a.delta_bias = delta_bias; a.A = A; a.D = D; a.h0 = h0; a.dlast = dlast;
+    a.dx = dx; a.ddelta = ddelta; a.dz = z ? dz : nullptr; a.dB = dB; a.dC = dC;
+    a.dA = dA; a.dD = D ? dD : nullptr; a.ddelta_bias = delta_bias ? ddelta_bias : nullptr;
+    a.dh0 = dh0;
+    a.batch = batch; a.seqlen = seqlen; a.dim = d_inner; a.dstate = d_state;
+    a.softplus = delta_softplus ? 1 : 0;
+    a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

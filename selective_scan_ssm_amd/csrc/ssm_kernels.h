@@ -41,4 +41,20 @@ hipError_t launch_sm1_scan(const ScanArgs &a, hipStream_t s);
 // One decode step.
 hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
 
+struct BwdArgs {
+    const void *x, *delta, *z, *B, *C, *dout;     // io dtype
+    const float *delta_bias, *A, *D, *h0, *dlast;
+    void *dx, *ddelta, *dz, *dB, *dC;             // io dtype
+    float *dA, *dD, *ddelta_bias, *dh0;
+    int64_t batch, seqlen, dim, dstate;
+    int softplus;
+    int bf16;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Backward of the forward scan, 1 <= dstate <= 16.
+size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
+
 }  // namespace ssm

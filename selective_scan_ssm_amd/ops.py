@@ -150,3 +150,49 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, delt
                               _ptr(y), Bt, Dd, N, _IO[io], _stream(x.device))
     _check(rc, "ssm_state_update")
     return y
+
+
+def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, dlast=None, workspace=None):
+    """Gradient of `scan_fwd`.  Same inputs, plus dout = dL/dy (like x) and
+    dlast = dL/dlast_state ((batch, d_inner, d_state) fp32, optional).  Returns
+    a dict: dx, ddelta, dB, dC (dtype of x), dA, dh0 (fp32), and dz, dD,
+    ddelta_bias (fp32 for dD / ddelta_bias) when z, D, delta_bias are given."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, Dd = x.shape
+    N = A.shape[-1]
+    _dev(x, "x", io)
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(dout, "dout", io, x.shape)
+    _dev(B, "B", io, (Bt, T, N))
+    _dev(C, "C", io, (Bt, T, N))
+    _dev(A, "A", torch.float32, (Dd, N))
+    _dev(D, "D", torch.float32, (Dd,))
+    _dev(delta_bias, "delta_bias", torch.float32, (Dd,))
+    _dev(h0, "h0", torch.float32, (Bt, Dd, N))
+    _dev(dlast, "dlast", torch.float32, (Bt, Dd, N))
+    dev = x.device
+    g = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x), dB=torch.empty_like(B),
+             dC=torch.empty_like(C), dA=torch.empty((Dd, N), dtype=torch.float32, device=dev),
+             dh0=torch.empty((Bt, Dd, N), dtype=torch.float32, device=dev),
+             dz=torch.empty_like(x) if z is not None else None,
+             dD=torch.empty((Dd,), dtype=torch.float32, device=dev) if D is not None else None,
+             ddelta_bias=torch.empty((Dd,), dtype=torch.float32, device=dev) if delta_bias is not None else None)
+    need = lib.ssm_scan_bwd_workspace_bytes(Bt, T, Dd, N, _IO[io])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("ssm_scan_bwd_workspace_bytes: invalid arguments")
+    ws = None
+    if need:
+        ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
+            need, dtype=torch.uint8, device=dev)
+    rc = lib.ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
+                          _ptr(dlast), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["ddelta_bias"]),
+                          _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                          _ptr(g["dh0"]), Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(dev))
+    _check(rc, "ssm_scan_bwd")
+    return g

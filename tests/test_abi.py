@@ -169,3 +169,68 @@ def test_state_update_alias(lib):
     a = scan_args()
     a["y"] = a["x"]
     assert call_step(lib, a) == EALIAS
+
+
+# ------------------------------------------------------------------ backward
+def bwd_args(batch=2, seqlen=16, dim=8, dstate=4, io=F32, **over):
+    f = FakeDev()
+    a = dict(x=f(), delta=f(), delta_bias=f(), softplus=1, A=f(), B=f(), C=f(), D=f(), z=f(),
+             h0=f(), dout=f(), dlast=f(), dx=f(), ddelta=f(), ddelta_bias=f(), dA=f(), dB=f(),
+             dC=f(), dD=f(), dz=f(), dh0=f(), batch=batch, seqlen=seqlen, dim=dim, dstate=dstate,
+             io=io, ws=f(), ws_bytes=16, stream=None)   # workspace too small: never launches
+    a.update(over)
+    return a
+
+
+def call_bwd(lib, a):
+    return lib.ssm_scan_bwd(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"],
+                            a["C"], a["D"], a["z"], a["h0"], a["dout"], a["dlast"], a["dx"],
+                            a["ddelta"], a["ddelta_bias"], a["dA"], a["dB"], a["dC"], a["dD"],
+                            a["dz"], a["dh0"], a["batch"], a["seqlen"], a["dim"], a["dstate"],
+                            a["io"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(), EWS), (dict(ws=None, ws_bytes=0), EWS),
+    (dict(x=None), ENULL), (dict(dout=None), ENULL), (dict(dx=None), ENULL),
+    (dict(ddelta=None), ENULL), (dict(dA=None), ENULL), (dict(dB=None), ENULL),
+    (dict(dC=None), ENULL), (dict(dz=None), ENULL), (dict(A=None), ENULL),
+    (dict(dstate=0), ESHAPE), (dict(dstate=17), ESHAPE), (dict(batch=-1), ESHAPE),
+    (dict(seqlen=-1), ESHAPE), (dict(batch=70000), ESHAPE),
+    # one batch row of x must span less than 2 GiB (32-bit offsets)
+    (dict(seqlen=1 << 16, dim=1 << 14), ESHAPE), (dict(seqlen=1 << 27, dstate=16), ESHAPE),
+    (dict(io=2), EDTYPE),
+    (dict(dx=0x7f0000000002), EALIGN), (dict(io=BF16, dB=0x7f0000000001), EALIGN),
+    (dict(dA=0x7f0000000002), EALIGN), (dict(dlast=0x7f0000000006), EALIGN),
+])
+def test_bwd_validation(lib, over, code):
+    assert call_bwd(lib, bwd_args(**over)) == code
+
+
+def test_bwd_optional_outputs(lib):
+    # without z, dz may be NULL; dD, ddelta_bias, dh0 and dlast are optional
+    a = bwd_args(z=None, dz=None, dD=None, ddelta_bias=None, dh0=None, dlast=None)
+    assert call_bwd(lib, a) == EWS          # valid up to the (too small) workspace
+
+
+def test_bwd_alias_detection(lib):
+    a = bwd_args()
+    a["dx"] = a["x"] + 64
+    assert call_bwd(lib, a) == EALIAS
+    a = bwd_args()
+    a["dB"] = a["dC"]
+    assert call_bwd(lib, a) == EALIAS
+    a = bwd_args()
+    a["dh0"] = a["dlast"]
+    assert call_bwd(lib, a) == EALIAS
+
+
+def test_bwd_workspace_sizes(lib):
+    # checkpoints every 16 steps + per-tile partials of dB, dC + per-row sums
+    need = lib.ssm_scan_bwd_workspace_bytes(4, 8192, 5120, 16, BF16)
+    ckpt = 4 * 512 * 5120 * 16 * 4
+    parts = 2 * 80 * 4 * 8192 * 16 * 4
+    assert ckpt + parts <= need < ckpt + parts + (4 << 20)
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 16, 8, 0, F32) == (1 << 64) - 1
+    assert lib.ssm_scan_bwd_workspace_bytes(2, 16, 8, 4, 9) == (1 << 64) - 1
+    assert lib.ssm_scan_bwd_workspace_bytes(0, 0, 0, 4, F32) == 0

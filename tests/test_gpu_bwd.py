@@ -1,0 +1,187 @@
+"""GPU parity of the backward (ssm_scan_bwd through the C ABI) against the fp64
+oracle's gradient (oracle_selective_scan_bwd, pinned by finite differences) on
+the same seeded inputs.
+
+Tolerances (max relative error with an rms floor, gpu_util.err):
+  * bf16 io: 2e-2 for every gradient, as for the forward;
+  * fp32 io: 1e-5 for the per-chain gradients (dx, ddelta, dz, dh0), whose
+    arithmetic is one reverse sweep of the same depth as the forward's; 5e-5
+    for the gradients summed over the batch, the sequence or the channels (dA,
+    dD, ddelta_bias over batch x seqlen terms; dB, dC over d_inner terms).
+    Those sums are formed in fp32 in a different order from the oracle's fp64
+    ones; with K terms of mixed sign the rounding of such a sum grows like
+    sqrt(K) u sum|terms| / |sum|, a few 1e-6 at the sizes below.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import gpu_util as G
+import oracle
+from selective_scan_ssm_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+PER_CHAIN = ("dx", "ddelta", "dz", "dh0")
+SUMMED = ("dA", "dB", "dC", "dD", "ddelta_bias")
+TOL_F32_SUMMED = 5e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_scan_ssm_amd import _lib
+    _lib.load()
+    assert len(_lib.hip_runtimes_mapped()) == 1
+
+
+def grads_inputs(inp, seed, with_dlast=True):
+    """dL/dy in the io dtype (as stored) and dL/dlast_state in fp32."""
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    if inp["io"] == gen.BF16:
+        dout = gen.bf16_from_f32(dout)
+    dlast = rng.standard_normal((inp["batch"], inp["d_inner"], inp["d_state"])).astype(np.float32) \
+        if with_dlast else None
+    return dout, dlast
+
+
+def run_bwd_gpu(inp, dout, dlast, softplus=True):
+    from selective_scan_ssm_amd import ops
+    t = G.device_inputs(inp)
+    g = ops.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], G.to_torch(dout, inp["io"]),
+                     D=t["D"], z=t["z"], delta_bias=t["delta_bias"], delta_softplus=softplus,
+                     h0=t["h0"], dlast=G.to_torch(dlast, gen.F32))
+    torch.cuda.synchronize()
+    return {k: G.from_torch(v) for k, v in g.items()}
+
+
+def run_bwd_oracle(inp, dout, dlast, softplus=True, d_index=None, b_index=None):
+    d = G.decoded(inp)
+    go = gen.to_f64(dout, inp["io"])
+    dl = None if dlast is None else np.asarray(dlast, np.float64)
+    if b_index is not None:
+        bi = np.asarray(b_index)
+        pick = lambda a: None if a is None else np.ascontiguousarray(a[bi])
+        d = dict(d, x=pick(d["x"]), delta=pick(d["delta"]), z=pick(d["z"]), B=pick(d["B"]),
+                 C=pick(d["C"]), h0=pick(d["h0"]))
+        go, dl = pick(go), pick(dl)
+    if d_index is not None:
+        di = np.asarray(d_index)
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :, di])
+        d = dict(d, x=sl(d["x"]), delta=sl(d["delta"]), z=sl(d["z"]), A=d["A"][di],
+                 D=None if d["D"] is None else d["D"][di],
+                 delta_bias=None if d["delta_bias"] is None else d["delta_bias"][di],
+                 h0=None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, di]))
+        go = np.ascontiguousarray(go[:, :, di])
+        dl = None if dl is None else np.ascontiguousarray(dl[:, di])
+    return oracle.selective_scan_bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], go, D=d["D"],
+                                     z=d["z"], delta_bias=d["delta_bias"], delta_softplus=softplus,
+                                     h0=d["h0"], dlast=dl, threads=G.ORACLE_THREADS)
+
+
+def tol_for(io, key):
+    if io == gen.BF16:
+        return 2e-2
+    return 1e-5 if key in PER_CHAIN else TOL_F32_SUMMED
+
+
+def compare(g, o, io, keys, tag):
+    worst = {}
+    for k in keys:
+        if o.get(k) is None:
+            assert g.get(k) is None, k
+            continue
+        e = G.err(g[k], o[k])
+        worst[k] = e
+    G.say(f"[bwd] {tag} " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+    for k, e in worst.items():
+        assert e <= tol_for(io, k), (tag, k, e)
+
+
+def check_bwd(inp, softplus=True, with_dlast=True, seed=0, tag=""):
+    G.say(f"[bwd] {tag} B={inp['batch']} T={inp['seqlen']} D={inp['d_inner']} N={inp['d_state']} "
+          f"io={inp['io']}")
+    dout, dlast = grads_inputs(inp, seed, with_dlast)
+    g = run_bwd_gpu(inp, dout, dlast, softplus)
+    o = run_bwd_oracle(inp, dout, dlast, softplus)
+    compare(g, o, inp["io"], PER_CHAIN + SUMMED, tag)
+
+
+# --------------------------------------------------------------- small shapes
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 9, 16])
+def test_bwd_fp32_every_width(N):
+    # 3 channel tiles (the last ragged), 7 blocks of 16 steps (the last ragged)
+    inp = gen.make_inputs(2, 100, 130, N, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=400 + N)
+    check_bwd(inp, seed=N, tag=f"f32-N{N}")
+
+
+def test_bwd_bf16_mamba_layer_shape():
+    inp = gen.make_inputs(2, 300, 200, 16, io=gen.BF16, seed=411)
+    check_bwd(inp, seed=11, tag="bf16-N16")
+
+
+def test_bwd_options_off():
+    # no gate, no D, no bias, softplus off (positive Delta), no h0, no dL/dlast
+    inp = gen.make_inputs(1, 77, 70, 16, io=gen.F32, seed=412, with_z=False, with_D=False,
+                          with_bias=False)
+    inp["delta"] = (np.abs(inp["delta"]) * np.float32(0.05)).astype(np.float32)
+    check_bwd(inp, softplus=False, with_dlast=False, seed=12, tag="f32-plain")
+
+
+def test_bwd_sm1_shape_long():
+    # d_state 1 over a long sequence (the SM1 distributions: fast decays, h0 ~ N(0,1))
+    inp = gen.make_inputs(2, 1000, 96, 1, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=413)
+    check_bwd(inp, seed=13, tag="f32-sm1-long")
+
+
+def test_bwd_empty_sequence():
+    inp = gen.make_inputs(2, 0, 70, 16, io=gen.F32, h0_kind="normal", seed=414)
+    dout, dlast = grads_inputs(inp, 14)
+    g = run_bwd_gpu(inp, dout, dlast)
+    assert np.array_equal(g["dh0"], dlast.astype(np.float64))
+    assert not g["dA"].any() and not g["dD"].any() and not g["ddelta_bias"].any()
+
+
+def test_bwd_deterministic():
+    inp = gen.make_inputs(2, 64, 130, 16, io=gen.BF16, seed=415)
+    dout, dlast = grads_inputs(inp, 15)
+    g1 = run_bwd_gpu(inp, dout, dlast)
+    g2 = run_bwd_gpu(inp, dout, dlast)
+    for k, v in g1.items():
+        if v is not None:
+            assert np.array_equal(v, g2[k]), k
+
+
+# -------------------------------------------------- the layer shapes, full size
+def test_bwd_mamba130m_layer_full_row0():
+    """The 130m-shaped layer (batch 8, seqlen 2048, d_inner 1536, d_state 16,
+    bf16) in one launch; batch row 0 checked in full (every channel, so dB, dC
+    of that row too) against the oracle run on that row."""
+    inp = gen.workload_inputs(2)
+    dout, dlast = grads_inputs(inp, 21)
+    g = run_bwd_gpu(inp, dout, dlast)
+    o = run_bwd_oracle(inp, dout, dlast, b_index=[0])
+    row0 = {k: (None if g[k] is None else g[k][:1]) for k in ("dx", "ddelta", "dz", "dh0", "dB", "dC")}
+    compare(row0, o, gen.BF16, ("dx", "ddelta", "dz", "dh0", "dB", "dC"), "w2-row0")
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert np.all(np.isfinite(g[k])), k
+
+
+def test_bwd_mamba2p8b_layer_full_sampled():
+    """The 2.8b-shaped layer (batch 4, seqlen 8192, d_inner 5120, d_state 16,
+    bf16) in one launch; the per-chain gradients and dA, dD, ddelta_bias of
+    sampled channels against the oracle run on those channels."""
+    inp = gen.workload_inputs(3)
+    dout, dlast = grads_inputs(inp, 22)
+    g = run_bwd_gpu(inp, dout, dlast)
+    d_index = np.r_[0:8, 2560:2568, 5112:5120]
+    o = run_bwd_oracle(inp, dout, dlast, d_index=d_index)
+    sub = dict(dx=g["dx"][:, :, d_index], ddelta=g["ddelta"][:, :, d_index], dz=g["dz"][:, :, d_index],
+               dh0=g["dh0"][:, d_index], dA=g["dA"][d_index], dD=g["dD"][d_index],
+               ddelta_bias=g["ddelta_bias"][d_index])
+    compare(sub, o, gen.BF16, ("dx", "ddelta", "dz", "dh0", "dA", "dD", "ddelta_bias"), "w3-sampled")
+    for k in ("dB", "dC"):
+        assert np.all(np.isfinite(g[k])), k
