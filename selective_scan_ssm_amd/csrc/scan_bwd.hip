@@ -8,8 +8,9 @@
 // derivative of the forward definition, statement by statement.
 //
 // Three launches:
-//   1. ckpt_kernel   -- the forward recurrence again, writing the state that
-//                       enters every block of kBT steps (no output).
+//   1. checkpoints   -- the forward recurrence again, writing the state that
+//                       enters every block of kBT steps and no output: the
+//                       forward row kernel at d_state 16, ckpt_kernel else.
 //   2. bwd_kernel    -- walks the blocks from last to first.  For a block it
 //                       recomputes the kBT states from the checkpoint (kept in
 //                       registers), then runs the adjoint g = dL/dh backwards
@@ -130,6 +131,7 @@ template <int NPW> struct PowV { static constexpr int v = (4 * NPW <= 4) ? 4 : (
 template <typename IO, int NPW>
 __global__ __launch_bounds__(kBThreads) void ckpt_kernel(BwdParams p) {
     using M = typename MathFor<IO>::type;
+    using R = typename Io<IO>::raw;
     constexpr uint32_t es = sizeof(IO);
     __shared__ float2 sDX[2][kBT][kBTile];            // (Delta, Delta x)
     __shared__ float sB[2][kBT][16];
@@ -158,32 +160,50 @@ __global__ __launch_bounds__(kBThreads) void ckpt_kernel(BwdParams p) {
     const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * es, static_cast<uint32_t>(T * N * es));
 
     // wave w discretises steps 4w .. 4w+3 of a block; thread tid stages B of
-    // step tid / 16, state tid % 16 (zero past N or past the sequence)
-    auto produce = [&](int blk, int buf) __attribute__((always_inline)) {
+    // step tid / 16, state tid % 16 (zero past N or past the sequence).  The
+    // raw words of a block are loaded one block ahead of their conversion.
+    struct Raw {
+        R d[4], x[4];
+        R b;
+    };
+    auto load_raw = [&](Raw &r, int blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t t = static_cast<int64_t>(blk) * kBT + 4 * w + k;
+            const uint32_t vo = (active && t < T) ? static_cast<uint32_t>((t * dim + ch) * es) : kOffNone;
+            r.x[k] = Io<IO>::load(rx, vo, 0);
+            r.d[k] = Io<IO>::load(rd, vo, 0);
+        }
+        const int k = tid / 16, n = tid % 16;
+        const int64_t t = static_cast<int64_t>(blk) * kBT + k;
+        const uint32_t bo = (n < N && t < T) ? static_cast<uint32_t>((t * N + n) * es) : kOffNone;
+        r.b = Io<IO>::load(rB, bo, 0);
+    };
+    auto produce = [&](const Raw &r, int blk, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int kk = 4 * w + k;
             const int64_t t = static_cast<int64_t>(blk) * kBT + kk;
             const bool in = active && t < T;
-            const uint32_t vo = in ? static_cast<uint32_t>((t * dim + ch) * es) : kOffNone;
-            const float xv = Io<IO>::f32(Io<IO>::load(rx, vo, 0));
-            const float v = Io<IO>::f32(Io<IO>::load(rd, vo, 0)) + bias;
+            const float xv = Io<IO>::f32(r.x[k]);
+            const float v = Io<IO>::f32(r.d[k]) + bias;
             float dt = p.softplus ? M::softplus(v) : v;
             dt = in ? dt : 0.0f;
             sDX[buf][kk][lane] = make_float2(dt, dt * xv);
         }
-        const int k = tid / 16, n = tid % 16;
-        const int64_t t = static_cast<int64_t>(blk) * kBT + k;
-        const uint32_t bo = (n < N && t < T) ? static_cast<uint32_t>((t * N + n) * es) : kOffNone;
-        sB[buf][k][n] = Io<IO>::f32(Io<IO>::load(rB, bo, 0));
+        sB[buf][tid / 16][tid % 16] = Io<IO>::f32(r.b);
     };
 
     float *ck = p.ckpt + (static_cast<int64_t>(b) * p.nblk * dim + ch) * N;
-    if (p.nblk > 0) produce(0, 0);
+    Raw raw;
+    if (p.nblk > 0) {
+        load_raw(raw, 0);
+        produce(raw, 0, 0);
+    }
+    if (p.nblk > 1) load_raw(raw, 1);
     __syncthreads();
     for (int blk = 0; blk < p.nblk; ++blk) {
         const int cur = blk & 1;
-        if (blk + 1 < p.nblk) produce(blk + 1, cur ^ 1);
         if (active) {
 #pragma unroll
             for (int i = 0; i < NPW; ++i)
@@ -195,14 +215,25 @@ __global__ __launch_bounds__(kBThreads) void ckpt_kernel(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < NPW; ++i) h[i] = M::step(q.x * A2[i], h[i], q.y * sB[cur][k][w * NPW + i]);
         }
+        if (blk + 1 < p.nblk) {
+            produce(raw, blk + 1, cur ^ 1);          // loaded during this block's scan
+            if (blk + 2 < p.nblk) load_raw(raw, blk + 2);
+        }
         __syncthreads();
     }
 }
 
 // ===========================================================================
 // 2. the reverse sweep
+//
+// Two waves per SIMD (two workgroups per CU: 68 KB of LDS each) where the
+// registers allow it; the fp32 sweep over 16 states needs more than 256
+// registers per lane with the accurate expm1 and runs one wave per SIMD.
+template <typename IO, int NPW> struct BwdWaves { static constexpr int v = 2; };
+template <> struct BwdWaves<float, 4> { static constexpr int v = 1; };
+
 template <typename IO, int NPW>
-__global__ __launch_bounds__(kBThreads) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWaves<IO, NPW>::v, 2))) void bwd_kernel(BwdParams p) {
     using M = typename MathFor<IO>::type;
     using R = typename Io<IO>::raw;
     constexpr uint32_t es = sizeof(IO);
@@ -317,45 +348,39 @@ __global__ __launch_bounds__(kBThreads) void bwd_kernel(BwdParams p) {
         if ((lane & ((1 << shift) - 1)) == 0 && idx < 4 * NPW && n < N && t < T) dst[part0 + t * N + n] = s;
     };
 
-    Raw cur, nxt;
-    if (p.nblk > 0) {
-        load_raw(cur, p.nblk - 1);
-        produce(cur, p.nblk - 1);
-    }
-    __syncthreads();
-    for (int blk = p.nblk - 1; blk >= 0; --blk) {
-        if (blk > 0) load_raw(nxt, blk - 1);     // in flight during the sweep
-
-        // ---- recompute the block's states from its checkpoint
-        float hs[kBT + 1][NPW], fk[kBT][NPW];
+    // steps [s0, s0 + kBT/2) of block blk from the state hin entering them:
+    // recompute and keep the states and decay factors, write the readout
+    // partials, then run the adjoint back through them
+    auto sweep_half = [&](int s0, const float (&hin)[NPW], int blk) __attribute__((always_inline)) {
+        constexpr int H = kBT / 2;
+        float hs[H + 1][NPW], fk[H][NPW];
 #pragma unroll
-        for (int i = 0; i < NPW; ++i) hs[0][i] = cur.ck[i];
+        for (int i = 0; i < NPW; ++i) hs[0][i] = hin[i];
 #pragma unroll
-        for (int k = 0; k < kBT; ++k) {
-            const float4 q = sP[k][lane];
+        for (int k = 0; k < H; ++k) {
+            const float4 q = sP[s0 + k][lane];
             float yv = 0.0f;
 #pragma unroll
             for (int i = 0; i < NPW; ++i) {
                 fk[k][i] = M::factor(q.x * A2[i]);
-                hs[k + 1][i] = M::apply(fk[k][i], hs[k][i], q.y * sB[k][w * NPW + i]);
-                yv = fmaf(sC[k][w * NPW + i], hs[k + 1][i], yv);
+                hs[k + 1][i] = M::apply(fk[k][i], hs[k][i], q.y * sB[s0 + k][w * NPW + i]);
+                yv = fmaf(sC[s0 + k][w * NPW + i], hs[k + 1][i], yv);
             }
-            if (gate) sY[w][k][lane] = yv;
+            if (gate) sY[w][s0 + k][lane] = yv;
         }
-        // ---- adjoint sweep, last step first
 #pragma unroll
-        for (int kc = kBT / 4 - 1; kc >= 0; --kc) {
+        for (int kc = H / 4 - 1; kc >= 0; --kc) {
             float vB[V], vC[V];
 #pragma unroll
             for (int m = 0; m < V; ++m) vB[m] = vC[m] = 0.0f;
 #pragma unroll
             for (int kk = 3; kk >= 0; --kk) {
-                const int k = 4 * kc + kk;
-                const float4 q = sP[k][lane];            // Delta, Delta x, dy, x
+                const int k = 4 * kc + kk, st = s0 + k;
+                const float4 q = sP[st][lane];           // Delta, Delta x, dy, x
                 float ddt = 0.0f, dxp = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NPW; ++i) {
-                    const float bk = sB[k][w * NPW + i], ck = sC[k][w * NPW + i];
+                    const float bk = sB[st][w * NPW + i], ck = sC[st][w * NPW + i];
                     g[i] = fmaf(q.z, ck, g[i]);                      // dL/dh_t
                     const float ah = M::apply(fk[k][i], hs[k][i], 0.0f);   // a_t h_{t-1}
                     const float qa = g[i] * ah;
@@ -368,11 +393,37 @@ __global__ __launch_bounds__(kBThreads) void bwd_kernel(BwdParams p) {
                     vC[kk * NPW + i] = q.z * hs[k + 1][i];
                     g[i] = M::apply(fk[k][i], g[i], 0.0f);           // dL/dh_{t-1}
                 }
-                sQ[w][k][lane] = make_float2(ddt, dxp);
+                sQ[w][st][lane] = make_float2(ddt, dxp);
             }
-            flush(vB, p.dBp, blk, kc);
-            flush(vC, p.dCp, blk, kc);
+            flush(vB, p.dBp, blk, s0 / 4 + kc);
+            flush(vC, p.dCp, blk, s0 / 4 + kc);
         }
+    };
+
+    Raw cur, nxt;
+    if (p.nblk > 0) {
+        load_raw(cur, p.nblk - 1);
+        produce(cur, p.nblk - 1);
+    }
+    __syncthreads();
+    for (int blk = p.nblk - 1; blk >= 0; --blk) {
+        if (blk > 0) load_raw(nxt, blk - 1);     // in flight during the sweep
+
+        // ---- the block in two halves of kBT / 2 steps, the later half first:
+        // the state entering the later half is recomputed (not kept) from the
+        // checkpoint, then each half keeps its states and decay factors in
+        // registers while the adjoint runs back through it
+        float hmid[NPW];
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) hmid[i] = cur.ck[i];
+#pragma unroll
+        for (int k = 0; k < kBT / 2; ++k) {
+            const float4 q = sP[k][lane];
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) hmid[i] = M::step(q.x * A2[i], hmid[i], q.y * sB[k][w * NPW + i]);
+        }
+        sweep_half(kBT / 2, hmid, blk);
+        sweep_half(0, cur.ck, blk);
         __syncthreads();
 
         // ---- finish wave w's steps: sum the four waves' partials in order
@@ -481,14 +532,26 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ReduceParams r) {
 // ---- workspace
 struct BwdLayout {
     int64_t nblk, n_dt;
-    size_t ckpt_off, dBp_off, dCp_off, dAp_off, dDp_off, dbp_off, total;
+    size_t fwd_off, fwd_bytes, ckpt_off, dBp_off, dCp_off, dAp_off, dDp_off, dbp_off, total;
 };
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
+// At d_state 16 the checkpoints come from the forward row kernel (run with no
+// y), which needs its own workspace; other widths use ckpt_kernel.
+bool ckpt_by_forward(int64_t N) { return N == 16; }
+ScanArgs ckpt_forward_args(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int bf16) {
+    ScanArgs f{};
+    f.batch = batch; f.seqlen = seqlen; f.dim = dim; f.dstate = N; f.bf16 = bf16;
+    return f;
+}
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int bf16) {
     BwdLayout l;
     l.nblk = (seqlen + kBT - 1) / kBT;
     l.n_dt = (dim + kBTile - 1) / kBTile;
     size_t o = 0;
+    l.fwd_off = 0;
+    l.fwd_bytes = (ckpt_by_forward(N) && batch > 0 && dim > 0 && seqlen > 0)
+                      ? scan_fwd_workspace(ckpt_forward_args(batch, seqlen, dim, N, bf16)) : 0;
+    o = align256(l.fwd_bytes);
     l.ckpt_off = o; o = align256(o + sizeof(float) * size_t(batch) * l.nblk * dim * N);
     l.dBp_off = o;  o = align256(o + sizeof(float) * size_t(l.n_dt) * batch * seqlen * N);
     l.dCp_off = o;  o = align256(o + sizeof(float) * size_t(l.n_dt) * batch * seqlen * N);
@@ -500,7 +563,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N) {
 }
 
 template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
-    const BwdLayout l = bwd_layout(a.batch, a.seqlen, a.dim, a.dstate);
+    const BwdLayout l = bwd_layout(a.batch, a.seqlen, a.dim, a.dstate, a.bf16);
     // batch == 0 or d_inner == 0 leaves only the reduction, which writes the
     // zero sums (dB, dC over no channel, dA, dD, dbias over no batch row)
     char *ws = static_cast<char *>(a.workspace);
@@ -520,7 +583,21 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
     p.N = static_cast<int>(a.dstate); p.softplus = a.softplus;
     if (l.n_dt > 0 && a.batch > 0) {
         const dim3 grid(static_cast<unsigned>(l.n_dt), static_cast<unsigned>(a.batch));
-        hipLaunchKernelGGL((ckpt_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
+        if (ckpt_by_forward(a.dstate)) {
+            ScanArgs f = ckpt_forward_args(a.batch, a.seqlen, a.dim, a.dstate, a.bf16);
+            f.x = a.x; f.delta = a.delta; f.z = a.z; f.B = a.B; f.C = a.C;
+            f.delta_bias = a.delta_bias; f.A = a.A; f.D = a.D; f.h0 = a.h0;
+            f.y = nullptr; f.last_state = nullptr;
+            f.softplus = a.softplus;
+            f.workspace = ws + l.fwd_off; f.workspace_bytes = l.fwd_bytes;
+            f.ckpt = p.ckpt;
+            if (a.seqlen > 0) {
+                const hipError_t e = launch_scan_fwd(f, s);
+                if (e != hipSuccess) return e;
+            }
+        } else {
+            hipLaunchKernelGGL((ckpt_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
+        }
         hipLaunchKernelGGL((bwd_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
     }
     ReduceParams r;
@@ -549,8 +626,8 @@ template <typename T> hipError_t launch_bwd_npw(const BwdArgs &a, hipStream_t s)
 
 }  // namespace
 
-size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
-    return bwd_layout(batch, seqlen, dim, dstate).total;
+size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16) {
+    return bwd_layout(batch, seqlen, dim, dstate, bf16).total;
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {

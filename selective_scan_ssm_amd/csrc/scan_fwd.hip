@@ -80,7 +80,8 @@ struct Params {
     float *last;
     uint32_t *words;     // [0] ticket, [1] error flag, [64 ..) per-tile progress
     float *hbuf;         // per tile: d_state x 64 carried states
-    int64_t seqlen, dim;
+    float *ckpt;         // row kernel, optional: state entering each 16-step block
+    int64_t seqlen, dim, nblk;
     int n_dt, n_tiles, seg_len, n_segs, softplus;
 };
 
@@ -560,7 +561,10 @@ template <> struct Wide4<float> {
     static __device__ __forceinline__ float get(const raw &v, int i) { return __uint_as_float(v[i]); }
 };
 
-template <typename T, int FL>
+// CK = true: also record the state entering every block in p.ckpt (y may
+// then be absent); a separate instantiation, so the forward proper carries
+// none of it
+template <typename T, int FL, bool CK = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void scan_rows_kernel(Params p) {
     using M = typename MathFor<T>::type;
@@ -608,7 +612,9 @@ void scan_rows_kernel(Params p) {
     const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + e0);
     const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + e0);
     const rsrc_t rz = make_rsrc(static_cast<const char *>(has_z ? p.z : p.x) + e0);
-    const rsrc_t ry = make_rsrc(static_cast<char *>(p.y) + e0);
+    // y may be absent when the block states are recorded: its stores then go
+    // to an empty descriptor and are dropped
+    const rsrc_t ry = (!CK || p.y) ? make_rsrc(static_cast<char *>(p.y) + e0) : make_rsrc(p.x, 0u);
     // B / C of the segment; rows past its end read 0
     const uint32_t bc_bytes = static_cast<uint32_t>(steps) * N * es;
     const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * static_cast<int64_t>(es), bc_bytes);
@@ -708,6 +714,11 @@ void scan_rows_kernel(Params p) {
     // whole group of arithmetic.
     auto block = [&](Pre &pr, BCRaw &bcn, float4 &bcq, int j, auto full) __attribute__((always_inline)) {
         constexpr bool F = decltype(full)::value;
+        if (CK && active) {                         // the state entering this block
+            const int64_t blk = t_begin / kRowTB + j;
+            *reinterpret_cast<float4 *>(p.ckpt + ((b * p.nblk + blk) * dim + d) * N + n0) =
+                make_float4(h[0], h[1], h[2], h[3]);
+        }
         stash_bc(bcn, j + 1);                       // loaded one block ago
         load_bc(bcn, j + 2);
         const float *buf = bc_lds + (j & 1) * kRowBCWords + bc_row;
@@ -827,6 +838,8 @@ template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a
     p.seqlen = a.seqlen; p.dim = a.dim;
     p.n_dt = l.n_dt; p.n_tiles = l.n_tiles; p.seg_len = l.seg_len; p.n_segs = l.n_segs;
     p.softplus = a.softplus;
+    p.ckpt = nullptr;
+    p.nblk = 0;
     const int64_t nclear = static_cast<int64_t>(l.hbuf_off / sizeof(uint32_t));   // ticket + progress
     hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
                        p.words, nclear);
@@ -835,7 +848,7 @@ template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a
     return hipGetLastError();
 }
 
-template <typename T, int FL> hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
+template <typename T, int FL, bool CK> hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
     const Layout l = make_layout(a.batch, a.seqlen, a.dim, 16, sizeof(T));
     char *ws = static_cast<char *>(a.workspace);
     Params p;
@@ -847,6 +860,8 @@ template <typename T, int FL> hipError_t launch_rows(const ScanArgs &a, hipStrea
     p.seqlen = a.seqlen; p.dim = a.dim;
     p.n_dt = l.n_dt; p.n_tiles = l.n_tiles; p.seg_len = l.seg_len; p.n_segs = l.n_segs;
     p.softplus = a.softplus;
+    p.ckpt = a.ckpt;
+    p.nblk = (a.seqlen + kRowTB - 1) / kRowTB;
     // ticket, error word and the tagged carried states (tag 0 = not written)
     const int64_t nclear = static_cast<int64_t>(l.total / sizeof(uint32_t));
     hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
@@ -858,14 +873,17 @@ template <typename T, int FL> hipError_t launch_rows(const ScanArgs &a, hipStrea
     const int64_t jobs = static_cast<int64_t>(l.n_tiles) * l.n_segs;
     const int64_t workers = static_cast<int64_t>(cus) * SSM_ROWS_WG_PER_CU;
     const unsigned grid = static_cast<unsigned>(jobs < workers ? jobs : workers);
-    hipLaunchKernelGGL((scan_rows_kernel<T, FL>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((scan_rows_kernel<T, FL, CK>), dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     // d_state 16 with softplus and gate (the Mamba layer) gets the kernel
     // with both flags fixed at compile time
-    if (rows_path(a.dstate)) return (a.softplus && a.z) ? launch_rows<T, 1>(a, s) : launch_rows<T, 0>(a, s);
+    if (rows_path(a.dstate)) {
+        if (a.ckpt) return (a.softplus && a.z) ? launch_rows<T, 1, true>(a, s) : launch_rows<T, 0, true>(a, s);
+        return (a.softplus && a.z) ? launch_rows<T, 1, false>(a, s) : launch_rows<T, 0, false>(a, s);
+    }
     switch (a.dstate) {
 #define SSM_CASE(NN) \
     case NN: return launch<NN, waves_for<NN>(), T, 0>(a, s);

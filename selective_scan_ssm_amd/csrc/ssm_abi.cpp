@@ -215,7 +215,7 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inn
     if (check_dtype(io_dtype) || batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 ||
         d_state > SSM_MAX_D_STATE)
         return static_cast<size_t>(-1);
-    return ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state);
+    return ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state, io_dtype == SSM_BF16);
 }
 
 int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
@@ -269,7 +269,7 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
         for (int j = i + 1; j < n_out; ++j)
             if (overlap(outs[i], outs[j])) return SSM_ERR_ALIAS;
     if (batch == 0 && d_inner == 0) return SSM_OK;
-    const size_t need = ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state);
+    const size_t need = ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state, io_dtype == SSM_BF16);
     if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
     if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
     ssm::BwdArgs a;

@@ -18,6 +18,9 @@ struct ScanArgs {
     int bf16;                            // io dtype: 1 = bf16, 0 = fp32
     void *workspace;
     size_t workspace_bytes;
+    // optional (d_state 16 only): the state entering every 16-step block,
+    // (batch, ceil(seqlen / 16), dim, 16) fp32, for the backward's sweep
+    float *ckpt = nullptr;
 };
 
 struct StepArgs {
@@ -54,7 +57,7 @@ struct BwdArgs {
 };
 
 // Backward of the forward scan, 1 <= dstate <= 16.
-size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 
 }  // namespace ssm
