@@ -377,7 +377,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
             for (int kk = 3; kk >= 0; --kk) {
                 const int k = 4 * kc + kk, st = s0 + k;
                 const float4 q = sP[st][lane];           // Delta, Delta x, dy, x
-                float ddt = 0.0f, dxp = 0.0f;
+                // dL/dDelta = sum_n g (A a h_{t-1}) + x sum_n g B, dx = Delta sum_n g B
+                float ddt = 0.0f, sgb = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NPW; ++i) {
                     const float bk = sB[st][w * NPW + i], ck = sC[st][w * NPW + i];
@@ -386,14 +387,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
                     const float qa = g[i] * ah;
                     ddt = fmaf(qa, Ar[i], ddt);
                     dA[i] = fmaf(qa, q.x, dA[i]);
-                    const float gb = g[i] * bk;
-                    ddt = fmaf(gb, q.w, ddt);
-                    dxp = fmaf(gb, q.x, dxp);
+                    sgb = fmaf(g[i], bk, sgb);
                     vB[kk * NPW + i] = g[i] * q.y;
                     vC[kk * NPW + i] = q.z * hs[k + 1][i];
                     g[i] = M::apply(fk[k][i], g[i], 0.0f);           // dL/dh_{t-1}
                 }
-                sQ[w][st][lane] = make_float2(ddt, dxp);
+                sQ[w][st][lane] = make_float2(fmaf(sgb, q.w, ddt), sgb * q.x);
             }
             flush(vB, p.dBp, blk, s0 / 4 + kc);
             flush(vC, p.dCp, blk, s0 / 4 + kc);
