@@ -16,6 +16,9 @@ bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 0..4]
 
+--backward times ssm_scan_bwd (the gradient of the scan; workloads 1, 2, 3)
+instead, one call per step, against the backward's own VALU roofline.
+
 Profiling helpers (no GPU work of their own beyond what they state):
     python bench.py --copy-calibration       1 GiB device copy, for the
                                              FETCH_SIZE / WRITE_SIZE scale
@@ -48,6 +51,18 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 #  add, log2 (2), max, fma = 9), Delta*x, SiLU (scale, exp2 (2), add,
 #  rcp (2), mul = 7), D*x fma, gate mul, rounding convert -> 23
 SLOTS_PER_ITEM, SLOTS_PER_ELEM = 6, 23
+# Minimal fp32 VALU lane-slots of the backward (ssm_scan_bwd, bf16 io):
+#  per (t, d, n) item: the state again (Delta*A mul, exp2 (2), Delta*x*B mul,
+#  decay*h + u fma, C*h fma for the gate's derivative = 6), then the adjoint:
+#  g += dy C, a h_{t-1}, g (a h_{t-1}), its A term of dL/dDelta, its Delta
+#  term of dA, g B into the per-step sum, g Delta x for dB, dy h for dC,
+#  g *= a (= 9), and one add each for the channel sums of dB and dC -> 17
+#  per (t, d) element: 4 widening converts, softplus (9), Delta*x, SiLU and
+#  its derivative (scale, exp2 (2), add, rcp (2), z*s, dy mul, (1 - s), z(1-s)+1,
+#  dz product (2) = 12), sigmoid of the softplus input (scale, exp2 (2), add,
+#  rcp (2) = 6), dL/dDelta (fma, mul), dx (2), D*x for the readout, dD and dbias
+#  sums (2), 3 rounding converts -> 40
+BWD_SLOTS_PER_ITEM, BWD_SLOTS_PER_ELEM = 17, 40
 COPY_CAL_BYTES = 1 << 30
 
 SOURCES = {
@@ -84,6 +99,25 @@ def algorithmic_bytes(w, io_bytes):
         b += Bt * Dd * N * 4
     b += Bt * Dd * N * 4
     return b
+
+
+def bwd_algorithmic_bytes(w, io_bytes):
+    """Bytes the backward must move once: x, delta, z, dL/dy read and dx,
+    ddelta, dz written per element; B, C read and dB, dC written per (b, t, n);
+    A, D, bias read and dA, dD, dbias written; h0 read and dh0 written."""
+    Bt, T, Dd, N = w.batch, w.seqlen, w.d_inner, w.d_state
+    b = 7 * Bt * T * Dd * io_bytes
+    b += 4 * Bt * T * N * io_bytes
+    b += 2 * (Dd * N + 2 * Dd) * 4
+    if w.h0_kind != "none":
+        b += Bt * Dd * N * 4
+    b += Bt * Dd * N * 4
+    return b
+
+
+def bwd_valu_slots(w):
+    items = w.batch * w.seqlen * w.d_inner * w.d_state
+    return items * BWD_SLOTS_PER_ITEM + w.batch * w.seqlen * w.d_inner * BWD_SLOTS_PER_ELEM
 
 
 def valu_slots(w):
@@ -325,6 +359,121 @@ def bench_workload(args, dev):
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
 
 
+def cpu_baseline_bwd(inp, dout, w, seconds_target):
+    """The fp64 oracle gradient on a bounded sample: all batches over the full
+    sequence and the first `nd` channels."""
+    import numpy as np
+    import oracle
+    from selective_scan_ssm_amd import inputs as gen
+    io = inp["io"]
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(16, threads))
+    per_core = 2.5e6 * 16 / max(1, w.d_state)         # the forward's rate / ~3
+    nd = int(min(w.d_inner, max(64, seconds_target * per_core / (w.batch * w.seqlen))))
+    sl = lambda a: None if a is None else np.ascontiguousarray(gen.to_f64(a[:, :, :nd], io))
+    x, dl, z, go = sl(inp["x"]), sl(inp["delta"]), sl(inp["z"]), sl(dout)
+    B, C = gen.to_f64(inp["B"], io), gen.to_f64(inp["C"], io)
+    h0 = None if inp["h0"] is None else np.ascontiguousarray(inp["h0"][:, :nd])
+    bias = None if inp["delta_bias"] is None else inp["delta_bias"][:nd]
+    D = None if inp["D"] is None else inp["D"][:nd]
+    t0 = time.perf_counter()
+    oracle.selective_scan_bwd(x, dl, np.ascontiguousarray(inp["A"][:nd]), B, C, go, D=D, z=z,
+                              delta_bias=bias, h0=h0, threads=threads)
+    dt = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * nd
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"gradient, all {w.batch} batches x {w.seqlen} steps x first {nd} of {w.d_inner} "
+                      f"channels ({elems} elements, d_state {w.d_state}), fp64, {dt:.2f} s wall"}
+
+
+def bench_backward(args, dev):
+    """ssm_scan_bwd (the gradient of the scan) on a scan workload: one step =
+    one backward call with dL/dy resident in HBM."""
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import _lib, ops
+    from selective_scan_ssm_amd import inputs as gen
+    lib = _lib.load()
+    w = gen.WORKLOADS[args.workload]
+    if w.kind not in ("scan", "sm1"):
+        raise SystemExit("--backward needs a scan workload (1, 2 or 3)")
+    io = w.io
+    io_code = _lib.SSM_BF16 if io == gen.BF16 else _lib.SSM_F32
+    log(f"[bench] backward, workload {args.workload} ({w.name}): generating inputs")
+    inp = gen.workload_inputs(args.workload)
+    rng = np.random.default_rng(1000 + args.workload)
+    dout = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    if io == gen.BF16:
+        dout = gen.bf16_from_f32(dout)
+    stream = torch.cuda.current_stream(dev)
+    io_b = 2 if io == gen.BF16 else 4
+    alg = bwd_algorithmic_bytes(w, io_b)
+    nset = max(1, math.ceil(600e6 / alg)) if args.rotate is None else args.rotate
+    sets = []
+    for _ in range(nset):
+        t = device_set(inp, dev)
+        t["dout"] = upload(dout, io, dev)
+        sets.append(t)
+    N = w.d_state
+    need = lib.ssm_scan_bwd_workspace_bytes(w.batch, w.seqlen, w.d_inner, N, io_code)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    cur = [0]
+
+    def step():
+        s = sets[cur[0] % len(sets)]
+        cur[0] += 1
+        ops.scan_bwd(s["x"], s["delta"], s["A"], s["B"], s["C"], s["dout"], D=s["D"], z=s["z"],
+                     delta_bias=s["delta_bias"], h0=s["h0"], workspace=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean(step_ms))
+    elems = w.batch * w.seqlen * w.d_inner
+    slots = bwd_valu_slots(w)
+    ach = slots / (call_ms * 1e-3) / 1e12
+    hbm = alg / (call_ms * 1e-3) / 1e9
+    kname = "ssm_scan_bwd (checkpoint pass + bwd_kernel + bwd_reduce_kernel, timed as one call)"
+    if N > 1:       # d_state 16: the per-item work bounds it, as in the forward
+        roof = {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                "unit": "T fp32 VALU lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
+                "traffic": None, "kernel": kname, "algorithmic_slots_per_launch": slots,
+                "hbm_achieved_GBs": round(hbm, 1), "hbm_peak_GBs": HBM_PEAK_GBS,
+                "hbm_frac": round(hbm / HBM_PEAK_GBS, 4)}
+    else:           # d_state 1: bytes bound it, as in the SM1 forward
+        roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kname}
+    roof.update({"launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+                 "algorithmic_bytes_per_launch": alg})
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle gradient on a sample)")
+        cpu = cpu_baseline_bwd(inp, dout, w, args.cpu_seconds)
+    cfg = {"workload": w.name + "-backward", "batch": w.batch, "seqlen": w.seqlen,
+           "d_inner": w.d_inner, "d_state": N, "io": io, "state": "fp32", "seed": args.workload}
+    if len(sets) > 1:
+        cfg["rotated_input_sets"] = len(sets)
+    return {"metric": "selective-scan bwd elements/s (B*T*D)",
+            "value": elems / (ms_per_step * 1e-3), "unit": "elements/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
 def copy_calibration():
     """A plain device copy of COPY_CAL_BYTES, three times: under rocprofv3
     --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the counter scale."""
@@ -425,6 +574,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle sample size in core-seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time ssm_scan_bwd (the gradient) on a scan workload instead of the forward")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "COMMAND"))
     ap.add_argument("--summarize-traffic", nargs=7,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
@@ -461,7 +612,7 @@ def main():
         return
     from selective_scan_ssm_amd import _lib
     _lib.load()
-    rec = bench_workload(args, torch.device("cuda:0"))
+    rec = (bench_backward if args.backward else bench_workload)(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)
 
 
