@@ -56,6 +56,11 @@ def _bind(lib):
                                               _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
                                               _dp, _dp, _L, _L, _L, _L, _L, _L]
     lib.oracle_selective_scan_bwd.restype = None
+    lib.oracle_causal_conv1d.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
+                                         _L, _L, _L, _L, _L, _L]
+    lib.oracle_causal_conv1d.restype = None
+    lib.oracle_conv1d_update.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_int, _L, _L, _L, _L, _L]
+    lib.oracle_conv1d_update.restype = None
     return lib
 
 
@@ -217,3 +222,41 @@ def selective_scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None,
     return dict(dx=dx, ddelta=ddelta, dA=tot["dA"], dB=tot["dB"], dC=tot["dC"], dh0=dh0,
                 dD=tot["dD"] if D is not None else None,
                 ddelta_bias=tot["dbias"] if delta_bias is not None else None, dz=dz)
+
+
+def causal_conv1d(x, weight, bias=None, state=None, silu=True, threads: int = 1, lib=None):
+    """Causal depthwise conv1d (+ SiLU) of ssm_oracle.c.  x: (Bt, T, Dd);
+    weight: (Dd, K); bias: (Dd,); state: (Bt, Dd, K-1) inputs before the
+    sequence (oldest first) or None.  Returns (out (Bt,T,Dd), state_out
+    (Bt,Dd,K-1)) in fp64."""
+    lib = lib or load()
+    x, weight, bias, state = _f64(x), _f64(weight), _f64(bias), _f64(state)
+    Bt, T, Dd = x.shape
+    K = weight.shape[1]
+    assert weight.shape == (Dd, K) and K >= 1
+    assert bias is None or bias.shape == (Dd,)
+    assert state is None or state.shape == (Bt, Dd, K - 1)
+    out = np.zeros((Bt, T, Dd))
+    st_out = np.zeros((Bt, Dd, K - 1))
+
+    def go(c0, c1):
+        lib.oracle_causal_conv1d(_ptr(x), _ptr(weight), _ptr(bias), _ptr(state), _ptr(out),
+                                 _ptr(st_out), int(bool(silu)), Bt, T, Dd, K, c0, c1)
+
+    _run_chains(go, Bt * Dd, threads)
+    return out, st_out
+
+
+def conv1d_update(state, x, weight, bias=None, silu=True, lib=None):
+    """One decode token.  state: (Bt, Dd, K-1) (not modified: the new state is
+    returned); x: (Bt, Dd).  Returns (out (Bt, Dd), new_state)."""
+    lib = lib or load()
+    st = _f64(state).copy()
+    x, weight, bias = _f64(x), _f64(weight), _f64(bias)
+    Bt, Dd = x.shape
+    K = weight.shape[1]
+    assert st.shape == (Bt, Dd, K - 1)
+    out = np.zeros((Bt, Dd))
+    lib.oracle_conv1d_update(_ptr(st), _ptr(x), _ptr(weight), _ptr(bias), _ptr(out),
+                             int(bool(silu)), Bt, Dd, K, 0, Bt * Dd)
+    return out, st

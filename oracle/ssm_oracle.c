@@ -43,6 +43,10 @@
  *   oracle_state_update        -- one decode step: the scan with T = 1, state in/out
  *   oracle_sm1_scan            -- the d_state = 1 special case (same definition)
  *   oracle_selective_scan_bwd  -- the gradient of the general scan (below)
+ *   oracle_causal_conv1d       -- the block's causal depthwise convolution + SiLU
+ *                                 that produces the scan's x (below)
+ *   oracle_conv1d_update       -- the same for one decode token, with the rolling
+ *                                 window of past inputs
  */
 #include <math.h>
 #include <stddef.h>
@@ -279,4 +283,82 @@ void oracle_selective_scan_bwd(const double *x, const double *delta, const doubl
     free(hs);
     free(dts);
     free(vs);
+}
+
+/* ---------------------------------------------------------------------------
+ * The causal depthwise convolution in front of the scan.
+ *
+ * youngju.dev guide, section 5, "complete Mamba implementation": the x branch
+ * of the input projection goes through nn.Conv1d with groups = d_inner (one
+ * filter per channel), kernel size d_conv, padding d_conv - 1 on both sides
+ * and the output cut to the first seqlen steps (causal), then SiLU, and only
+ * then into the selective scan.  Written out for one channel d with filter
+ * w[d, 0..K-1] (PyTorch's Conv1d is a cross-correlation):
+ *     out[t] = bias[d] + sum_{k=0}^{K-1} w[d, k] * x[t - (K - 1) + k]
+ * where x at a step before 0 is the value the caller hands in as the state
+ * (the K - 1 inputs before the sequence, oldest first) or 0 without one.
+ *
+ * Layouts: x, out (B, T, D); w (D, K); bias (D) or NULL; state_in, state_out
+ * (B, D, K - 1) or NULL.  state_out receives the last K - 1 inputs of the
+ * extended sequence (state_in followed by x), oldest first, which is the
+ * state the next call (or the decode step) continues from.  silu != 0 applies
+ * SiLU to out.
+ */
+void oracle_causal_conv1d(const double *x, const double *w, const double *bias,
+                          const double *state_in, double *out, double *state_out, int silu_on,
+                          long nbatch, long seqlen, long dim, long width,
+                          long chain_begin, long chain_end)
+{
+    const long H = width - 1;      /* inputs of history */
+    for (long c = chain_begin; c < chain_end && c < nbatch * dim; ++c) {
+        const long b = c / dim;
+        const long d = c % dim;
+        /* the extended input: step s in [-H, T) */
+        for (long t = 0; t < seqlen; ++t) {
+            double acc = bias ? bias[d] : 0.0;
+            for (long k = 0; k < width; ++k) {
+                const long s = t - H + k;
+                double v;
+                if (s >= 0)
+                    v = x[(b * seqlen + s) * dim + d];
+                else
+                    v = state_in ? state_in[(b * dim + d) * H + (H + s)] : 0.0;
+                acc += w[d * width + k] * v;
+            }
+            out[(b * seqlen + t) * dim + d] = silu_on ? silu(acc) : acc;
+        }
+        if (state_out)
+            for (long j = 0; j < H; ++j) {
+                const long s = seqlen - H + j;     /* extended step of state slot j */
+                double v;
+                if (s >= 0)
+                    v = x[(b * seqlen + s) * dim + d];
+                else
+                    v = state_in ? state_in[(b * dim + d) * H + (H + s)] : 0.0;
+                state_out[(b * dim + d) * H + j] = v;
+            }
+    }
+}
+
+/* One decode token: x, out (B, D); state (B, D, K - 1) in/out (read, then
+ * replaced by the window shifted by one with x appended). */
+void oracle_conv1d_update(double *state, const double *x, const double *w, const double *bias,
+                          double *out, int silu_on, long nbatch, long dim, long width,
+                          long chain_begin, long chain_end)
+{
+    const long H = width - 1;
+    for (long c = chain_begin; c < chain_end && c < nbatch * dim; ++c) {
+        const long b = c / dim;
+        const long d = c % dim;
+        double *st = &state[(b * dim + d) * H];
+        double acc = bias ? bias[d] : 0.0;
+        for (long k = 0; k < H; ++k)
+            acc += w[d * width + k] * st[k];
+        acc += w[d * width + H] * x[b * dim + d];
+        out[b * dim + d] = silu_on ? silu(acc) : acc;
+        for (long k = 0; k + 1 < H; ++k)
+            st[k] = st[k + 1];
+        if (H > 0)
+            st[H - 1] = x[b * dim + d];
+    }
 }

@@ -411,4 +411,69 @@ def pin_bwd_A_zero_closed_form(lib):
     assert _rel(g["ddelta_bias"], (ddt * expit(v)).sum(axis=(0, 1))) < 1e-12
 
 
+# -------------------------------------------------------- causal conv1d pins
+# The block's depthwise causal convolution (oracle_causal_conv1d) against
+# numpy's full convolution (np.convolve), an impulse response written out by
+# hand, and the decode / continuation identities.
+
+def _conv_case(seed, Bt=2, T=37, Dd=5, K=4):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((Bt, T, Dd)), rng.standard_normal((Dd, K)),
+            rng.standard_normal(Dd), rng.standard_normal((Bt, Dd, K - 1)))
+
+
+def conv_reference(x, w, bias, state, silu):
+    """np.convolve of each channel's history + inputs with the reversed filter."""
+    Bt, T, Dd = x.shape
+    K = w.shape[1]
+    out = np.zeros_like(x)
+    for b in range(Bt):
+        for d in range(Dd):
+            hist = np.zeros(K - 1) if state is None else state[b, d]
+            ext = np.concatenate([hist, x[b, :, d]])
+            full = np.convolve(ext, w[d, ::-1])
+            out[b, :, d] = full[K - 1:K - 1 + T] + (0.0 if bias is None else bias[d])
+    return out * expit(out) if silu else out
+
+
+def pin_conv_numpy_convolve(lib):
+    for K in (1, 2, 4):
+        x, w, bias, state = _conv_case(40 + K, K=K)
+        for st, sl, bi in ((None, True, bias), (state, True, bias), (state, False, None)):
+            out, so = oracle.causal_conv1d(x, w, bi, st, silu=sl, lib=lib)
+            assert _rel(out, conv_reference(x, w, bi, st, sl)) < 1e-14, (K, st is None, sl)
+            ext = np.concatenate([np.zeros((2, 5, K - 1)) if st is None else st,
+                                  np.transpose(x, (0, 2, 1))], axis=2)
+            assert np.array_equal(so, ext[:, :, ext.shape[2] - (K - 1):]), K
+
+
+def pin_conv_impulse_response(lib):
+    """A unit impulse at step 5 of one channel returns the filter, last tap first."""
+    K, T = 4, 12
+    w = np.array([[0.5, -1.25, 2.0, 3.0]])
+    x = np.zeros((1, T, 1))
+    x[0, 5, 0] = 1.0
+    out, _ = oracle.causal_conv1d(x, w, None, None, silu=False, lib=lib)
+    expect = np.zeros(T)
+    expect[5:9] = [3.0, 2.0, -1.25, 0.5]
+    assert np.array_equal(out[0, :, 0], expect), out[0, :, 0]
+
+
+def pin_conv_decode_and_continuation(lib):
+    x, w, bias, state = _conv_case(47, T=20)
+    out, so = oracle.causal_conv1d(x, w, bias, state, silu=True, lib=lib)
+    st = state
+    steps = []
+    for t in range(20):
+        o, st = oracle.conv1d_update(st, x[:, t], w, bias, silu=True, lib=lib)
+        steps.append(o)
+    assert _rel(np.stack(steps, axis=1), out) < 1e-15 and np.array_equal(st, so)
+    o1, s1 = oracle.causal_conv1d(x[:, :7], w, bias, state, silu=True, lib=lib)
+    o2, s2 = oracle.causal_conv1d(x[:, 7:], w, bias, s1, silu=True, lib=lib)
+    assert _rel(np.concatenate([o1, o2], axis=1), out) < 1e-15 and np.array_equal(s2, so)
+    # a sequence shorter than the window keeps part of the incoming state
+    o3, s3 = oracle.causal_conv1d(x[:, :2], w, bias, state, silu=True, lib=lib)
+    assert np.array_equal(s3, np.concatenate([state[:, :, 2:], np.transpose(x[:, :2], (0, 2, 1))], axis=2))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -65,6 +65,21 @@ MUTANTS = [
     ("bwd: step decay sign", "const double a = exp(dt * A[d * dstate + n]);",
      "const double a = exp(-dt * A[d * dstate + n]);"),
     ("bwd: softplus derivative at Delta", "vs[t] = v;", "vs[t] = dt;"),
+    # the causal convolution
+    ("conv: filter reversed", "acc += w[d * width + k] * v;", "acc += w[d * width + (H - k)] * v;"),
+    ("conv: history one step late", "const long s = t - H + k;", "const long s = t - width + k;"),
+    ("conv: bias dropped", "double acc = bias ? bias[d] : 0.0;\n            for (long k = 0; k < width; ++k)",
+     "double acc = 0.0;\n            for (long k = 0; k < width; ++k)"),
+    ("conv decode: bias dropped", "double acc = bias ? bias[d] : 0.0;\n        for (long k = 0; k < H; ++k)",
+     "double acc = 0.0;\n        for (long k = 0; k < H; ++k)"),
+    ("conv: SiLU dropped", "out[(b * seqlen + t) * dim + d] = silu_on ? silu(acc) : acc;",
+     "out[(b * seqlen + t) * dim + d] = acc;"),
+    ("conv: state ignored", "v = state_in ? state_in[(b * dim + d) * H + (H + s)] : 0.0;\n                acc",
+     "v = 0.0;\n                acc"),
+    ("conv: state_out from the start", "const long s = seqlen - H + j;", "const long s = j;"),
+    ("conv decode: window not shifted", "st[k] = st[k + 1];", "st[k] = st[k];"),
+    ("conv decode: newest tap on the oldest input", "acc += w[d * width + H] * x[b * dim + d];",
+     "acc += w[d * width] * x[b * dim + d];"),
 ]
 
 
