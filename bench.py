@@ -17,7 +17,9 @@ bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--workload 0..4]
 
 --backward times ssm_scan_bwd (the gradient of the scan; workloads 1, 2, 3)
-instead, one call per step, against the backward's own VALU roofline.
+instead, one call per step, against the backward's own VALU roofline; --conv
+times the block's causal conv1d + SiLU (ssm_causal_conv1d_fwd, width 4) over
+the workload's x against the HBM roofline.
 
 Profiling helpers (no GPU work of their own beyond what they state):
     python bench.py --copy-calibration       1 GiB device copy, for the
@@ -474,6 +476,83 @@ def bench_backward(args, dev):
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
 
 
+def bench_conv(args, dev):
+    """ssm_causal_conv1d_fwd (width 4, SiLU) over the x of a scan workload:
+    one step = one convolution of the whole (batch, seqlen, d_inner) tensor."""
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import _lib, ops
+    from selective_scan_ssm_amd import inputs as gen
+    import oracle
+    _lib.load()
+    w = gen.WORKLOADS[args.workload]
+    if w.kind not in ("scan", "sm1"):
+        raise SystemExit("--conv needs a scan workload (1, 2 or 3)")
+    io, K = w.io, 4
+    io_b = 2 if io == gen.BF16 else 4
+    log(f"[bench] conv1d, workload {args.workload} ({w.name}): generating inputs")
+    inp = gen.workload_inputs(args.workload)
+    rng = np.random.default_rng(2000 + args.workload)
+    wt = (rng.standard_normal((w.d_inner, K)) * 0.5).astype(np.float32)
+    bias = rng.standard_normal(w.d_inner).astype(np.float32)
+    alg = 2 * w.batch * w.seqlen * w.d_inner * io_b + w.d_inner * (K + 1) * 4
+    nset = max(1, math.ceil(600e6 / alg)) if args.rotate is None else args.rotate
+    xs = [upload(inp["x"], io, dev) for _ in range(nset)]
+    outs = [torch.empty_like(xs[0]) for _ in range(nset)]
+    wd, bd = upload(wt, gen.F32, dev), upload(bias, gen.F32, dev)
+    stream = torch.cuda.current_stream(dev)
+    cur = [0]
+
+    def step():
+        i = cur[0] % nset
+        cur[0] += 1
+        ops.causal_conv1d(xs[i], wd, bd, silu=True, out=outs[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean(step_ms))
+    hbm = alg / (call_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "ssm_causal_conv1d_fwd (conv1d_kernel)",
+            "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+            "algorithmic_bytes_per_launch": alg}
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        nd = int(min(w.d_inner, max(64, args.cpu_seconds * 4e7 / (w.batch * w.seqlen))))
+        xs64 = np.ascontiguousarray(gen.to_f64(inp["x"][:, :, :nd], io))
+        t1 = time.perf_counter()
+        oracle.causal_conv1d(xs64, wt[:nd], bias[:nd], None, silu=True, threads=threads)
+        dt = time.perf_counter() - t1
+        el = w.batch * w.seqlen * nd
+        cpu = {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+               "sample": f"conv1d, all {w.batch} batches x {w.seqlen} steps x first {nd} of "
+                         f"{w.d_inner} channels ({el} elements, width 4), fp64, {dt:.2f} s wall"}
+    elems = w.batch * w.seqlen * w.d_inner
+    cfg = {"workload": w.name + "-conv1d", "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.d_inner,
+           "width": K, "io": io, "seed": args.workload}
+    if nset > 1:
+        cfg["rotated_input_sets"] = nset
+    return {"metric": "causal conv1d + SiLU elements/s (B*T*D)", "value": elems / (ms_per_step * 1e-3),
+            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
 def copy_calibration():
     """A plain device copy of COPY_CAL_BYTES, three times: under rocprofv3
     --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the counter scale."""
@@ -576,6 +655,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (the gradient) on a scan workload instead of the forward")
+    ap.add_argument("--conv", action="store_true",
+                    help="time ssm_causal_conv1d_fwd (width 4, SiLU) on a scan workload's x instead")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "COMMAND"))
     ap.add_argument("--summarize-traffic", nargs=7,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
@@ -612,7 +693,8 @@ def main():
         return
     from selective_scan_ssm_amd import _lib
     _lib.load()
-    rec = (bench_backward if args.backward else bench_workload)(args, torch.device("cuda:0"))
+    fn = bench_backward if args.backward else (bench_conv if args.conv else bench_workload)
+    rec = fn(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)
 
 

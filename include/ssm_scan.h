@@ -61,6 +61,7 @@ extern "C" {
 
 #define SSM_ABI_VERSION 1
 #define SSM_MAX_D_STATE 16
+#define SSM_MAX_CONV_WIDTH 4
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
 
@@ -169,6 +170,39 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
  * invalid arguments. */
 size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                     int64_t d_state, int io_dtype);
+
+/*
+ * ssm_causal_conv1d_fwd -- the causal depthwise convolution (+ SiLU) that
+ * produces the scan's input x in a Mamba block (youngju.dev guide, section 5,
+ * "complete Mamba implementation": nn.Conv1d with groups = d_inner, kernel
+ * size d_conv, padding d_conv - 1 and the output cut to seqlen, then SiLU):
+ *     out[b,t,d] = bias[d] + sum_{k<width} weight[d,k] * x[b, t - (width-1) + k, d]
+ *     (then SiLU when apply_silu)
+ *   x, out        : (batch, seqlen, d_inner) io dtype
+ *   weight        : (d_inner, width) fp32;  bias: (d_inner) fp32, optional
+ *   conv_state_in : (batch, d_inner, width - 1) io dtype, optional -- the
+ *                   inputs before step 0, oldest first (NULL: zeros)
+ *   conv_state_out: same shape, optional -- the last width - 1 inputs of
+ *                   (conv_state_in, x): the window a following call or
+ *                   ssm_causal_conv1d_update continues from
+ *   width in [1, SSM_MAX_CONV_WIDTH]; seqlen * d_inner of one batch row must
+ *   span less than 2 GiB.  Outputs may not overlap inputs.
+ */
+int ssm_causal_conv1d_fwd(const void *x, const float *weight, const float *bias,
+                          const void *conv_state_in, void *out, void *conv_state_out,
+                          int apply_silu, int64_t batch, int64_t seqlen, int64_t d_inner,
+                          int64_t width, int io_dtype, void *stream);
+
+/*
+ * ssm_causal_conv1d_update -- one decode token of the same convolution: the
+ * window conv_state (batch, d_inner, width - 1) io dtype is read, out (batch,
+ * d_inner) is computed over (window, x), and the window is shifted by one
+ * with x appended, in place (the constant-size state of O(1) decoding,
+ * "Windows SM1" page, detailed sections).
+ */
+int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weight,
+                             const float *bias, void *out, int apply_silu, int64_t batch,
+                             int64_t d_inner, int64_t width, int io_dtype, void *stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ssm_status_string(int status);

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",
-           "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_status_string",
-           "ssm_abi_version")
+           "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_causal_conv1d_fwd",
+           "ssm_causal_conv1d_update", "ssm_status_string", "ssm_abi_version")
 ABI_VERSION = 1
 
 _lib = None
@@ -54,6 +54,11 @@ def _bind(lib):
     lib.ssm_scan_bwd.restype = _int
     lib.ssm_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _int]
     lib.ssm_scan_bwd_workspace_bytes.restype = _sz
+    lib.ssm_causal_conv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64,
+                                          _int, _vp]
+    lib.ssm_causal_conv1d_fwd.restype = _int
+    lib.ssm_causal_conv1d_update.argtypes = [_vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp]
+    lib.ssm_causal_conv1d_update.restype = _int
     lib.ssm_status_string.argtypes = [_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []

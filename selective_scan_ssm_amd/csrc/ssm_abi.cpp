@@ -285,4 +285,67 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
     return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+int ssm_causal_conv1d_fwd(const void *x, const float *weight, const float *bias,
+                          const void *conv_state_in, void *out, void *conv_state_out,
+                          int apply_silu, int64_t batch, int64_t seqlen, int64_t d_inner,
+                          int64_t width, int io_dtype, void *stream) {
+    if (int r = check_dtype(io_dtype)) return r;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || width < 1 || width > SSM_MAX_CONV_WIDTH)
+        return SSM_ERR_SHAPE;
+    if (batch > kMaxGridY) return SSM_ERR_SHAPE;
+    const size_t es = io_size(io_dtype);
+    const int64_t n_btd = mul3(batch, seqlen, d_inner), n_bdh = mul3(batch, d_inner, width - 1);
+    if (n_btd < 0 || n_bdh < 0) return SSM_ERR_SHAPE;
+    if (mul3(seqlen, d_inner, static_cast<int64_t>(es)) > (int64_t(1) << 31) - 1) return SSM_ERR_SHAPE;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    if (!weight) return SSM_ERR_NULL;
+    if (n_btd > 0 && (!x || !out)) return SSM_ERR_NULL;
+    const void *io_ptrs[] = {x, out, conv_state_in, conv_state_out};
+    for (const void *p : io_ptrs)
+        if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+    if (!aligned(weight, 4) || (bias && !aligned(bias, 4))) return SSM_ERR_ALIGN;
+    const Range ins[] = {range(x, n_btd, es), range(weight, d_inner * width, 4), range(bias, d_inner, 4),
+                         range(conv_state_in, n_bdh, es)};
+    const Range outs[] = {range(out, n_btd, es), range(conv_state_out, n_bdh, es)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    ssm::ConvArgs a;
+    a.x = x; a.weight = weight; a.bias = bias; a.state_in = conv_state_in;
+    a.out = out; a.state_out = conv_state_out;
+    a.batch = batch; a.seqlen = seqlen; a.dim = d_inner;
+    a.width = static_cast<int>(width); a.silu = apply_silu ? 1 : 0;
+    a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    return hip_status(ssm::launch_conv1d(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weight,
+                             const float *bias, void *out, int apply_silu, int64_t batch,
+                             int64_t d_inner, int64_t width, int io_dtype, void *stream) {
+    if (int r = check_dtype(io_dtype)) return r;
+    if (batch < 0 || d_inner < 0 || width < 1 || width > SSM_MAX_CONV_WIDTH) return SSM_ERR_SHAPE;
+    const size_t es = io_size(io_dtype);
+    const int64_t n_bd = mul3(batch, d_inner, 1), n_bdh = mul3(batch, d_inner, width - 1);
+    if (n_bd < 0 || n_bdh < 0 || n_bd >= (int64_t(1) << 31)) return SSM_ERR_SHAPE;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    if (!x || !weight || !out || (width > 1 && !conv_state)) return SSM_ERR_NULL;
+    const void *io_ptrs[] = {x, out, conv_state};
+    for (const void *p : io_ptrs)
+        if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+    if (!aligned(weight, 4) || (bias && !aligned(bias, 4))) return SSM_ERR_ALIGN;
+    const Range ins[] = {range(x, n_bd, es), range(weight, d_inner * width, 4), range(bias, d_inner, 4)};
+    const Range outs[] = {range(out, n_bd, es), range(conv_state, n_bdh, es)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    ssm::ConvUpdateArgs a;
+    a.state = conv_state; a.x = x; a.weight = weight; a.bias = bias; a.out = out;
+    a.batch = batch; a.dim = d_inner;
+    a.width = static_cast<int>(width); a.silu = apply_silu ? 1 : 0;
+    a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    return hip_status(ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

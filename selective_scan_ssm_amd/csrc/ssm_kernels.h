@@ -60,4 +60,25 @@ struct BwdArgs {
 size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 
+struct ConvArgs {
+    const void *x;                        // io dtype (batch, seqlen, dim)
+    const float *weight, *bias;           // (dim, width), (dim)
+    const void *state_in;                 // io dtype (batch, dim, width - 1) or null
+    void *out, *state_out;
+    int64_t batch, seqlen, dim;
+    int width, silu, bf16;
+};
+struct ConvUpdateArgs {
+    void *state;                          // io dtype (batch, dim, width - 1), in place
+    const void *x;                        // (batch, dim)
+    const float *weight, *bias;
+    void *out;
+    int64_t batch, dim;
+    int width, silu, bf16;
+};
+
+// Causal depthwise conv1d (+ SiLU), whole sequence and one decode token.
+hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
+hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);
+
 }  // namespace ssm

@@ -196,3 +196,48 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
                           _ptr(g["dh0"]), Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(dev))
     _check(rc, "ssm_scan_bwd")
     return g
+
+
+def causal_conv1d(x, weight, bias=None, conv_state=None, silu=True, return_state=False, out=None):
+    """Causal depthwise conv1d (+ SiLU) of the Mamba block's x branch.
+    x: (batch, seqlen, d_inner) fp32 or bf16; weight: (d_inner, width) fp32;
+    bias: (d_inner,) fp32; conv_state: (batch, d_inner, width - 1) like x, the
+    inputs before the sequence.  Returns out, or (out, new conv_state)."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, Dd = x.shape
+    K = weight.shape[-1]
+    _dev(x, "x", io)
+    _dev(weight, "weight", torch.float32, (Dd, K))
+    _dev(bias, "bias", torch.float32, (Dd,))
+    _dev(conv_state, "conv_state", io, (Bt, Dd, K - 1))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    st = torch.empty((Bt, Dd, K - 1), dtype=io, device=x.device) if return_state else None
+    rc = lib.ssm_causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(y),
+                                   _ptr(st), int(bool(silu)), Bt, T, Dd, K, _IO[io], _stream(x.device))
+    _check(rc, "ssm_causal_conv1d_fwd")
+    return (y, st) if return_state else y
+
+
+def causal_conv1d_update(conv_state, x, weight, bias=None, silu=True, out=None):
+    """One decode token: conv_state (batch, d_inner, width - 1) is updated in
+    place; x: (batch, d_inner).  Returns out (batch, d_inner)."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, Dd = x.shape
+    K = weight.shape[-1]
+    _dev(conv_state, "conv_state", io, (Bt, Dd, K - 1))
+    _dev(x, "x", io)
+    _dev(weight, "weight", torch.float32, (Dd, K))
+    _dev(bias, "bias", torch.float32, (Dd,))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    rc = lib.ssm_causal_conv1d_update(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), _ptr(y),
+                                      int(bool(silu)), Bt, Dd, K, _IO[io], _stream(x.device))
+    _check(rc, "ssm_causal_conv1d_update")
+    return y

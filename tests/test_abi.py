@@ -234,3 +234,55 @@ def test_bwd_workspace_sizes(lib):
     assert lib.ssm_scan_bwd_workspace_bytes(2, 16, 8, 0, F32) == (1 << 64) - 1
     assert lib.ssm_scan_bwd_workspace_bytes(2, 16, 8, 4, 9) == (1 << 64) - 1
     assert lib.ssm_scan_bwd_workspace_bytes(0, 0, 0, 4, F32) == 0
+
+
+# ------------------------------------------------------- causal conv1d
+def conv_args(batch=2, seqlen=16, dim=8, width=4, io=F32, **over):
+    f = FakeDev()
+    a = dict(x=f(), w=f(), bias=f(), st_in=f(), out=f(), st_out=f(), silu=1, batch=batch,
+             seqlen=seqlen, dim=dim, width=width, io=io, stream=None)
+    a.update(over)
+    return a
+
+
+def call_conv(lib, a):
+    return lib.ssm_causal_conv1d_fwd(a["x"], a["w"], a["bias"], a["st_in"], a["out"], a["st_out"],
+                                     a["silu"], a["batch"], a["seqlen"], a["dim"], a["width"],
+                                     a["io"], a["stream"])
+
+
+def call_conv_update(lib, a):
+    return lib.ssm_causal_conv1d_update(a["st_in"], a["x"], a["w"], a["bias"], a["out"], a["silu"],
+                                        a["batch"], a["dim"], a["width"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), ENULL), (dict(out=None), ENULL), (dict(w=None), ENULL),
+    (dict(width=0), ESHAPE), (dict(width=5), ESHAPE), (dict(batch=-1), ESHAPE),
+    (dict(seqlen=-1), ESHAPE), (dict(batch=70000), ESHAPE), (dict(seqlen=1 << 20, dim=1 << 10), ESHAPE),
+    (dict(io=4), EDTYPE), (dict(x=0x7f0000000002), EALIGN), (dict(io=BF16, out=0x7f0000000001), EALIGN),
+    (dict(w=0x7f0000000002), EALIGN), (dict(batch=0), OK), (dict(dim=0), OK),
+])
+def test_conv_validation(lib, over, code):
+    assert call_conv(lib, conv_args(**over)) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), ENULL), (dict(st_in=None), ENULL), (dict(out=None), ENULL),
+    (dict(width=9), ESHAPE), (dict(io=9), EDTYPE), (dict(st_in=0x7f0000000002), EALIGN),
+    (dict(batch=0), OK),
+])
+def test_conv_update_validation(lib, over, code):
+    assert call_conv_update(lib, conv_args(**over)) == code
+
+
+def test_conv_alias(lib):
+    a = conv_args()
+    a["out"] = a["x"]
+    assert call_conv(lib, a) == EALIAS
+    a = conv_args()
+    a["st_out"] = a["st_in"]
+    assert call_conv(lib, a) == EALIAS
+    a = conv_args()
+    a["out"] = a["st_in"]
+    assert call_conv_update(lib, a) == EALIAS
