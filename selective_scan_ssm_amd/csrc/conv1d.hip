@@ -23,8 +23,15 @@
 namespace ssm {
 namespace {
 
-constexpr int kChunk = 128;        // steps per wave
-constexpr int kAhead = 8;          // rows in flight per lane
+#ifndef SSM_CONV_CHUNK
+#define SSM_CONV_CHUNK 128
+#endif
+#ifndef SSM_CONV_AHEAD
+#define SSM_CONV_AHEAD 8
+#endif
+constexpr int kChunk = SSM_CONV_CHUNK;   // steps per wave
+constexpr int kAhead = SSM_CONV_AHEAD;   // rows in flight per lane
+static_assert(kChunk % kAhead == 0, "chunks end on a load group");
 constexpr int kConvWaves = 4;      // waves per workgroup (consecutive chunks)
 
 struct ConvParams {
