@@ -72,10 +72,11 @@ SOURCES = {
     "rows": ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "sm1": ["selective_scan_ssm_amd/csrc/sm1_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "conv": ["selective_scan_ssm_amd/csrc/conv1d.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
 # the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
-                 "decode": "state_update_rows_kernel"}
+                 "decode": "state_update_rows_kernel", "conv": "conv1d_kernel"}
 
 
 def kind_of(w):
@@ -525,7 +526,7 @@ def bench_conv(args, dev):
     call_ms = float(np.mean(step_ms))
     hbm = alg / (call_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("conv", w.name + "-conv1d"),
             "kernel": "ssm_causal_conv1d_fwd (conv1d_kernel)",
             "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
             "algorithmic_bytes_per_launch": alg}
@@ -669,13 +670,18 @@ def main():
     if args.summarize_traffic:
         from selective_scan_ssm_amd import inputs as gen
         wl, fd, wd, cfd, cwd, kcmd, ccmd = args.summarize_traffic
-        w = gen.WORKLOADS[int(wl)]
-        kind = kind_of(w)
-        alg = algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
+        if wl.startswith("conv"):      # "conv3": the conv1d over workload 3's x
+            w = gen.WORKLOADS[int(wl[4:])]
+            kind, wname = "conv", w.name + "-conv1d"
+            alg = 2 * w.batch * w.seqlen * w.d_inner * (2 if w.io == gen.BF16 else 4) + w.d_inner * 5 * 4
+        else:
+            w = gen.WORKLOADS[int(wl)]
+            kind, wname = kind_of(w), w.name
+            alg = algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
         cmds = [kcmd.replace("{COUNTER}", c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
         cmds += [ccmd.replace("{COUNTER}", c) for c in ("FETCH_SIZE", "WRITE_SIZE")]
-        text = summarize_traffic(kind, w.name, fd, wd, cfd, cwd, cmds, alg)
-        with open(traffic_file(kind, w.name), "w") as f:
+        text = summarize_traffic(kind, wname, fd, wd, cfd, cwd, cmds, alg)
+        with open(traffic_file(kind, wname), "w") as f:
             f.write(text)
         sys.stdout.write(text)
         return
