@@ -260,3 +260,30 @@ def conv1d_update(state, x, weight, bias=None, silu=True, lib=None):
     lib.oracle_conv1d_update(_ptr(st), _ptr(x), _ptr(weight), _ptr(bias), _ptr(out),
                              int(bool(silu)), Bt, Dd, K, 0, Bt * Dd)
     return out, st
+
+
+def sequence_order(height: int, width: int, direction: int):
+    """The order in which the 2-D scans of the youngju.dev guide's VMamba
+    section (section 9, image processing) visit the height x width patches:
+    0 row-major (left to right, top to bottom), 1 its reverse, 2 column-major
+    (the patch grid transposed), 3 its reverse.  Returns perm with
+    perm[s] = the row-major index of the patch at scan step s."""
+    idx = np.arange(height * width).reshape(height, width)
+    seq = idx.reshape(-1) if direction in (0, 1) else idx.T.reshape(-1)
+    return seq[::-1].copy() if direction in (1, 3) else seq
+
+
+def scan_2d(x, delta, A, B, C, height, width, direction, D=None, z=None, delta_bias=None,
+            delta_softplus=True, h0=None, threads: int = 1, lib=None):
+    """One direction of the 2-D scan: the sequence (row-major patches, axis 1)
+    is visited in `sequence_order`, scanned, and y is returned at each patch's
+    own (row-major) position; last_state is the state after the last visited
+    patch."""
+    perm = sequence_order(height, width, direction)
+    pick = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a)[:, perm])
+    y, last = selective_scan(pick(x), pick(delta), A, pick(B), pick(C), D=D, z=pick(z),
+                             delta_bias=delta_bias, delta_softplus=delta_softplus, h0=h0,
+                             threads=threads, lib=lib)
+    out = np.empty_like(y)
+    out[:, perm] = y
+    return out, last

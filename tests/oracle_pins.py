@@ -476,4 +476,50 @@ def pin_conv_decode_and_continuation(lib):
     assert np.array_equal(s3, np.concatenate([state[:, :, 2:], np.transpose(x[:, :2], (0, 2, 1))], axis=2))
 
 
+# --------------------------------------------------------------- 2-D scan pins
+# The four visiting orders of the 2-D scan (oracle.scan_2d) against their
+# definitions written another way: the reverse order as the brute-force
+# recurrence run backwards in time, the column-major orders as the row-major
+# ones on the transposed patch grid, and orders that coincide on 1 x W grids.
+
+def pin_scan2d_reverse_is_backward_recurrence(lib):
+    i = _small(seed=50, Bt=2, T=12, Dd=3, N=2)
+    y, last = oracle.scan_2d(i["x"], i["delta"], i["A"], i["B"], i["C"], 3, 4, 1, D=i["D"], z=i["z"],
+                             delta_bias=i["delta_bias"], h0=i["h0"], lib=lib)
+    rev = lambda a: None if a is None else a[:, ::-1]
+    yb, lb = brute_force(rev(i["x"]), rev(i["delta"]), i["A"], rev(i["B"]), rev(i["C"]), i["D"],
+                         rev(i["z"]), i["delta_bias"], True, i["h0"])
+    assert _rel(y, yb[:, ::-1]) < 1e-12 and _rel(last, lb) < 1e-12
+
+
+def pin_scan2d_column_major_is_transposed_grid(lib):
+    H, W = 3, 5
+    i = _small(seed=51, Bt=1, T=H * W, Dd=2, N=3)
+    grid_t = lambda a: None if a is None else np.ascontiguousarray(
+        a.reshape(a.shape[0], H, W, -1).transpose(0, 2, 1, 3).reshape(a.shape[0], H * W, -1))
+    for direction in (2, 3):
+        y, last = oracle.scan_2d(i["x"], i["delta"], i["A"], i["B"], i["C"], H, W, direction, D=i["D"],
+                                 z=i["z"], delta_bias=i["delta_bias"], h0=i["h0"], lib=lib)
+        yt, lt = oracle.scan_2d(grid_t(i["x"]), grid_t(i["delta"]), i["A"], grid_t(i["B"]), grid_t(i["C"]),
+                                W, H, direction - 2, D=i["D"], z=grid_t(i["z"]),
+                                delta_bias=i["delta_bias"], h0=i["h0"], lib=lib)
+        # yt is in the transposed grid's row-major order: transpose back
+        back = yt.reshape(1, W, H, -1).transpose(0, 2, 1, 3).reshape(1, H * W, -1)
+        assert _rel(y, back) < 1e-14 and _rel(last, lt) < 1e-14, direction
+
+
+def pin_scan2d_degenerate_grids(lib):
+    i = _small(seed=52, Bt=2, T=7, Dd=3, N=2)
+    y0, l0 = _scan(lib, i)
+    a = dict(D=i["D"], z=i["z"], delta_bias=i["delta_bias"], h0=i["h0"], lib=lib)
+    args = (i["x"], i["delta"], i["A"], i["B"], i["C"])
+    for H, W, direction in ((1, 7, 0), (7, 1, 0), (7, 1, 2), (1, 7, 2)):   # a line: all the same order
+        y, last = oracle.scan_2d(*args, H, W, direction, **a)
+        assert np.array_equal(y, y0) and np.array_equal(last, l0), (H, W, direction)
+    # and the two reversed orders of a line agree
+    y1, l1 = oracle.scan_2d(*args, 1, 7, 1, **a)
+    y3, l3 = oracle.scan_2d(*args, 7, 1, 3, **a)
+    assert np.array_equal(y1, y3) and np.array_equal(l1, l3)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
