@@ -172,6 +172,34 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inn
                                     int64_t d_state, int io_dtype);
 
 /*
+ * ssm_scan_fwd_2d -- one direction of the 2-D scan of the youngju.dev guide's
+ * VMamba section (section 9, image processing): the sequence axis holds
+ * height x width patches in row-major order, and the scan visits them in
+ *   direction 0: row-major (left to right, top to bottom)
+ *   direction 1: the reverse of 0 (right to left, bottom to top)
+ *   direction 2: column-major (top to bottom, left to right: the grid transposed)
+ *   direction 3: the reverse of 2
+ * y is written at each patch's own (row-major) position, so the four
+ * directions' outputs align for the block's sum; last_state is the state
+ * after the last visited patch.  Same tensors and conventions as
+ * ssm_scan_fwd with seqlen = height * width (height = 1 gives the plain
+ * reversed 1-D scan with direction 1).  The orders are realised by gathering
+ * the inputs into scan order and scattering y back, so the workspace
+ * (ssm_scan_2d_workspace_bytes) holds a copy of x, delta, z, B, C and y.
+ *   direction outside [0, 3] or negative height / width: SSM_ERR_SHAPE.
+ */
+int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                    const float *A, const void *B, const void *C, const float *D, const void *z,
+                    const float *h0, void *y, float *last_state, int64_t batch, int64_t height,
+                    int64_t width, int64_t d_inner, int64_t d_state, int direction, int io_dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of ssm_scan_fwd_2d (has_z: whether z is given); (size_t)-1
+ * for invalid arguments. */
+size_t ssm_scan_2d_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t d_inner,
+                                   int64_t d_state, int has_z, int io_dtype);
+
+/*
  * ssm_causal_conv1d_fwd -- the causal depthwise convolution (+ SiLU) that
  * produces the scan's input x in a Mamba block (youngju.dev guide, section 5,
  * "complete Mamba implementation": nn.Conv1d with groups = d_inner, kernel

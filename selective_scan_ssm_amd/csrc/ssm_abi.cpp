@@ -285,6 +285,41 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
     return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t ssm_scan_2d_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t d_inner,
+                                   int64_t d_state, int has_z, int io_dtype) {
+    if (check_dtype(io_dtype) || batch < 0 || height < 0 || width < 0 || d_inner < 0 || d_state < 1 ||
+        d_state > SSM_MAX_D_STATE)
+        return static_cast<size_t>(-1);
+    const int64_t L = mul3(height, width, 1);
+    if (L < 0) return static_cast<size_t>(-1);
+    ssm::ScanArgs a = make_args(nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr, batch, L, d_inner, d_state,
+                                io_dtype, nullptr, 0);
+    return ssm::scan_2d_workspace(a, has_z != 0);
+}
+
+int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                    const float *A, const void *B, const void *C, const float *D, const void *z,
+                    const float *h0, void *y, float *last_state, int64_t batch, int64_t height,
+                    int64_t width, int64_t d_inner, int64_t d_state, int direction, int io_dtype,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (direction < 0 || direction > 3) return SSM_ERR_SHAPE;
+    if (height < 0 || width < 0) return SSM_ERR_SHAPE;
+    const int64_t L = mul3(height, width, 1);
+    if (L < 0) return SSM_ERR_SHAPE;
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, L, d_inner,
+                          d_state, io_dtype);
+    if (r) return r;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, L, d_inner, d_state, io_dtype, workspace,
+                                workspace_bytes);
+    const size_t need = ssm::scan_2d_workspace(a, z != nullptr);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_scan_2d(a, height, width, direction, static_cast<hipStream_t>(stream)));
+}
+
 int ssm_causal_conv1d_fwd(const void *x, const float *weight, const float *bias,
                           const void *conv_state_in, void *out, void *conv_state_out,
                           int apply_silu, int64_t batch, int64_t seqlen, int64_t d_inner,

@@ -60,6 +60,10 @@ struct BwdArgs {
 size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 
+// The 2-D scan orders: gather into scan order, the forward scan, scatter y.
+size_t scan_2d_workspace(const ScanArgs &a, bool has_z);
+hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int direction, hipStream_t s);
+
 struct ConvArgs {
     const void *x;                        // io dtype (batch, seqlen, dim)
     const float *weight, *bias;           // (dim, width), (dim)

@@ -241,3 +241,43 @@ def causal_conv1d_update(conv_state, x, weight, bias=None, silu=True, out=None):
                                       int(bool(silu)), Bt, Dd, K, _IO[io], _stream(x.device))
     _check(rc, "ssm_causal_conv1d_update")
     return y
+
+
+def scan_fwd_2d(x, delta, A, B, C, height, width, direction, D=None, z=None, delta_bias=None,
+                delta_softplus=True, h0=None, return_last_state=False, out=None, workspace=None):
+    """One direction (0 row-major, 1 reverse, 2 column-major, 3 reverse
+    column-major) of the 2-D scan over height x width patches held row-major
+    on the sequence axis; y comes back at each patch's position."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, Dd = x.shape
+    N = A.shape[-1]
+    if T != height * width:
+        raise ValueError("seqlen must be height * width")
+    _dev(x, "x", io)
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(B, "B", io, (Bt, T, N))
+    _dev(C, "C", io, (Bt, T, N))
+    _dev(A, "A", torch.float32, (Dd, N))
+    _dev(D, "D", torch.float32, (Dd,))
+    _dev(delta_bias, "delta_bias", torch.float32, (Dd,))
+    _dev(h0, "h0", torch.float32, (Bt, Dd, N))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    last = torch.empty((Bt, Dd, N), dtype=torch.float32, device=x.device) if return_last_state else None
+    need = lib.ssm_scan_2d_workspace_bytes(Bt, height, width, Dd, N, int(z is not None), _IO[io])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("ssm_scan_2d_workspace_bytes: invalid arguments")
+    ws = None
+    if need:
+        ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
+            need, dtype=torch.uint8, device=x.device)
+    rc = lib.ssm_scan_fwd_2d(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                             _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
+                             Bt, height, width, Dd, N, int(direction), _IO[io], _ptr(ws), need,
+                             _stream(x.device))
+    _check(rc, "ssm_scan_fwd_2d")
+    return (y, last) if return_last_state else y

@@ -286,3 +286,29 @@ def test_conv_alias(lib):
     a = conv_args()
     a["out"] = a["st_in"]
     assert call_conv_update(lib, a) == EALIAS
+
+
+# ------------------------------------------------------------- 2-D scan
+def call_2d(lib, a, height=4, width=4, direction=1):
+    return lib.ssm_scan_fwd_2d(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"],
+                               a["C"], a["D"], a["z"], a["h0"], a["y"], a["last"], a["batch"],
+                               height, width, a["dim"], a["dstate"], direction, a["io"], a["ws"],
+                               a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,kw,code", [
+    (dict(), dict(direction=4), ESHAPE), (dict(), dict(direction=-1), ESHAPE),
+    (dict(), dict(height=-1), ESHAPE), (dict(), dict(height=1 << 40, width=1 << 40), ESHAPE),
+    (dict(x=None), dict(), ENULL), (dict(dstate=0), dict(), ESHAPE), (dict(io=3), dict(), EDTYPE),
+    (dict(ws_bytes=16), dict(), EWS), (dict(ws=None, ws_bytes=0), dict(), EWS),
+    (dict(batch=0), dict(), OK),
+])
+def test_scan_2d_validation(lib, over, kw, code):
+    assert call_2d(lib, scan_args(**over), **kw) == code
+
+
+def test_scan_2d_workspace(lib):
+    # a copy of x, delta, z, B, C, y plus the forward's own workspace
+    need = lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 16, 1, BF16)
+    assert need >= 2 * 64 * (4 * 96 + 2 * 16) * 2
+    assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 0, 1, BF16) == (1 << 64) - 1
