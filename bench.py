@@ -292,9 +292,20 @@ def bench_workload(args, dev):
         launches = 1
         cur = [0]
 
+        if args.direction is not None:
+            if kind == "sm1":
+                raise SystemExit("--direction runs ssm_scan_fwd_2d: use workload 2 or 3")
+            need = lib.ssm_scan_2d_workspace_bytes(w.batch, 1, w.seqlen, w.d_inner, N, 1, io_code)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
         def step():
             s = sets[cur[0] % len(sets)]
             cur[0] += 1
+            if args.direction is not None:      # the 1-D scan in the given order (height 1)
+                ops.scan_fwd_2d(s["x"], s["delta"], s["A"], s["B"], s["C"], 1, w.seqlen, args.direction,
+                                D=s["D"], z=s["z"], delta_bias=s["delta_bias"], h0=s["h0"],
+                                out=s["y"], workspace=ws)
+                return
             fn = ops.sm1_scan_fwd if kind == "sm1" else ops.scan_fwd
             fn(s["x"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                delta_bias=s["delta_bias"], h0=s["h0"], return_last_state=True, out=s["y"],
@@ -323,8 +334,10 @@ def bench_workload(args, dev):
     io_b = 2 if io == gen.BF16 else 4
     alg = algorithmic_bytes(w, io_b)
     hbm_gbs = alg / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(kind, w.name)
-    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)", "rows": "ssm_scan_fwd (scan_rows_kernel)",
+    traffic = traffic_from_profile(kind, w.name) if args.direction is None else None
+    kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)",
+             "rows": "ssm_scan_fwd (scan_rows_kernel)" if args.direction is None else
+                     "ssm_scan_fwd_2d (gather + scan_rows_kernel + scatter, timed as one call)",
              "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
              "decode": "ssm_state_update (state_update_rows_kernel)"}[kind]
     if kind in ("scan", "rows") and w.d_state > 1:
@@ -348,7 +361,8 @@ def bench_workload(args, dev):
         log("[bench] cpu baseline (oracle on a sample)")
         cpu = cpu_baseline(inp0, w, args.cpu_seconds)
 
-    cfg = {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.d_inner,
+    cfg = {"workload": w.name + ("" if args.direction is None else f"-order{args.direction}"),
+           "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.d_inner,
            "d_state": w.d_state, "io": io, "state": "fp32", "seed": args.workload}
     if kind == "decode":
         cfg["layers"] = w.layers
@@ -656,6 +670,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (the gradient) on a scan workload instead of the forward")
+    ap.add_argument("--direction", type=int, default=None,
+                    help="scan order through ssm_scan_fwd_2d (height 1): 0 forward, 1 reversed")
     ap.add_argument("--conv", action="store_true",
                     help="time ssm_causal_conv1d_fwd (width 4, SiLU) on a scan workload's x instead")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "COMMAND"))
