@@ -61,6 +61,9 @@ def _bind(lib):
     lib.oracle_causal_conv1d.restype = None
     lib.oracle_conv1d_update.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_int, _L, _L, _L, _L, _L]
     lib.oracle_conv1d_update.restype = None
+    lib.oracle_ssd_scan.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
+                                    _dp, _dp, _L, _L, _L, _L, _L, _L, _L]
+    lib.oracle_ssd_scan.restype = None
     return lib
 
 
@@ -287,3 +290,29 @@ def scan_2d(x, delta, A, B, C, height, width, direction, D=None, z=None, delta_b
     out = np.empty_like(y)
     out[:, perm] = y
     return out, last
+
+
+def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+             threads: int = 1, lib=None):
+    """The Mamba-2 multi-head scan, step by step in fp64 (oracle_ssd_scan).
+    x, z: (Bt, T, H, P); dt: (Bt, T, H); A, D, dt_bias: (H,); B, C: (Bt, T, N);
+    h0: (Bt, H, P, N).  Returns (y (Bt, T, H, P), last_state (Bt, H, P, N))."""
+    lib = lib or load()
+    x, dt, A, B, C = _f64(x), _f64(dt), _f64(A), _f64(B), _f64(C)
+    D, z, dt_bias, h0 = _f64(D), _f64(z), _f64(dt_bias), _f64(h0)
+    Bt, T, H, P = x.shape
+    N = B.shape[2]
+    assert dt.shape == (Bt, T, H) and A.shape == (H,)
+    assert B.shape == (Bt, T, N) and C.shape == (Bt, T, N)
+    assert z is None or z.shape == x.shape
+    assert h0 is None or h0.shape == (Bt, H, P, N)
+    y = np.zeros((Bt, T, H, P), dtype=np.float64)
+    last = np.zeros((Bt, H, P, N), dtype=np.float64)
+
+    def go(c0, c1):
+        lib.oracle_ssd_scan(_ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(A),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
+                            Bt, T, H, P, N, c0, c1)
+
+    _run_chains(go, Bt * H * P, threads)
+    return y, last

@@ -47,6 +47,7 @@
  *                                 that produces the scan's x (below)
  *   oracle_conv1d_update       -- the same for one decode token, with the rolling
  *                                 window of past inputs
+ *   oracle_ssd_scan            -- the Mamba-2 multi-head scan (scalar decay per head)
  */
 #include <math.h>
 #include <stddef.h>
@@ -360,5 +361,76 @@ void oracle_conv1d_update(double *state, const double *x, const double *w, const
             st[k] = st[k + 1];
         if (H > 0)
             st[H - 1] = x[b * dim + d];
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * The Mamba-2 scan (youngju.dev guide, section 6 "Mamba 2"): a multi-head SSM
+ * whose decay is one scalar per head.  The block's input projection gives,
+ * per step, x and z (H heads of P channels each), one B and one C of N
+ * values shared by every head, and one dt per head; A is a scalar per head
+ * (the block keeps one A_log per head; A = -exp(A_log) as for Mamba-1).  The
+ * section's sketch of the operation is the same recurrence as Mamba-1,
+ * x[t] = A[t] x[t-1] + B[t] u[t], y[t] = C[t]^T x[t]; here, with the
+ * discretisation of the Mamba-1 sections, every channel p of head h carries
+ * an N-vector state:
+ *
+ *   Delta = softplus(dt[b,t,h] + dt_bias[h])       (or without the softplus)
+ *   s[n] <- exp(Delta * A[h]) * s[n] + Delta * B[b,t,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n C[b,t,n] s[n] + D[h] x[b,t,h,p]) * SiLU(z[b,t,h,p])
+ *
+ * The section's chunked evaluation (matrix products inside a chunk, the
+ * recurrence between chunks) is an algorithm for the same result and is not
+ * used here: this is the step-by-step definition.
+ *
+ * Layouts: x, z, y (B, T, H, P); dt (B, T, H); B, C (B, T, N); A, D,
+ * dt_bias (H); h0, last_state (B, H, P, N).  Optional: dt_bias, D, z, h0,
+ * last_state (NULL).  Chains c = (b * H + h) * P + p are independent.
+ */
+void oracle_ssd_scan(const double *x, const double *dt, const double *dt_bias, int dt_softplus,
+                     const double *A, const double *Bm, const double *Cm, const double *Dv,
+                     const double *z, const double *h0, double *y, double *last_state,
+                     long nbatch, long seqlen, long nheads, long headdim, long dstate,
+                     long chain_begin, long chain_end)
+{
+    if (dstate < 1)
+        return;
+    double s[dstate];
+    const long nchains = nbatch * nheads * headdim;
+    for (long c = chain_begin; c < chain_end && c < nchains; ++c) {
+        const long p = c % headdim;
+        const long h = (c / headdim) % nheads;
+        const long b = c / (headdim * nheads);
+
+        for (long n = 0; n < dstate; ++n)
+            s[n] = h0 ? h0[c * dstate + n] : 0.0;
+
+        for (long t = 0; t < seqlen; ++t) {
+            const long bt = b * seqlen + t;                 /* row of (B, T, .) */
+            const long xi = (bt * nheads + h) * headdim + p;  /* element of (B, T, H, P) */
+            const double xv = x[xi];
+
+            double v = dt[bt * nheads + h];
+            if (dt_bias)
+                v += dt_bias[h];
+            const double delta = dt_softplus ? softplus(v) : v;
+            const double decay = exp(delta * A[h]);
+
+            for (long n = 0; n < dstate; ++n)
+                s[n] = decay * s[n] + delta * Bm[bt * dstate + n] * xv;
+
+            double out = 0.0;
+            for (long n = 0; n < dstate; ++n)
+                out += Cm[bt * dstate + n] * s[n];
+            if (Dv)
+                out += Dv[h] * xv;
+            if (z)
+                out *= silu(z[xi]);
+            y[xi] = out;
+        }
+
+        if (last_state)
+            for (long n = 0; n < dstate; ++n)
+                last_state[c * dstate + n] = s[n];
     }
 }

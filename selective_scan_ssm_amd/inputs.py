@@ -142,3 +142,76 @@ def workload_inputs(cfg: int, seed: Optional[int] = None, layer: int = 0, **over
               a_kind=w.a_kind, h0_kind=w.h0_kind, seed=cfg if seed is None else seed, layer=layer)
     kw.update(over)
     return make_inputs(**kw)
+
+
+# ------------------------------------------------------------- Mamba-2 (SSD)
+# The multi-head scan of the youngju.dev guide's Mamba 2 section: the block is
+# Mamba2Block(d_model, d_state=64, n_heads=8, chunk_size=64) with head size
+# d_model / n_heads, one A_log per head drawn from N(0, 1), and an input
+# projection that yields x and z (d_model each), B and C (d_state each, shared
+# by the heads) and dt (one per head).
+#   x, z, dt, B, C ~ N(0, 1)
+#   A[h]          = -exp(A_log[h]), A_log[h] ~ N(0, 1)
+#   dt_bias[h]    = log(expm1(dt_h)), dt_h log-uniform in [1e-3, 1e-1]
+#   D[h]          ~ N(0, 1)
+#   h0            zero / N(0, 1) / absent
+
+@dataclasses.dataclass(frozen=True)
+class SsdWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    n_heads: int
+    d_state: int
+    io: str
+    h0_kind: str = "none"
+
+    @property
+    def headdim(self) -> int:
+        return self.d_model // self.n_heads
+
+
+SSD_WORKLOADS = {
+    "mamba2-2.7b-ssd-layer-bf16": SsdWorkload("mamba2-2.7b-ssd-layer-bf16", 4, 8192, 2560, 8, 64, BF16),
+    "mamba2-130m-ssd-layer-bf16": SsdWorkload("mamba2-130m-ssd-layer-bf16", 8, 2048, 768, 8, 64, BF16),
+}
+
+
+def make_ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, d_state: int,
+                    io: str = F32, h0_kind: str = "zero", seed: int = 0, with_z: bool = True,
+                    with_D: bool = True, with_bias: bool = True) -> dict:
+    """Draw one set of Mamba-2 scan inputs: x, z (B,T,H,P), dt (B,T,H), B, C
+    (B,T,N) in the io dtype; A, D, dt_bias (H) and h0 (B,H,P,N) in fp32."""
+    Bb, T, H, P, N = batch, seqlen, nheads, headdim, d_state
+    out = {"io": io, "batch": Bb, "seqlen": T, "nheads": H, "headdim": P, "d_state": N}
+    out["x"] = _store(_normal(seed, "x", (Bb, T, H, P)), io)
+    out["dt"] = _store(_normal(seed, "delta", (Bb, T, H)), io)
+    out["z"] = _store(_normal(seed, "z", (Bb, T, H, P)), io) if with_z else None
+    out["B"] = _store(_normal(seed, "B", (Bb, T, N)), io)
+    out["C"] = _store(_normal(seed, "C", (Bb, T, N)), io)
+    if with_bias:
+        r = _rng(seed, "bias")
+        dtv = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), size=H))
+        out["dt_bias"] = np.log(np.expm1(dtv)).astype(np.float32)
+    else:
+        out["dt_bias"] = None
+    out["A"] = (-np.exp(_normal(seed, "A", (H,)))).astype(np.float32)
+    out["D"] = _normal(seed, "D", (H,)) if with_D else None
+    if h0_kind == "zero":
+        out["h0"] = np.zeros((Bb, H, P, N), dtype=np.float32)
+    elif h0_kind == "normal":
+        out["h0"] = _normal(seed, "h0", (Bb, H, P, N))
+    elif h0_kind == "none":
+        out["h0"] = None
+    else:
+        raise ValueError(h0_kind)
+    return out
+
+
+def ssd_workload_inputs(name: str, seed: int = 0, **over) -> dict:
+    w = SSD_WORKLOADS[name]
+    kw = dict(batch=w.batch, seqlen=w.seqlen, nheads=w.n_heads, headdim=w.headdim, d_state=w.d_state,
+              io=w.io, h0_kind=w.h0_kind, seed=seed)
+    kw.update(over)
+    return make_ssd_inputs(**kw)

@@ -522,4 +522,119 @@ def pin_scan2d_degenerate_grids(lib):
     assert np.array_equal(y1, y3) and np.array_equal(l1, l3)
 
 
+# The Mamba-2 multi-head scan (oracle.ssd_scan) against its duality form and
+# the Mamba-1 scan it specialises (youngju.dev guide, section 6 "Mamba 2":
+# the SSM with a scalar decay per head is a semiseparable matrix acting on
+# the sequence, i.e. a masked attention-like product).
+
+def _ssd_small(seed=60, Bt=2, T=19, H=3, P=4, N=5, h0_kind="normal", **kw):
+    i = gen.make_ssd_inputs(Bt, T, H, P, N, io=gen.F32, h0_kind=h0_kind, seed=seed, **kw)
+    return {k: (v.astype(np.float64) if isinstance(v, np.ndarray) else v) for k, v in i.items()}
+
+
+def _ssd(lib, i, **over):
+    kw = dict(D=i["D"], z=i["z"], dt_bias=i["dt_bias"], dt_softplus=True, h0=i["h0"])
+    kw.update(over)
+    return oracle.ssd_scan(i["x"], i["dt"], i["A"], i["B"], i["C"], lib=lib, **kw)
+
+
+def ssd_matrix_form(x, dt, A, B, C, D=None, z=None, bias=None, softplus=True, h0=None):
+    """y = M x per (batch, head) with the lower-triangular semiseparable matrix
+    M[t, s] = (C_t . B_s) Delta_s exp(sum_{s<r<=t} Delta_r A_h), plus the decayed
+    initial state read out by C; last state likewise.  Exponent sums are taken
+    term by term (no cumulative-sum differences)."""
+    x, dt, B, C = (np.asarray(a, np.float64) for a in (x, dt, B, C))
+    Bt, T, H, P = x.shape
+    N = B.shape[2]
+    delta = ref_delta(dt, bias, softplus)                                 # (Bt,T,H)
+    y = np.zeros((Bt, T, H, P))
+    last = np.zeros((Bt, H, P, N))
+    for b in range(Bt):
+        G = C[b] @ B[b].T                                                 # (T,T): C_t . B_s
+        for h in range(H):
+            a = delta[b, :, h] * A[h]
+            E = np.zeros((T + 1, T + 1))                                  # E[t,s] = sum_{s<r<=t} a_r
+            for t in range(T):
+                for s_ in range(t + 1):
+                    E[t, s_] = sum(a[r] for r in range(s_ + 1, t + 1))
+            M = np.zeros((T, T))
+            for t in range(T):
+                for s_ in range(t + 1):
+                    M[t, s_] = G[t, s_] * delta[b, s_, h] * math.exp(E[t, s_])
+            yh = M @ x[b, :, h, :]                                        # (T,P)
+            to_end = np.array([math.exp(sum(a[r] for r in range(s_ + 1, T))) for s_ in range(T)])
+            lh = (x[b, :, h, :] * (delta[b, :, h] * to_end)[:, None]).T @ B[b]   # (P,N)
+            if h0 is not None:
+                dec = np.array([math.exp(sum(a[r] for r in range(t + 1))) for t in range(T)])
+                yh = yh + (C[b] * dec[:, None]) @ np.asarray(h0[b, h], np.float64).T
+                lh = lh + math.exp(float(np.sum(a))) * np.asarray(h0[b, h], np.float64)
+            if D is not None:
+                yh = yh + D[h] * x[b, :, h, :]
+            y[b, :, h, :] = ref_gate(yh, None if z is None else np.asarray(z, np.float64)[b, :, h, :])
+            last[b, h] = lh
+    return y, last
+
+
+def pin_ssd_semiseparable_matrix_form(lib):
+    i = _ssd_small()
+    y, last = _ssd(lib, i)
+    ym, lm = ssd_matrix_form(i["x"], i["dt"], i["A"], i["B"], i["C"], i["D"], i["z"], i["dt_bias"],
+                             True, i["h0"])
+    assert _rel(y, ym) < 1e-12 and _rel(last, lm) < 1e-12
+    # no options: no gate, skip, bias, softplus or initial state
+    j = _ssd_small(seed=61, T=13, H=2, P=3, N=4, h0_kind="none", with_z=False, with_D=False,
+                   with_bias=False)
+    j["dt"] = np.abs(j["dt"]) * 0.3
+    y, last = _ssd(lib, j, dt_softplus=False)
+    ym, lm = ssd_matrix_form(j["x"], j["dt"], j["A"], j["B"], j["C"], softplus=False)
+    assert _rel(y, ym) < 1e-12 and _rel(last, lm) < 1e-12
+
+
+def pin_ssd_is_mamba1_with_tied_decay(lib):
+    """P channels of head h scanned by the Mamba-1 scan with A[d, n] = A_h,
+    Delta[d] = Delta_h, D[d] = D_h for every one of the head's channels."""
+    i = _ssd_small(seed=62, T=23, H=3, P=4, N=3)
+    Bt, T, H, P, N = 2, 23, 3, 4, 3
+    rep = lambda v: np.repeat(np.asarray(v, np.float64), P, axis=-1)
+    y1, l1 = oracle.selective_scan(i["x"].reshape(Bt, T, H * P), rep(i["dt"]),
+                                   np.repeat(i["A"], P)[:, None] * np.ones((1, N)), i["B"], i["C"],
+                                   D=rep(i["D"]), z=i["z"].reshape(Bt, T, H * P),
+                                   delta_bias=rep(i["dt_bias"]), h0=i["h0"].reshape(Bt, H * P, N), lib=lib)
+    y, last = _ssd(lib, i)
+    assert _rel(y, y1.reshape(y.shape)) < 1e-14 and _rel(last, l1.reshape(last.shape)) < 1e-14
+
+
+def pin_ssd_A_zero_running_sum(lib):
+    i = _ssd_small(seed=63, T=17, H=2, P=3, N=4)
+    i["A"] = np.zeros_like(i["A"])
+    y, last = _ssd(lib, i, D=None, z=None)
+    delta = ref_delta(i["dt"], i["dt_bias"], True)                        # (Bt,T,H)
+    inc = delta[..., None, None] * i["x"][..., None] * i["B"][:, :, None, None, :]   # (Bt,T,H,P,N)
+    s = i["h0"][:, None] + np.cumsum(inc, axis=1)
+    assert _rel(y, np.einsum("btn,bthpn->bthp", i["C"], s)) < 1e-12
+    assert _rel(last, s[:, -1]) < 1e-12
+
+
+def pin_ssd_delta_zero_keeps_state(lib):
+    i = _ssd_small(seed=64, T=9, H=2, P=3, N=4)
+    i["dt"] = np.zeros_like(i["dt"])
+    y, last = _ssd(lib, i, dt_bias=None, dt_softplus=False)
+    assert np.array_equal(last, i["h0"])
+    ref = np.einsum("btn,bhpn->bthp", i["C"], i["h0"]) + i["D"][None, None, :, None] * i["x"]
+    assert _rel(y, ref_gate(ref, i["z"])) < 1e-13
+
+
+def pin_ssd_continuation(lib):
+    i = _ssd_small(seed=65, T=21, H=2, P=3, N=4)
+    y, last = _ssd(lib, i)
+    cut = lambda a, sl: None if a is None else a[:, sl]
+    a, b = slice(0, 8), slice(8, None)
+    j = dict(i, x=cut(i["x"], a), dt=cut(i["dt"], a), z=cut(i["z"], a), B=cut(i["B"], a), C=cut(i["C"], a))
+    y1, l1 = _ssd(lib, j)
+    k = dict(i, x=cut(i["x"], b), dt=cut(i["dt"], b), z=cut(i["z"], b), B=cut(i["B"], b), C=cut(i["C"], b),
+             h0=l1)
+    y2, l2 = _ssd(lib, k)
+    assert _rel(np.concatenate([y1, y2], axis=1), y) < 1e-13 and _rel(l2, last) < 1e-13
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -80,6 +80,26 @@ MUTANTS = [
     ("conv decode: window not shifted", "st[k] = st[k + 1];", "st[k] = st[k];"),
     ("conv decode: newest tap on the oldest input", "acc += w[d * width + H] * x[b * dim + d];",
      "acc += w[d * width] * x[b * dim + d];"),
+    # the Mamba-2 multi-head scan
+    ("ssd: decay of head 0", "const double decay = exp(delta * A[h]);",
+     "const double decay = exp(delta * A[0]);"),
+    ("ssd: decay sign", "const double decay = exp(delta * A[h]);",
+     "const double decay = exp(-delta * A[h]);"),
+    ("ssd: input without Delta", "s[n] = decay * s[n] + delta * Bm[bt * dstate + n] * xv;",
+     "s[n] = decay * s[n] + Bm[bt * dstate + n] * xv;"),
+    ("ssd: dt of head 0", "double v = dt[bt * nheads + h];", "double v = dt[bt * nheads];"),
+    ("ssd: bias of head 0", "v += dt_bias[h];", "v += dt_bias[0];"),
+    ("ssd: softplus dropped", "const double delta = dt_softplus ? softplus(v) : v;",
+     "const double delta = v;"),
+    ("ssd: x in (B, T, P, H) order", "const long xi = (bt * nheads + h) * headdim + p;",
+     "const long xi = (bt * headdim + p) * nheads + h;"),
+    ("ssd: head from the wrong digit", "const long h = (c / headdim) % nheads;",
+     "const long h = c % nheads;"),
+    ("ssd: C replaced by B", "out += Cm[bt * dstate + n] * s[n];", "out += Bm[bt * dstate + n] * s[n];"),
+    ("ssd: D of head 0", "out += Dv[h] * xv;", "out += Dv[0] * xv;"),
+    ("ssd: gate by z", "out *= silu(z[xi]);", "out *= z[xi];"),
+    ("ssd: h0 ignored", "s[n] = h0 ? h0[c * dstate + n] : 0.0;", "s[n] = 0.0;"),
+    ("ssd: last state not final", "last_state[c * dstate + n] = s[n];", "last_state[c * dstate + n] = 0.0;"),
 ]
 
 
