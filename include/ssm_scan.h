@@ -232,6 +232,36 @@ int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weigh
                              const float *bias, void *out, int apply_silu, int64_t batch,
                              int64_t d_inner, int64_t width, int io_dtype, void *stream);
 
+/*
+ * ssd_scan_fwd -- the Mamba-2 multi-head scan ("Mamba State Space Models
+ * complete guide", youngju.dev, section 6 "Mamba 2": a multi-head SSM whose
+ * decay is one scalar per head; the block's input projection yields x and z
+ * per head, one B and one C per step shared by the heads, and one dt per
+ * head).  For every batch row b, head h and channel p < headdim:
+ *     Delta = softplus(dt[b,t,h] + dt_bias[h])        (softplus only if dt_softplus)
+ *     s[n] <- exp(Delta * A[h]) s[n] + Delta * B[b,t,n] * x[b,t,h,p]
+ *     y[b,t,h,p] = (sum_n C[b,t,n] s[n] + D[h] x[b,t,h,p]) * SiLU(z[b,t,h,p])
+ * starting from h0[b,h,p,:] (zeros if NULL); last_state receives s after the
+ * last step.  Evaluated in chunks of 64 steps with matrix products inside a
+ * chunk and the recurrence between chunks (the section's SSD evaluation).
+ *
+ *   x, z, y       : (batch, seqlen, nheads, headdim) io dtype, row-major
+ *   dt            : (batch, seqlen, nheads) io dtype
+ *   B, C          : (batch, seqlen, dstate) io dtype
+ *   A             : (nheads) fp32, required (negative for a decaying state)
+ *   D, dt_bias    : (nheads) fp32, optional
+ *   h0, last_state: (batch, nheads, headdim, dstate) fp32, optional
+ * Supported: headdim a multiple of 16; dstate 32 or 64, and 128 for bf16 io,
+ * else SSM_ERR_SHAPE.  x, z, y, B, C, h0, last_state must be 16-byte aligned
+ * (SSM_ERR_ALIGN); one batch row of x (plus 128 steps) must span less than
+ * 2 GiB (SSM_ERR_SHAPE).  Outputs may not overlap inputs (SSM_ERR_ALIAS).
+ * All pointers are device memory, owned by the caller; nothing is allocated.
+ */
+int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                 int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ssm_status_string(int status);
 

@@ -383,4 +383,52 @@ int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weigh
     return hip_status(ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream)));
 }
 
+int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                 int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *stream) {
+    if (int r = check_dtype(io_dtype)) return r;
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0) return SSM_ERR_SHAPE;
+    if (!ssm::ssd_supported(headdim, dstate, io_dtype == SSM_BF16)) return SSM_ERR_SHAPE;
+    const size_t es = io_size(io_dtype);
+    const int64_t hp = mul3(nheads, headdim, 1);
+    const int64_t n_bthp = mul3(batch, seqlen, hp < 0 ? -1 : hp);
+    const int64_t n_bth = mul3(batch, seqlen, nheads);
+    const int64_t n_btn = mul3(batch, seqlen, dstate);
+    const int64_t n_bhpn = mul3(batch, hp < 0 ? -1 : hp, dstate);
+    if (hp < 0 || n_bthp < 0 || n_bth < 0 || n_btn < 0 || n_bhpn < 0) return SSM_ERR_SHAPE;
+    // 32-bit byte offsets within one batch row, including the chunk fetched past the end
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    if (mul3(seqlen + 128, hp, es) > lim || mul3(seqlen + 128, dstate, es) > lim ||
+        mul3(seqlen + 128, nheads, es) > lim)
+        return SSM_ERR_SHAPE;
+    if (mul3(batch, hp / 16, 1) > lim) return SSM_ERR_SHAPE;      // workgroups (1-D grid)
+    if (batch == 0 || nheads == 0) return SSM_OK;
+    if (!A) return SSM_ERR_NULL;
+    if (seqlen > 0 && (!x || !dt || !B || !C || !y)) return SSM_ERR_NULL;
+    const void *v16[] = {x, z, y, B, C, h0, last_state};
+    for (const void *p : v16)
+        if (p && !aligned(p, 16)) return SSM_ERR_ALIGN;
+    if (dt && !aligned(dt, es)) return SSM_ERR_ALIGN;
+    const void *f_ptrs[] = {dt_bias, A, D};
+    for (const void *p : f_ptrs)
+        if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+    const Range outs[] = {range(y, seqlen > 0 ? n_bthp : 0, es), range(last_state, n_bhpn, 4)};
+    const Range ins[] = {range(x, n_bthp, es), range(dt, n_bth, es),    range(z, n_bthp, es),
+                         range(B, n_btn, es),  range(C, n_btn, es),     range(A, nheads, 4),
+                         range(D, nheads, 4),  range(dt_bias, nheads, 4), range(h0, n_bhpn, 4)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    ssm::SsdArgs a;
+    a.x = x; a.dt = dt; a.z = z; a.B = B; a.C = C;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.h0 = h0;
+    a.y = y; a.last_state = last_state;
+    a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.headdim = headdim; a.dstate = dstate;
+    a.softplus = dt_softplus ? 1 : 0;
+    a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    return hip_status(ssm::launch_ssd_scan(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

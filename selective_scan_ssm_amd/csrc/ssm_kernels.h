@@ -81,6 +81,19 @@ struct ConvUpdateArgs {
     int width, silu, bf16;
 };
 
+struct SsdArgs {
+    const void *x, *dt, *z, *B, *C;       // io dtype
+    const float *dt_bias, *A, *D, *h0;    // (H), (H), (H), (batch, H, P, N)
+    void *y;
+    float *last_state;
+    int64_t batch, seqlen, nheads, headdim, dstate;
+    int softplus, bf16;
+};
+
+// Mamba-2 multi-head scan (chunked, MFMA).
+bool ssd_supported(int64_t headdim, int64_t dstate, int bf16);
+hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t s);
+
 // Causal depthwise conv1d (+ SiLU), whole sequence and one decode token.
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);

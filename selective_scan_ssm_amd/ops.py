@@ -281,3 +281,38 @@ def scan_fwd_2d(x, delta, A, B, C, height, width, direction, D=None, z=None, del
                              _stream(x.device))
     _check(rc, "ssm_scan_fwd_2d")
     return (y, last) if return_last_state else y
+
+
+def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+                 return_last_state=False, out=None, last_state_out=None):
+    """Mamba-2 multi-head scan.  x, z: (batch, seqlen, nheads, headdim) fp32 or
+    bf16; dt: (batch, seqlen, nheads); B, C: (batch, seqlen, dstate) same dtype;
+    A, D, dt_bias: (nheads,) fp32; h0: (batch, nheads, headdim, dstate) fp32.
+    Returns y (same dtype as x) or (y, last_state fp32)."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, H, P = x.shape
+    N = B.shape[-1]
+    _dev(x, "x", io)
+    _dev(dt, "dt", io, (Bt, T, H))
+    _dev(z, "z", io, x.shape)
+    _dev(B, "B", io, (Bt, T, N))
+    _dev(C, "C", io, (Bt, T, N))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(D, "D", torch.float32, (H,))
+    _dev(dt_bias, "dt_bias", torch.float32, (H,))
+    _dev(h0, "h0", torch.float32, (Bt, H, P, N))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    last = None
+    if return_last_state:
+        last = last_state_out if last_state_out is not None else torch.empty(
+            (Bt, H, P, N), dtype=torch.float32, device=x.device)
+        _dev(last, "last_state_out", torch.float32, (Bt, H, P, N))
+    rc = lib.ssd_scan_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(A), _ptr(B),
+                          _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last), Bt, T, H, P, N,
+                          _IO[io], _stream(x.device))
+    _check(rc, "ssd_scan_fwd")
+    return (y, last) if return_last_state else y

@@ -312,3 +312,53 @@ def test_scan_2d_workspace(lib):
     need = lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 16, 1, BF16)
     assert need >= 2 * 64 * (4 * 96 + 2 * 16) * 2
     assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 0, 1, BF16) == (1 << 64) - 1
+
+
+# ------------------------------------------------------ Mamba-2 multi-head scan
+def ssd_args(batch=2, seqlen=16, nheads=3, headdim=32, dstate=64, io=F32, **over):
+    f = FakeDev()
+    a = dict(x=f(), dt=f(), dt_bias=f(), softplus=1, A=f(), B=f(), C=f(), D=f(), z=f(), h0=f(), y=f(),
+             last=f(), batch=batch, seqlen=seqlen, nheads=nheads, headdim=headdim, dstate=dstate, io=io,
+             stream=None)
+    a.update(over)
+    return a
+
+
+def call_ssd(lib, a):
+    return lib.ssd_scan_fwd(a["x"], a["dt"], a["dt_bias"], a["softplus"], a["A"], a["B"], a["C"], a["D"],
+                            a["z"], a["h0"], a["y"], a["last"], a["batch"], a["seqlen"], a["nheads"],
+                            a["headdim"], a["dstate"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), ENULL), (dict(dt=None), ENULL), (dict(A=None), ENULL), (dict(B=None), ENULL),
+    (dict(C=None), ENULL), (dict(y=None), ENULL),
+    (dict(dstate=16), ESHAPE), (dict(dstate=48), ESHAPE), (dict(dstate=128), ESHAPE),
+    (dict(io=BF16, dstate=256), ESHAPE), (dict(headdim=24), ESHAPE), (dict(headdim=0), ESHAPE),
+    (dict(batch=-1), ESHAPE), (dict(seqlen=-1), ESHAPE), (dict(nheads=-2), ESHAPE),
+    (dict(seqlen=1 << 24, nheads=8, headdim=64), ESHAPE),      # one batch row past 2 GiB
+    (dict(io=2), EDTYPE),
+    (dict(x=0x7f0000000008), EALIGN), (dict(B=0x7f0000000004), EALIGN), (dict(h0=0x7f0000000008), EALIGN),
+    (dict(A=0x7f0000000002), EALIGN), (dict(io=BF16, dt=0x7f0000000001), EALIGN),
+    (dict(batch=0), OK), (dict(nheads=0), OK), (dict(batch=0, x=None, y=None), OK),
+])
+def test_ssd_validation(lib, over, code):
+    assert call_ssd(lib, ssd_args(**over)) == code
+
+
+def test_ssd_supported_shapes_pass_validation_rules(lib):
+    # bf16 io also takes d_state 128; fp32 does not (its LDS staging would not fit)
+    assert call_ssd(lib, ssd_args(io=BF16, dstate=128, batch=0)) == OK
+    assert call_ssd(lib, ssd_args(io=F32, dstate=128, batch=0)) == ESHAPE
+
+
+def test_ssd_alias_detection(lib):
+    a = ssd_args()
+    a["y"] = a["x"] + 64
+    assert call_ssd(lib, a) == EALIAS
+    a = ssd_args()
+    a["last"] = a["h0"]
+    assert call_ssd(lib, a) == EALIAS
+    a = ssd_args()
+    a["y"] = a["last"]
+    assert call_ssd(lib, a) == EALIAS

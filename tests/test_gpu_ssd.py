@@ -1,0 +1,151 @@
+"""GPU parity of the Mamba-2 multi-head scan (ssd_scan_fwd through the C ABI)
+against the fp64 oracle (oracle_ssd_scan, pinned by the semiseparable-matrix
+form and by the Mamba-1 scan with tied decays) on the same seeded inputs.
+
+Tolerances as for the Mamba-1 scan (gpu_util.err, max relative error with an
+rms floor): 1e-5 for fp32 io, 2e-2 for bf16 io.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import gpu_util as G
+import oracle
+from selective_scan_ssm_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+IO = ("x", "dt", "z", "B", "C")
+F32 = ("A", "D", "dt_bias", "h0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_scan_ssm_amd import _lib
+    _lib.load()
+    assert len(_lib.hip_runtimes_mapped()) == 1
+
+
+def run_gpu(inp, softplus=True):
+    from selective_scan_ssm_amd import ops
+    t = {k: G.to_torch(inp[k], inp["io"]) for k in IO}
+    t.update({k: G.to_torch(inp[k], gen.F32) for k in F32})
+    y, last = ops.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               dt_bias=t["dt_bias"], dt_softplus=softplus, h0=t["h0"], return_last_state=True)
+    torch.cuda.synchronize()
+    return G.from_torch(y), G.from_torch(last)
+
+
+def decoded(inp):
+    d = {k: (None if inp[k] is None else gen.to_f64(inp[k], inp["io"])) for k in IO}
+    d.update({k: (None if inp[k] is None else np.asarray(inp[k], np.float64)) for k in F32})
+    return d
+
+
+def run_oracle(inp, softplus=True, heads=None, chans=None):
+    """The oracle on all chains, or on heads x channels (every batch row)."""
+    d = decoded(inp)
+    if heads is not None:
+        hi, pi = np.asarray(heads), np.asarray(chans)
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, hi][:, :, :, pi])
+        d = dict(d, x=sub(d["x"]), z=sub(d["z"]), dt=np.ascontiguousarray(d["dt"][:, :, hi]), A=d["A"][hi],
+                 D=None if d["D"] is None else d["D"][hi],
+                 dt_bias=None if d["dt_bias"] is None else d["dt_bias"][hi],
+                 h0=None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, hi][:, :, pi]))
+    return oracle.ssd_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                           dt_softplus=softplus, h0=d["h0"], threads=G.ORACLE_THREADS)
+
+
+def check(inp, softplus=True, tag=""):
+    G.say(f"[ssd] {tag} B={inp['batch']} T={inp['seqlen']} H={inp['nheads']} P={inp['headdim']} "
+          f"N={inp['d_state']} io={inp['io']}")
+    y, last = run_gpu(inp, softplus)
+    yo, lo = run_oracle(inp, softplus)
+    ey, el = G.err(y, yo), G.err(last, lo)
+    tol = G.TOL[inp["io"]]
+    G.say(f"[ssd] {tag} err_y={ey:.2e} err_last={el:.2e} (tol {tol:g})")
+    assert ey <= tol and el <= tol, (tag, ey, el)
+
+
+# --------------------------------------------------------------- small shapes
+@pytest.mark.parametrize("N", [32, 64])
+def test_ssd_fp32_ragged(N):
+    # 3 chunks (the last 22 steps), 32-channel tiles, h0 given, every option on
+    inp = gen.make_ssd_inputs(2, 150, 3, 32, N, io=gen.F32, h0_kind="normal", seed=700 + N)
+    check(inp, tag=f"f32-N{N}")
+
+
+def test_ssd_fp32_16_channel_tiles_options_off():
+    # headdim 48 (three 16-channel tiles), one full chunk, no z / D / bias / softplus / h0
+    inp = gen.make_ssd_inputs(3, 64, 2, 48, 32, io=gen.F32, h0_kind="none", seed=710, with_z=False,
+                              with_D=False, with_bias=False)
+    inp["dt"] = (np.abs(inp["dt"]) * np.float32(0.2)).astype(np.float32)
+    check(inp, softplus=False, tag="f32-plain")
+
+
+def test_ssd_fp32_fast_decay():
+    # heads with |A| up to e^4: chunk-relative decays underflow inside a chunk
+    inp = gen.make_ssd_inputs(1, 200, 4, 32, 64, io=gen.F32, h0_kind="normal", seed=711)
+    inp["A"] = (-np.exp(np.array([-4.0, 0.0, 2.5, 4.0]))).astype(np.float32)
+    inp["dt_bias"] = np.full(4, 0.5, np.float32)
+    check(inp, tag="f32-fast-decay")
+
+
+@pytest.mark.parametrize("N,P,T", [(64, 64, 300), (128, 32, 130), (32, 16, 65)])
+def test_ssd_bf16(N, P, T):
+    inp = gen.make_ssd_inputs(2, T, 4, P, N, io=gen.BF16, h0_kind="normal", seed=720 + N + P)
+    check(inp, tag=f"bf16-N{N}-P{P}")
+
+
+def test_ssd_one_step_and_empty():
+    inp = gen.make_ssd_inputs(2, 1, 2, 32, 64, io=gen.F32, h0_kind="normal", seed=730)
+    check(inp, tag="T1")
+    inp = gen.make_ssd_inputs(2, 0, 2, 32, 64, io=gen.F32, h0_kind="normal", seed=731)
+    y, last = run_gpu(inp)
+    assert y.size == 0 and np.array_equal(last, inp["h0"].astype(np.float64))
+
+
+def test_ssd_deterministic_and_continuation():
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_ssd_inputs(2, 256, 2, 64, 64, io=gen.F32, h0_kind="normal", seed=732)
+    y1, l1 = run_gpu(inp)
+    y2, l2 = run_gpu(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
+    # the same sequence in two calls (split off the 64-step grid), the second from the first's state
+    t = {k: G.to_torch(inp[k], gen.F32) for k in IO + F32}
+    cut = 100
+    a = {k: t[k][:, :cut].contiguous() for k in IO}
+    b = {k: t[k][:, cut:].contiguous() for k in IO}
+    ya, la = ops.ssd_scan_fwd(a["x"], a["dt"], t["A"], a["B"], a["C"], D=t["D"], z=a["z"], dt_bias=t["dt_bias"],
+                              h0=t["h0"], return_last_state=True)
+    yb, lb = ops.ssd_scan_fwd(b["x"], b["dt"], t["A"], b["B"], b["C"], D=t["D"], z=b["z"], dt_bias=t["dt_bias"],
+                              h0=la, return_last_state=True)
+    torch.cuda.synchronize()
+    yo, lo = run_oracle(inp)
+    ey = G.err(np.concatenate([G.from_torch(ya), G.from_torch(yb)], axis=1), yo)
+    el = G.err(G.from_torch(lb), lo)
+    G.say(f"[ssd] continuation err_y={ey:.2e} err_last={el:.2e}")
+    assert ey <= 1e-5 and el <= 1e-5
+
+
+# -------------------------------------------------- the layer shapes, full size
+@pytest.mark.parametrize("name", ["mamba2-130m-ssd-layer-bf16", "mamba2-2.7b-ssd-layer-bf16"])
+def test_ssd_layer_full_sampled(name):
+    """One launch at the full layer shape; sampled heads x channels (every
+    batch row, every step) against the oracle run on exactly those chains."""
+    inp = gen.ssd_workload_inputs(name, seed=740)
+    G.say(f"[ssd] {name} full size")
+    y, last = run_gpu(inp)
+    H, P = inp["nheads"], inp["headdim"]
+    heads = [0, H // 2, H - 1]
+    chans = list(range(0, 8)) + list(range(P - 8, P))
+    yo, lo = run_oracle(inp, heads=heads, chans=chans)
+    ys = y[:, :, heads][:, :, :, chans]
+    ls = last[:, heads][:, :, chans]
+    ey, el = G.err(ys, yo), G.err(ls, lo)
+    G.say(f"[ssd] {name} sampled err_y={ey:.2e} err_last={el:.2e}")
+    assert ey <= 2e-2 and el <= 2e-2
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(last))
