@@ -43,8 +43,13 @@ namespace ssm {
 namespace {
 
 constexpr int kQ = 64;          // chunk length (steps)
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: 4, one per 16-step block of a chunk, each owning that
+// block's output tiles for every 16-channel block of the workgroup; or
+// (WIDE) 4 per 16-channel block, one output tile each.  The wide form halves
+// each wave's chain of dependent LDS reads and MFMAs, which pays when there is
+// at most one workgroup per CU; with more, two narrow workgroups share a CU
+// better (the wide one saturates a CU's LDS on its own).
+template <int PT, bool WIDE> constexpr int waves_for() { return WIDE ? 4 * (PT / 16) : 4; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -110,15 +115,58 @@ template <> struct Mma<float> {
     }
 };
 
-// exp(x) for a chunk-relative exponent x <= 0
-__device__ __forceinline__ float ssd_exp(FastMath, float x) { return fast_exp2(x * kLog2e); }
-__device__ __forceinline__ float ssd_exp(PreciseMath, float x) { return expm1_accurate(x) + 1.0f; }
-// h <- exp(x) h (the carried state's decay over a chunk)
-__device__ __forceinline__ f32x4_t ssd_decay(FastMath, float x, f32x4_t h) { return h * fast_exp2(x * kLog2e); }
-__device__ __forceinline__ f32x4_t ssd_decay(PreciseMath, float x, f32x4_t h) {
-    const float f = expm1_accurate(x);
-    return f32x4_t{fmaf(f, h[0], h[0]), fmaf(f, h[1], h[1]), fmaf(f, h[2], h[2]), fmaf(f, h[3], h[3])};
-}
+// Chunk prefix sums of a_t = Delta_t A in "scaled" units: log2 units (a
+// log2(e)) with fp32 sums for FastMath, natural units with fp64 sums for
+// PreciseMath.  exp of a difference d of two prefixes, and of the carried
+// state's decay over a chunk, in those units.
+template <typename M> struct Steps;
+template <> struct Steps<FastMath> {
+    using real = float;
+    static constexpr float kScale = kLog2e;
+    static __device__ __forceinline__ float ex(float d) { return fast_exp2(d); }
+    static __device__ __forceinline__ f32x4_t decay(float d, f32x4_t h) { return h * fast_exp2(d); }
+    // inclusive prefix over the 64 lanes: row_shr 1, 2, 4, 8 inside each row of
+    // 16 lanes (bound_ctrl: 0 from outside the row), then the row totals
+    template <int CTRL> static __device__ __forceinline__ float shr(float v) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+    }
+    static __device__ __forceinline__ float prefix(float v, int lane) {
+        v += shr<0x111>(v);
+        v += shr<0x112>(v);
+        v += shr<0x114>(v);
+        v += shr<0x118>(v);
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+        const int row = lane >> 4;
+        return v + ((row >= 1 ? r0 : 0.0f) + (row >= 2 ? r1 : 0.0f) + (row >= 3 ? r2 : 0.0f));
+    }
+    // v of lane l, l the same in every lane
+    static __device__ __forceinline__ float lane_value(float v, int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+    }
+    // v of lane l, l per lane
+    static __device__ __forceinline__ float gather(float v, int l) { return __shfl(v, l); }
+};
+template <> struct Steps<PreciseMath> {
+    using real = double;
+    static constexpr float kScale = 1.0f;
+    static __device__ __forceinline__ float ex(float d) { return expm1_accurate(d) + 1.0f; }
+    static __device__ __forceinline__ f32x4_t decay(float d, f32x4_t h) {
+        const float f = expm1_accurate(d);
+        return f32x4_t{fmaf(f, h[0], h[0]), fmaf(f, h[1], h[1]), fmaf(f, h[2], h[2]), fmaf(f, h[3], h[3])};
+    }
+    static __device__ __forceinline__ double prefix(double v, int lane) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double u = __shfl_up(v, o);
+            if (lane >= o) v += u;
+        }
+        return v;
+    }
+    static __device__ __forceinline__ double lane_value(double v, int l) { return __shfl(v, l); }
+    static __device__ __forceinline__ double gather(double v, int l) { return __shfl(v, l); }
+};
 
 // io rows of four consecutive elements (8 bytes bf16, 16 bytes fp32)
 template <typename T> struct Quad;
@@ -199,16 +247,20 @@ template <> struct Elem<float> {
 };
 
 // Staging piece size: the bytes that make one piece per thread for a chunk
-// row pair of `row_bytes` (two rows of 64 / 2 pairs x row_bytes / piece =
-// 256 pieces), capped at 16 bytes (then a whole number of pieces per thread).
-constexpr int piece_bytes(int row_bytes) { return row_bytes / 8 > 16 ? 16 : row_bytes / 8; }
+// of rows of `row_bytes` taken two rows at a time (32 row pairs x row_bytes /
+// piece = threads), capped at 16 bytes (then a whole number per thread).
+constexpr int piece_bytes(int row_bytes, int threads) {
+    return row_bytes * 32 / threads > 16 ? 16 : row_bytes * 32 / threads;
+}
 
-template <typename T, int N, int PT>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
+template <typename T, int N, int PT, bool WIDE>
+__global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel(SsdParams p) {
     using MM = Mma<T>;
     using E = typename MM::E;
     using EL = Elem<T>;
     using Math = typename MathFor<T>::type;
+    using ST = Steps<Math>;
+    using SR = typename ST::real;
     using QD = Quad<T>;
     constexpr uint32_t es = sizeof(T);
     constexpr int NS = MM::NS;                      // terms of a computed operand
@@ -216,11 +268,18 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
     constexpr int LN = N + PAD;                     // rows with n contiguous
     constexpr int LQ = kQ + PAD;                    // rows with s contiguous
     constexpr int NPT = PT / 16, NNT = N / 16;
+    constexpr int kWaves = waves_for<PT, WIDE>(), kThreads = 64 * kWaves;
+    constexpr int NPW = NPT * 4 / kWaves;           // 16-channel blocks per wave (output tiles)
+    static_assert(NPW >= 1 && NPW * kWaves == NPT * 4, "waves x tiles");
     constexpr int NSTILE = NNT * NPT;               // 16x16 state tiles
     constexpr int NST = (NSTILE + kWaves - 1) / kWaves;
     constexpr int KB = MM::KB, KPL = MM::KPL;
-    // staging pieces: two rows (steps s, s + 1) x PBB bytes of B and C, PXB of x
-    constexpr int PBB = piece_bytes(N * es), PXB = piece_bytes(PT * es);
+    // staging pieces: two rows (steps s, s + 1) x PBB bytes of B and C, PXB of
+    // x.  B / C piece u (read from L2) covers the step pair u % 32 and element
+    // group u / 32, so its transposed LDS writes fall in distinct banks; x
+    // piece u (streamed from HBM) covers element group u % (PT / VX) of step
+    // pair u / (PT / VX), so a wave reads whole rows.
+    constexpr int PBB = piece_bytes(N * es, kThreads), PXB = piece_bytes(PT * es, kThreads);
     constexpr int VB = PBB / es, VX = PXB / es;     // io elements per piece
     constexpr int UBT = (kQ / 2) * (N / VB) / kThreads, UXT = (kQ / 2) * (PT / VX) / kThreads;
     static_assert(UBT >= 1 && UXT >= 1 && (kQ / 2) * (N / VB) == UBT * kThreads &&
@@ -230,14 +289,17 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
     using VXt = typename Vec<PXB>::t;
 
     // one chunk's operands; the state copy alternates between two buffers
-    __shared__ __attribute__((aligned(16))) E sC[kQ][LN];
-    __shared__ __attribute__((aligned(16))) E sB[kQ][LN];
-    __shared__ __attribute__((aligned(16))) E sBw[NS][N][LQ];
-    __shared__ __attribute__((aligned(16))) E sX[PT][LQ];
-    __shared__ __attribute__((aligned(16))) E sM[NS][kQ][LQ];
-    __shared__ __attribute__((aligned(16))) E sS[2][NS][PT][LN];
-    __shared__ double sSd[kQ];                      // prefix of a over the chunk
-    __shared__ float sDl[kQ];                       // Delta
+    __shared__ __attribute__((aligned(16))) E sC[kQ][LN];       // C[t][n]
+    __shared__ __attribute__((aligned(16))) E sB[kQ][LN];       // B[s][n]
+    __shared__ __attribute__((aligned(16))) E sBt[N][LQ];       // B[s][n] at [n][s]
+    __shared__ __attribute__((aligned(16))) E sX[PT][LQ];       // x[s][p] at [p][s]
+    __shared__ __attribute__((aligned(16))) E sXw[NS][PT][LQ];  // w_s x[s][p] at [p][s]
+    __shared__ __attribute__((aligned(16))) E sM[NS][kQ][LQ];   // M[t][s]
+    __shared__ __attribute__((aligned(16))) E sS[2][NS][PT][LN];// S_in[p][n]
+    __shared__ SR sSt[kQ];                          // prefix s_t (scaled units)
+    __shared__ __attribute__((aligned(16))) float sDl[kQ];      // Delta_t
+    __shared__ __attribute__((aligned(16))) float sU[kQ];       // Delta_s exp(s_e(s) - s_s)
+    __shared__ float sR[3][kQ];                     // exp(s_t - s_(16 i + 15))
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -269,37 +331,39 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
     const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + b * L * N * es, static_cast<uint32_t>(L) * rowN);
     const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + b * L * N * es, static_cast<uint32_t>(L) * rowN);
 
-    const float Ah = p.A[h];
+    const float Ah = p.A[h] * ST::kScale;
     const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
     const float Dh = p.D ? p.D[h] : 0.0f;
     const bool has_z = p.z != nullptr;
 
     // per-thread staging coordinates and chunk-relative byte offsets
-    int sB0[UBT], nB0[UBT], sX0[UXT], qX0[UXT];
-    uint32_t oB[UBT], oX[UXT], oZ[NPT];
+    const int sp = 2 * (tid % 32);                  // step pair of every B / C piece of this thread
+    int nB0[UBT], qX0[UXT], sX0[UXT];
+    uint32_t oB[UBT], oX[UXT];
 #pragma unroll
     for (int i = 0; i < UBT; ++i) {
-        const int u = tid + i * kThreads;
-        sB0[i] = 2 * (u / (N / VB));
-        nB0[i] = (u % (N / VB)) * VB;
-        oB[i] = sB0[i] * rowN + nB0[i] * es;
+        nB0[i] = ((tid + i * kThreads) / 32) * VB;
+        oB[i] = sp * rowN + nB0[i] * es;
     }
 #pragma unroll
     for (int i = 0; i < UXT; ++i) {
         const int u = tid + i * kThreads;
-        sX0[i] = 2 * (u / (PT / VX));
         qX0[i] = (u % (PT / VX)) * VX;
+        sX0[i] = 2 * (u / (PT / VX));
         oX[i] = sX0[i] * rowX + hp0 + qX0[i] * es;
     }
+    // the output tiles of this wave: steps 16 jw .. + 15, channels 16 (pw0 + c) .. + 15, c < NPW
+    const int jw = w % 4, pw0 = (w / 4) * NPW;
+    uint32_t oZ[NPW];
 #pragma unroll
-    for (int pi = 0; pi < NPT; ++pi) oZ[pi] = (w * 16 + l16) * rowX + hp0 + (pi * 16 + kq * 4) * es;
+    for (int c = 0; c < NPW; ++c) oZ[c] = (jw * 16 + l16) * rowX + hp0 + ((pw0 + c) * 16 + kq * 4) * es;
     const uint32_t oDT = lane * rowH + static_cast<uint32_t>(h * es);
 
     // ---- registers of the chunk being fetched
     VBt rb[UBT][2], rc[UBT][2];
     VXt rx[UXT][2];
     typename Io<T>::raw rdt;
-    typename QD::raw rz[NPT], rzn[NPT];
+    typename QD::raw rz[NPW], rzn[NPW];
 
     auto fetch = [&](uint32_t t0) __attribute__((always_inline)) {
         const uint32_t cN = t0 * rowN, cX = t0 * rowX;
@@ -317,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
         }
         rdt = Io<T>::template load<kStream>(rDT, t0 * rowH + oDT, 0);
 #pragma unroll
-        for (int pi = 0; pi < NPT; ++pi) rzn[pi] = QD::load(rZ, cX + oZ[pi]);
+        for (int c = 0; c < NPW; ++c) rzn[c] = QD::load(rZ, cX + oZ[c]);
     };
 
     // ---- initial state: accumulators (fp32) and the operand copy
@@ -348,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
     // followed by, so the staging waits for the fetched data only, not for
     // the previous chunk's stores, on every path into the loop
 #pragma unroll
-    for (int pi = 0; pi < NPT; ++pi) {
+    for (int c = 0; c < NPW; ++c) {
         const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         QD::store(zero4, rY, kOffNone);
     }
@@ -361,115 +425,76 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
         const bool valid = static_cast<int64_t>(t0) + lane < L;
         const float v = Io<T>::f32(rdt) + bias;
         const float delta = valid ? (p.softplus ? Math::softplus(v) : v) : 0.0f;
-        double S = static_cast<double>(delta * Ah);
+        const SR S = ST::prefix(static_cast<SR>(delta * Ah), lane);
+        const SR Send = ST::lane_value(S, 63);
+        const float wx = delta * ST::ex(static_cast<float>(Send - S));           // state weight of step t
+        const float eS = ST::ex(static_cast<float>(S));                           // decay from the chunk start
+        const SR Sblk = ST::gather(S, lane | 15);
+        const float u = delta * ST::ex(static_cast<float>(Sblk - S));             // to the end of its 16-block
+        const float r0 = ST::ex(static_cast<float>(S - ST::lane_value(S, 15)));   // from the end of block 0
+        const float r1 = ST::ex(static_cast<float>(S - ST::lane_value(S, 31)));
+        const float r2 = ST::ex(static_cast<float>(S - ST::lane_value(S, 47)));
+        float xw0[UXT], xw1[UXT];
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const double u = __shfl_up(S, o);
-            if (lane >= o) S += u;
+        for (int i = 0; i < UXT; ++i) {
+            xw0[i] = __shfl(wx, sX0[i]);
+            xw1[i] = __shfl(wx, sX0[i] + 1);
         }
-        const double Send = __shfl(S, 63);
-        const float wgt = delta * ssd_exp(Math{}, static_cast<float>(Send - S));
-        const float eS = ssd_exp(Math{}, static_cast<float>(S));
 
         // ---- stage the chunk into LDS (every reader of the previous chunk is done)
         __syncthreads();
         if (w == 0) {
-            sSd[lane] = S;
+            sSt[lane] = S;
             sDl[lane] = delta;
+            sU[lane] = u;
+            sR[0][lane] = r0;
+            sR[1][lane] = r1;
+            sR[2][lane] = r2;
         }
 #pragma unroll
         for (int i = 0; i < UBT; ++i) {
-            const int sb = sB0[i], n0 = nB0[i];
-            const float w0 = __shfl(wgt, sb), w1 = __shfl(wgt, sb + 1);
-            *reinterpret_cast<VBt *>(&sB[sb][n0]) = rb[i][0];
-            *reinterpret_cast<VBt *>(&sB[sb + 1][n0]) = rb[i][1];
-            *reinterpret_cast<VBt *>(&sC[sb][n0]) = rc[i][0];
-            *reinterpret_cast<VBt *>(&sC[sb + 1][n0]) = rc[i][1];
+            const int n0 = nB0[i];
+            *reinterpret_cast<VBt *>(&sB[sp][n0]) = rb[i][0];
+            *reinterpret_cast<VBt *>(&sB[sp + 1][n0]) = rb[i][1];
+            *reinterpret_cast<VBt *>(&sC[sp][n0]) = rc[i][0];
+            *reinterpret_cast<VBt *>(&sC[sp + 1][n0]) = rc[i][1];
 #pragma unroll
-            for (int e = 0; e < VB; ++e) {
-                const float b0 = EL::f32(rb[i][0], e) * w0, b1 = EL::f32(rb[i][1], e) * w1;
-#pragma unroll
-                for (int q2 = 0; q2 < NS; ++q2)
-                    MM::put2(&sBw[q2][n0 + e][sb], MM::enc(MM::term(b0, q2)), MM::enc(MM::term(b1, q2)));
-            }
+            for (int e = 0; e < VB; ++e) MM::put2(&sBt[n0 + e][sp], EL::raw(rb[i][0], e), EL::raw(rb[i][1], e));
         }
 #pragma unroll
         for (int i = 0; i < UXT; ++i) {
+            const int q0 = qX0[i], sx = sX0[i];
 #pragma unroll
-            for (int e = 0; e < VX; ++e)
-                MM::put2(&sX[qX0[i] + e][sX0[i]], EL::raw(rx[i][0], e), EL::raw(rx[i][1], e));
+            for (int e = 0; e < VX; ++e) {
+                MM::put2(&sX[q0 + e][sx], EL::raw(rx[i][0], e), EL::raw(rx[i][1], e));
+                const float x0 = EL::f32(rx[i][0], e) * xw0[i], x1 = EL::f32(rx[i][1], e) * xw1[i];
+#pragma unroll
+                for (int q2 = 0; q2 < NS; ++q2)
+                    MM::put2(&sXw[q2][q0 + e][sx], MM::enc(MM::term(x0, q2)), MM::enc(MM::term(x1, q2)));
+            }
         }
 #pragma unroll
-        for (int pi = 0; pi < NPT; ++pi) rz[pi] = rzn[pi];
+        for (int c = 0; c < NPW; ++c) rz[c] = rzn[c];
         fetch(t0 + kQ);          // the next chunk (past the end: empty reads)
         __syncthreads();
 
-        // ---- M = (C B^T) masked, scaled by Delta_s exp(s_t - s_s), over the
-        // ten 16x16 blocks with s-block i <= t-block j (block q = j (j+1) / 2 + i)
-        for (int q = w; q < 10; q += kWaves) {
-            const int j = (q >= 1) + (q >= 3) + (q >= 6);
-            const int i = q - j * (j + 1) / 2;
-            f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
-            const E *pa = &sB[i * 16 + l16][kq * KPL];
-            const E *pb = &sC[j * 16 + l16][kq * KPL];
+        // ---- before M is needed: this wave's carried-state readout
+        // Y_off^T = S_in C^T (steps 16 jw .., its channel blocks) and its state
+        // tiles S^T <- exp(s_Q) S^T + B^T (w x); both read only staged operands
+        const int t = jw * 16 + l16;
+        f32x4_t acc[NPW];
 #pragma unroll
-            for (int kk = 0; kk < N / KB; ++kk) g = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), g);
-            const int t = j * 16 + l16, s0 = i * 16 + kq * 4;
-            const double st = sSd[t];
-            float m[4];
+        for (int c = 0; c < NPW; ++c) {
+            acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            const E *pb = &sC[t][kq * KPL];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = s0 + e;
-                m[e] = s <= t ? g[e] * sDl[s] * ssd_exp(Math{}, static_cast<float>(st - sSd[s])) : 0.0f;
-            }
+            for (int q2 = 0; q2 < NS; ++q2) {
+                const E *pa = &sS[k][q2][(pw0 + c) * 16 + l16][kq * KPL];
 #pragma unroll
-            for (int q2 = 0; q2 < NS; ++q2)
-                MM::put4(&sM[q2][t][s0], MM::term(m[0], q2), MM::term(m[1], q2), MM::term(m[2], q2),
-                         MM::term(m[3], q2));
-        }
-        __syncthreads();
-
-        // ---- Y^T for this wave's 16 steps (t-block w), all channel blocks
-        {
-            const int j = w;
-            const int t = j * 16 + l16;
-            const float est = __shfl(eS, t);
-            constexpr int kmax = kQ / KB;
-            const int nkd = (16 * (j + 1) + KB - 1) / KB;
-            const bool tvalid = static_cast<int64_t>(t0) + t < L;
-#pragma unroll
-            for (int pi = 0; pi < NPT; ++pi) {
-                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                const E *pb = &sC[t][kq * KPL];
-#pragma unroll
-                for (int q2 = 0; q2 < NS; ++q2) {
-                    const E *pa = &sS[k][q2][pi * 16 + l16][kq * KPL];
-#pragma unroll
-                    for (int kk = 0; kk < N / KB; ++kk)
-                        acc = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), acc);
-                }
-                acc *= est;
-                const E *pa2 = &sX[pi * 16 + l16][kq * KPL];
-#pragma unroll
-                for (int q2 = 0; q2 < NS; ++q2) {
-                    const E *pb2 = &sM[q2][t][kq * KPL];
-#pragma unroll
-                    for (int kk = 0; kk < kmax; ++kk)
-                        if (kk < nkd) acc = MM::mma(MM::load(pa2 + kk * KB), MM::load(pb2 + kk * KB), acc);
-                }
-                float yv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int pp = pi * 16 + kq * 4 + e;
-                    float o = fmaf(Dh, MM::dec(sX[pp][t]), acc[e]);
-                    if (has_z) o *= silu(QD::get(rz[pi], e));
-                    yv[e] = o;
-                }
-                QD::store(yv, rY, tvalid ? t0 * rowX + oZ[pi] : kOffNone);
+                for (int kk = 0; kk < N / KB; ++kk)
+                    acc[c] = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), acc[c]);
             }
         }
-
-        // ---- state: S^T <- exp(s_Q) S^T + (B w)^T X, and its operand copy
         {
             const float send = static_cast<float>(Send);
 #pragma unroll
@@ -477,21 +502,90 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
                 const int q = w + kWaves * r;
                 if (q < NSTILE) {
                     const int ni = q / NPT, pi = q % NPT;
-                    f32x4_t a = ssd_decay(Math{}, send, acc_s[r]);
-                    const E *pb = &sX[pi * 16 + l16][kq * KPL];
+                    f32x4_t a = ST::decay(send, acc_s[r]);
+                    const E *pa = &sBt[ni * 16 + l16][kq * KPL];
 #pragma unroll
-                    for (int q2 = 0; q2 < NS; ++q2) {
-                        const E *pa = &sBw[q2][ni * 16 + l16][kq * KPL];
+                    for (int kk = 0; kk < kQ / KB; ++kk) {
+                        const typename MM::frag fa = MM::load(pa + kk * KB);
 #pragma unroll
-                        for (int kk = 0; kk < kQ / KB; ++kk)
-                            a = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), a);
+                        for (int q2 = 0; q2 < NS; ++q2)
+                            a = MM::mma(fa, MM::load(&sXw[q2][pi * 16 + l16][kq * KPL] + kk * KB), a);
                     }
                     acc_s[r] = a;
+                    // the copy read by the next chunk (the other buffer: its
+                    // last readers finished before this chunk's staging)
 #pragma unroll
                     for (int q2 = 0; q2 < NS; ++q2)
                         MM::put4(&sS[k ^ 1][q2][pi * 16 + l16][ni * 16 + kq * 4], MM::term(a[0], q2),
                                  MM::term(a[1], q2), MM::term(a[2], q2), MM::term(a[3], q2));
                 }
+            }
+        }
+
+        // ---- M = (C B^T) masked, times Delta_s exp(s_t - s_s), over the ten
+        // 16x16 blocks with s-block i <= t-block j: blocks 0..3 the diagonal
+        // (exp per element), blocks 4..9 below it, where the factor splits as
+        // u_s r_t^(i) (both at most 1); wave w takes blocks w, w + W, w + 2 W
+#pragma unroll
+        for (int rr = 0; rr < 3; ++rr) {
+            const int qb = w + kWaves * rr;
+            if (qb >= 10) break;
+            const bool diag = qb < 4;
+            const int q = qb - 4;                       // off-diagonal: q = j (j - 1) / 2 + i
+            const int j = diag ? qb : 1 + (q >= 1) + (q >= 3);
+            const int i = diag ? qb : q - j * (j - 1) / 2;
+            f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
+            const E *pa = &sB[i * 16 + l16][kq * KPL];
+            const E *pb = &sC[j * 16 + l16][kq * KPL];
+#pragma unroll
+            for (int kk = 0; kk < N / KB; ++kk) g = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), g);
+            const int tm = j * 16 + l16, s0 = i * 16 + kq * 4;
+            float m[4];
+            if (diag) {
+                const f32x4_t dq = *reinterpret_cast<const f32x4_t *>(&sDl[s0]);
+                const SR st = sSt[tm];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    m[e] = s0 + e <= tm ? g[e] * dq[e] * ST::ex(static_cast<float>(st - sSt[s0 + e])) : 0.0f;
+            } else {
+                const f32x4_t uq = *reinterpret_cast<const f32x4_t *>(&sU[s0]);
+                const float rt = sR[i][tm];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = g[e] * uq[e] * rt;
+            }
+#pragma unroll
+            for (int q2 = 0; q2 < NS; ++q2)
+                MM::put4(&sM[q2][tm][s0], MM::term(m[0], q2), MM::term(m[1], q2), MM::term(m[2], q2),
+                         MM::term(m[3], q2));
+        }
+        __syncthreads();
+
+        // ---- Y^T += X^T M^T for this wave's tiles, then D skip, gate, store
+        {
+            const float est = __shfl(eS, t);
+            constexpr int kmax = kQ / KB;
+            const int nkd = (16 * (jw + 1) + KB - 1) / KB;
+            const bool tvalid = static_cast<int64_t>(t0) + t < L;
+#pragma unroll
+            for (int c = 0; c < NPW; ++c) {
+                f32x4_t a = acc[c] * est;
+                const E *pa2 = &sX[(pw0 + c) * 16 + l16][kq * KPL];
+#pragma unroll
+                for (int q2 = 0; q2 < NS; ++q2) {
+                    const E *pb2 = &sM[q2][t][kq * KPL];
+#pragma unroll
+                    for (int kk = 0; kk < kmax; ++kk)
+                        if (kk < nkd) a = MM::mma(MM::load(pa2 + kk * KB), MM::load(pb2 + kk * KB), a);
+                }
+                float yv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pp = (pw0 + c) * 16 + kq * 4 + e;
+                    float o = fmaf(Dh, MM::dec(sX[pp][t]), a[e]);
+                    if (has_z) o *= silu(QD::get(rz[c], e));
+                    yv[e] = o;
+                }
+                QD::store(yv, rY, tvalid ? t0 * rowX + oZ[c] : kOffNone);
             }
         }
     }
@@ -509,17 +603,25 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SsdParams p) {
     }
 }
 
-template <typename T, int N, int PT>
-hipError_t launch(const SsdParams &p, int64_t batch, hipStream_t s) {
-    const int64_t blocks = batch * p.nheads * (p.headdim / PT);
-    hipLaunchKernelGGL((ssd_chunk_kernel<T, N, PT>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, p);
+template <typename T, int N, int PT, bool WIDE>
+hipError_t launch(const SsdParams &p, int64_t blocks, hipStream_t s) {
+    hipLaunchKernelGGL((ssd_chunk_kernel<T, N, PT, WIDE>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * waves_for<PT, WIDE>()), 0, s, p);
     return hipGetLastError();
 }
 
+// 32-channel tiles when the head size allows; the wide form when the grid
+// leaves every CU at most one workgroup
 template <typename T, int N>
 hipError_t launch_pt(const SsdParams &p, int64_t batch, hipStream_t s) {
-    if (p.headdim % 32 == 0) return launch<T, N, 32>(p, batch, s);
-    return launch<T, N, 16>(p, batch, s);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    if (p.headdim % 32 == 0) {
+        const int64_t blocks = batch * p.nheads * (p.headdim / 32);
+        return blocks <= cus ? launch<T, N, 32, true>(p, blocks, s) : launch<T, N, 32, false>(p, blocks, s);
+    }
+    return launch<T, N, 16, false>(p, batch * p.nheads * (p.headdim / 16), s);
 }
 
 }  // namespace
