@@ -19,7 +19,9 @@ bounded sample of the same workload.
 --backward times ssm_scan_bwd (the gradient of the scan; workloads 1, 2, 3)
 instead, one call per step, against the backward's own VALU roofline; --conv
 times the block's causal conv1d + SiLU (ssm_causal_conv1d_fwd, width 4) over
-the workload's x against the HBM roofline.
+the workload's x against the HBM roofline; --ssd [NAME] times the Mamba-2
+multi-head scan (ssd_scan_fwd) on a Mamba2Block-shaped layer (default
+mamba2-2.7b-ssd-layer-bf16) against the HBM roofline.
 
 Profiling helpers (no GPU work of their own beyond what they state):
     python bench.py --copy-calibration       1 GiB device copy, for the
@@ -73,10 +75,11 @@ SOURCES = {
     "sm1": ["selective_scan_ssm_amd/csrc/sm1_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "conv": ["selective_scan_ssm_amd/csrc/conv1d.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "ssd": ["selective_scan_ssm_amd/csrc/ssd_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
 # the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
-                 "decode": "state_update_rows_kernel", "conv": "conv1d_kernel"}
+                 "decode": "state_update_rows_kernel", "conv": "conv1d_kernel", "ssd": "ssd_chunk_kernel"}
 
 
 def kind_of(w):
@@ -568,6 +571,94 @@ def bench_conv(args, dev):
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
 
 
+def ssd_algorithmic_bytes(w, io_bytes):
+    """x, z read and y written (B T H P each), dt (B T H), B and C (B T N),
+    and the per-head A, D, dt_bias (fp32)."""
+    Bt, T, H, P, N = w.batch, w.seqlen, w.n_heads, w.headdim, w.d_state
+    return (3 * Bt * T * H * P + Bt * T * H + 2 * Bt * T * N) * io_bytes + 3 * H * 4
+
+
+def bench_ssd(args, dev):
+    """ssd_scan_fwd over a Mamba2Block-shaped layer: one step = one launch
+    over the whole (batch, seqlen, heads, head size) input."""
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import _lib, ops
+    from selective_scan_ssm_amd import inputs as gen
+    import oracle
+    _lib.load()
+    w = gen.SSD_WORKLOADS[args.ssd]
+    io = w.io
+    io_b = 2 if io == gen.BF16 else 4
+    log(f"[bench] ssd scan, {w.name}: generating inputs")
+    inp = gen.ssd_workload_inputs(w.name, seed=1)
+    alg = ssd_algorithmic_bytes(w, io_b)
+    nset = max(1, math.ceil(600e6 / alg)) if args.rotate is None else args.rotate
+    sets = []
+    for _ in range(nset):
+        t = {k: upload(inp[k], io, dev) for k in ("x", "dt", "z", "B", "C")}
+        t.update({k: upload(inp[k], gen.F32, dev) for k in ("A", "D", "dt_bias")})
+        t["y"] = torch.empty_like(t["x"])
+        sets.append(t)
+    stream = torch.cuda.current_stream(dev)
+    cur = [0]
+
+    def step():
+        t = sets[cur[0] % nset]
+        cur[0] += 1
+        ops.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"], dt_bias=t["dt_bias"],
+                         out=t["y"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean(step_ms))
+    hbm = alg / (call_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("ssd", w.name),
+            "kernel": "ssd_scan_fwd (ssd_chunk_kernel)",
+            "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+            "algorithmic_bytes_per_launch": alg}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on every batch row and head, the first nc channels of each
+        # head (about 5e8 state updates -- one channel, step and n -- per core-second)
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        nc = int(min(w.headdim, max(1, args.cpu_seconds * 5e8 / (w.batch * w.seqlen * w.n_heads * w.d_state))))
+        f64 = lambda a: np.ascontiguousarray(gen.to_f64(a, io))
+        xs = np.ascontiguousarray(f64(inp["x"])[:, :, :, :nc])
+        zs = np.ascontiguousarray(f64(inp["z"])[:, :, :, :nc])
+        t1 = time.perf_counter()
+        oracle.ssd_scan(xs, f64(inp["dt"]), inp["A"], f64(inp["B"]), f64(inp["C"]), D=inp["D"], z=zs,
+                        dt_bias=inp["dt_bias"], threads=threads)
+        dt = time.perf_counter() - t1
+        el = w.batch * w.seqlen * w.n_heads * nc
+        cpu = {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+               "sample": f"all {w.batch} batch rows x {w.seqlen} steps x {w.n_heads} heads x first {nc} of "
+                         f"{w.headdim} channels ({el} elements, d_state {w.d_state}), fp64, {dt:.2f} s wall"}
+    elems = w.batch * w.seqlen * w.n_heads * w.headdim
+    cfg = {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "d_model": w.d_model,
+           "n_heads": w.n_heads, "headdim": w.headdim, "d_state": w.d_state, "chunk": 64, "io": io}
+    if nset > 1:
+        cfg["rotated_input_sets"] = nset
+    return {"metric": "Mamba-2 SSD scan elements/s (B*T*H*P)", "value": elems / (ms_per_step * 1e-3),
+            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
 def copy_calibration():
     """A plain device copy of COPY_CAL_BYTES, three times: under rocprofv3
     --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the counter scale."""
@@ -674,6 +765,8 @@ def main():
                     help="scan order through ssm_scan_fwd_2d (height 1): 0 forward, 1 reversed")
     ap.add_argument("--conv", action="store_true",
                     help="time ssm_causal_conv1d_fwd (width 4, SiLU) on a scan workload's x instead")
+    ap.add_argument("--ssd", nargs="?", const="mamba2-2.7b-ssd-layer-bf16", default=None,
+                    help="time ssd_scan_fwd (the Mamba-2 multi-head scan) on the named layer shape instead")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "COMMAND"))
     ap.add_argument("--summarize-traffic", nargs=7,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
@@ -686,7 +779,11 @@ def main():
     if args.summarize_traffic:
         from selective_scan_ssm_amd import inputs as gen
         wl, fd, wd, cfd, cwd, kcmd, ccmd = args.summarize_traffic
-        if wl.startswith("conv"):      # "conv3": the conv1d over workload 3's x
+        if wl.startswith("ssd:"):      # "ssd:NAME": the Mamba-2 scan on that layer shape
+            w = gen.SSD_WORKLOADS[wl[4:]]
+            kind, wname = "ssd", w.name
+            alg = ssd_algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
+        elif wl.startswith("conv"):    # "conv3": the conv1d over workload 3's x
             w = gen.WORKLOADS[int(wl[4:])]
             kind, wname = "conv", w.name + "-conv1d"
             alg = 2 * w.batch * w.seqlen * w.d_inner * (2 if w.io == gen.BF16 else 4) + w.d_inner * 5 * 4
@@ -715,7 +812,8 @@ def main():
         return
     from selective_scan_ssm_amd import _lib
     _lib.load()
-    fn = bench_backward if args.backward else (bench_conv if args.conv else bench_workload)
+    fn = (bench_backward if args.backward else bench_conv if args.conv else
+          bench_ssd if args.ssd is not None else bench_workload)
     rec = fn(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)
 
