@@ -8,34 +8,36 @@
 //   y[t, p]  = (sum_n C[t, n] S[p, n] + D[h] x[t, p]) SiLU(z[t, p]).
 // B and C (one per step) are shared by all heads.
 //
-// One workgroup (4 waves) owns (b, h, a tile of PT channels) and walks the
-// sequence in chunks of Q = 64 steps, keeping the state S (PT x N, fp32) in
-// MFMA accumulators.  With s_t the prefix sum of a over the chunk (fp64) and
-// S_in the state entering the chunk, chunk c is three products:
-//   G^T = B C^T (Q x Q; only s <= t blocks), masked into
+// A workgroup owns (b, h, a tile of PT channels) and walks the sequence in
+// chunks of Q = 64 steps.  With s_t the prefix sum of a over the chunk and
+// S_in the state entering it, a chunk is
+//   G^T = B C^T (16x16 blocks with s-block <= t-block), masked into
 //   M[t, s] = G[t, s] Delta_s exp(s_t - s_s)  (s <= t), 0 above,
-//   Y^T   = X^T M^T + (S_in C^T) diag(exp(s_t))             (PT x Q)
-//   S^T   = exp(s_Q) S_in^T + (B diag(w))^T X, w_s = Delta_s exp(s_Q - s_s).
-// bf16 io uses v_mfma_f32_16x16x32_bf16 (M, S_in and B w rounded to bf16 as
-// operands, every sum and the carried state in fp32); fp32 io uses
-// v_mfma_f32_16x16x4_f32 with fp32 operands throughout.
+//   Y^T   = (S_in C^T) diag(exp(s_t)) + X^T M^T,
+//   S^T   = exp(s_Q) S_in^T + B^T (w X),  w_s = Delta_s exp(s_Q - s_s).
+// Every wave owns one 16-channel block and two 16-step blocks of each chunk
+// ({0, 3} or {1, 2}: equal triangular work) and keeps its channel block's
+// whole state (N x 16, fp32) in MFMA accumulators; the two waves of a channel
+// block keep identical copies.  M and S_in never go through LDS: an MFMA's
+// contraction may visit K in any order that both operands share, so the
+// accumulator tiles of G^T (and of the state) serve directly as the M^T (and
+// S_in) operands, the other operand reading the same K values from LDS.  LDS
+// holds only the staged chunk: B and C (rows = steps, n contiguous), B^T, x^T
+// and (w x)^T (rows = n / channels, steps contiguous); two barriers per chunk.
 //
-// The prefix sums are taken in fp64 so that exp(s_t - s_s) keeps full fp32
-// accuracy even when the chunk's total decay is large (an fp32 prefix would
-// lose |s| * 2^-24 absolutely in every difference).
+// bf16 io uses v_mfma_f32_16x16x32_bf16, every sum and the state in fp32;
+// fp32 io uses v_mfma_f32_16x16x4_f32 with fp32 operands throughout.  bf16
+// operands that are computed (M, S_in, w x) are carried as two bf16 terms,
+// hi = bf16(v) and lo = bf16(v - hi), each product with them two MFMAs: a
+// single bf16 rounding of these operands costs up to 3e-2 relative error in y
+// at the layer shapes, the two-term form about 2^-17.  x, z, B, C are bf16
+// already and enter exactly.
 //
-// bf16 operands that are computed (M, S_in, B w) are carried as two bf16
-// terms, hi = bf16(v) and lo = bf16(v - hi), and each product with them is two
-// MFMAs: a single bf16 rounding of these operands costs up to 3e-2 relative
-// error in y at the layer shapes, the two-term form about 2^-17.  x, z, B, C
-// are bf16 already and enter exactly.
-//
-// LDS: C and B natural (rows t / s, n contiguous), B w and X transposed (rows
-// n / p, s contiguous), M (rows t, s contiguous), S_in (rows p, n contiguous;
-// two buffers, written by one chunk and read by the next).  Every MFMA
-// operand fragment is then one contiguous read along its K axis.  Three
-// barriers per chunk: before staging (the previous chunk's readers are done),
-// after staging, after M.
+// Prefix sums: fp64 for fp32 io, so exp(s_t - s_s) keeps full fp32 accuracy
+// when a chunk's total decay is large (an fp32 prefix loses |s| 2^-24
+// absolutely in every difference); fp32 (DPP) for bf16 io, far below bf16.
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_kernels.h"
 
@@ -43,13 +45,6 @@ namespace ssm {
 namespace {
 
 constexpr int kQ = 64;          // chunk length (steps)
-// Waves per workgroup: 4, one per 16-step block of a chunk, each owning that
-// block's output tiles for every 16-channel block of the workgroup; or
-// (WIDE) 4 per 16-channel block, one output tile each.  The wide form halves
-// each wave's chain of dependent LDS reads and MFMAs, which pays when there is
-// at most one workgroup per CU; with more, two narrow workgroups share a CU
-// better (the wide one saturates a CU's LDS on its own).
-template <int PT, bool WIDE> constexpr int waves_for() { return WIDE ? 4 * (PT / 16) : 4; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -253,9 +248,49 @@ constexpr int piece_bytes(int row_bytes, int threads) {
     return row_bytes * 32 / threads > 16 ? 16 : row_bytes * 32 / threads;
 }
 
-template <typename T, int N, int PT, bool WIDE>
-__global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel(SsdParams p) {
+// MFMA operands taken straight from accumulator tiles.  A 16x16 accumulator
+// tile gives lane (g = l / 16, l16) rows 4 g .. 4 g + 3 of column l16.  The
+// contraction of an MFMA may visit its K slots in any order as long as both
+// operands use the same one, so a 32-wide K range made of two 16-row tiles
+// (a, b) is visited as K = {4 g .. 4 g + 3} of a, then {4 g .. 4 g + 3} of b
+// (16 + 4 g ..) for lane group g -- the values the lane already holds.  The
+// other operand reads the same K values from an LDS row (two 8-byte pieces).
+template <typename T> struct PermK;
+template <> struct PermK<bf16_t> {
+    using frag = bf16x8_t;
+    static constexpr int kSteps = 1;              // MFMAs per 32-wide K range
+    static __device__ __forceinline__ frag from_tiles(const f32x4_t &a, const f32x4_t &b, int, int q2) {
+        using MM = Mma<bf16_t>;
+        const u16x8_t u = {MM::enc(MM::term(a[0], q2)), MM::enc(MM::term(a[1], q2)), MM::enc(MM::term(a[2], q2)),
+                           MM::enc(MM::term(a[3], q2)), MM::enc(MM::term(b[0], q2)), MM::enc(MM::term(b[1], q2)),
+                           MM::enc(MM::term(b[2], q2)), MM::enc(MM::term(b[3], q2))};
+        return __builtin_bit_cast(frag, u);
+    }
+    // row points at K = 0 of the 32-wide range
+    static __device__ __forceinline__ frag from_lds(const uint16_t *row, int g, int) {
+        const u16x4_t lo = *reinterpret_cast<const u16x4_t *>(row + 4 * g);
+        const u16x4_t hi = *reinterpret_cast<const u16x4_t *>(row + 16 + 4 * g);
+        const u16x8_t u = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(frag, u);
+    }
+};
+template <> struct PermK<float> {
+    using frag = float;
+    static constexpr int kSteps = 8;              // 32 K values, 4 per MFMA
+    static __device__ __forceinline__ frag from_tiles(const f32x4_t &a, const f32x4_t &b, int st, int) {
+        return st < 4 ? a[st] : b[st - 4];
+    }
+    static __device__ __forceinline__ frag from_lds(const float *row, int g, int st) {
+        return row[16 * (st / 4) + 4 * g + (st % 4)];
+    }
+};
+
+template <int PT> constexpr int waves_for() { return 2 * (PT / 16); }
+
+template <typename T, int N, int PT>
+__global__ __launch_bounds__(64 * waves_for<PT>()) void ssd_chunk_kernel(SsdParams p) {
     using MM = Mma<T>;
+    using PK = PermK<T>;
     using E = typename MM::E;
     using EL = Elem<T>;
     using Math = typename MathFor<T>::type;
@@ -267,12 +302,8 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
     constexpr int PAD = 16 / sizeof(E);             // 16 bytes of row padding
     constexpr int LN = N + PAD;                     // rows with n contiguous
     constexpr int LQ = kQ + PAD;                    // rows with s contiguous
-    constexpr int NPT = PT / 16, NNT = N / 16;
-    constexpr int kWaves = waves_for<PT, WIDE>(), kThreads = 64 * kWaves;
-    constexpr int NPW = NPT * 4 / kWaves;           // 16-channel blocks per wave (output tiles)
-    static_assert(NPW >= 1 && NPW * kWaves == NPT * 4, "waves x tiles");
-    constexpr int NSTILE = NNT * NPT;               // 16x16 state tiles
-    constexpr int NST = (NSTILE + kWaves - 1) / kWaves;
+    constexpr int NNT = N / 16;
+    constexpr int kWaves = waves_for<PT>(), kThreads = 64 * kWaves;
     constexpr int KB = MM::KB, KPL = MM::KPL;
     // staging pieces: two rows (steps s, s + 1) x PBB bytes of B and C, PXB of
     // x.  B / C piece u (read from L2) covers the step pair u % 32 and element
@@ -284,18 +315,16 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
     constexpr int UBT = (kQ / 2) * (N / VB) / kThreads, UXT = (kQ / 2) * (PT / VX) / kThreads;
     static_assert(UBT >= 1 && UXT >= 1 && (kQ / 2) * (N / VB) == UBT * kThreads &&
                   (kQ / 2) * (PT / VX) == UXT * kThreads, "one or more whole pieces per thread");
-    static_assert(N % KB == 0 && kQ % KB == 0, "tile shapes");
+    static_assert(N % 32 == 0 && kQ == 64, "tile shapes");
     using VBt = typename Vec<PBB>::t;
     using VXt = typename Vec<PXB>::t;
 
-    // one chunk's operands; the state copy alternates between two buffers
+    // one chunk's operands (single buffer: a barrier before and after staging)
     __shared__ __attribute__((aligned(16))) E sC[kQ][LN];       // C[t][n]
     __shared__ __attribute__((aligned(16))) E sB[kQ][LN];       // B[s][n]
     __shared__ __attribute__((aligned(16))) E sBt[N][LQ];       // B[s][n] at [n][s]
     __shared__ __attribute__((aligned(16))) E sX[PT][LQ];       // x[s][p] at [p][s]
     __shared__ __attribute__((aligned(16))) E sXw[NS][PT][LQ];  // w_s x[s][p] at [p][s]
-    __shared__ __attribute__((aligned(16))) E sM[NS][kQ][LQ];   // M[t][s]
-    __shared__ __attribute__((aligned(16))) E sS[2][NS][PT][LN];// S_in[p][n]
     __shared__ SR sSt[kQ];                          // prefix s_t (scaled units)
     __shared__ __attribute__((aligned(16))) float sDl[kQ];      // Delta_t
     __shared__ __attribute__((aligned(16))) float sU[kQ];       // Delta_s exp(s_e(s) - s_s)
@@ -305,6 +334,9 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kq = lane >> 4;
+    // this wave: 16-channel block pw; 16-step blocks {0, 3} (tp = 0) or {1, 2}
+    // (tp = 1) of every chunk -- the two pairs carry equal triangular work
+    const int pw = w >> 1, tp = w & 1;
 
     // block -> (b, h, channel tile); consecutive logical blocks (same batch
     // row, so the same B and C) are kept on one XCD when the count allows
@@ -352,18 +384,21 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
         sX0[i] = 2 * (u / (PT / VX));
         oX[i] = sX0[i] * rowX + hp0 + qX0[i] * es;
     }
-    // the output tiles of this wave: steps 16 jw .. + 15, channels 16 (pw0 + c) .. + 15, c < NPW
-    const int jw = w % 4, pw0 = (w / 4) * NPW;
-    uint32_t oZ[NPW];
+    // the output tiles of this wave: steps 16 jr .. + 15 (jr = its two 16-step
+    // blocks), channels 16 pw .. + 15
+    int jr[2];
+    jr[0] = tp ? 1 : 0;
+    jr[1] = tp ? 2 : 3;
+    uint32_t oZ[2];
 #pragma unroll
-    for (int c = 0; c < NPW; ++c) oZ[c] = (jw * 16 + l16) * rowX + hp0 + ((pw0 + c) * 16 + kq * 4) * es;
+    for (int r = 0; r < 2; ++r) oZ[r] = (jr[r] * 16 + l16) * rowX + hp0 + (pw * 16 + kq * 4) * es;
     const uint32_t oDT = lane * rowH + static_cast<uint32_t>(h * es);
 
     // ---- registers of the chunk being fetched
     VBt rb[UBT][2], rc[UBT][2];
     VXt rx[UXT][2];
     typename Io<T>::raw rdt;
-    typename QD::raw rz[NPW], rzn[NPW];
+    typename QD::raw rz[2], rzn[2];
 
     auto fetch = [&](uint32_t t0) __attribute__((always_inline)) {
         const uint32_t cN = t0 * rowN, cX = t0 * rowX;
@@ -381,30 +416,20 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
         }
         rdt = Io<T>::template load<kStream>(rDT, t0 * rowH + oDT, 0);
 #pragma unroll
-        for (int c = 0; c < NPW; ++c) rzn[c] = QD::load(rZ, cX + oZ[c]);
+        for (int r = 0; r < 2; ++r) rzn[r] = QD::load(rZ, cX + oZ[r]);
     };
 
-    // ---- initial state: accumulators (fp32) and the operand copy
-    f32x4_t acc_s[NST];
+    // ---- the state of this wave's channel block, all N: tiles S^T[16 ni ..][16 pw ..]
+    // (lane: n = 16 ni + 4 kq + v, p = 16 pw + l16), fp32 accumulators
+    f32x4_t acc_s[NNT];
 #pragma unroll
-    for (int r = 0; r < NST; ++r) {
-        const int q = w + kWaves * r;
-        acc_s[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (q < NSTILE) {
-            const int ni = q / NPT, pi = q % NPT;
-            const int n = ni * 16 + kq * 4, pp = pi * 16 + l16;
-            if (p.h0) {
-                const float *src = p.h0 + (((b * H + h) * P + p0 + pp) * N + n);
-                acc_s[r] = *reinterpret_cast<const f32x4_t *>(src);
-            }
-            const f32x4_t a = acc_s[r];
-#pragma unroll
-            for (int q2 = 0; q2 < NS; ++q2)
-                MM::put4(&sS[0][q2][pp][n], MM::term(a[0], q2), MM::term(a[1], q2), MM::term(a[2], q2),
-                         MM::term(a[3], q2));
+    for (int ni = 0; ni < NNT; ++ni) {
+        acc_s[ni] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.h0) {
+            const float *src = p.h0 + (((b * H + h) * P + p0 + pw * 16 + l16) * N + ni * 16 + kq * 4);
+            acc_s[ni] = *reinterpret_cast<const f32x4_t *>(src);
         }
     }
-    for (int i = tid; i < NS * kQ * LQ; i += kThreads) (&sM[0][0][0])[i] = MM::enc(0.0f);
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
     fetch(0);
@@ -412,13 +437,12 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
     // followed by, so the staging waits for the fetched data only, not for
     // the previous chunk's stores, on every path into the loop
 #pragma unroll
-    for (int c = 0; c < NPW; ++c) {
+    for (int r = 0; r < 2; ++r) {
         const float zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         QD::store(zero4, rY, kOffNone);
     }
 
     for (int64_t c = 0; c < nchunks; ++c) {
-        const int k = static_cast<int>(c & 1);      // state buffer read by this chunk
         const uint32_t t0 = static_cast<uint32_t>(c * kQ);
 
         // ---- per-step quantities (lane = step), every wave the same
@@ -428,7 +452,6 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
         const SR S = ST::prefix(static_cast<SR>(delta * Ah), lane);
         const SR Send = ST::lane_value(S, 63);
         const float wx = delta * ST::ex(static_cast<float>(Send - S));           // state weight of step t
-        const float eS = ST::ex(static_cast<float>(S));                           // decay from the chunk start
         const SR Sblk = ST::gather(S, lane | 15);
         const float u = delta * ST::ex(static_cast<float>(Sblk - S));             // to the end of its 16-block
         const float r0 = ST::ex(static_cast<float>(S - ST::lane_value(S, 15)));   // from the end of block 0
@@ -474,154 +497,128 @@ __global__ __launch_bounds__((64 * waves_for<PT, WIDE>())) void ssd_chunk_kernel
             }
         }
 #pragma unroll
-        for (int c = 0; c < NPW; ++c) rz[c] = rzn[c];
+        for (int r = 0; r < 2; ++r) rz[r] = rzn[r];
         fetch(t0 + kQ);          // the next chunk (past the end: empty reads)
         __syncthreads();
 
-        // ---- before M is needed: this wave's carried-state readout
-        // Y_off^T = S_in C^T (steps 16 jw .., its channel blocks) and its state
-        // tiles S^T <- exp(s_Q) S^T + B^T (w x); both read only staged operands
-        const int t = jw * 16 + l16;
-        f32x4_t acc[NPW];
+        // ---- this wave's two output tiles Y^T[16 pw ..][16 j ..], with its
+        // 16-step blocks known at compile time (no branches in the unrolled body)
+        const int prow = pw * 16 + l16;               // A-operand row (channel) of this lane
+        auto tiles = [&](auto tpc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NPW; ++c) {
-            acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            const E *pb = &sC[t][kq * KPL];
+            for (int r = 0; r < 2; ++r) {
+                const int j = decltype(tpc)::value ? 1 + r : 3 * r;
+                const int t = j * 16 + l16;               // B-operand column (step) of this lane
+                // M^T tiles (s-block i, t-block j), i <= j: G^T = B C^T masked and
+                // scaled by Delta_s exp(s_t - s_s) (u_s r_t below the diagonal)
+                f32x4_t m[4];
+                const SR st_t = sSt[t];
 #pragma unroll
-            for (int q2 = 0; q2 < NS; ++q2) {
-                const E *pa = &sS[k][q2][(pw0 + c) * 16 + l16][kq * KPL];
+                for (int i = 0; i < 4; ++i) {
+                    m[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (i <= j) {
+                        f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const E *pa = &sB[i * 16 + l16][kq * KPL];
+                        const E *pb = &sC[t][kq * KPL];
 #pragma unroll
-                for (int kk = 0; kk < N / KB; ++kk)
-                    acc[c] = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), acc[c]);
-            }
-        }
-        {
-            const float send = static_cast<float>(Send);
+                        for (int kk = 0; kk < N / KB; ++kk)
+                            g = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), g);
+                        const int s0 = i * 16 + kq * 4;
+                        if (i == j) {
+                            const f32x4_t dq = *reinterpret_cast<const f32x4_t *>(&sDl[s0]);
 #pragma unroll
-            for (int r = 0; r < NST; ++r) {
-                const int q = w + kWaves * r;
-                if (q < NSTILE) {
-                    const int ni = q / NPT, pi = q % NPT;
-                    f32x4_t a = ST::decay(send, acc_s[r]);
-                    const E *pa = &sBt[ni * 16 + l16][kq * KPL];
+                            for (int e = 0; e < 4; ++e)
+                                m[i][e] = s0 + e <= t ? g[e] * dq[e] * ST::ex(static_cast<float>(st_t - sSt[s0 + e])) : 0.0f;
+                        } else {
+                            const f32x4_t uq = *reinterpret_cast<const f32x4_t *>(&sU[s0]);
+                            const float rt = sR[i][t];
 #pragma unroll
-                    for (int kk = 0; kk < kQ / KB; ++kk) {
-                        const typename MM::frag fa = MM::load(pa + kk * KB);
-#pragma unroll
-                        for (int q2 = 0; q2 < NS; ++q2)
-                            a = MM::mma(fa, MM::load(&sXw[q2][pi * 16 + l16][kq * KPL] + kk * KB), a);
+                            for (int e = 0; e < 4; ++e) m[i][e] = g[e] * uq[e] * rt;
+                        }
                     }
-                    acc_s[r] = a;
-                    // the copy read by the next chunk (the other buffer: its
-                    // last readers finished before this chunk's staging)
+                }
+                // carried-state readout S_in C^T, scaled by exp(s_t): A = the state
+                // tiles (K = n in the tile-pair order), B = C rows from LDS
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kp = 0; kp < N / 32; ++kp)
 #pragma unroll
                     for (int q2 = 0; q2 < NS; ++q2)
-                        MM::put4(&sS[k ^ 1][q2][pi * 16 + l16][ni * 16 + kq * 4], MM::term(a[0], q2),
-                                 MM::term(a[1], q2), MM::term(a[2], q2), MM::term(a[3], q2));
+#pragma unroll
+                        for (int stp = 0; stp < PK::kSteps; ++stp)
+                            acc = MM::mma(PK::from_tiles(acc_s[2 * kp], acc_s[2 * kp + 1], stp, q2),
+                                          PK::from_lds(&sC[t][32 * kp], kq, stp), acc);
+                acc *= ST::ex(static_cast<float>(st_t));
+                // + X^T M^T: A = x rows from LDS, B = the M^T tiles (K = s, tile pairs)
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp) {
+                    if (2 * kp <= j) {
+#pragma unroll
+                        for (int q2 = 0; q2 < NS; ++q2)
+#pragma unroll
+                            for (int stp = 0; stp < PK::kSteps; ++stp)
+                                acc = MM::mma(PK::from_lds(&sX[prow][32 * kp], kq, stp),
+                                              PK::from_tiles(m[2 * kp], m[2 * kp + 1], stp, q2), acc);
+                    }
                 }
-            }
-        }
-
-        // ---- M = (C B^T) masked, times Delta_s exp(s_t - s_s), over the ten
-        // 16x16 blocks with s-block i <= t-block j: blocks 0..3 the diagonal
-        // (exp per element), blocks 4..9 below it, where the factor splits as
-        // u_s r_t^(i) (both at most 1); wave w takes blocks w, w + W, w + 2 W
-#pragma unroll
-        for (int rr = 0; rr < 3; ++rr) {
-            const int qb = w + kWaves * rr;
-            if (qb >= 10) break;
-            const bool diag = qb < 4;
-            const int q = qb - 4;                       // off-diagonal: q = j (j - 1) / 2 + i
-            const int j = diag ? qb : 1 + (q >= 1) + (q >= 3);
-            const int i = diag ? qb : q - j * (j - 1) / 2;
-            f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
-            const E *pa = &sB[i * 16 + l16][kq * KPL];
-            const E *pb = &sC[j * 16 + l16][kq * KPL];
-#pragma unroll
-            for (int kk = 0; kk < N / KB; ++kk) g = MM::mma(MM::load(pa + kk * KB), MM::load(pb + kk * KB), g);
-            const int tm = j * 16 + l16, s0 = i * 16 + kq * 4;
-            float m[4];
-            if (diag) {
-                const f32x4_t dq = *reinterpret_cast<const f32x4_t *>(&sDl[s0]);
-                const SR st = sSt[tm];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    m[e] = s0 + e <= tm ? g[e] * dq[e] * ST::ex(static_cast<float>(st - sSt[s0 + e])) : 0.0f;
-            } else {
-                const f32x4_t uq = *reinterpret_cast<const f32x4_t *>(&sU[s0]);
-                const float rt = sR[i][tm];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) m[e] = g[e] * uq[e] * rt;
-            }
-#pragma unroll
-            for (int q2 = 0; q2 < NS; ++q2)
-                MM::put4(&sM[q2][tm][s0], MM::term(m[0], q2), MM::term(m[1], q2), MM::term(m[2], q2),
-                         MM::term(m[3], q2));
-        }
-        __syncthreads();
-
-        // ---- Y^T += X^T M^T for this wave's tiles, then D skip, gate, store
-        {
-            const float est = __shfl(eS, t);
-            constexpr int kmax = kQ / KB;
-            const int nkd = (16 * (jw + 1) + KB - 1) / KB;
-            const bool tvalid = static_cast<int64_t>(t0) + t < L;
-#pragma unroll
-            for (int c = 0; c < NPW; ++c) {
-                f32x4_t a = acc[c] * est;
-                const E *pa2 = &sX[(pw0 + c) * 16 + l16][kq * KPL];
-#pragma unroll
-                for (int q2 = 0; q2 < NS; ++q2) {
-                    const E *pb2 = &sM[q2][t][kq * KPL];
-#pragma unroll
-                    for (int kk = 0; kk < kmax; ++kk)
-                        if (kk < nkd) a = MM::mma(MM::load(pa2 + kk * KB), MM::load(pb2 + kk * KB), a);
-                }
+                // D skip, gate, store (lane: channels 16 pw + 4 kq + e, step t)
                 float yv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int pp = (pw0 + c) * 16 + kq * 4 + e;
-                    float o = fmaf(Dh, MM::dec(sX[pp][t]), a[e]);
-                    if (has_z) o *= silu(QD::get(rz[c], e));
+                    float o = fmaf(Dh, MM::dec(sX[pw * 16 + kq * 4 + e][t]), acc[e]);
+                    if (has_z) o *= silu(QD::get(rz[r], e));
                     yv[e] = o;
                 }
-                QD::store(yv, rY, tvalid ? t0 * rowX + oZ[c] : kOffNone);
+                QD::store(yv, rY, static_cast<int64_t>(t0) + t < L ? t0 * rowX + oZ[r] : kOffNone);
+            }
+        };
+        if (tp == 0)
+            tiles(std::integral_constant<int, 0>{});
+        else
+            tiles(std::integral_constant<int, 1>{});
+
+        // ---- state: S^T <- exp(s_Q) S^T + B^T (w x)  (both waves of the channel
+        // block keep the same copy)
+        {
+            const float send = static_cast<float>(Send);
+#pragma unroll
+            for (int ni = 0; ni < NNT; ++ni) {
+                f32x4_t a = ST::decay(send, acc_s[ni]);
+                const E *pa = &sBt[ni * 16 + l16][kq * KPL];
+#pragma unroll
+                for (int kk = 0; kk < kQ / KB; ++kk) {
+                    const typename MM::frag fa = MM::load(pa + kk * KB);
+#pragma unroll
+                    for (int q2 = 0; q2 < NS; ++q2)
+                        a = MM::mma(fa, MM::load(&sXw[q2][prow][kq * KPL] + kk * KB), a);
+                }
+                acc_s[ni] = a;
             }
         }
     }
 
-    if (p.last) {
+    // one copy of the final state: the wave of each channel block with tp = 0
+    if (p.last && tp == 0) {
 #pragma unroll
-        for (int r = 0; r < NST; ++r) {
-            const int q = w + kWaves * r;
-            if (q < NSTILE) {
-                const int ni = q / NPT, pi = q % NPT;
-                float *dst = p.last + (((b * H + h) * P + p0 + pi * 16 + l16) * N + ni * 16 + kq * 4);
-                *reinterpret_cast<f32x4_t *>(dst) = acc_s[r];
-            }
+        for (int ni = 0; ni < NNT; ++ni) {
+            float *dst = p.last + (((b * H + h) * P + p0 + pw * 16 + l16) * N + ni * 16 + kq * 4);
+            *reinterpret_cast<f32x4_t *>(dst) = acc_s[ni];
         }
     }
 }
 
-template <typename T, int N, int PT, bool WIDE>
+template <typename T, int N, int PT>
 hipError_t launch(const SsdParams &p, int64_t blocks, hipStream_t s) {
-    hipLaunchKernelGGL((ssd_chunk_kernel<T, N, PT, WIDE>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * waves_for<PT, WIDE>()), 0, s, p);
+    hipLaunchKernelGGL((ssd_chunk_kernel<T, N, PT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * waves_for<PT>()),
+                       0, s, p);
     return hipGetLastError();
 }
 
-// 32-channel tiles when the head size allows; the wide form when the grid
-// leaves every CU at most one workgroup
+// 32-channel tiles when the head size allows
 template <typename T, int N>
 hipError_t launch_pt(const SsdParams &p, int64_t batch, hipStream_t s) {
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 0;
-    if (p.headdim % 32 == 0) {
-        const int64_t blocks = batch * p.nheads * (p.headdim / 32);
-        return blocks <= cus ? launch<T, N, 32, true>(p, blocks, s) : launch<T, N, 32, false>(p, blocks, s);
-    }
-    return launch<T, N, 16, false>(p, batch * p.nheads * (p.headdim / 16), s);
+    if (p.headdim % 32 == 0) return launch<T, N, 32>(p, batch * p.nheads * (p.headdim / 32), s);
+    return launch<T, N, 16>(p, batch * p.nheads * (p.headdim / 16), s);
 }
 
 }  // namespace

@@ -102,8 +102,8 @@ def test_ssd_bf16(N, P, T):
 
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 def test_ssd_more_workgroups_than_cus(io):
-    # 4 x 72 heads x one 32-channel tile = 288 workgroups: the launch takes the
-    # 4-wave form (small grids above take the 8-wave one); ragged last chunk
+    # 4 x 72 heads x one 32-channel tile = 288 workgroups, more than the CUs:
+    # several share a CU; ragged last chunk
     inp = gen.make_ssd_inputs(4, 70, 72, 32, 64, io=io, h0_kind="normal", seed=733)
     check(inp, tag=f"{io}-288wg")
 
