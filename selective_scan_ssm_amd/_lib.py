@@ -94,8 +94,7 @@ def load(path: str = LIB_PATH):
             return _lib
         if not os.path.exists(path):
             raise LibraryMissing(
-                f"{path} is not built; run `python -m selective_scan_ssm_amd.build` "
-                "(or __graft_entry__.build()) first")
+                f"{path} is not built; run `python -m selective_scan_ssm_amd.build` first")
         lib = _bind(ctypes.CDLL(path))
         if lib.ssm_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libssmscan ABI {lib.ssm_abi_version()} != {ABI_VERSION}")
