@@ -45,28 +45,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
-# fp32 VALU issue slots of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
-# (157.3 TFLOP/s = this x 2 for packed-fp32 x 2 for FMA; packed fp32 is not used.)
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Minimal fp32 VALU lane-slots of the fast (bf16 io) arithmetic:
-#  per (t, d, n) item: Delta*A mul, exp2 (half rate: 2 slots), Delta*x*B mul,
-#  decay*h + u fma, C*h fma  -> 6
-#  per (t, d) element: 3 widening converts, softplus (add bias, scale, exp2 (2),
-#  add, log2 (2), max, fma = 9), Delta*x, SiLU (scale, exp2 (2), add,
-#  rcp (2), mul = 7), D*x fma, gate mul, rounding convert -> 23
-SLOTS_PER_ITEM, SLOTS_PER_ELEM = 6, 23
-# Minimal fp32 VALU lane-slots of the backward (ssm_scan_bwd, bf16 io):
-#  per (t, d, n) item: the state again (Delta*A mul, exp2 (2), Delta*x*B mul,
-#  decay*h + u fma, C*h fma for the gate's derivative = 6), then the adjoint:
+# fp32 VALU issue rate of the chip, in fma lane-operations: MI355X's published
+# fp32 vector peak 157.3 TFLOP/s is 78.6 T fma/s = 256 CUs x 4 SIMDs x 32
+# lanes x 2.4 GHz.  Plain (not packed) fp32 fma issues at that width on gfx950:
+# `bench.py --microbench` measures 58.9 T/s at 8 waves per SIMD (the rest is
+# the clock under load), 47.8 T/s at 2 and 26.2 T/s at 1.
+VALU_PEAK_TSLOTS = 256 * 4 * 32 * 2.4e9 / 1e12
+# Transcendentals in fma slots, as measured by the same microbenchmark (issue
+# rate of fma over that of the op, 8 waves per SIMD): v_exp_f32 3.1, v_log_f32
+# and v_rcp_f32 4.6.
+EXP2, LOG2, RCP = 3.1, 4.6, 4.6
+# Minimal fp32 VALU slots of the fast (bf16 io) arithmetic:
+#  per (t, d, n) item: Delta*A mul, exp2, Delta*x*B mul, decay*h + u fma,
+#  C*h fma  -> 4 + EXP2
+#  per (t, d) element: 3 widening converts, softplus (add bias, scale, exp2,
+#  add, log2, max, fma), Delta*x, SiLU (scale, exp2, add, rcp, mul), D*x fma,
+#  gate mul, rounding convert
+SLOTS_PER_ITEM = 4 + EXP2
+SLOTS_PER_ELEM = 3 + (5 + EXP2 + LOG2) + 1 + (3 + EXP2 + RCP) + 3
+# Minimal fp32 VALU slots of the backward (ssm_scan_bwd, bf16 io):
+#  per (t, d, n) item: the state again (Delta*A mul, exp2, Delta*x*B mul,
+#  decay*h + u fma, C*h fma for the gate's derivative), then the adjoint:
 #  g += dy C, a h_{t-1}, g (a h_{t-1}), its A term of dL/dDelta, its Delta
 #  term of dA, g B into the per-step sum, g Delta x for dB, dy h for dC,
-#  g *= a (= 9), and one add each for the channel sums of dB and dC -> 17
-#  per (t, d) element: 4 widening converts, softplus (9), Delta*x, SiLU and
-#  its derivative (scale, exp2 (2), add, rcp (2), z*s, dy mul, (1 - s), z(1-s)+1,
-#  dz product (2) = 12), sigmoid of the softplus input (scale, exp2 (2), add,
-#  rcp (2) = 6), dL/dDelta (fma, mul), dx (2), D*x for the readout, dD and dbias
-#  sums (2), 3 rounding converts -> 40
-BWD_SLOTS_PER_ITEM, BWD_SLOTS_PER_ELEM = 17, 40
+#  g *= a (9), and one add each for the channel sums of dB and dC
+#  per (t, d) element: 4 widening converts, softplus, Delta*x, SiLU and its
+#  derivative (scale, exp2, add, rcp, z*s, dy mul, (1 - s), z(1-s)+1, dz
+#  product (2)), sigmoid of the softplus input (scale, exp2, add, rcp),
+#  dL/dDelta (fma, mul), dx (2), D*x for the readout, dD and dbias sums (2),
+#  3 rounding converts
+BWD_SLOTS_PER_ITEM = (4 + EXP2) + 9 + 2
+BWD_SLOTS_PER_ELEM = 4 + (5 + EXP2 + LOG2) + 1 + (8 + EXP2 + RCP) + (2 + EXP2 + RCP) + 2 + 2 + 1 + 2 + 3
 COPY_CAL_BYTES = 1 << 30
 
 SOURCES = {
@@ -190,9 +199,20 @@ def cpu_baseline(inp, w, seconds_target):
                           delta_bias=bias, h0=h0, threads=threads)
     dt = time.perf_counter() - t0
     elems = w.batch * w.seqlen * nd
+    # the same oracle on one thread, over the first nd1 of those channels
+    nd1 = max(1, nd // threads)
+    t1 = time.perf_counter()
+    oracle.selective_scan(np.ascontiguousarray(x[:, :, :nd1]), np.ascontiguousarray(dl[:, :, :nd1]),
+                          np.ascontiguousarray(inp["A"][:nd1]), B, C, D=None if D is None else D[:nd1],
+                          z=None if z is None else np.ascontiguousarray(z[:, :, :nd1]),
+                          delta_bias=None if bias is None else bias[:nd1],
+                          h0=None if h0 is None else np.ascontiguousarray(h0[:, :nd1]), threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "value_1_thread": w.batch * w.seqlen * nd1 / dt1,
             "sample": f"all {w.batch} batches x {w.seqlen} steps x first {nd} of {w.d_inner} channels "
-                      f"({elems} elements, d_state {w.d_state}), fp64, {dt:.2f} s wall"}
+                      f"({elems} elements, d_state {w.d_state}), fp64, {dt:.2f} s wall; one thread: "
+                      f"first {nd1} channels, {dt1:.2f} s"}
 
 
 def upload(a, io, dev):
@@ -347,7 +367,7 @@ def bench_workload(args, dev):
         slots = valu_slots(w)
         ach = slots / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
-                "unit": "T fp32 VALU lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
+                "unit": "T fp32 fma-equivalent lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
                 "traffic": traffic, "kernel": kname,
                 "algorithmic_slots_per_launch": slots,
                 "hbm_achieved_GBs": round(hbm_gbs, 1), "hbm_peak_GBs": HBM_PEAK_GBS,
@@ -357,6 +377,8 @@ def bench_workload(args, dev):
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname}
     roof.update({"launch_ms_mean": round(launch_ms, 5),
                  "launch_ms_min": round(min(step_ms) / launches, 5),
+                 "launch_ms_median": round(float(np.median(step_ms)) / launches, 5),
+                 "launch_ms_max": round(max(step_ms) / launches, 5),
                  "algorithmic_bytes_per_launch": alg})
 
     cpu = None
@@ -469,7 +491,7 @@ def bench_backward(args, dev):
     kname = "ssm_scan_bwd (checkpoint pass + bwd_kernel + bwd_reduce_kernel, timed as one call)"
     if N > 1:       # d_state 16: the per-item work bounds it, as in the forward
         roof = {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
-                "unit": "T fp32 VALU lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
+                "unit": "T fp32 fma-equivalent lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
                 "traffic": None, "kernel": kname, "algorithmic_slots_per_launch": slots,
                 "hbm_achieved_GBs": round(hbm, 1), "hbm_peak_GBs": HBM_PEAK_GBS,
                 "hbm_frac": round(hbm / HBM_PEAK_GBS, 4)}
@@ -477,6 +499,7 @@ def bench_backward(args, dev):
         roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kname}
     roof.update({"launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+                 "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
                  "algorithmic_bytes_per_launch": alg})
     cpu = None
     if not args.no_cpu_baseline:
@@ -546,6 +569,7 @@ def bench_conv(args, dev):
             "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("conv", w.name + "-conv1d"),
             "kernel": "ssm_causal_conv1d_fwd (conv1d_kernel)",
             "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+            "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
             "algorithmic_bytes_per_launch": alg}
     cpu = None
     if not args.no_cpu_baseline:
@@ -629,6 +653,7 @@ def bench_ssd(args, dev):
             "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("ssd", w.name),
             "kernel": "ssd_scan_fwd (ssd_chunk_kernel)",
             "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+            "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
             "algorithmic_bytes_per_launch": alg}
     cpu = None
     if not args.no_cpu_baseline:
@@ -657,6 +682,80 @@ def bench_ssd(args, dev):
             "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
+def device_record():
+    """Name, CUs and (best effort) the current clocks of GPU 0."""
+    import subprocess
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    rec = {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": pr.multi_processor_count}
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+        rec["clocks"] = [ln.split(":", 1)[1].strip() for ln in out.splitlines() if "sclk" in ln or "mclk" in ln][:4]
+    except Exception:                                 # noqa: BLE001 -- the record is optional
+        pass
+    return rec
+
+
+def bench_micro(args, dev):
+    """Measured ceilings: a 1 GiB 16-byte copy (read + write bandwidth), and
+    the issue rate of fp32 fma and of v_exp_f32 over the whole chip."""
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import _lib
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    nbytes = COPY_CAL_BYTES
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def copy():
+        rc = lib.ssm_mb_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
+        if rc:
+            raise RuntimeError(_lib.status_string(rc))
+
+    ms = timed(copy, 10)
+    copy_gbs = 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+    del src, dst
+    iters = 4096
+    out = torch.empty(256 * 4 * 8 // 4 * 256, dtype=torch.float32, device=dev)
+    rates = {}
+    for wps in (1, 2, 8):                              # waves per SIMD over the whole chip
+        blocks = 256 * 4 * wps // 4
+        for op, name in ((0, "fma"), (1, "exp2"), (2, "log2"), (3, "rcp")):
+            if wps != 8 and op != 0:
+                continue
+            def run(op=op, blocks=blocks):
+                rc = lib.ssm_mb_valu(op, out.data_ptr(), blocks, iters, sh)
+                if rc:
+                    raise RuntimeError(_lib.status_string(rc))
+            ms = timed(run, 10)
+            rates[f"{name}_{wps}w"] = blocks * 256 * iters * 8 / (float(np.median(ms)) * 1e-3) / 1e12
+    fma = rates["fma_8w"]
+    return {"metric": "measured ceilings", "copy_read_write_GBs": round(copy_gbs, 1),
+            "copy_frac_of_8TBs": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "valu_T_lane_ops_per_s": {k: round(v, 3) for k, v in rates.items()},
+            "valu_peak_T_slots": round(VALU_PEAK_TSLOTS, 3),
+            "fma_frac_of_peak": round(fma / VALU_PEAK_TSLOTS, 4),
+            "fma_slots_each": {k: round(fma / rates[f"{k}_8w"], 3) for k in ("exp2", "log2", "rcp")},
+            "device": device_record(),
+            "note": "copy: 1 GiB, 16-byte non-temporal loads and stores; VALU: 256 lanes per workgroup, "
+                    "1, 2 or 8 waves per SIMD over 256 CUs, 4096 steps x 8 independent chains per lane"}
 
 
 def copy_calibration():
@@ -767,6 +866,8 @@ def main():
                     help="time ssm_causal_conv1d_fwd (width 4, SiLU) on a scan workload's x instead")
     ap.add_argument("--ssd", nargs="?", const="mamba2-2.7b-ssd-layer-bf16", default=None,
                     help="time ssd_scan_fwd (the Mamba-2 multi-head scan) on the named layer shape instead")
+    ap.add_argument("--microbench", action="store_true",
+                    help="measure the copy bandwidth and the fp32 fma / v_exp_f32 issue rates instead")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("DIR", "COMMAND"))
     ap.add_argument("--summarize-traffic", nargs=7,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR",
@@ -813,7 +914,7 @@ def main():
     from selective_scan_ssm_amd import _lib
     _lib.load()
     fn = (bench_backward if args.backward else bench_conv if args.conv else
-          bench_ssd if args.ssd is not None else bench_workload)
+          bench_ssd if args.ssd is not None else bench_micro if args.microbench else bench_workload)
     rec = fn(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)
 

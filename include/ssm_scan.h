@@ -262,6 +262,23 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
                  const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
                  int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *stream);
 
+/*
+ * Measurement helpers -- not part of any scan.  They give the benchmark the
+ * measured ceilings its roofline fractions are read against.
+ *
+ * ssm_mb_copy: dst = src for `bytes` bytes with 16-byte non-temporal loads
+ *   and stores (grid-stride).  bytes a multiple of 16, both pointers 16-byte
+ *   aligned (SSM_ERR_ALIGN), buffers not overlapping (SSM_ERR_ALIAS).
+ * ssm_mb_valu: `blocks` workgroups of 256 lanes, each lane running 8
+ *   independent chains of `iters` steps of one fp32 operation -- op 0:
+ *   fma(x, 0.999, 0.001); op 1: 2^-x (v_exp_f32); op 2: log2(x + 2)
+ *   (v_log_f32); op 3: 1 / (x + 1) (v_rcp_f32) -- and writing one sum per lane
+ *   to out (blocks * 256 floats).  op outside [0, 3] or negative sizes:
+ *   SSM_ERR_SHAPE.
+ */
+int ssm_mb_copy(const void *src, void *dst, size_t bytes, void *stream);
+int ssm_mb_valu(int op, float *out, int64_t blocks, int64_t iters, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ssm_status_string(int status);
 

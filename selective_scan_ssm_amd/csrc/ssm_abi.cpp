@@ -431,4 +431,21 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
     return hip_status(ssm::launch_ssd_scan(a, static_cast<hipStream_t>(stream)));
 }
 
+int ssm_mb_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return SSM_OK;
+    if (!src || !dst) return SSM_ERR_NULL;
+    if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return SSM_ERR_ALIGN;
+    if (overlap(range(src, static_cast<int64_t>(bytes), 1), range(dst, static_cast<int64_t>(bytes), 1)))
+        return SSM_ERR_ALIAS;
+    return hip_status(ssm::launch_mb_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_mb_valu(int op, float *out, int64_t blocks, int64_t iters, void *stream) {
+    if (op < 0 || op > 3 || blocks < 0 || iters < 0 || blocks > (int64_t(1) << 31) - 1) return SSM_ERR_SHAPE;
+    if (blocks == 0) return SSM_OK;
+    if (!out) return SSM_ERR_NULL;
+    if (!aligned(out, 4)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_mb_valu(op, out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

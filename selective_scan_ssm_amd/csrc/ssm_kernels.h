@@ -98,4 +98,8 @@ hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t s);
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);
 
+// Measurement helpers (copy bandwidth, fp32 VALU issue rate).
+hipError_t launch_mb_copy(const void *src, void *dst, uint64_t bytes, hipStream_t s);
+hipError_t launch_mb_valu(int op, float *out, int64_t blocks, int64_t iters, hipStream_t s);
+
 }  // namespace ssm

@@ -362,3 +362,27 @@ def test_ssd_alias_detection(lib):
     a = ssd_args()
     a["y"] = a["last"]
     assert call_ssd(lib, a) == EALIAS
+
+
+# ------------------------------------------------------ measurement helpers
+@pytest.mark.parametrize("args,code", [
+    (dict(src=None), ENULL), (dict(bytes_=24), EALIGN), (dict(src=0x7f0000000008), EALIGN),
+    (dict(dst="src+16"), EALIAS), (dict(bytes_=0, src=None, dst=None), OK),
+])
+def test_mb_copy_validation(lib, args, code):
+    f = FakeDev()
+    src, dst = f(), f()
+    a = dict(src=src, dst=dst, bytes_=1 << 20)
+    a.update(args)
+    if a["dst"] == "src+16":
+        a["dst"] = a["src"] + 16
+    assert lib.ssm_mb_copy(a["src"], a["dst"], a["bytes_"], None) == code
+
+
+@pytest.mark.parametrize("op,blocks,iters,out,code", [
+    (4, 1, 1, True, ESHAPE), (-1, 1, 1, True, ESHAPE), (0, -1, 1, True, ESHAPE), (0, 1, -1, True, ESHAPE),
+    (0, 1, 1, False, ENULL), (3, 0, 1, False, OK),
+])
+def test_mb_valu_validation(lib, op, blocks, iters, out, code):
+    ptr = FakeDev()() if out else None
+    assert lib.ssm_mb_valu(op, ptr, blocks, iters, None) == code
