@@ -282,3 +282,43 @@ def test_deterministic_and_guard_bands():
     assert torch.equal(r[0][1], r[1][1])
     assert torch.all(canary[:1024] == 3.5) and torch.all(canary[1024 + n:] == 3.5)
     assert torch.all(lcan[:1024] == -7.0) and torch.all(lcan[1024 + 2 * 200 * 16:] == -7.0)
+
+
+# ------------------------------------------------------------ maximum sizes
+def test_sequence_beyond_one_gib_segment():
+    """A sequence whose (seqlen, d_inner) slab is 4.3 GB per tensor: buffer
+    offsets inside a segment are 32-bit, so the scan must cut it into more
+    segments (here 5 of 84,000 steps) than it would for load balance alone.
+    Inputs are drawn on the device (N(0,1) bf16 x, delta, z, B, C; A = -(n+1);
+    S4-initialised delta bias; N(0,1) D and h0); sampled channels over the
+    whole sequence are checked against the fp64 oracle."""
+    import oracle
+    from selective_scan_ssm_amd import ops
+    Bt, T, Dd, N = 1, 420_000, 5120, 16
+    G.say(f"[parity] >1 GiB segment: B={Bt} T={T} D={Dd} N={N} bf16")
+    gen_ = torch.Generator(device="cuda").manual_seed(4201)
+    rnd = lambda *s: torch.randn(*s, generator=gen_, device="cuda", dtype=torch.float32)
+    x = rnd(Bt, T, Dd).to(torch.bfloat16)
+    delta = rnd(Bt, T, Dd).to(torch.bfloat16)
+    z = rnd(Bt, T, Dd).to(torch.bfloat16)
+    B = rnd(Bt, T, N).to(torch.bfloat16)
+    C = rnd(Bt, T, N).to(torch.bfloat16)
+    A = -(torch.arange(N, device="cuda", dtype=torch.float32) + 1.0).expand(Dd, N).contiguous()
+    dt0 = torch.exp(torch.rand(Dd, generator=gen_, device="cuda") * (np.log(1e-1) - np.log(1e-3)) + np.log(1e-3))
+    bias = torch.log(torch.expm1(dt0)).float()
+    D = rnd(Dd)
+    h0 = rnd(Bt, Dd, N)
+    y, last = ops.scan_fwd(x, delta, A, B, C, D=D, z=z, delta_bias=bias, h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    di = np.r_[0:4, 2558:2562, 5116:5120]
+    col = lambda t: G.from_torch(t[:, :, di].contiguous())
+    yo, lo = oracle.selective_scan(col(x), col(delta), A[di].cpu().double().numpy(), G.from_torch(B),
+                                   G.from_torch(C), D=D[di].cpu().double().numpy(), z=col(z),
+                                   delta_bias=bias[di].cpu().double().numpy(), delta_softplus=True,
+                                   h0=h0[:, di].cpu().double().numpy(), threads=G.ORACLE_THREADS)
+    ey = G.err(col(y), yo)
+    el = G.err(G.from_torch(last[:, di].contiguous()), lo)
+    G.say(f"[parity] >1 GiB segment err_y={ey:.3e} err_last={el:.3e}")
+    assert ey <= 2e-2 and el <= 2e-2
+    assert bool(torch.isfinite(last).all())
+    del x, delta, z, y
