@@ -65,6 +65,14 @@ def test_segments_ragged_many_tiles(io, tol):
     check(inp, d_index=d_index, tol=tol, tag=f"segments-{io}")
 
 
+def test_two_workgroups_per_cu_many_tiles():
+    # 16 batch rows x 80 channel tiles = 1280 tiles: the d_state-16 kernel runs
+    # two persistent workgroups per CU; ragged 1500-step sequence in segments
+    inp = gen.make_inputs(16, 1500, 5120, 16, io=gen.BF16, h0_kind="normal", seed=311)
+    d_index = np.r_[0:8, 2600:2608, 5112:5120]
+    check(inp, d_index=d_index, tag="two-per-cu")
+
+
 def test_workload4_decode_bf16_two_layers():
     from selective_scan_ssm_amd import ops
     for layer in range(2):
