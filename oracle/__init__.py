@@ -61,6 +61,7 @@ def _bind(lib):
     lib.oracle_causal_conv1d.restype = None
     lib.oracle_conv1d_update.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_int, _L, _L, _L, _L, _L]
     lib.oracle_conv1d_update.restype = None
+    lib.oracle_dt_proj.argtypes = [_dp, _L, _dp, _dp, _L, _L, _L, _L, _L]
     lib.oracle_ssd_scan.argtypes = [_dp, _dp, _dp, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
                                     _dp, _dp, _L, _L, _L, _L, _L, _L, _L]
     lib.oracle_ssd_scan.restype = None
@@ -316,3 +317,21 @@ def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=
 
     _run_chains(go, Bt * H * P, threads)
     return y, last
+
+
+def dt_proj(xdt, W, threads: int = 1, lib=None):
+    """delta = xdt[:, :rank] @ W.T, row by row in fp64 (oracle_dt_proj).
+    xdt: (M, ldx) with ldx >= rank; only its first rank = W.shape[1] columns
+    are read.  W: (D, rank).  Returns (M, D)."""
+    lib = lib or load()
+    xdt, W = _f64(xdt), _f64(W)
+    M, ldx = xdt.shape
+    D, rank = W.shape
+    assert ldx >= rank
+    out = np.zeros((M, D), dtype=np.float64)
+
+    def go(r0, r1):
+        lib.oracle_dt_proj(_ptr(xdt), ldx, _ptr(W), _ptr(out), M, rank, D, r0, r1)
+
+    _run_chains(go, M, threads)
+    return out

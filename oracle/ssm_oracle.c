@@ -48,6 +48,7 @@
  *   oracle_conv1d_update       -- the same for one decode token, with the rolling
  *                                 window of past inputs
  *   oracle_ssd_scan            -- the Mamba-2 multi-head scan (scalar decay per head)
+ *   oracle_dt_proj             -- the projection that produces the scan's delta input
  */
 #include <math.h>
 #include <stddef.h>
@@ -432,5 +433,32 @@ void oracle_ssd_scan(const double *x, const double *dt, const double *dt_bias, i
         if (last_state)
             for (long n = 0; n < dstate; ++n)
                 last_state[c * dstate + n] = s[n];
+    }
+}
+
+
+/*
+ * dt_proj: the projection that produces the scan's delta input ("Mamba State
+ * Space Models complete guide" (youngju.dev), section 5, the MambaBlock of the
+ * complete implementation: a linear layer from dt_rank = d_model / 16 inputs
+ * to d_inner outputs, applied to the first dt_rank columns of the x_proj
+ * output, then softplus).  Its bias is the scan's delta_bias, which the scan
+ * adds inside the softplus, so the product alone is computed here:
+ *     out[m, d] = sum_{k=0}^{rank-1} xdt[m * ldx + k] * W[d * rank + k]
+ * Layouts: xdt rows of stride ldx >= rank, of which only the first `rank`
+ * columns are read (the rest of an x_proj row holds B and C); W (dim, rank)
+ * row-major, the layer's weight; out (rows, dim).  Rows [row_begin, row_end)
+ * are computed.
+ */
+void oracle_dt_proj(const double *xdt, long ldx, const double *W, double *out,
+                    long rows, long rank, long dim, long row_begin, long row_end)
+{
+    for (long m = row_begin; m < row_end && m < rows; ++m) {
+        for (long d = 0; d < dim; ++d) {
+            double acc = 0.0;
+            for (long k = 0; k < rank; ++k)
+                acc += xdt[m * ldx + k] * W[d * rank + k];
+            out[m * dim + d] = acc;
+        }
     }
 }

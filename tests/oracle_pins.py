@@ -637,4 +637,53 @@ def pin_ssd_continuation(lib):
     assert _rel(np.concatenate([y1, y2], axis=1), y) < 1e-13 and _rel(l2, last) < 1e-13
 
 
+# ------------------------------------------------------------------ dt_proj
+# delta = xdt[:, :rank] @ W.T (youngju.dev guide, section 5 MambaBlock: the
+# dt_proj linear layer; its bias is the scan's delta_bias).
+
+def pin_dt_proj_unit_rows(lib):
+    """Row k of the identity picks column k of W.  The columns past `rank` of
+    each row hold NaN, so reading any of them would show."""
+    rank, D = 5, 7
+    W = np.arange(D * rank, dtype=np.float64).reshape(D, rank) * 0.25 - 3.0
+    xdt = np.full((rank, rank + 3), np.nan)
+    xdt[:, :rank] = np.eye(rank)
+    out = oracle.dt_proj(xdt, W, lib=lib)
+    assert np.array_equal(out, W.T), out
+
+
+def pin_dt_proj_integer_brute_force(lib):
+    """Small integers: every product and sum is exact in fp64, so the result
+    must equal the integer sum written out with Python ints."""
+    rng = np.random.default_rng(77)
+    M, rank, D, ldx = 4, 6, 3, 9
+    xi = rng.integers(-4, 5, size=(M, ldx))
+    Wi = rng.integers(-4, 5, size=(D, rank))
+    expect = [[sum(int(xi[m, k]) * int(Wi[d, k]) for k in range(rank)) for d in range(D)] for m in range(M)]
+    out = oracle.dt_proj(xi.astype(np.float64), Wi.astype(np.float64), lib=lib)
+    assert np.array_equal(out, np.array(expect, dtype=np.float64)), (out, expect)
+
+
+def pin_dt_proj_rank_one(lib):
+    """W = u v^T: every output row is u times the scalar v . x_m."""
+    rng = np.random.default_rng(78)
+    M, rank, D = 6, 8, 11
+    u, v = rng.standard_normal(D), rng.standard_normal(rank)
+    xdt = rng.standard_normal((M, rank + 2))
+    out = oracle.dt_proj(xdt, np.outer(u, v), lib=lib)
+    expect = np.outer(xdt[:, :rank] @ v, u)
+    assert _rel(out, expect) < 1e-13, _rel(out, expect)
+
+
+def pin_dt_proj_linearity(lib):
+    """Linear in its input rows: f(a x1 + b x2) = a f(x1) + b f(x2)."""
+    rng = np.random.default_rng(79)
+    M, rank, D = 5, 7, 9
+    W = rng.standard_normal((D, rank))
+    x1, x2 = rng.standard_normal((M, rank)), rng.standard_normal((M, rank))
+    lhs = oracle.dt_proj(2.0 * x1 - 0.5 * x2, W, lib=lib)
+    rhs = 2.0 * oracle.dt_proj(x1, W, lib=lib) - 0.5 * oracle.dt_proj(x2, W, lib=lib)
+    assert _rel(lhs, rhs) < 1e-13
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

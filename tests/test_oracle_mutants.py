@@ -100,6 +100,16 @@ MUTANTS = [
     ("ssd: gate by z", "out *= silu(z[xi]);", "out *= z[xi];"),
     ("ssd: h0 ignored", "s[n] = h0 ? h0[c * dstate + n] : 0.0;", "s[n] = 0.0;"),
     ("ssd: last state not final", "last_state[c * dstate + n] = s[n];", "last_state[c * dstate + n] = 0.0;"),
+    # dt_proj
+    ("dt_proj: W transposed", "acc += xdt[m * ldx + k] * W[d * rank + k];",
+     "acc += xdt[m * ldx + k] * W[k * dim + d];"),
+    ("dt_proj: row stride ignored", "acc += xdt[m * ldx + k] * W[d * rank + k];",
+     "acc += xdt[m * rank + k] * W[d * rank + k];"),
+    ("dt_proj: whole row read", "for (long k = 0; k < rank; ++k)\n                acc +=",
+     "for (long k = 0; k < ldx; ++k)\n                acc +="),
+    ("dt_proj: first column dropped", "for (long k = 0; k < rank; ++k)\n                acc +=",
+     "for (long k = 1; k < rank; ++k)\n                acc +="),
+    ("dt_proj: output transposed", "out[m * dim + d] = acc;", "out[d * rows + m] = acc;"),
 ]
 
 
