@@ -19,7 +19,9 @@ bounded sample of the same workload.
 --backward times ssm_scan_bwd (the gradient of the scan; workloads 1, 2, 3)
 instead, one call per step, against the backward's own VALU roofline; --conv
 times the block's causal conv1d + SiLU (ssm_causal_conv1d_fwd, width 4) over
-the workload's x against the HBM roofline; --ssd [NAME] times the Mamba-2
+the workload's x against the HBM roofline; --dt-proj times the projection to
+delta (ssm_dt_proj, MFMA) of the workload's layer against the HBM roofline,
+its output write being the bound; --ssd [NAME] times the Mamba-2
 multi-head scan (ssd_scan_fwd) on a Mamba2Block-shaped layer (default
 mamba2-2.7b-ssd-layer-bf16) against the HBM roofline.
 
@@ -85,10 +87,12 @@ SOURCES = {
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "conv": ["selective_scan_ssm_amd/csrc/conv1d.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "ssd": ["selective_scan_ssm_amd/csrc/ssd_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "dtproj": ["selective_scan_ssm_amd/csrc/dt_proj.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
 # the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
-                 "decode": "state_update_rows_kernel", "conv": "conv1d_kernel", "ssd": "ssd_chunk_kernel"}
+                 "decode": "state_update_rows_kernel", "conv": "conv1d_kernel", "ssd": "ssd_chunk_kernel",
+                 "dtproj": "dt_proj_kernel"}
 
 
 def kind_of(w):
@@ -517,6 +521,99 @@ def bench_backward(args, dev):
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
 
 
+def dtproj_shape(w):
+    """dt_proj of a scan workload's layer: rows B*T, rank = d_model / 16 with
+    d_model = d_inner / 2 (expand 2), x_proj rows of rank + 2 d_state."""
+    rank = max(1, (w.d_inner // 2) // 16)
+    return w.batch * w.seqlen, rank, w.d_inner, rank + 2 * w.d_state
+
+
+def dtproj_algorithmic_bytes(rows, rank, dim, io_b):
+    # the rank columns of each x_proj row and W read once, delta written once
+    return (rows * rank + dim * rank + rows * dim) * io_b
+
+
+def bench_dtproj(args, dev):
+    """ssm_dt_proj over a scan workload's layer: one step = the projection of
+    all (batch x seqlen) x_proj rows to delta (rows x d_inner)."""
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import _lib, ops
+    from selective_scan_ssm_amd import inputs as gen
+    import oracle
+    _lib.load()
+    w = gen.WORKLOADS[args.workload]
+    if w.kind != "scan":
+        raise SystemExit("--dt-proj needs a Mamba layer workload (2 or 3)")
+    io = w.io
+    io_b = 2 if io == gen.BF16 else 4
+    rows, rank, dim, ldx = dtproj_shape(w)
+    log(f"[bench] dt_proj, workload {args.workload} ({w.name}): rows {rows} rank {rank} d_inner {dim}")
+    inp = gen.make_dtproj_inputs(rows, rank, dim, ldx, io=io, seed=args.workload)
+    alg = dtproj_algorithmic_bytes(rows, rank, dim, io_b)
+    flops = 2 * rows * rank * dim
+    nset = max(1, math.ceil(600e6 / alg)) if args.rotate is None else args.rotate
+    xds = [upload(inp["x_dbl"], io, dev) for _ in range(nset)]
+    Wd = upload(inp["W"], io, dev)
+    outs = [torch.empty((rows, dim), dtype=xds[0].dtype, device=dev) for _ in range(nset)]
+    stream = torch.cuda.current_stream(dev)
+    cur = [0]
+
+    def step():
+        i = cur[0] % nset
+        cur[0] += 1
+        ops.dt_proj(xds[i][:, :rank], Wd, out=outs[i])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = float(np.mean(step_ms))
+    hbm = alg / (call_ms * 1e-3) / 1e9
+    name = w.name + "-dt_proj"
+    mfma_peak = 2500.0 if io == gen.BF16 else 157.3
+    roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("dtproj", name),
+            "kernel": "ssm_dt_proj (dt_proj_kernel)",
+            "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+            "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
+            "algorithmic_bytes_per_launch": alg,
+            "mfma": {"achieved": round(flops / (call_ms * 1e-3) / 1e12, 2), "peak": mfma_peak,
+                     "unit": "TFLOP/s", "flops_per_launch": flops}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        # about 3e9 multiply-adds per core-second (measured): size the sample to
+        # about `cpu_seconds` core-seconds
+        nr = int(min(rows, max(64, args.cpu_seconds * 3e9 / (rank * dim))))
+        x64 = gen.to_f64(inp["x_dbl"][:nr], io)
+        t1 = time.perf_counter()
+        oracle.dt_proj(x64, gen.to_f64(inp["W"], io), threads=threads)
+        dt = time.perf_counter() - t1
+        cpu = {"value": nr * dim / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+               "sample": f"dt_proj, the first {nr} of {rows} rows, all {dim} channels, rank {rank}, "
+                         f"fp64, {dt:.2f} s wall"}
+    cfg = {"workload": name, "rows": rows, "rank": rank, "d_inner": dim, "x_proj_row": ldx, "io": io,
+           "seed": args.workload}
+    if nset > 1:
+        cfg["rotated_input_sets"] = nset
+    return {"metric": "dt_proj elements/s (rows*d_inner)", "value": rows * dim / (ms_per_step * 1e-3),
+            "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
 def bench_conv(args, dev):
     """ssm_causal_conv1d_fwd (width 4, SiLU) over the x of a scan workload:
     one step = one convolution of the whole (batch, seqlen, d_inner) tensor."""
@@ -864,6 +961,8 @@ def main():
                     help="scan order through ssm_scan_fwd_2d (height 1): 0 forward, 1 reversed")
     ap.add_argument("--conv", action="store_true",
                     help="time ssm_causal_conv1d_fwd (width 4, SiLU) on a scan workload's x instead")
+    ap.add_argument("--dt-proj", action="store_true",
+                    help="time ssm_dt_proj (the projection to delta) of a scan workload's layer instead")
     ap.add_argument("--ssd", nargs="?", const="mamba2-2.7b-ssd-layer-bf16", default=None,
                     help="time ssd_scan_fwd (the Mamba-2 multi-head scan) on the named layer shape instead")
     ap.add_argument("--microbench", action="store_true",
@@ -884,6 +983,11 @@ def main():
             w = gen.SSD_WORKLOADS[wl[4:]]
             kind, wname = "ssd", w.name
             alg = ssd_algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
+        elif wl.startswith("dtproj"):  # "dtproj3": dt_proj of workload 3's layer
+            w = gen.WORKLOADS[int(wl[6:])]
+            kind, wname = "dtproj", w.name + "-dt_proj"
+            rows, rank, dim, _ = dtproj_shape(w)
+            alg = dtproj_algorithmic_bytes(rows, rank, dim, 2 if w.io == gen.BF16 else 4)
         elif wl.startswith("conv"):    # "conv3": the conv1d over workload 3's x
             w = gen.WORKLOADS[int(wl[4:])]
             kind, wname = "conv", w.name + "-conv1d"
@@ -913,7 +1017,7 @@ def main():
         return
     from selective_scan_ssm_amd import _lib
     _lib.load()
-    fn = (bench_backward if args.backward else bench_conv if args.conv else
+    fn = (bench_backward if args.backward else bench_conv if args.conv else bench_dtproj if args.dt_proj else
           bench_ssd if args.ssd is not None else bench_micro if args.microbench else bench_workload)
     rec = fn(args, torch.device("cuda:0"))
     print(json.dumps(rec), flush=True)

@@ -233,6 +233,27 @@ int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weigh
                              int64_t d_inner, int64_t width, int io_dtype, void *stream);
 
 /*
+ * ssm_dt_proj -- the projection that produces the scan's delta input in a
+ * Mamba block (youngju.dev guide, section 5, "complete Mamba implementation":
+ * dt_proj, a linear layer from dt_rank = d_model / 16 inputs to d_inner
+ * outputs, applied to the first dt_rank columns of each x_proj output row,
+ * then softplus; its bias is the scan's delta_bias, which ssm_scan_fwd adds
+ * inside the softplus, so only the product is formed here):
+ *     delta[m, d] = sum_{k < rank} xdt[m * ldx + k] * W[d * rank + k]
+ *   xdt  : rows x ldx, io dtype (rows = batch * seqlen); only the first `rank`
+ *          columns of each row are read (an x_proj row holds dt, then B, C)
+ *   W    : (d_inner, rank), io dtype: the layer's weight, row-major
+ *   delta: (rows, d_inner), io dtype, written; fp32 accumulation on the
+ *          matrix cores, rounded once to the io dtype
+ *   ldx >= rank; rank and ldx multiples of 8 (bf16) or 4 (fp32); d_inner a
+ *   multiple of 4: else SSM_ERR_SHAPE.  xdt, W and delta 16-byte aligned:
+ *   else SSM_ERR_ALIGN.  delta may not overlap xdt or W (SSM_ERR_ALIAS).
+ *   rows == 0 or d_inner == 0: nothing is enqueued.
+ */
+int ssm_dt_proj(const void *xdt, int64_t ldx, const void *W, void *delta, int64_t rows,
+                int64_t rank, int64_t d_inner, int io_dtype, void *stream);
+
+/*
  * ssd_scan_fwd -- the Mamba-2 multi-head scan ("Mamba State Space Models
  * complete guide", youngju.dev, section 6 "Mamba 2": a multi-head SSM whose
  * decay is one scalar per head; the block's input projection yields x and z

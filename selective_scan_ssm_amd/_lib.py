@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG, "libssmscan.so")
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",
            "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_causal_conv1d_fwd",
-           "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd", "ssm_mb_copy", "ssm_mb_valu",
+           "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd", "ssm_dt_proj", "ssm_mb_copy", "ssm_mb_valu",
            "ssm_status_string", "ssm_abi_version")
 ABI_VERSION = 1
 
@@ -68,6 +68,8 @@ def _bind(lib):
     lib.ssd_scan_fwd.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i64, _i64, _i64, _i64, _i64, _int, _vp]
     lib.ssd_scan_fwd.restype = _int
+    lib.ssm_dt_proj.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _vp]
+    lib.ssm_dt_proj.restype = _int
     lib.ssm_mb_copy.argtypes = [_vp, _vp, _sz, _vp]
     lib.ssm_mb_copy.restype = _int
     lib.ssm_mb_valu.argtypes = [_int, _vp, _i64, _i64, _vp]

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssmscan.so")
 ARCH = "gfx950"
 
-SOURCES = ["scan_fwd.hip", "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip", "ssd_scan.hip", "microbench.hip", "ssm_abi.cpp"]
+SOURCES = ["scan_fwd.hip", "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip", "ssd_scan.hip", "dt_proj.hip", "microbench.hip", "ssm_abi.cpp"]
 
 # Packed fp32 VALU forms are switched off (plain fp32 VALU only); code object
 # v5 is what the HIP runtime shipped with torch loads.

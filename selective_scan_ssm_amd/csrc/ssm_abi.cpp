@@ -355,6 +355,29 @@ int ssm_causal_conv1d_fwd(const void *x, const float *weight, const float *bias,
     return hip_status(ssm::launch_conv1d(a, static_cast<hipStream_t>(stream)));
 }
 
+int ssm_dt_proj(const void *xdt, int64_t ldx, const void *W, void *delta, int64_t rows,
+                int64_t rank, int64_t d_inner, int io_dtype, void *stream) {
+    if (int r = check_dtype(io_dtype)) return r;
+    const int64_t pe = io_dtype == SSM_BF16 ? 8 : 4;   // elements per 16-byte piece
+    if (rows < 0 || d_inner < 0 || rank < 1 || ldx < rank) return SSM_ERR_SHAPE;
+    if (rank % pe || ldx % pe || d_inner % 4) return SSM_ERR_SHAPE;
+    const int64_t n_x = mul3(rows, ldx, 1), n_w = mul3(d_inner, rank, 1), n_o = mul3(rows, d_inner, 1);
+    if (n_x < 0 || n_w < 0 || n_o < 0) return SSM_ERR_SHAPE;
+    // one workgroup per 128 x 128 tile of delta, numbered in 32 bits
+    if (mul3((rows + 127) / 128, (d_inner + 127) / 128, 1) > (int64_t(1) << 31) - 1) return SSM_ERR_SHAPE;
+    if (rows == 0 || d_inner == 0) return SSM_OK;
+    if (!xdt || !W || !delta) return SSM_ERR_NULL;
+    if (!aligned(xdt, 16) || !aligned(W, 16) || !aligned(delta, 16)) return SSM_ERR_ALIGN;
+    const size_t es = io_size(io_dtype);
+    const Range o = range(delta, n_o, es);
+    if (overlap(o, range(xdt, n_x, es)) || overlap(o, range(W, n_w, es))) return SSM_ERR_ALIAS;
+    ssm::DtProjArgs a;
+    a.xdt = xdt; a.W = W; a.out = delta;
+    a.rows = rows; a.rank = rank; a.dim = d_inner; a.ldx = ldx;
+    a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    return hip_status(ssm::launch_dt_proj(a, static_cast<hipStream_t>(stream)));
+}
+
 int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weight,
                              const float *bias, void *out, int apply_silu, int64_t batch,
                              int64_t d_inner, int64_t width, int io_dtype, void *stream) {

@@ -94,6 +94,16 @@ struct SsdArgs {
 bool ssd_supported(int64_t headdim, int64_t dstate, int bf16);
 hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t s);
 
+// dt_proj: delta (rows, dim) = xdt[:, :rank] (row stride ldx) x W^T, W (dim, rank);
+// all three in the io dtype, fp32 accumulation on the matrix cores.
+struct DtProjArgs {
+    const void *xdt, *W;
+    void *out;
+    int64_t rows, rank, dim, ldx;
+    int bf16;
+};
+hipError_t launch_dt_proj(const DtProjArgs &a, hipStream_t s);
+
 // Causal depthwise conv1d (+ SiLU), whole sequence and one decode token.
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);

@@ -28,7 +28,7 @@ F32 = "f32"
 BF16 = "bf16"
 
 # tensor ids inside one seed
-_TID = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "bias": 6, "A": 7, "D": 8, "h0": 9}
+_TID = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "bias": 6, "A": 7, "D": 8, "h0": 9, "x_dbl": 10, "W_dt": 11}
 
 
 def bf16_from_f32(a: np.ndarray) -> np.ndarray:
@@ -215,3 +215,16 @@ def ssd_workload_inputs(name: str, seed: int = 0, **over) -> dict:
               io=w.io, h0_kind=w.h0_kind, seed=seed)
     kw.update(over)
     return make_ssd_inputs(**kw)
+
+
+def make_dtproj_inputs(rows: int, rank: int, dim: int, ldx: int, io: str = BF16, seed: int = 0) -> dict:
+    """Inputs of dt_proj (youngju.dev guide, section 5 MambaBlock: a linear
+    layer dt_rank -> d_inner, dt_init "random" with dt_scale 1): x_dbl
+    (rows, ldx), the x_proj output whose first `rank` columns are the dt input
+    and the rest (B, C) are not read, ~ N(0, 1); W (dim, rank) ~ U(-s, s) with
+    s = rank^-1/2, the layer's random init.  Both stored in the io dtype."""
+    out = {"io": io, "rows": rows, "rank": rank, "dim": dim, "ldx": ldx}
+    out["x_dbl"] = _store(_normal(seed, "x_dbl", (rows, ldx)), io)
+    s = rank ** -0.5
+    out["W"] = _store(_rng(seed, "W_dt").uniform(-s, s, size=(dim, rank)).astype(np.float32), io)
+    return out

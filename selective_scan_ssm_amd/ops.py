@@ -198,6 +198,34 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
     return g
 
 
+def dt_proj(xdt, W, out=None):
+    """delta = xdt @ W.T, the Mamba block's dt_proj without its bias (the bias
+    is the scan's delta_bias).  xdt: (rows, rank) or (batch, seqlen, rank),
+    fp32 or bf16, whose last axis is contiguous and whose rows are evenly
+    strided: typically the first rank columns of the x_proj output, a view.
+    W: (d_inner, rank) in the same dtype.  Returns delta (..., d_inner)."""
+    lib = _lib.load()
+    if xdt.dtype not in _IO:
+        raise ValueError("xdt must be float32 or bfloat16")
+    io = xdt.dtype
+    if xdt.dim() not in (2, 3) or xdt.stride(-1) != 1:
+        raise ValueError("xdt must be 2-D or 3-D with a contiguous last axis")
+    if xdt.dim() == 3 and xdt.shape[0] > 1 and xdt.stride(0) != xdt.shape[1] * xdt.stride(1):
+        raise ValueError("the rows of xdt must be evenly strided")
+    rank = xdt.shape[-1]
+    rows = xdt.numel() // rank if rank else 0
+    ldx = xdt.stride(-2)
+    Dd = W.shape[0]
+    if not xdt.is_cuda:
+        raise ValueError("xdt must be a GPU tensor")
+    _dev(W, "W", io, (Dd, rank))
+    y = out if out is not None else torch.empty(tuple(xdt.shape[:-1]) + (Dd,), dtype=io, device=xdt.device)
+    _dev(y, "out", io, tuple(xdt.shape[:-1]) + (Dd,))
+    rc = lib.ssm_dt_proj(_ptr(xdt), ldx, _ptr(W), _ptr(y), rows, rank, Dd, _IO[io], _stream(xdt.device))
+    _check(rc, "ssm_dt_proj")
+    return y
+
+
 def causal_conv1d(x, weight, bias=None, conv_state=None, silu=True, return_state=False, out=None):
     """Causal depthwise conv1d (+ SiLU) of the Mamba block's x branch.
     x: (batch, seqlen, d_inner) fp32 or bf16; weight: (d_inner, width) fp32;

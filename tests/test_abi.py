@@ -386,3 +386,42 @@ def test_mb_copy_validation(lib, args, code):
 def test_mb_valu_validation(lib, op, blocks, iters, out, code):
     ptr = FakeDev()() if out else None
     assert lib.ssm_mb_valu(op, ptr, blocks, iters, None) == code
+
+
+# ------------------------------------------------------------------ dt_proj
+def dtp_args(rows=256, rank=160, dim=512, ldx=192, io=BF16, **over):
+    f = FakeDev()
+    a = dict(xdt=f(), ldx=ldx, W=f(), out=f(), rows=rows, rank=rank, dim=dim, io=io, stream=None)
+    a.update(over)
+    return a
+
+
+def call_dtp(lib, a):
+    return lib.ssm_dt_proj(a["xdt"], a["ldx"], a["W"], a["out"], a["rows"], a["rank"], a["dim"], a["io"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(xdt=None), ENULL), (dict(W=None), ENULL), (dict(out=None), ENULL),
+    (dict(rank=0), ESHAPE), (dict(rank=-8), ESHAPE), (dict(rows=-1), ESHAPE), (dict(dim=-4), ESHAPE),
+    (dict(rank=164), ESHAPE),                  # bf16 rank not a multiple of 8
+    (dict(ldx=196), ESHAPE),                   # bf16 row stride not a multiple of 8
+    (dict(ldx=152), ESHAPE),                   # row stride below the rank
+    (dict(dim=510), ESHAPE),                   # d_inner not a multiple of 4
+    (dict(io=F32, rank=162, ldx=192), ESHAPE),
+    (dict(rows=1 << 62, ldx=1 << 8), ESHAPE),  # element count overflows
+    (dict(io=5), EDTYPE),
+    (dict(xdt=0x7f0000000008), EALIGN), (dict(W=0x7f0000000004), EALIGN), (dict(out=0x7f0000000002), EALIGN),
+    (dict(rows=0), OK), (dict(dim=0), OK), (dict(rows=0, xdt=None, out=None), OK),
+])
+def test_dt_proj_validation(lib, over, code):
+    assert call_dtp(lib, dtp_args(**over)) == code
+
+
+def test_dt_proj_alias_detection(lib):
+    a = dtp_args()
+    a["out"] = a["xdt"] + 4096
+    assert call_dtp(lib, a) == EALIAS
+    a = dtp_args()
+    a["out"] = a["W"]
+    assert call_dtp(lib, a) == EALIAS
