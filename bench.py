@@ -397,7 +397,7 @@ def bench_workload(args, dev):
         cfg["layers"] = w.layers
     elif len(sets) > 1:
         cfg["rotated_input_sets"] = len(sets)
-    return {"metric": "selective-scan fwd elements/s (B*T*D) and achieved HBM GB/s as % of peak",
+    return {"metric": "selective-scan fwd elements/s (B\u00b7T\u00b7D) and achieved HBM GB/s as % of peak",
             "value": elems / (ms_per_step * 1e-3), "unit": "elements/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
