@@ -157,3 +157,38 @@ def test_ssd_layer_full_sampled(name):
     G.say(f"[ssd] {name} sampled err_y={ey:.2e} err_last={el:.2e}")
     assert ey <= 2e-2 and el <= 2e-2
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(last))
+
+
+def test_ssd_largest_batch_row():
+    """One batch row just under the 2 GiB span the kernel's 32-bit buffer
+    offsets allow ((seqlen + 128) x heads x head size x 2 bytes < 2^31): 400,000
+    steps of the 2.7b layer's width (8 heads x 320, d_state 64), 2.05 GB per
+    tensor.  Inputs are drawn on the device (N(0,1) x, dt, z, B, C; A = -exp of
+    N(0,1) per head; the S4 dt bias; N(0,1) D and h0); sampled heads x
+    channels over the whole sequence are checked against the oracle."""
+    from selective_scan_ssm_amd import ops
+    Bt, T, H, P, N = 1, 400_000, 8, 320, 64
+    assert (T + 128) * H * P * 2 < (1 << 31)
+    G.say(f"[ssd] largest batch row: T={T} H={H} P={P} N={N} bf16")
+    g = torch.Generator(device="cuda").manual_seed(4202)
+    rnd = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
+    x, z = rnd(Bt, T, H, P).to(torch.bfloat16), rnd(Bt, T, H, P).to(torch.bfloat16)
+    dt = rnd(Bt, T, H).to(torch.bfloat16)
+    B, C = rnd(Bt, T, N).to(torch.bfloat16), rnd(Bt, T, N).to(torch.bfloat16)
+    A = -torch.exp(rnd(H))
+    dt0 = torch.exp(torch.rand(H, generator=g, device="cuda") * (np.log(1e-1) - np.log(1e-3)) + np.log(1e-3))
+    dt_bias = torch.log(torch.expm1(dt0)).float()
+    D, h0 = rnd(H), rnd(Bt, H, P, N)
+    y, last = ops.ssd_scan_fwd(x, dt, A, B, C, D=D, z=z, dt_bias=dt_bias, h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    heads, chans = [0, 7], [0, 1, 318, 319]
+    sub = lambda t: G.from_torch(t[:, :, heads][:, :, :, chans].contiguous())
+    f64 = lambda t: t.detach().cpu().double().numpy()
+    yo, lo = oracle.ssd_scan(sub(x), G.from_torch(dt[:, :, heads].contiguous()), f64(A[heads]), G.from_torch(B),
+                             G.from_torch(C), D=f64(D[heads]), z=sub(z), dt_bias=f64(dt_bias[heads]),
+                             h0=f64(h0[:, heads][:, :, chans]), threads=G.ORACLE_THREADS)
+    ey = G.err(sub(y), yo)
+    el = G.err(G.from_torch(last[:, heads][:, :, chans].contiguous()), lo)
+    G.say(f"[ssd] largest batch row err_y={ey:.2e} err_last={el:.2e}")
+    assert ey <= 2e-2 and el <= 2e-2
+    assert bool(torch.isfinite(last).all())
