@@ -185,3 +185,39 @@ def test_bwd_mamba2p8b_layer_full_sampled():
     compare(sub, o, gen.BF16, ("dx", "ddelta", "dz", "dh0", "dA", "dD", "ddelta_bias"), "w3-sampled")
     for k in ("dB", "dC"):
         assert np.all(np.isfinite(g[k])), k
+
+
+def test_bwd_largest_batch_row():
+    """One batch row just under the 2 GiB span the backward's 32-bit offsets
+    allow (seqlen x d_inner x 2 bytes < 2^31): 200,000 steps x 5120 channels,
+    d_state 16, bf16, 2.05 GB per tensor.  Inputs drawn on the device (N(0,1)
+    x, delta, z, B, C, dL/dy; A = -(n+1); S4 delta bias; N(0,1) D, h0 and
+    dL/dlast); the per-chain gradients and dA, dD, ddelta_bias of sampled
+    channels against the oracle run on those channels (dB and dC sum over
+    every channel: checked finite)."""
+    from selective_scan_ssm_amd import ops
+    Bt, T, Dd, N = 1, 200_000, 5120, 16
+    assert T * Dd * 2 < (1 << 31)
+    G.say(f"[bwd] largest batch row: T={T} D={Dd} N={N} bf16")
+    g = torch.Generator(device="cuda").manual_seed(4203)
+    rnd = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
+    x, dl, z, dy = (rnd(Bt, T, Dd).to(torch.bfloat16) for _ in range(4))
+    B, C = rnd(Bt, T, N).to(torch.bfloat16), rnd(Bt, T, N).to(torch.bfloat16)
+    A = -(torch.arange(N, device="cuda", dtype=torch.float32) + 1.0).expand(Dd, N).contiguous()
+    dt0 = torch.exp(torch.rand(Dd, generator=g, device="cuda") * (np.log(1e-1) - np.log(1e-3)) + np.log(1e-3))
+    bias = torch.log(torch.expm1(dt0)).float()
+    D, h0, dlast = rnd(Dd), rnd(Bt, Dd, N), rnd(Bt, Dd, N)
+    gr = ops.scan_bwd(x, dl, A, B, C, dy, D=D, z=z, delta_bias=bias, h0=h0, dlast=dlast)
+    torch.cuda.synchronize()
+    di = np.r_[0:4, 2558:2562, 5116:5120]
+    col = lambda t: G.from_torch(t[:, :, di].contiguous())
+    f64 = lambda t: t.detach().cpu().double().numpy()
+    o = oracle.selective_scan_bwd(col(x), col(dl), f64(A[di]), G.from_torch(B), G.from_torch(C), col(dy),
+                                  D=f64(D[di]), z=col(z), delta_bias=f64(bias[di]), h0=f64(h0[:, di]),
+                                  dlast=f64(dlast[:, di]), threads=G.ORACLE_THREADS)
+    sub = dict(dx=col(gr["dx"]), ddelta=col(gr["ddelta"]), dz=col(gr["dz"]),
+               dh0=G.from_torch(gr["dh0"][:, di].contiguous()), dA=G.from_torch(gr["dA"][di].contiguous()),
+               dD=G.from_torch(gr["dD"][di].contiguous()), ddelta_bias=G.from_torch(gr["ddelta_bias"][di].contiguous()))
+    compare(sub, o, gen.BF16, ("dx", "ddelta", "dz", "dh0", "dA", "dD", "ddelta_bias"), "largest-row")
+    for k in ("dB", "dC"):
+        assert bool(torch.isfinite(gr[k]).all()), k

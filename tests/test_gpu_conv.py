@@ -102,3 +102,29 @@ def test_conv_mamba2p8b_shape_sampled():
     e = G.err(G.from_torch(out)[:, :, di], oo)
     G.say(f"[conv] w3-shape sampled err={e:.2e}")
     assert e <= 2e-2
+
+
+def test_conv_largest_batch_row():
+    """One batch row just under the 2 GiB span of 32-bit offsets (seqlen x
+    d_inner x 2 bytes < 2^31): 200,000 steps x 5120 channels, bf16, width 4,
+    with an incoming window; drawn on the device; sampled channels over the
+    whole sequence against the oracle, the outgoing window exactly."""
+    from selective_scan_ssm_amd import ops
+    Bt, T, Dd, K = 1, 200_000, 5120, 4
+    assert T * Dd * 2 < (1 << 31)
+    G.say(f"[conv] largest batch row: T={T} D={Dd} width={K} bf16")
+    g = torch.Generator(device="cuda").manual_seed(4204)
+    x = torch.randn(Bt, T, Dd, generator=g, device="cuda").to(torch.bfloat16)
+    st = torch.randn(Bt, Dd, K - 1, generator=g, device="cuda").to(torch.bfloat16)
+    w = torch.randn(Dd, K, generator=g, device="cuda") * 0.5
+    b = torch.randn(Dd, generator=g, device="cuda")
+    out, so = ops.causal_conv1d(x, w, b, conv_state=st, silu=True, return_state=True)
+    torch.cuda.synchronize()
+    di = np.r_[0:4, 2558:2562, 5116:5120]
+    oo, oso = oracle.causal_conv1d(G.from_torch(x[:, :, di].contiguous()), w[di].cpu().double().numpy(),
+                                   b[di].cpu().double().numpy(), G.from_torch(st[:, di].contiguous()), silu=True,
+                                   threads=G.ORACLE_THREADS)
+    e = G.err(G.from_torch(out[:, :, di].contiguous()), oo)
+    G.say(f"[conv] largest batch row err={e:.2e}")
+    assert e <= 2e-2
+    assert np.array_equal(G.from_torch(so[:, di].contiguous()), oso)
