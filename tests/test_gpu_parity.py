@@ -330,3 +330,36 @@ def test_sequence_beyond_one_gib_segment():
     assert ey <= 2e-2 and el <= 2e-2
     assert bool(torch.isfinite(last).all())
     del x, delta, z, y
+
+
+def test_decode_largest_grid():
+    """Decode near the largest grid its 32-bit lane count allows (batch x
+    d_inner rounded to 64 x 4 lanes < 2^32): 200,000 states of the 2.8b layer
+    (5120 x 16 fp32, 65.5 GB in place), bf16 inputs, drawn on the device;
+    sampled batch rows in full against the oracle."""
+    import oracle
+    from selective_scan_ssm_amd import ops
+    Bt, Dd, N = 200_000, 5120, 16
+    assert Bt * Dd * 4 < (1 << 32)
+    G.say(f"[parity] decode largest grid: B={Bt} D={Dd} N={N} bf16")
+    g = torch.Generator(device="cuda").manual_seed(4205)
+    rnd = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
+    state = rnd(Bt, Dd, N)
+    rows = [0, 1, Bt // 2, Bt - 1]
+    s0 = state[rows].cpu().double().numpy()
+    x, dl, z = (rnd(Bt, Dd).to(torch.bfloat16) for _ in range(3))
+    B, C = rnd(Bt, N).to(torch.bfloat16), rnd(Bt, N).to(torch.bfloat16)
+    A = -(torch.arange(N, device="cuda", dtype=torch.float32) + 1.0).expand(Dd, N).contiguous()
+    dt0 = torch.exp(torch.rand(Dd, generator=g, device="cuda") * (np.log(1e-1) - np.log(1e-3)) + np.log(1e-3))
+    bias = torch.log(torch.expm1(dt0)).float()
+    D = rnd(Dd)
+    y = ops.state_update(state, x, dl, A, B, C, D=D, z=z, delta_bias=bias)
+    torch.cuda.synchronize()
+    pick = lambda t: G.from_torch(t[rows].contiguous())
+    f64 = lambda t: t.detach().cpu().double().numpy()
+    yo, so = oracle.state_update(s0, pick(x), pick(dl), f64(A), pick(B), pick(C), D=f64(D), z=pick(z),
+                                 delta_bias=f64(bias))
+    ey, es = G.err(pick(y), yo), G.err(f64(state[rows]), so)
+    G.say(f"[parity] decode largest grid err_y={ey:.3e} err_state={es:.3e}")
+    assert ey <= 2e-2 and es <= 2e-2
+    del state
