@@ -147,3 +147,21 @@ def test_scan2d_random(case):
     ey, el = G.err(G.from_torch(y), yo), G.err(G.from_torch(last), lo)
     G.say(f"[sweep] 2d case {case}: err_y={ey:.2e} err_last={el:.2e}")
     assert ey <= G.TOL[io] and el <= G.TOL[io]
+
+
+# ------------------------------------------------------------ dt_proj
+@pytest.mark.parametrize("case", range(8))
+def test_dtproj_random(case):
+    from selective_scan_ssm_amd import ops
+    r = draw(case, 6)
+    io = gen.BF16 if r.random() < 0.5 else gen.F32
+    pe = 8 if io == gen.BF16 else 4
+    rows, rank, dim = int(r.integers(1, 700)), pe * int(r.integers(1, 30)), 4 * int(r.integers(1, 200))
+    ldx = rank + pe * int(r.integers(0, 12))
+    G.say(f"[sweep] dt_proj case {case}: rows={rows} rank={rank} dim={dim} ldx={ldx} io={io}")
+    inp = gen.make_dtproj_inputs(rows, rank, dim, ldx, io=io, seed=600 + case)
+    got = ops.dt_proj(G.to_torch(inp["x_dbl"], io)[:, :rank], G.to_torch(inp["W"], io))
+    torch.cuda.synchronize()
+    e = G.err(G.from_torch(got), oracle.dt_proj(gen.to_f64(inp["x_dbl"], io), gen.to_f64(inp["W"], io)))
+    G.say(f"[sweep] dt_proj case {case}: err={e:.2e}")
+    assert e <= G.TOL[io]
