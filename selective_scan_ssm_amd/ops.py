@@ -208,13 +208,16 @@ def dt_proj(xdt, W, out=None):
     if xdt.dtype not in _IO:
         raise ValueError("xdt must be float32 or bfloat16")
     io = xdt.dtype
-    if xdt.dim() not in (2, 3) or xdt.stride(-1) != 1:
+    if xdt.dim() not in (2, 3) or (xdt.shape[-1] > 1 and xdt.stride(-1) != 1):
         raise ValueError("xdt must be 2-D or 3-D with a contiguous last axis")
-    if xdt.dim() == 3 and xdt.shape[0] > 1 and xdt.stride(0) != xdt.shape[1] * xdt.stride(1):
-        raise ValueError("the rows of xdt must be evenly strided")
     rank = xdt.shape[-1]
     rows = xdt.numel() // rank if rank else 0
-    ldx = xdt.stride(-2)
+    # the stride between consecutive rows, from the leading axes of size > 1
+    # (torch may report any stride for an axis of size 1)
+    lead = [(n, st) for n, st in zip(xdt.shape[:-1], xdt.stride()[:-1]) if n > 1]
+    if len(lead) == 2 and lead[0][1] != lead[1][0] * lead[1][1]:
+        raise ValueError("the rows of xdt must be evenly strided")
+    ldx = lead[-1][1] if lead else rank
     Dd = W.shape[0]
     if not xdt.is_cuda:
         raise ValueError("xdt must be a GPU tensor")

@@ -76,6 +76,11 @@ def test_dt_proj_batch_seqlen_view_and_empty():
     x = torch.zeros((0, 80), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((96, 48), dtype=torch.bfloat16, device="cuda")
     assert ops.dt_proj(x[:, :48], w).shape == (0, 96)
+    # one row, and (batch, 1, rank): the row stride comes from the axes longer than 1
+    one = gen.make_dtproj_inputs(1, 48, 96, 80, io=gen.BF16, seed=953)
+    assert G.err(run(one), expect(one)) <= 2e-2
+    five = gen.make_dtproj_inputs(5, 48, 96, 80, io=gen.BF16, seed=954)
+    assert G.err(run(five, rows_3d=(5, 1)), expect(five)) <= 2e-2
 
 
 def test_dt_proj_mamba2p8b_layer_sampled():
