@@ -505,6 +505,38 @@ def bench_backward(args, dev):
     roof.update({"launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
                  "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
                  "algorithmic_bytes_per_launch": alg})
+    # A training step's alternative: the forward records the checkpoints
+    # (ssm_scan_fwd_ckpt) and the backward reuses them (ssm_scan_bwd_ckpt),
+    # against the plain forward and the self-contained backward timed above.
+    log("[bench] forward with checkpoints and the backward that reuses them")
+    fws_need = lib.ssm_scan_workspace_bytes(w.batch, w.seqlen, w.d_inner, N, io_code)
+    fws = torch.empty(max(fws_need, 1), dtype=torch.uint8, device=dev)
+    ck = torch.empty(ops.ckpt_shape(w.batch, w.seqlen, w.d_inner, N), dtype=torch.float32, device=dev)
+    s0 = sets[0]
+    y0 = torch.empty_like(s0["x"])
+    fwd_args = (s0["x"], s0["delta"], s0["A"], s0["B"], s0["C"])
+    fwd_kw = dict(D=s0["D"], z=s0["z"], delta_bias=s0["delta_bias"], h0=s0["h0"], out=y0, workspace=fws)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return round(float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs])), 5)
+
+    fwd_ms = timed(lambda: ops.scan_fwd(*fwd_args, **fwd_kw))
+    fwd_ck_ms = timed(lambda: ops.scan_fwd(*fwd_args, ckpt_out=ck, **fwd_kw))
+    bwd_ck_ms = timed(lambda: ops.scan_bwd(*fwd_args, s0["dout"], D=s0["D"], z=s0["z"], delta_bias=s0["delta_bias"],
+                                           h0=s0["h0"], workspace=ws, ckpt=ck))
+    roof["with_forward_checkpoints"] = {
+        "fwd_ms": fwd_ms, "fwd_ckpt_ms": fwd_ck_ms, "bwd_ckpt_ms": bwd_ck_ms,
+        "step_ms": round(fwd_ck_ms + bwd_ck_ms, 5), "step_ms_self_contained": round(fwd_ms + call_ms, 5),
+        "note": "training step = forward + backward; the self-contained backward reruns the forward for "
+                "its checkpoints, the pair ssm_scan_fwd_ckpt / ssm_scan_bwd_ckpt records them once"}
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle gradient on a sample)")

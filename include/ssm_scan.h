@@ -172,6 +172,42 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inn
                                     int64_t d_state, int io_dtype);
 
 /*
+ * Saved checkpoints for training.  The backward recomputes the states of each
+ * 16-step block from the state entering it (the "saved chunk carries" of a
+ * checkpointed reverse sweep).  ssm_scan_bwd computes these checkpoints with
+ * a forward pass of its own; a training step that runs the forward anyway
+ * can record them there and hand them to ssm_scan_bwd_ckpt, which then skips
+ * that pass.
+ *
+ * ssm_scan_ckpt_bytes -- bytes of the checkpoints for this shape:
+ *   batch x ceil(seqlen / 16) x d_inner x d_state fp32, (size_t)-1 for
+ *   invalid arguments.
+ *
+ * ssm_scan_fwd_ckpt -- ssm_scan_fwd (same arguments, same y and last_state,
+ *   same workspace) that also writes `ckpt`: ckpt[b, j, d, n] is the state
+ *   h[n] of chain (b, d) entering step 16 j (h0 for j = 0).  ckpt must be
+ *   16-byte aligned (SSM_ERR_ALIGN), non-NULL when seqlen > 0 (SSM_ERR_NULL)
+ *   and overlap no other argument (SSM_ERR_ALIAS).  At d_state 16 it is one
+ *   pass; at other widths the forward and a checkpoint pass.
+ *
+ * ssm_scan_bwd_ckpt -- ssm_scan_bwd with `ckpt` as written by
+ *   ssm_scan_fwd_ckpt on the same inputs (read only; same errors as above);
+ *   the gradients are those ssm_scan_bwd returns.  Same workspace size.
+ */
+size_t ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
+int ssm_scan_fwd_ckpt(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                      const float *A, const void *B, const void *C, const float *D, const void *z,
+                      const float *h0, void *y, float *last_state, float *ckpt, int64_t batch,
+                      int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+int ssm_scan_bwd_ckpt(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                      const float *A, const void *B, const void *C, const float *D, const void *z,
+                      const float *h0, const void *dout, const float *dlast, const float *ckpt, void *dx,
+                      void *ddelta, float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
+                      float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      int io_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ssm_scan_fwd_2d -- one direction of the 2-D scan of the youngju.dev guide's
  * VMamba section (section 9, image processing): the sequence axis holds
  * height x width patches in row-major order, and the scan visits them in

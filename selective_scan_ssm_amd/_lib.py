@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",
-           "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_causal_conv1d_fwd",
+           "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_scan_ckpt_bytes",
+           "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd", "ssm_dt_proj", "ssm_mb_copy", "ssm_mb_valu",
            "ssm_status_string", "ssm_abi_version")
 ABI_VERSION = 1
@@ -55,6 +56,15 @@ def _bind(lib):
     lib.ssm_scan_bwd.restype = _int
     lib.ssm_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _int]
     lib.ssm_scan_bwd_workspace_bytes.restype = _sz
+    lib.ssm_scan_ckpt_bytes.argtypes = [_i64, _i64, _i64, _i64]
+    lib.ssm_scan_ckpt_bytes.restype = _sz
+    lib.ssm_scan_fwd_ckpt.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.ssm_scan_fwd_ckpt.restype = _int
+    lib.ssm_scan_bwd_ckpt.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.ssm_scan_bwd_ckpt.restype = _int
     lib.ssm_causal_conv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64,
                                           _int, _vp]
     lib.ssm_causal_conv1d_fwd.restype = _int

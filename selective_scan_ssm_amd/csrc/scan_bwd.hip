@@ -570,7 +570,8 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
     p.x = a.x; p.delta = a.delta; p.z = a.z; p.B = a.B; p.C = a.C; p.dout = a.dout;
     p.A = a.A; p.D = a.D; p.bias = a.delta_bias; p.h0 = a.h0; p.dlast = a.dlast;
     p.dx = a.dx; p.ddelta = a.ddelta; p.dz = a.dz;
-    p.ckpt = reinterpret_cast<float *>(ws + l.ckpt_off);
+    // checkpoints recorded by the caller's forward, or computed here
+    p.ckpt = a.ckpt_in ? const_cast<float *>(a.ckpt_in) : reinterpret_cast<float *>(ws + l.ckpt_off);
     p.dBp = reinterpret_cast<float *>(ws + l.dBp_off);
     p.dCp = reinterpret_cast<float *>(ws + l.dCp_off);
     p.dAp = reinterpret_cast<float *>(ws + l.dAp_off);
@@ -582,7 +583,9 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
     p.N = static_cast<int>(a.dstate); p.softplus = a.softplus;
     if (l.n_dt > 0 && a.batch > 0) {
         const dim3 grid(static_cast<unsigned>(l.n_dt), static_cast<unsigned>(a.batch));
-        if (ckpt_by_forward(a.dstate)) {
+        if (a.ckpt_in) {
+            // nothing to do: the forward recorded them
+        } else if (ckpt_by_forward(a.dstate)) {
             ScanArgs f = ckpt_forward_args(a.batch, a.seqlen, a.dim, a.dstate, a.bf16);
             f.x = a.x; f.delta = a.delta; f.z = a.z; f.B = a.B; f.C = a.C;
             f.delta_bias = a.delta_bias; f.A = a.A; f.D = a.D; f.h0 = a.h0;
@@ -614,6 +617,31 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
     return hipGetLastError();
 }
 
+// the checkpoint pass alone, for a forward that records them at d_state != 16
+template <typename T, int NPW> hipError_t launch_ckpt_t(const ScanArgs &f, hipStream_t s) {
+    BwdParams p{};
+    p.x = f.x; p.delta = f.delta; p.B = f.B;
+    p.A = f.A; p.bias = f.delta_bias; p.h0 = f.h0;
+    p.ckpt = f.ckpt;
+    p.seqlen = f.seqlen; p.dim = f.dim;
+    const int64_t n_dt = (f.dim + kBTile - 1) / kBTile;
+    p.n_dt = static_cast<int>(n_dt);
+    p.nblk = static_cast<int>((f.seqlen + kBT - 1) / kBT);
+    p.N = static_cast<int>(f.dstate); p.softplus = f.softplus;
+    const dim3 grid(static_cast<unsigned>(n_dt), static_cast<unsigned>(f.batch));
+    hipLaunchKernelGGL((ckpt_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T> hipError_t launch_ckpt_npw(const ScanArgs &f, hipStream_t s) {
+    switch ((f.dstate + 3) / 4) {
+    case 1: return launch_ckpt_t<T, 1>(f, s);
+    case 2: return launch_ckpt_t<T, 2>(f, s);
+    case 3: return launch_ckpt_t<T, 3>(f, s);
+    default: return launch_ckpt_t<T, 4>(f, s);
+    }
+}
+
 template <typename T> hipError_t launch_bwd_npw(const BwdArgs &a, hipStream_t s) {
     switch ((a.dstate + 3) / 4) {
     case 1: return launch_bwd_t<T, 1>(a, s);
@@ -631,6 +659,16 @@ size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
     return a.bf16 ? launch_bwd_npw<bf16_t>(a, s) : launch_bwd_npw<float>(a, s);
+}
+
+hipError_t launch_scan_fwd_ckpt(const ScanArgs &a, hipStream_t s) {
+    // d_state 16: the row kernel writes y, last_state and the checkpoints in one pass
+    if (ckpt_by_forward(a.dstate)) return launch_scan_fwd(a, s);
+    ScanArgs f = a;
+    f.ckpt = nullptr;
+    const hipError_t e = launch_scan_fwd(f, s);
+    if (e != hipSuccess || a.batch == 0 || a.dim == 0 || a.seqlen == 0) return e;
+    return a.bf16 ? launch_ckpt_npw<bf16_t>(a, s) : launch_ckpt_npw<float>(a, s);
 }
 
 }  // namespace ssm

@@ -218,12 +218,17 @@ size_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inn
     return ssm::scan_bwd_workspace(batch, seqlen, d_inner, d_state, io_dtype == SSM_BF16);
 }
 
-int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
-                 const float *A, const void *B, const void *C, const float *D, const void *z,
-                 const float *h0, const void *dout, const float *dlast, void *dx, void *ddelta,
-                 float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
-                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                 int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// ssm_scan_bwd and ssm_scan_bwd_ckpt: ckpt == nullptr computes the checkpoints
+int scan_bwd_impl(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                  const float *A, const void *B, const void *C, const float *D, const void *z,
+                  const float *h0, const void *dout, const float *dlast, void *dx, void *ddelta,
+                  float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
+                  float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                  int io_dtype, void *workspace, size_t workspace_bytes, void *stream,
+                  const float *ckpt, bool ckpt_given) {
     if (int r = check_dtype(io_dtype)) return r;
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > SSM_MAX_D_STATE)
         return SSM_ERR_SHAPE;
@@ -243,6 +248,10 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
     if (n_btd > 0 && (!x || !delta || !dout || !dx || !ddelta)) return SSM_ERR_NULL;
     if (n_btd > 0 && z && !dz) return SSM_ERR_NULL;
     if (n_btn > 0 && (!B || !C || !dB || !dC)) return SSM_ERR_NULL;
+    const int64_t n_ck = mul3(mul3(batch, (seqlen + 15) / 16, d_inner), d_state, 1);
+    if (n_ck < 0) return SSM_ERR_SHAPE;
+    if (ckpt_given && n_btd > 0 && !ckpt) return SSM_ERR_NULL;
+    if (ckpt && !aligned(ckpt, 16)) return SSM_ERR_ALIGN;
     const void *io_ptrs[] = {x, delta, B, C, z, dout, dx, ddelta, dB, dC, dz};
     for (const void *p : io_ptrs)
         if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
@@ -254,7 +263,7 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
                          range(B, n_btn, es),         range(C, n_btn, es),
                          range(A, n_dn, 4),           range(D, d_inner, 4),
                          range(delta_bias, d_inner, 4), range(h0, n_bdn, 4),
-                         range(dlast, n_bdn, 4)};
+                         range(dlast, n_bdn, 4),      range(ckpt, n_ck, 4)};
     const Range outs[] = {range(dx, n_btd, es),        range(ddelta, n_btd, es),
                           range(z ? dz : nullptr, n_btd, es), range(dB, n_btn, es),
                           range(dC, n_btn, es),        range(dA, n_dn, 4),
@@ -282,7 +291,73 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int 
     a.softplus = delta_softplus ? 1 : 0;
     a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.ckpt_in = ckpt;
     return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                 const float *A, const void *B, const void *C, const float *D, const void *z,
+                 const float *h0, const void *dout, const float *dlast, void *dx, void *ddelta,
+                 float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
+                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                 int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return scan_bwd_impl(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, dout, dlast, dx, ddelta,
+                         ddelta_bias, dA, dB, dC, dD, dz, dh0, batch, seqlen, d_inner, d_state, io_dtype,
+                         workspace, workspace_bytes, stream, nullptr, false);
+}
+
+int ssm_scan_bwd_ckpt(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                      const float *A, const void *B, const void *C, const float *D, const void *z,
+                      const float *h0, const void *dout, const float *dlast, const float *ckpt, void *dx,
+                      void *ddelta, float *ddelta_bias, float *dA, void *dB, void *dC, float *dD, void *dz,
+                      float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      int io_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return scan_bwd_impl(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, dout, dlast, dx, ddelta,
+                         ddelta_bias, dA, dB, dC, dD, dz, dh0, batch, seqlen, d_inner, d_state, io_dtype,
+                         workspace, workspace_bytes, stream, ckpt, true);
+}
+
+size_t ssm_scan_ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > SSM_MAX_D_STATE)
+        return static_cast<size_t>(-1);
+    const int64_t n = mul3(mul3(batch, (seqlen + 15) / 16, d_inner), d_state, 4);
+    return n < 0 ? static_cast<size_t>(-1) : static_cast<size_t>(n);
+}
+
+int ssm_scan_fwd_ckpt(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                      const float *A, const void *B, const void *C, const float *D, const void *z,
+                      const float *h0, void *y, float *last_state, float *ckpt, int64_t batch,
+                      int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, seqlen,
+                          d_inner, d_state, io_dtype);
+    if (r) return r;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    const int64_t n_ck = mul3(mul3(batch, (seqlen + 15) / 16, d_inner), d_state, 1);
+    if (n_ck < 0) return SSM_ERR_SHAPE;
+    if (n_ck > 0 && !ckpt) return SSM_ERR_NULL;
+    if (ckpt && !aligned(ckpt, 16)) return SSM_ERR_ALIGN;
+    const size_t es = io_size(io_dtype);
+    const int64_t n_btd = mul3(batch, seqlen, d_inner), n_btn = mul3(batch, seqlen, d_state);
+    const int64_t n_bdn = mul3(batch, d_inner, d_state);
+    const Range ck = range(ckpt, n_ck, 4);
+    const Range others[] = {range(x, n_btd, es),  range(delta, n_btd, es), range(z, n_btd, es),
+                            range(B, n_btn, es),  range(C, n_btn, es),     range(A, d_inner * d_state, 4),
+                            range(D, d_inner, 4), range(delta_bias, d_inner, 4), range(h0, n_bdn, 4),
+                            range(y, seqlen > 0 ? n_btd : 0, es), range(last_state, n_bdn, 4)};
+    for (const Range &o : others)
+        if (overlap(ck, o)) return SSM_ERR_ALIAS;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, seqlen, d_inner, d_state, io_dtype, workspace,
+                                workspace_bytes);
+    a.ckpt = ckpt;
+    const size_t need = ssm::scan_fwd_workspace(a);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_scan_fwd_ckpt(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t ssm_scan_2d_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t d_inner,

@@ -18,8 +18,9 @@ struct ScanArgs {
     int bf16;                            // io dtype: 1 = bf16, 0 = fp32
     void *workspace;
     size_t workspace_bytes;
-    // optional (d_state 16 only): the state entering every 16-step block,
-    // (batch, ceil(seqlen / 16), dim, 16) fp32, for the backward's sweep
+    // optional (read by the d_state-16 kernel; launch_scan_fwd_ckpt covers the
+    // other widths): the state entering every 16-step block,
+    // (batch, ceil(seqlen / 16), dim, dstate) fp32, for the backward's sweep
     float *ckpt = nullptr;
 };
 
@@ -54,11 +55,19 @@ struct BwdArgs {
     int bf16;
     void *workspace;
     size_t workspace_bytes;
+    // optional: the checkpoints a forward recorded (scan_ckpt_bytes); given,
+    // the backward skips its own checkpoint pass
+    const float *ckpt_in = nullptr;
 };
 
 // Backward of the forward scan, 1 <= dstate <= 16.
 size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
+// The forward that also records the state entering every 16-step block in
+// a.ckpt, (batch, ceil(seqlen / 16), dim, dstate) fp32, the layout the
+// backward reads: one launch at d_state 16, the forward and a checkpoint pass
+// otherwise.
+hipError_t launch_scan_fwd_ckpt(const ScanArgs &a, hipStream_t s);
 
 // The 2-D scan orders: gather into scan order, the forward scan, scatter y.
 size_t scan_2d_workspace(const ScanArgs &a, bool has_z);

@@ -44,11 +44,13 @@ def _stream(device) -> int:
 
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
-             return_last_state=False, out=None, last_state_out=None, workspace=None):
+             return_last_state=False, out=None, last_state_out=None, workspace=None, ckpt_out=None):
     """Selective scan.  x, delta, z: (batch, seqlen, d_inner) fp32 or bf16;
     B, C: (batch, seqlen, d_state) same dtype; A: (d_inner, d_state) fp32;
     D, delta_bias: (d_inner,) fp32; h0: (batch, d_inner, d_state) fp32.
-    Returns y (same dtype as x) or (y, last_state fp32)."""
+    Returns y (same dtype as x) or (y, last_state fp32).  ckpt_out: an fp32
+    tensor of ckpt_shape(...) that also receives the state entering every
+    16-step block (ssm_scan_fwd_ckpt), for scan_bwd(..., ckpt=ckpt_out)."""
     lib = _lib.load()
     if x.dtype not in _IO:
         raise ValueError("x must be float32 or bfloat16")
@@ -78,11 +80,23 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     if need:
         ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
             need, dtype=torch.uint8, device=x.device)
-    rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
-                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
-                          Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(x.device))
-    _check(rc, "ssm_scan_fwd")
+    if ckpt_out is not None:
+        _dev(ckpt_out, "ckpt_out", torch.float32, ckpt_shape(Bt, T, Dd, N))
+        rc = lib.ssm_scan_fwd_ckpt(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                   _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
+                                   _ptr(ckpt_out), Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(x.device))
+        _check(rc, "ssm_scan_fwd_ckpt")
+    else:
+        rc = lib.ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last),
+                              Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(x.device))
+        _check(rc, "ssm_scan_fwd")
     return (y, last) if return_last_state else y
+
+
+def ckpt_shape(batch, seqlen, d_inner, d_state):
+    """Shape of the saved checkpoints: (batch, ceil(seqlen / 16), d_inner, d_state)."""
+    return (batch, (seqlen + 15) // 16, d_inner, d_state)
 
 
 def sm1_scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
@@ -153,11 +167,13 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, delt
 
 
 def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
-             h0=None, dlast=None, workspace=None):
+             h0=None, dlast=None, workspace=None, ckpt=None):
     """Gradient of `scan_fwd`.  Same inputs, plus dout = dL/dy (like x) and
     dlast = dL/dlast_state ((batch, d_inner, d_state) fp32, optional).  Returns
     a dict: dx, ddelta, dB, dC (dtype of x), dA, dh0 (fp32), and dz, dD,
-    ddelta_bias (fp32 for dD / ddelta_bias) when z, D, delta_bias are given."""
+    ddelta_bias (fp32 for dD / ddelta_bias) when z, D, delta_bias are given.
+    ckpt: the checkpoints scan_fwd(..., ckpt_out=) recorded on the same inputs
+    (ssm_scan_bwd_ckpt); the backward then skips its own checkpoint pass."""
     lib = _lib.load()
     if x.dtype not in _IO:
         raise ValueError("x must be float32 or bfloat16")
@@ -189,12 +205,20 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
     if need:
         ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
             need, dtype=torch.uint8, device=dev)
-    rc = lib.ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
-                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
-                          _ptr(dlast), _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["ddelta_bias"]),
-                          _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-                          _ptr(g["dh0"]), Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(dev))
-    _check(rc, "ssm_scan_bwd")
+    outs = (_ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["ddelta_bias"]), _ptr(g["dA"]), _ptr(g["dB"]),
+            _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]))
+    if ckpt is not None:
+        _dev(ckpt, "ckpt", torch.float32, ckpt_shape(Bt, T, Dd, N))
+        rc = lib.ssm_scan_bwd_ckpt(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                                   _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
+                                   _ptr(dlast), _ptr(ckpt), *outs, Bt, T, Dd, N, _IO[io], _ptr(ws), need,
+                                   _stream(dev))
+        _check(rc, "ssm_scan_bwd_ckpt")
+    else:
+        rc = lib.ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)),
+                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dout),
+                              _ptr(dlast), *outs, Bt, T, Dd, N, _IO[io], _ptr(ws), need, _stream(dev))
+        _check(rc, "ssm_scan_bwd")
     return g
 
 

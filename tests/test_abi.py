@@ -425,3 +425,50 @@ def test_dt_proj_alias_detection(lib):
     a = dtp_args()
     a["out"] = a["W"]
     assert call_dtp(lib, a) == EALIAS
+
+
+# ------------------------------------------------- checkpoints saved by the forward
+def test_ckpt_bytes(lib):
+    # batch x ceil(seqlen / 16) x d_inner x d_state fp32
+    assert lib.ssm_scan_ckpt_bytes(2, 33, 8, 4) == 2 * 3 * 8 * 4 * 4
+    assert lib.ssm_scan_ckpt_bytes(1, 0, 8, 16) == 0
+    assert lib.ssm_scan_ckpt_bytes(1, 16, 8, 0) == (1 << 64) - 1
+    assert lib.ssm_scan_ckpt_bytes(-1, 16, 8, 4) == (1 << 64) - 1
+
+
+def call_fwd_ckpt(lib, a, ckpt):
+    return lib.ssm_scan_fwd_ckpt(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"], a["C"],
+                                 a["D"], a["z"], a["h0"], a["y"], a["last"], ckpt, a["batch"], a["seqlen"],
+                                 a["dim"], a["dstate"], a["io"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_fwd_ckpt_validation(lib):
+    # d_state 16 always needs a workspace: a valid call stops at the 16-byte one
+    base = dict(dstate=16, ws_bytes=16)
+    a = scan_args(**base)
+    ck = FakeDev().base + (1 << 36)
+    assert call_fwd_ckpt(lib, a, ck) == EWS
+    assert call_fwd_ckpt(lib, a, None) == ENULL
+    assert call_fwd_ckpt(lib, a, ck + 8) == EALIGN
+    assert call_fwd_ckpt(lib, a, a["y"]) == EALIAS
+    assert call_fwd_ckpt(lib, a, a["h0"]) == EALIAS
+    assert call_fwd_ckpt(lib, scan_args(batch=0, **base), None) == OK
+    assert call_fwd_ckpt(lib, scan_args(dstate=17, ws_bytes=16), ck) == ESHAPE
+
+
+def call_bwd_ckpt(lib, a, ckpt):
+    return lib.ssm_scan_bwd_ckpt(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"], a["C"],
+                                 a["D"], a["z"], a["h0"], a["dout"], a["dlast"], ckpt, a["dx"], a["ddelta"],
+                                 a["ddelta_bias"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dh0"],
+                                 a["batch"], a["seqlen"], a["dim"], a["dstate"], a["io"], a["ws"],
+                                 a["ws_bytes"], a["stream"])
+
+
+def test_bwd_ckpt_validation(lib):
+    a = bwd_args()
+    ck = FakeDev().base + (1 << 36)
+    assert call_bwd_ckpt(lib, a, ck) == EWS              # valid up to the (too small) workspace
+    assert call_bwd_ckpt(lib, a, None) == ENULL
+    assert call_bwd_ckpt(lib, a, ck + 4) == EALIGN
+    assert call_bwd_ckpt(lib, a, a["dx"]) == EALIAS      # an output over the checkpoints
+    assert call_bwd_ckpt(lib, a, a["dh0"]) == EALIAS

@@ -221,3 +221,39 @@ def test_bwd_largest_batch_row():
     compare(sub, o, gen.BF16, ("dx", "ddelta", "dz", "dh0", "dA", "dD", "ddelta_bias"), "largest-row")
     for k in ("dB", "dC"):
         assert bool(torch.isfinite(gr[k]).all()), k
+
+
+@pytest.mark.parametrize("io,N,T", [(gen.BF16, 16, 300), (gen.F32, 16, 75), (gen.F32, 4, 130), (gen.BF16, 7, 40)])
+def test_bwd_with_forward_checkpoints(io, N, T):
+    """ssm_scan_fwd_ckpt + ssm_scan_bwd_ckpt: the forward's y and last_state
+    are those of ssm_scan_fwd and the gradients those of ssm_scan_bwd, bit for
+    bit; the checkpoint of block j is the state after the first 16 j steps
+    (the oracle's last_state of that prefix)."""
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(2, T, 200, N, io=io, a_kind="sm1", h0_kind="normal", seed=340 + N)
+    t = G.device_inputs(inp)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], h0=t["h0"])
+    y1, l1 = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], return_last_state=True, **kw)
+    ck = torch.empty(ops.ckpt_shape(2, T, 200, N), dtype=torch.float32, device="cuda")
+    y2, l2 = ops.scan_fwd(t["x"], t["delta"], t["A"], t["B"], t["C"], return_last_state=True, ckpt_out=ck, **kw)
+    dout, dlast = grads_inputs(inp, 41)
+    dd, dl = G.to_torch(dout, io), G.to_torch(dlast, gen.F32)
+    g1 = ops.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dd, dlast=dl, **kw)
+    g2 = ops.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], dd, dlast=dl, ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(l1, l2)
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
+    c = G.from_torch(ck)
+    assert np.array_equal(c[:, 0], inp["h0"].astype(np.float64))
+    d = G.decoded(inp)
+    for j in (1, (T - 1) // 16):
+        s = 16 * j
+        pre = lambda a: None if a is None else np.ascontiguousarray(a[:, :s])
+        _, lo = oracle.selective_scan(pre(d["x"]), pre(d["delta"]), d["A"], pre(d["B"]), pre(d["C"]), D=d["D"],
+                                      z=pre(d["z"]), delta_bias=d["delta_bias"], h0=d["h0"],
+                                      threads=G.ORACLE_THREADS)
+        e = G.err(c[:, j], lo)
+        G.say(f"[bwd] checkpoint block {j} ({io}, N={N}) err={e:.2e}")
+        assert e <= (1e-5 if io == gen.F32 else 2e-2), (j, e)
