@@ -1052,6 +1052,8 @@ def main():
     fn = (bench_backward if args.backward else bench_conv if args.conv else bench_dtproj if args.dt_proj else
           bench_ssd if args.ssd is not None else bench_micro if args.microbench else bench_workload)
     rec = fn(args, torch.device("cuda:0"))
+    # the GPU's name, CUs and clocks, read after the timed region
+    rec.setdefault("device", device_record())
     print(json.dumps(rec), flush=True)
 
 
