@@ -364,6 +364,8 @@ def bench_workload(args, dev):
     traffic = traffic_from_profile(kind, w.name) if args.direction is None else None
     kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)",
              "rows": "ssm_scan_fwd (scan_rows_kernel)" if args.direction is None else
+                     "ssm_scan_fwd_2d (scan_rows_kernel reading each segment from its end)"
+                     if args.direction == 1 else
                      "ssm_scan_fwd_2d (gather + scan_rows_kernel + scatter, timed as one call)",
              "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
              "decode": "ssm_state_update (state_update_rows_kernel)"}[kind]
@@ -814,14 +816,23 @@ def bench_ssd(args, dev):
 
 
 def device_record():
-    """Name, CUs and (best effort) the current clocks of GPU 0."""
-    import subprocess
+    """Name, CUs and (best effort) the current clocks of GPU 0, the clocks read
+    from the amdgpu driver's DPM tables in sysfs (the level marked '*'); no
+    child process is started, so the record is safe under a profiler that has
+    initialised the GPU before the program runs."""
+    import glob
     import torch
     pr = torch.cuda.get_device_properties(0)
     rec = {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": pr.multi_processor_count}
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-        rec["clocks"] = [ln.split(":", 1)[1].strip() for ln in out.splitlines() if "sclk" in ln or "mclk" in ln][:4]
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(cards) == 1:                           # one GPU: its clocks are unambiguous
+            clocks = []
+            for table in ("pp_dpm_sclk", "pp_dpm_mclk"):
+                with open(cards[0].replace("pp_dpm_sclk", table)) as f:
+                    clocks += [f"{table[-4:]} {ln.split(':', 1)[1].replace('*', '').strip()}"
+                               for ln in f if ln.rstrip().endswith("*")]
+            rec["clocks"] = clocks
     except Exception:                                 # noqa: BLE001 -- the record is optional
         pass
     return rec

@@ -4,7 +4,9 @@
 // column-major (the patch grid transposed), its reverse -- and y comes back
 // at each patch's own position.
 //
-// The orders are permutations of the sequence axis, so the path is:
+// The reversed row-major order at d_state 16 is read backwards in place by
+// the forward kernel.  Every other case is a permutation of the sequence
+// axis, so the path is:
 //   gather x, delta, z, B, C into scan order (permute_rows_kernel),
 //   the forward scan of this library on the gathered tensors,
 //   scatter y back to the patches' positions (the same kernel, inverse map).
@@ -95,6 +97,14 @@ hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int 
     if (a.batch == 0 || a.dim == 0) return hipSuccess;
     const Scan2dLayout l = scan2d_layout(a, a.z != nullptr);
     char *ws = static_cast<char *>(a.workspace);
+    if (direction == 1 && a.dstate == 16) {
+        // the reversed row-major order is the sequence read backwards: the
+        // d_state-16 kernel walks it in place, with no gathered copy
+        ScanArgs f = a;
+        f.reverse = 1;
+        f.workspace = ws + l.fwd_off; f.workspace_bytes = l.fwd_bytes;
+        return launch_scan_fwd(f, s);
+    }
     const size_t es = a.bf16 ? 2 : 4;
     const int64_t rd = a.dim * es, rn = a.dstate * es;
     ScanArgs f = a;

@@ -568,8 +568,10 @@ template <> struct Wide4<float> {
 
 // CK = true: also record the state entering every block in p.ckpt (y may
 // then be absent); a separate instantiation, so the forward proper carries
-// none of it
-template <typename T, int FL, bool CK = false>
+// none of it.  REV = true: the sequence is visited from its last step to its
+// first (step k of the scan reads and writes row seqlen - 1 - k), the 2-D
+// scan's reversed row-major order without a gathered copy.
+template <typename T, int FL, bool CK = false, bool REV = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void scan_rows_kernel(Params p) {
     using M = typename MathFor<T>::type;
@@ -612,7 +614,9 @@ void scan_rows_kernel(Params p) {
     const bool softplus_on = FL ? true : p.softplus != 0;
     const bool has_z = FL ? true : p.z != nullptr;
 
-    const int64_t row0 = b * seqlen + t_begin;
+    // descriptors start at the segment's lowest row: its first step, or its
+    // last one when the sequence is visited backwards
+    const int64_t row0 = REV ? b * seqlen + (seqlen - t_end) : b * seqlen + t_begin;
     const int64_t e0 = (row0 * dim + d0) * static_cast<int64_t>(es);
     const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + e0);
     const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + e0);
@@ -626,7 +630,18 @@ void scan_rows_kernel(Params p) {
     const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * static_cast<int64_t>(es), bc_bytes);
     const uint32_t row_bytes = static_cast<uint32_t>(dim * static_cast<int64_t>(es));
     const uint32_t vcol = col * es;
-    const uint32_t voff_full = vcol + static_cast<uint32_t>(rstep) * row_bytes;   // + group row in the scalar offset
+    // lane offset of its row in a whole group, the group's first row in the
+    // scalar offset.  Backwards, group step s is row 3 - s of the group, whose
+    // first row (in the scalar offset) is steps - 4 - (the group's first step):
+    // never negative for a whole block, so both halves stay in the segment.
+    const uint32_t voff_full = vcol + static_cast<uint32_t>(REV ? 3 - rstep : rstep) * row_bytes;
+    auto soff_full = [&](int j, int g) __attribute__((always_inline)) {
+        return static_cast<uint32_t>(REV ? steps - 4 - (j * kRowTB + 4 * g) : j * kRowTB + 4 * g) * row_bytes;
+    };
+    // the lane offset of segment step k
+    auto row_off = [&](int k) __attribute__((always_inline)) {
+        return vcol + static_cast<uint32_t>(REV ? steps - 1 - k : k) * row_bytes;
+    };
     // carried states of this tile: one 64-bit word per state, the value in
     // the low half and (segment + 1) of its writer in the high half
     uint64_t *hslot = reinterpret_cast<uint64_t *>(p.hbuf) + static_cast<int64_t>(tile) * N * kTile;
@@ -676,12 +691,12 @@ void scan_rows_kernel(Params p) {
     };
     auto load_group = [&](Pre &pr, int j, int g, auto full) __attribute__((always_inline)) {
         if constexpr (decltype(full)::value) {
-            const uint32_t so = static_cast<uint32_t>(j * kRowTB + 4 * g) * row_bytes;
+            const uint32_t so = soff_full(j, g);
             pr.d[g] = Io<T>::load(rd, voff_full, so);
             pr.x[g] = Io<T>::load(rx, voff_full, so);
             if (has_z) pr.z[g] = Io<T>::load(rz, voff_full, so);
         } else {
-            const uint32_t vo = vcol + static_cast<uint32_t>(lane_step(j, g)) * row_bytes;
+            const uint32_t vo = row_off(lane_step(j, g));
             pr.d[g] = Io<T>::load(rd, vo, 0);
             pr.x[g] = Io<T>::load(rx, vo, 0);
             if (has_z) pr.z[g] = Io<T>::load(rz, vo, 0);
@@ -692,7 +707,11 @@ void scan_rows_kernel(Params p) {
         typename W4::raw b, c;
     };
     auto load_bc = [&](BCRaw &v, int j) __attribute__((always_inline)) {
-        const uint32_t off = (static_cast<uint32_t>(j) * kRowTB * N + 4 * lane) * es;
+        // backwards, step j * 16 + lane / 4 is row steps - 1 - that step of the
+        // segment; past the end the offset wraps beyond the descriptor: zeros
+        const uint32_t off = REV ? static_cast<uint32_t>(((steps - 1 - (j * kRowTB + lane / 4)) * N + (lane % 4) * 4) *
+                                                         static_cast<int>(es))
+                                 : (static_cast<uint32_t>(j) * kRowTB * N + 4 * lane) * es;
         v.b = W4::load(rB, off);
         v.c = W4::load(rC, off);
     };
@@ -760,9 +779,9 @@ void scan_rows_kernel(Params p) {
             float out = fmaf(Dd, xv, row_reduce_scatter(part));
             if (has_z) out *= silu(widen(zw));
             if constexpr (F) {
-                Io<T>::store(out, ry, active ? voff_full : kOffNone, static_cast<uint32_t>(j * kRowTB + 4 * g) * row_bytes);
+                Io<T>::store(out, ry, active ? voff_full : kOffNone, soff_full(j, g));
             } else {
-                const uint32_t vo = (active && sl < steps) ? vcol + static_cast<uint32_t>(sl) * row_bytes : kOffNone;
+                const uint32_t vo = (active && sl < steps) ? row_off(sl) : kOffNone;
                 Io<T>::store(out, ry, vo, 0);
             }
             load_group(pr, j + 2, g, std::integral_constant<bool, F>{});
@@ -853,7 +872,7 @@ template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a
     return hipGetLastError();
 }
 
-template <typename T, int FL, bool CK> hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
+template <typename T, int FL, bool CK, bool REV = false> hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
     const Layout l = make_layout(a.batch, a.seqlen, a.dim, 16, sizeof(T));
     char *ws = static_cast<char *>(a.workspace);
     Params p;
@@ -879,7 +898,7 @@ template <typename T, int FL, bool CK> hipError_t launch_rows(const ScanArgs &a,
     const int per_cu = l.n_tiles >= kRowsTilesPerCuForTwo * cus ? 2 * SSM_ROWS_WG_PER_CU : SSM_ROWS_WG_PER_CU;
     const int64_t workers = static_cast<int64_t>(cus) * per_cu;
     const unsigned grid = static_cast<unsigned>(jobs < workers ? jobs : workers);
-    hipLaunchKernelGGL((scan_rows_kernel<T, FL, CK>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((scan_rows_kernel<T, FL, CK, REV>), dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -888,6 +907,8 @@ template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     // with both flags fixed at compile time
     if (rows_path(a.dstate)) {
         if (a.ckpt) return (a.softplus && a.z) ? launch_rows<T, 1, true>(a, s) : launch_rows<T, 0, true>(a, s);
+        if (a.reverse)
+            return (a.softplus && a.z) ? launch_rows<T, 1, false, true>(a, s) : launch_rows<T, 0, false, true>(a, s);
         return (a.softplus && a.z) ? launch_rows<T, 1, false>(a, s) : launch_rows<T, 0, false>(a, s);
     }
     switch (a.dstate) {

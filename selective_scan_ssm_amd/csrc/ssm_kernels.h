@@ -22,6 +22,10 @@ struct ScanArgs {
     // other widths): the state entering every 16-step block,
     // (batch, ceil(seqlen / 16), dim, dstate) fp32, for the backward's sweep
     float *ckpt = nullptr;
+    // 1: visit the sequence from its last step to its first (d_state 16 only;
+    // not with ckpt): y[t] is the readout after the steps t .. seqlen - 1 in
+    // that order, and last_state the state after step 0
+    int reverse = 0;
 };
 
 struct StepArgs {

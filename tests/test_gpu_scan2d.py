@@ -21,16 +21,30 @@ def need_gpu():
     _lib.load()
 
 
-def check_2d(inp, H, W, direction, tag=""):
+def check_2d(inp, H, W, direction, tag="", d_index=None):
+    """All chains against the oracle, or (d_index given) every output checked
+    finite and the channels d_index of every batch row against the oracle."""
     from selective_scan_ssm_amd import ops
+    G.say(f"[2d] {tag} B={inp['batch']} H={H} W={W} D={inp['d_inner']} dir={direction} io={inp['io']} "
+          f"N={inp['d_state']} sampled={d_index is not None}")
     t = G.device_inputs(inp)
     y, last = ops.scan_fwd_2d(t["x"], t["delta"], t["A"], t["B"], t["C"], H, W, direction, D=t["D"],
                               z=t["z"], delta_bias=t["delta_bias"], h0=t["h0"], return_last_state=True)
     torch.cuda.synchronize()
+    y, last = G.from_torch(y), G.from_torch(last)
     d = G.decoded(inp)
+    if d_index is not None:
+        assert np.all(np.isfinite(y)) and np.all(np.isfinite(last))
+        di = np.asarray(d_index)
+        y, last = y[:, :, di], last[:, di]
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :, di])
+        d = dict(d, x=sl(d["x"]), delta=sl(d["delta"]), z=sl(d["z"]), A=d["A"][di],
+                 D=None if d["D"] is None else d["D"][di],
+                 delta_bias=None if d["delta_bias"] is None else d["delta_bias"][di],
+                 h0=None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, di]))
     yo, lo = oracle.scan_2d(d["x"], d["delta"], d["A"], d["B"], d["C"], H, W, direction, D=d["D"],
                             z=d["z"], delta_bias=d["delta_bias"], h0=d["h0"], threads=G.ORACLE_THREADS)
-    ey, el = G.err(G.from_torch(y), yo), G.err(G.from_torch(last), lo)
+    ey, el = G.err(y, yo), G.err(last, lo)
     tol = G.TOL[inp["io"]]
     G.say(f"[2d] {tag} H={H} W={W} dir={direction} io={inp['io']} N={inp['d_state']} err_y={ey:.2e} err_last={el:.2e}")
     assert ey <= tol and el <= tol
@@ -63,3 +77,20 @@ def test_2d_vmamba_stage1_shape():
     inp = gen.make_inputs(2, 56 * 56, 192, 16, io=gen.BF16, seed=630)
     for direction in (1, 2):
         check_2d(inp, 56, 56, direction, tag="vmamba-56x56")
+
+
+@pytest.mark.parametrize("io", [gen.BF16, gen.F32])
+def test_2d_reverse_segments_ragged(io):
+    # the reversed 1-D scan at d_state 16 runs the row kernel backwards in
+    # place: 2007 steps make three segments (672, 672, 663 steps, the last one
+    # ending in a 7-step block) and 300 channels end in a partial channel tile
+    inp = gen.make_inputs(2, 2007, 300, 16, io=io, h0_kind="normal", seed=640)
+    check_2d(inp, 1, 2007, 1, tag="1d-reverse-segments")
+
+
+def test_2d_reverse_mamba2p8b_layer_sampled():
+    # the 2.8b layer (4 x 8192 x 5120, bf16) reversed, in the launch
+    # configuration the benchmark times: every output finite, channels of the
+    # first, a middle and the last channel tile against the oracle
+    inp = gen.workload_inputs(3)
+    check_2d(inp, 1, inp["seqlen"], 1, tag="w3-reverse", d_index=np.r_[0:16, 2500:2516, 5104:5120])
