@@ -95,6 +95,26 @@ KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "
                  "dtproj": "dt_proj_kernel"}
 
 
+def grid_of(spec, seqlen):
+    """(height, width) of the patch grid the 2-D leg scans: 'HxW', or one row."""
+    if spec is None:
+        return 1, seqlen
+    gh, gw = (int(v) for v in spec.lower().split("x"))
+    if gh * gw != seqlen:
+        raise SystemExit(f"--grid {spec}: {gh} x {gw} != the workload's {seqlen} steps")
+    return gh, gw
+
+
+def order_visit(direction, spec, seqlen):
+    """How the row kernel visits a 2-D order in place at d_state 16 (orders 2
+    and 3 of a one-row or one-column grid are orders 0 and 1)."""
+    gh, gw = grid_of(spec, seqlen)
+    d = direction - 2 if direction >= 2 and (gh == 1 or gw == 1) else direction
+    return ["the sequence as stored", "reading each segment from its end",
+            "computing each step's patch row, column-major",
+            "computing each step's patch row, column-major from the end"][d]
+
+
 def kind_of(w):
     if w.kind == "scan":
         return "rows" if w.d_state == 16 else "scan"
@@ -322,14 +342,15 @@ def bench_workload(args, dev):
         if args.direction is not None:
             if kind == "sm1":
                 raise SystemExit("--direction runs ssm_scan_fwd_2d: use workload 2 or 3")
-            need = lib.ssm_scan_2d_workspace_bytes(w.batch, 1, w.seqlen, w.d_inner, N, 1, io_code)
+            gh, gw = grid_of(args.grid, w.seqlen)
+            need = lib.ssm_scan_2d_workspace_bytes(w.batch, gh, gw, w.d_inner, N, 1, io_code)
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
         def step():
             s = sets[cur[0] % len(sets)]
             cur[0] += 1
-            if args.direction is not None:      # the 1-D scan in the given order (height 1)
-                ops.scan_fwd_2d(s["x"], s["delta"], s["A"], s["B"], s["C"], 1, w.seqlen, args.direction,
+            if args.direction is not None:      # the sequence as a patch grid (default: one row)
+                ops.scan_fwd_2d(s["x"], s["delta"], s["A"], s["B"], s["C"], gh, gw, args.direction,
                                 D=s["D"], z=s["z"], delta_bias=s["delta_bias"], h0=s["h0"],
                                 out=s["y"], workspace=ws)
                 return
@@ -364,9 +385,7 @@ def bench_workload(args, dev):
     traffic = traffic_from_profile(kind, w.name) if args.direction is None else None
     kname = {"scan": "ssm_scan_fwd (scan_fwd_kernel)",
              "rows": "ssm_scan_fwd (scan_rows_kernel)" if args.direction is None else
-                     "ssm_scan_fwd_2d (scan_rows_kernel reading each segment from its end)"
-                     if args.direction == 1 else
-                     "ssm_scan_fwd_2d (gather + scan_rows_kernel + scatter, timed as one call)",
+                     "ssm_scan_fwd_2d (scan_rows_kernel, " + order_visit(args.direction, args.grid, w.seqlen) + ")",
              "sm1": "sm1_scan_fwd (sm1_scan_kernel)",
              "decode": "ssm_state_update (state_update_rows_kernel)"}[kind]
     if kind in ("scan", "rows") and w.d_state > 1:
@@ -392,7 +411,8 @@ def bench_workload(args, dev):
         log("[bench] cpu baseline (oracle on a sample)")
         cpu = cpu_baseline(inp0, w, args.cpu_seconds)
 
-    cfg = {"workload": w.name + ("" if args.direction is None else f"-order{args.direction}"),
+    cfg = {"workload": w.name + ("" if args.direction is None else
+                                 f"-order{args.direction}-grid{'x'.join(map(str, grid_of(args.grid, w.seqlen)))}"),
            "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.d_inner,
            "d_state": w.d_state, "io": io, "state": "fp32", "seed": args.workload}
     if kind == "decode":
@@ -1000,6 +1020,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (the gradient) on a scan workload instead of the forward")
+    ap.add_argument("--grid", default=None, metavar="HxW",
+                    help="with --direction: the sequence as an H x W patch grid (default 1 x seqlen)")
     ap.add_argument("--direction", type=int, default=None,
                     help="scan order through ssm_scan_fwd_2d (height 1): 0 forward, 1 reversed")
     ap.add_argument("--conv", action="store_true",

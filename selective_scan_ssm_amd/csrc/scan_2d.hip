@@ -4,9 +4,11 @@
 // column-major (the patch grid transposed), its reverse -- and y comes back
 // at each patch's own position.
 //
-// The reversed row-major order at d_state 16 is read backwards in place by
-// the forward kernel.  Every other case is a permutation of the sequence
-// axis, so the path is:
+// Row-major order is the forward scan as stored.  At d_state 16 the row
+// kernel visits the other three in place: the reversed order read backwards,
+// the column-major orders with each step's patch row computed in the kernel
+// (sequences below 2^23 steps whose batch row spans under 2 GiB).  The
+// remaining cases (other d_state, larger grids) permute the sequence axis:
 //   gather x, delta, z, B, C into scan order (permute_rows_kernel),
 //   the forward scan of this library on the gathered tensors,
 //   scatter y back to the patches' positions (the same kernel, inverse map).
@@ -97,11 +99,19 @@ hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int 
     if (a.batch == 0 || a.dim == 0) return hipSuccess;
     const Scan2dLayout l = scan2d_layout(a, a.z != nullptr);
     char *ws = static_cast<char *>(a.workspace);
-    if (direction == 1 && a.dstate == 16) {
-        // the reversed row-major order is the sequence read backwards: the
-        // d_state-16 kernel walks it in place, with no gathered copy
+    // a grid of one row or one column is visited column-major in row-major order
+    if (direction >= 2 && (height == 1 || width == 1)) direction -= 2;
+    const size_t esz = a.bf16 ? 2 : 4;
+    const bool in_place = direction == 0 ||
+                          (a.dstate == 16 && (direction == 1 || (a.seqlen < (int64_t(1) << 23) &&
+                                                                 size_t(a.seqlen) * a.dim * esz < (size_t(1) << 31))));
+    if (in_place) {
+        // row-major: the sequence as stored, or read backwards; column-major at
+        // d_state 16: the kernel computes each step's patch row itself
         ScanArgs f = a;
-        f.reverse = 1;
+        f.reverse = direction & 1;
+        f.column_major = direction >= 2;
+        f.grid_h = height; f.grid_w = width;
         f.workspace = ws + l.fwd_off; f.workspace_bytes = l.fwd_bytes;
         return launch_scan_fwd(f, s);
     }

@@ -83,6 +83,8 @@ struct Params {
     float *ckpt;         // row kernel, optional: state entering each 16-step block
     int64_t seqlen, dim, nblk;
     int n_dt, n_tiles, seg_len, n_segs, softplus;
+    int grid_h, grid_w;  // row kernel, column-major visits: the patch grid
+    float inv_h;         // 1 / grid_h
 };
 
 struct Layout {
@@ -570,8 +572,11 @@ template <> struct Wide4<float> {
 // then be absent); a separate instantiation, so the forward proper carries
 // none of it.  REV = true: the sequence is visited from its last step to its
 // first (step k of the scan reads and writes row seqlen - 1 - k), the 2-D
-// scan's reversed row-major order without a gathered copy.
-template <typename T, int FL, bool CK = false, bool REV = false>
+// scan's reversed row-major order without a gathered copy.  COL = true: the
+// rows are patches of a grid_h x grid_w grid visited column by column (step
+// q reads and writes row (q mod grid_h) grid_w + q div grid_h, q counted
+// from the end when REV), the 2-D scan's column-major orders in place.
+template <typename T, int FL, bool CK = false, bool REV = false, bool COL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void scan_rows_kernel(Params p) {
     using M = typename MathFor<T>::type;
@@ -616,7 +621,8 @@ void scan_rows_kernel(Params p) {
 
     // descriptors start at the segment's lowest row: its first step, or its
     // last one when the sequence is visited backwards
-    const int64_t row0 = REV ? b * seqlen + (seqlen - t_end) : b * seqlen + t_begin;
+    // (column-major visits: the batch row's first row, every offset below 2^31)
+    const int64_t row0 = COL ? b * seqlen : (REV ? b * seqlen + (seqlen - t_end) : b * seqlen + t_begin);
     const int64_t e0 = (row0 * dim + d0) * static_cast<int64_t>(es);
     const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + e0);
     const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + e0);
@@ -625,7 +631,7 @@ void scan_rows_kernel(Params p) {
     // to an empty descriptor and are dropped
     const rsrc_t ry = (!CK || p.y) ? make_rsrc(static_cast<char *>(p.y) + e0) : make_rsrc(p.x, 0u);
     // B / C of the segment; rows past its end read 0
-    const uint32_t bc_bytes = static_cast<uint32_t>(steps) * N * es;
+    const uint32_t bc_bytes = static_cast<uint32_t>(COL ? seqlen : steps) * N * es;
     const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * static_cast<int64_t>(es), bc_bytes);
     const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * static_cast<int64_t>(es), bc_bytes);
     const uint32_t row_bytes = static_cast<uint32_t>(dim * static_cast<int64_t>(es));
@@ -641,6 +647,18 @@ void scan_rows_kernel(Params p) {
     // the lane offset of segment step k
     auto row_off = [&](int k) __attribute__((always_inline)) {
         return vcol + static_cast<uint32_t>(REV ? steps - 1 - k : k) * row_bytes;
+    };
+    // column-major visits: the row (inside the batch row) of segment step k.
+    // q < 2^23, so q and the fp32 quotient estimate are within one of the
+    // true quotient, and one correction each way makes it exact.
+    auto col_row = [&](int k) __attribute__((always_inline)) {
+        const int kk = static_cast<int>(t_begin) + k;
+        const int q = REV ? static_cast<int>(seqlen) - 1 - kk : kk;
+        int qd = static_cast<int>(static_cast<float>(q) * p.inv_h);
+        int qm = q - qd * p.grid_h;
+        if (qm < 0) { qm += p.grid_h; --qd; }
+        if (qm >= p.grid_h) { qm -= p.grid_h; ++qd; }
+        return static_cast<uint32_t>(qm * p.grid_w + qd);
     };
     // carried states of this tile: one 64-bit word per state, the value in
     // the low half and (segment + 1) of its writer in the high half
@@ -682,6 +700,7 @@ void scan_rows_kernel(Params p) {
     // of each group
     struct Pre {                                     // raw words, zero-extended at the load
         uint32_t d[NG], x[NG], z[NG];
+        uint32_t off[NG];                            // column-major visits: the lane's row offset
     };
     // the segment step this lane touches in group g of block j (clamped when
     // the block is not whole)
@@ -690,7 +709,13 @@ void scan_rows_kernel(Params p) {
         return s < steps ? s : steps - 1;
     };
     auto load_group = [&](Pre &pr, int j, int g, auto full) __attribute__((always_inline)) {
-        if constexpr (decltype(full)::value) {
+        if constexpr (COL) {                         // kept for the store of this step
+            const uint32_t vo = vcol + col_row(lane_step(j, g)) * row_bytes;
+            pr.off[g] = vo;
+            pr.d[g] = Io<T>::load(rd, vo, 0);
+            pr.x[g] = Io<T>::load(rx, vo, 0);
+            if (has_z) pr.z[g] = Io<T>::load(rz, vo, 0);
+        } else if constexpr (decltype(full)::value) {
             const uint32_t so = soff_full(j, g);
             pr.d[g] = Io<T>::load(rd, voff_full, so);
             pr.x[g] = Io<T>::load(rx, voff_full, so);
@@ -709,9 +734,15 @@ void scan_rows_kernel(Params p) {
     auto load_bc = [&](BCRaw &v, int j) __attribute__((always_inline)) {
         // backwards, step j * 16 + lane / 4 is row steps - 1 - that step of the
         // segment; past the end the offset wraps beyond the descriptor: zeros
-        const uint32_t off = REV ? static_cast<uint32_t>(((steps - 1 - (j * kRowTB + lane / 4)) * N + (lane % 4) * 4) *
-                                                         static_cast<int>(es))
-                                 : (static_cast<uint32_t>(j) * kRowTB * N + 4 * lane) * es;
+        uint32_t off;
+        if constexpr (COL) {
+            const int k = j * kRowTB + lane / 4;
+            off = k < steps ? (col_row(k) * N + (lane % 4) * 4) * es : kOffNone;
+        } else {
+            off = REV ? static_cast<uint32_t>(((steps - 1 - (j * kRowTB + lane / 4)) * N + (lane % 4) * 4) *
+                                              static_cast<int>(es))
+                      : (static_cast<uint32_t>(j) * kRowTB * N + 4 * lane) * es;
+        }
         v.b = W4::load(rB, off);
         v.c = W4::load(rC, off);
     };
@@ -778,7 +809,9 @@ void scan_rows_kernel(Params p) {
                                                  dts[src_row[k]], dtxs[src_row[k]], bcs[k], bcs[k]);
             float out = fmaf(Dd, xv, row_reduce_scatter(part));
             if (has_z) out *= silu(widen(zw));
-            if constexpr (F) {
+            if constexpr (COL) {
+                Io<T>::store(out, ry, (active && (F || sl < steps)) ? pr.off[g] : kOffNone, 0);
+            } else if constexpr (F) {
                 Io<T>::store(out, ry, active ? voff_full : kOffNone, soff_full(j, g));
             } else {
                 const uint32_t vo = (active && sl < steps) ? row_off(sl) : kOffNone;
@@ -872,7 +905,8 @@ template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a
     return hipGetLastError();
 }
 
-template <typename T, int FL, bool CK, bool REV = false> hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
+template <typename T, int FL, bool CK, bool REV = false, bool COL = false>
+hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
     const Layout l = make_layout(a.batch, a.seqlen, a.dim, 16, sizeof(T));
     char *ws = static_cast<char *>(a.workspace);
     Params p;
@@ -886,6 +920,9 @@ template <typename T, int FL, bool CK, bool REV = false> hipError_t launch_rows(
     p.softplus = a.softplus;
     p.ckpt = a.ckpt;
     p.nblk = (a.seqlen + kRowTB - 1) / kRowTB;
+    p.grid_h = static_cast<int>(a.grid_h);
+    p.grid_w = static_cast<int>(a.grid_w);
+    p.inv_h = a.grid_h > 0 ? 1.0f / static_cast<float>(a.grid_h) : 0.0f;
     // ticket, error word and the tagged carried states (tag 0 = not written)
     const int64_t nclear = static_cast<int64_t>(l.total / sizeof(uint32_t));
     hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
@@ -898,7 +935,7 @@ template <typename T, int FL, bool CK, bool REV = false> hipError_t launch_rows(
     const int per_cu = l.n_tiles >= kRowsTilesPerCuForTwo * cus ? 2 * SSM_ROWS_WG_PER_CU : SSM_ROWS_WG_PER_CU;
     const int64_t workers = static_cast<int64_t>(cus) * per_cu;
     const unsigned grid = static_cast<unsigned>(jobs < workers ? jobs : workers);
-    hipLaunchKernelGGL((scan_rows_kernel<T, FL, CK, REV>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((scan_rows_kernel<T, FL, CK, REV, COL>), dim3(grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -907,8 +944,13 @@ template <typename T> hipError_t dispatch_n(const ScanArgs &a, hipStream_t s) {
     // with both flags fixed at compile time
     if (rows_path(a.dstate)) {
         if (a.ckpt) return (a.softplus && a.z) ? launch_rows<T, 1, true>(a, s) : launch_rows<T, 0, true>(a, s);
+        const bool fl = a.softplus && a.z;
+        if (a.column_major && a.reverse)
+            return fl ? launch_rows<T, 1, false, true, true>(a, s) : launch_rows<T, 0, false, true, true>(a, s);
+        if (a.column_major)
+            return fl ? launch_rows<T, 1, false, false, true>(a, s) : launch_rows<T, 0, false, false, true>(a, s);
         if (a.reverse)
-            return (a.softplus && a.z) ? launch_rows<T, 1, false, true>(a, s) : launch_rows<T, 0, false, true>(a, s);
+            return fl ? launch_rows<T, 1, false, true>(a, s) : launch_rows<T, 0, false, true>(a, s);
         return (a.softplus && a.z) ? launch_rows<T, 1, false>(a, s) : launch_rows<T, 0, false>(a, s);
     }
     switch (a.dstate) {

@@ -26,6 +26,12 @@ struct ScanArgs {
     // not with ckpt): y[t] is the readout after the steps t .. seqlen - 1 in
     // that order, and last_state the state after step 0
     int reverse = 0;
+    // 1: the rows are patches of a grid_h x grid_w grid (seqlen = grid_h *
+    // grid_w) visited column by column, step q at row (q mod grid_h) grid_w +
+    // q div grid_h (q counted from the end with reverse); d_state 16 only, not
+    // with ckpt, seqlen < 2^23 and seqlen * dim * io bytes < 2^31
+    int column_major = 0;
+    int64_t grid_h = 0, grid_w = 0;
 };
 
 struct StepArgs {

@@ -94,3 +94,20 @@ def test_2d_reverse_mamba2p8b_layer_sampled():
     # first, a middle and the last channel tile against the oracle
     inp = gen.workload_inputs(3)
     check_2d(inp, 1, inp["seqlen"], 1, tag="w3-reverse", d_index=np.r_[0:16, 2500:2516, 5104:5120])
+
+
+@pytest.mark.parametrize("direction,io", [(2, gen.BF16), (3, gen.BF16), (2, gen.F32), (3, gen.F32)])
+def test_2d_column_major_segments_ragged(direction, io):
+    # the column-major orders at d_state 16 run the row kernel in place, each
+    # step's patch row computed in the kernel: a 45 x 47 grid (2115 steps,
+    # four segments, the last ending in a 3-step block), 300 channels
+    inp = gen.make_inputs(2, 45 * 47, 300, 16, io=io, h0_kind="normal", seed=650 + direction)
+    check_2d(inp, 45, 47, direction, tag="col-segments")
+
+
+@pytest.mark.parametrize("direction", [2, 3])
+def test_2d_column_major_mamba2p8b_layer_sampled(direction):
+    # the 2.8b layer's 8192 steps as a 64 x 128 grid, column-major, at full
+    # size: every output finite, three channel tiles against the oracle
+    inp = gen.workload_inputs(3)
+    check_2d(inp, 64, 128, direction, tag="w3-col", d_index=np.r_[0:16, 2500:2516, 5104:5120])
