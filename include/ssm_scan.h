@@ -219,9 +219,12 @@ int ssm_scan_bwd_ckpt(const void *x, const void *delta, const float *delta_bias,
  * directions' outputs align for the block's sum; last_state is the state
  * after the last visited patch.  Same tensors and conventions as
  * ssm_scan_fwd with seqlen = height * width (height = 1 gives the plain
- * reversed 1-D scan with direction 1).  The orders are realised by gathering
- * the inputs into scan order and scattering y back, so the workspace
- * (ssm_scan_2d_workspace_bytes) holds a copy of x, delta, z, B, C and y.
+ * reversed 1-D scan with direction 1).  Direction 0 is the forward scan as
+ * stored.  At d_state 16 the scan visits directions 1-3 in place (below 2^23
+ * steps with a batch row under 2 GiB for directions 2 and 3); every other
+ * case gathers the inputs into scan order and scatters y back.  The workspace
+ * size (ssm_scan_2d_workspace_bytes) covers the gathered copy of x, delta, z,
+ * B, C and y whichever path a call takes, so one size serves every direction.
  *   direction outside [0, 3] or negative height / width: SSM_ERR_SHAPE.
  */
 int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
