@@ -21,7 +21,7 @@ def need_gpu():
     _lib.load()
 
 
-def check_2d(inp, H, W, direction, tag="", d_index=None):
+def check_2d(inp, H, W, direction, tag="", d_index=None, softplus=True):
     """All chains against the oracle, or (d_index given) every output checked
     finite and the channels d_index of every batch row against the oracle."""
     from selective_scan_ssm_amd import ops
@@ -29,7 +29,8 @@ def check_2d(inp, H, W, direction, tag="", d_index=None):
           f"N={inp['d_state']} sampled={d_index is not None}")
     t = G.device_inputs(inp)
     y, last = ops.scan_fwd_2d(t["x"], t["delta"], t["A"], t["B"], t["C"], H, W, direction, D=t["D"],
-                              z=t["z"], delta_bias=t["delta_bias"], h0=t["h0"], return_last_state=True)
+                              z=t["z"], delta_bias=t["delta_bias"], delta_softplus=softplus, h0=t["h0"],
+                              return_last_state=True)
     torch.cuda.synchronize()
     y, last = G.from_torch(y), G.from_torch(last)
     d = G.decoded(inp)
@@ -43,7 +44,8 @@ def check_2d(inp, H, W, direction, tag="", d_index=None):
                  delta_bias=None if d["delta_bias"] is None else d["delta_bias"][di],
                  h0=None if d["h0"] is None else np.ascontiguousarray(d["h0"][:, di]))
     yo, lo = oracle.scan_2d(d["x"], d["delta"], d["A"], d["B"], d["C"], H, W, direction, D=d["D"],
-                            z=d["z"], delta_bias=d["delta_bias"], h0=d["h0"], threads=G.ORACLE_THREADS)
+                            z=d["z"], delta_bias=d["delta_bias"], delta_softplus=softplus, h0=d["h0"],
+                            threads=G.ORACLE_THREADS)
     ey, el = G.err(y, yo), G.err(last, lo)
     tol = G.TOL[inp["io"]]
     G.say(f"[2d] {tag} H={H} W={W} dir={direction} io={inp['io']} N={inp['d_state']} err_y={ey:.2e} err_last={el:.2e}")
@@ -111,3 +113,19 @@ def test_2d_column_major_mamba2p8b_layer_sampled(direction):
     # size: every output finite, three channel tiles against the oracle
     inp = gen.workload_inputs(3)
     check_2d(inp, 64, 128, direction, tag="w3-col", d_index=np.r_[0:16, 2500:2516, 5104:5120])
+
+
+@pytest.mark.parametrize("direction", [1, 2, 3])
+@pytest.mark.parametrize("variant", ["no_gate", "softplus_off"])
+def test_2d_in_place_without_gate_or_softplus(direction, variant):
+    # the in-place orders' second instantiation (no gate, or the step used as
+    # given): 2 images of 19 x 23 patches, 130 channels, d_state 16, bf16
+    io = gen.BF16
+    if variant == "no_gate":
+        inp = gen.make_inputs(2, 19 * 23, 130, 16, io=io, h0_kind="normal", seed=660 + direction, with_z=False)
+        check_2d(inp, 19, 23, direction, tag="no-gate")
+    else:
+        # the raw step must be >= 0: |N(0,1)| * 0.3, no bias
+        inp = gen.make_inputs(2, 19 * 23, 130, 16, io=io, h0_kind="normal", seed=670 + direction, with_bias=False)
+        inp["delta"] = gen.bf16_from_f32(np.abs(gen.f32_from_bf16(inp["delta"])) * np.float32(0.3))
+        check_2d(inp, 19, 23, direction, tag="softplus-off", softplus=False)
