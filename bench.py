@@ -343,7 +343,7 @@ def bench_workload(args, dev):
             if kind == "sm1":
                 raise SystemExit("--direction runs ssm_scan_fwd_2d: use workload 2 or 3")
             gh, gw = grid_of(args.grid, w.seqlen)
-            need = lib.ssm_scan_2d_workspace_bytes(w.batch, gh, gw, w.d_inner, N, 1, io_code)
+            need = lib.ssm_scan_2d_workspace_bytes(w.batch, gh, gw, w.d_inner, N, args.direction, 1, io_code)
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
         def step():
@@ -864,7 +864,7 @@ def bench_micro(args, dev):
     import numpy as np
     import torch
     from selective_scan_ssm_amd import _lib
-    lib = _lib.load()
+    lib = _lib.load_bench()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -887,7 +887,7 @@ def bench_micro(args, dev):
     def copy():
         rc = lib.ssm_mb_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)
         if rc:
-            raise RuntimeError(_lib.status_string(rc))
+            raise RuntimeError(f"ssm_mb_copy failed ({rc})")
 
     ms = timed(copy, 10)
     copy_gbs = 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
@@ -903,7 +903,7 @@ def bench_micro(args, dev):
             def run(op=op, blocks=blocks):
                 rc = lib.ssm_mb_valu(op, out.data_ptr(), blocks, iters, sh)
                 if rc:
-                    raise RuntimeError(_lib.status_string(rc))
+                    raise RuntimeError(f"ssm_mb_valu failed ({rc})")
             ms = timed(run, 10)
             rates[f"{name}_{wps}w"] = blocks * 256 * iters * 8 / (float(np.median(ms)) * 1e-3) / 1e12
     fma = rates["fma_8w"]

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_D_STATE 16
 #define SSM_MAX_CONV_WIDTH 4
 
@@ -73,7 +73,8 @@ typedef enum {
     SSM_ERR_ALIGN = -4,     /* a pointer is not aligned to its element size    */
     SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required         */
     SSM_ERR_HIP = -6,       /* the HIP runtime reported a launch error          */
-    SSM_ERR_ALIAS = -7      /* an output overlaps an input                      */
+    SSM_ERR_ALIAS = -7,     /* an output overlaps an input                      */
+    SSM_ERR_WAIT = -8       /* a segment's bounded wait gave up (ssm_scan_status) */
 } ssm_status_t;
 
 /*
@@ -223,8 +224,9 @@ int ssm_scan_bwd_ckpt(const void *x, const void *delta, const float *delta_bias,
  * stored.  At d_state 16 the scan visits directions 1-3 in place (below 2^23
  * steps with a batch row under 2 GiB for directions 2 and 3); every other
  * case gathers the inputs into scan order and scatters y back.  The workspace
- * size (ssm_scan_2d_workspace_bytes) covers the gathered copy of x, delta, z,
- * B, C and y whichever path a call takes, so one size serves every direction.
+ * size (ssm_scan_2d_workspace_bytes, for the same direction) is the forward
+ * scan's own workspace for the orders visited in place, and adds the gathered
+ * copies of x, delta, z, B, C and y for the others.
  *   direction outside [0, 3] or negative height / width: SSM_ERR_SHAPE.
  */
 int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
@@ -233,10 +235,11 @@ int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, i
                     int64_t width, int64_t d_inner, int64_t d_state, int direction, int io_dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes of ssm_scan_fwd_2d (has_z: whether z is given); (size_t)-1
- * for invalid arguments. */
+/* Workspace bytes of ssm_scan_fwd_2d in `direction` (has_z: whether z is
+ * given); (size_t)-1 for invalid arguments (direction outside [0, 3]
+ * included). */
 size_t ssm_scan_2d_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t d_inner,
-                                   int64_t d_state, int has_z, int io_dtype);
+                                   int64_t d_state, int direction, int has_z, int io_dtype);
 
 /*
  * ssm_causal_conv1d_fwd -- the causal depthwise convolution (+ SiLU) that
@@ -323,21 +326,31 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
                  int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *stream);
 
 /*
- * Measurement helpers -- not part of any scan.  They give the benchmark the
- * measured ceilings its roofline fractions are read against.
+ * ssm_scan_status -- whether the last forward scan that used `workspace`
+ * completed its segment hand-offs.  No page covers this; it is the error
+ * path of this library's own time split.
  *
- * ssm_mb_copy: dst = src for `bytes` bytes with 16-byte non-temporal loads
- *   and stores (grid-stride).  bytes a multiple of 16, both pointers 16-byte
- *   aligned (SSM_ERR_ALIGN), buffers not overlapping (SSM_ERR_ALIAS).
- * ssm_mb_valu: `blocks` workgroups of 256 lanes, each lane running 8
- *   independent chains of `iters` steps of one fp32 operation -- op 0:
- *   fma(x, 0.999, 0.001); op 1: 2^-x (v_exp_f32); op 2: log2(x + 2)
- *   (v_log_f32); op 3: 1 / (x + 1) (v_rcp_f32) -- and writing one sum per lane
- *   to out (blocks * 256 floats).  op outside [0, 3] or negative sizes:
- *   SSM_ERR_SHAPE.
+ * The d_state-16 scan (and the general scan on many channel tiles) cuts long
+ * sequences into segments; each segment waits for the state its predecessor
+ * hands on through the workspace.  That wait is bounded: if it ever gives up,
+ * the kernel sets an error word in the workspace and poisons the carried
+ * state with NaN, so every output that depends on it (y from that segment on,
+ * last_state) is NaN rather than a plausible wrong value.  This call
+ * synchronises `stream` (waits for the work enqueued on it), reads that word
+ * and returns
+ *   SSM_OK        the waits of the last call on this workspace all completed
+ *                 (also when that call needed no workspace wait at all);
+ *   SSM_ERR_WAIT  a wait gave up: that call's y and last_state are invalid;
+ *   SSM_ERR_NULL / SSM_ERR_WORKSPACE  workspace NULL or under 256 bytes;
+ *   SSM_ERR_HIP   the synchronisation or the copy failed (for example a
+ *                 fault of an earlier kernel on the stream).
+ * `workspace` is the workspace of the last ssm_scan_fwd, ssm_scan_fwd_ckpt or
+ * ssm_scan_fwd_2d call on `stream` (or of an sm1_scan_fwd call whose
+ * sm1_scan_workspace_bytes was nonzero), not yet reused.  The error word is
+ * cleared at the start of every such call.  Not capturable in a HIP graph
+ * (it synchronises); call it outside a capture.
  */
-int ssm_mb_copy(const void *src, void *dst, size_t bytes, void *stream);
-int ssm_mb_valu(int op, float *out, int64_t blocks, int64_t iters, void *stream);
+int ssm_scan_status(const void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ssm_status_string(int status);

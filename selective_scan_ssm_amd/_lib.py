@@ -19,9 +19,13 @@ SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",
            "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_scan_ckpt_bytes",
            "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt", "ssm_causal_conv1d_fwd",
-           "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd", "ssm_dt_proj", "ssm_mb_copy", "ssm_mb_valu",
+           "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd",
+           "ssm_dt_proj", "ssm_scan_status", "ssm_testing_scan_fwd_no_handoff",
            "ssm_status_string", "ssm_abi_version")
-ABI_VERSION = 1
+BENCH_LIB_PATH = os.path.join(PKG, "libssmbench.so")
+BENCH_EXPORTS = ("ssm_mb_copy", "ssm_mb_valu")
+ABI_VERSION = 2
+SSM_ERR_WAIT = -8
 
 _lib = None
 _lock = threading.Lock()
@@ -73,17 +77,19 @@ def _bind(lib):
     lib.ssm_scan_fwd_2d.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]
     lib.ssm_scan_fwd_2d.restype = _int
-    lib.ssm_scan_2d_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _int, _int]
+    lib.ssm_scan_2d_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _int, _int, _int]
     lib.ssm_scan_2d_workspace_bytes.restype = _sz
     lib.ssd_scan_fwd.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _i64, _i64, _i64, _i64, _i64, _int, _vp]
     lib.ssd_scan_fwd.restype = _int
     lib.ssm_dt_proj.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _vp]
     lib.ssm_dt_proj.restype = _int
-    lib.ssm_mb_copy.argtypes = [_vp, _vp, _sz, _vp]
-    lib.ssm_mb_copy.restype = _int
-    lib.ssm_mb_valu.argtypes = [_int, _vp, _i64, _i64, _vp]
-    lib.ssm_mb_valu.restype = _int
+    lib.ssm_scan_status.argtypes = [_vp, _sz, _vp]
+    lib.ssm_scan_status.restype = _int
+    lib.ssm_testing_scan_fwd_no_handoff.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _vp, _i64, _i64, _i64, _i64, _int, _vp, _sz,
+                                                    ctypes.c_uint32, _vp]
+    lib.ssm_testing_scan_fwd_no_handoff.restype = _int
     lib.ssm_status_string.argtypes = [_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []
@@ -119,6 +125,27 @@ def load(path: str = LIB_PATH):
             if len(rts) > 1:
                 raise RuntimeError(f"more than one HIP runtime mapped: {sorted(rts)}")
         _lib = lib
+        return lib
+
+
+_bench = None
+
+
+def load_bench(path: str = BENCH_LIB_PATH):
+    """Load libssmbench.so, the measurement helpers (include/ssm_bench.h)."""
+    global _bench
+    with _lock:
+        if _bench is not None:
+            return _bench
+        if not os.path.exists(path):
+            raise LibraryMissing(
+                f"{path} is not built; run `python -m selective_scan_ssm_amd.build` first")
+        lib = ctypes.CDLL(path)
+        lib.ssm_mb_copy.argtypes = [_vp, _vp, _sz, _vp]
+        lib.ssm_mb_copy.restype = _int
+        lib.ssm_mb_valu.argtypes = [_int, _vp, _i64, _i64, _vp]
+        lib.ssm_mb_valu.restype = _int
+        _bench = lib
         return lib
 
 

@@ -1,4 +1,7 @@
-"""Build libssmscan.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
+"""Build the gfx950 libraries in-tree with hipcc:
+
+    libssmscan.so  -- the scan kernels and their C ABI (include/ssm_scan.h)
+    libssmbench.so -- the benchmark's measurement helpers (include/ssm_bench.h)
 
     python -m selective_scan_ssm_amd.build
 
@@ -18,9 +21,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssmscan.so")
+BENCH_LIB = os.path.join(PKG, "libssmbench.so")
 ARCH = "gfx950"
 
-SOURCES = ["scan_fwd.hip", "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip", "ssd_scan.hip", "dt_proj.hip", "microbench.hip", "ssm_abi.cpp"]
+SOURCES = ["scan_fwd.hip", "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip",
+           "ssd_scan.hip", "dt_proj.hip", "ssm_abi.cpp"]
+BENCH_SOURCES = ["microbench.hip"]
 
 # Packed fp32 VALU forms are switched off (plain fp32 VALU only); code object
 # v5 is what the HIP runtime shipped with torch loads.
@@ -45,18 +51,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
+        print("built", lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], BENCH_LIB, verbose)
     return LIB
 
 

@@ -1,9 +1,14 @@
-// Measurement helpers behind the benchmark's roofline figures: the copy
-// bandwidth a 16-byte streaming kernel reaches on this HBM, and the issue
-// rate of the two fp32 VALU operations the scans are built from (fma, and
-// the v_exp_f32 behind every decay factor).  They are not part of any scan.
+// libssmbench.so (include/ssm_bench.h): measurement helpers behind the
+// benchmark's roofline figures -- the copy bandwidth a 16-byte streaming
+// kernel reaches on this HBM, and the issue rate of the fp32 VALU operations
+// the scans are built from (fma, and the v_exp_f32 behind every decay
+// factor).  They are not part of any scan and live in a library of their own,
+// apart from the scan library's C ABI.
+#include "ssm_bench.h"
+
+#include <cstdint>
+
 #include "ssm_device.h"
-#include "ssm_kernels.h"
 
 namespace ssm {
 namespace {
@@ -43,8 +48,6 @@ __global__ __launch_bounds__(256) void mb_valu_kernel(float *out, int64_t iters)
     out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
-}  // namespace
-
 hipError_t launch_mb_copy(const void *src, void *dst, uint64_t bytes, hipStream_t s) {
     const uint64_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
@@ -66,4 +69,30 @@ hipError_t launch_mb_valu(int op, float *out, int64_t blocks, int64_t iters, hip
     return hipGetLastError();
 }
 
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
+
+}  // namespace
 }  // namespace ssm
+
+extern "C" {
+
+int ssm_mb_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return SSM_MB_OK;
+    if (!src || !dst) return SSM_MB_ERR_ARG;
+    if (bytes % 16 != 0 || !ssm::aligned16(src) || !ssm::aligned16(dst)) return SSM_MB_ERR_ARG;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return SSM_MB_ERR_ARG;
+    return ssm::launch_mb_copy(src, dst, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_MB_OK
+                                                                                               : SSM_MB_ERR_HIP;
+}
+
+int ssm_mb_valu(int op, float *out, int64_t blocks, int64_t iters, void *stream) {
+    if (op < 0 || op > 3 || blocks < 0 || iters < 0 || blocks > (int64_t(1) << 31) - 1) return SSM_MB_ERR_ARG;
+    if (blocks == 0) return SSM_MB_OK;
+    if (!out || (reinterpret_cast<uintptr_t>(out) % 4) != 0) return SSM_MB_ERR_ARG;
+    return ssm::launch_mb_valu(op, out, blocks, iters, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_MB_OK
+               : SSM_MB_ERR_HIP;
+}
+
+}  // extern "C"

@@ -70,41 +70,55 @@ hipError_t permute(const void *src, void *dst, int64_t batch, int64_t H, int64_t
     return hipGetLastError();
 }
 
+// a grid of one row or one column is visited column-major in row-major order
+int effective_direction(int direction, int64_t height, int64_t width) {
+    return (direction >= 2 && (height == 1 || width == 1)) ? direction - 2 : direction;
+}
+// orders the scan kernels visit without a gathered copy
+bool visits_in_place(const ScanArgs &a, int direction) {
+    const size_t esz = a.bf16 ? 2 : 4;
+    return direction == 0 ||
+           (a.dstate == 16 && (direction == 1 || (a.seqlen < (int64_t(1) << 23) &&
+                                                  size_t(a.seqlen) * a.dim * esz < (size_t(1) << 31))));
+}
+
 struct Scan2dLayout {
-    size_t x_off, d_off, z_off, b_off, c_off, y_off, fwd_off, fwd_bytes, total;
+    size_t fwd_bytes, x_off, d_off, z_off, b_off, c_off, y_off, total;
 };
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
-Scan2dLayout scan2d_layout(const ScanArgs &a, bool has_z) {
+Scan2dLayout scan2d_layout(const ScanArgs &a, bool has_z, bool in_place) {
     const size_t es = a.bf16 ? 2 : 4;
     const size_t btd = size_t(a.batch) * a.seqlen * a.dim * es, btn = size_t(a.batch) * a.seqlen * a.dstate * es;
     Scan2dLayout l;
-    size_t o = 0;
+    l.fwd_bytes = scan_fwd_workspace(a);
+    size_t o = up256(l.fwd_bytes);
+    if (in_place) {
+        l.x_off = l.d_off = l.z_off = l.b_off = l.c_off = l.y_off = 0;
+        l.total = l.fwd_bytes;
+        return l;
+    }
     l.x_off = o; o = up256(o + btd);
     l.d_off = o; o = up256(o + btd);
     l.z_off = o; o = up256(o + (has_z ? btd : 0));
     l.b_off = o; o = up256(o + btn);
     l.c_off = o; o = up256(o + btn);
     l.y_off = o; o = up256(o + btd);
-    l.fwd_off = o;
-    l.fwd_bytes = scan_fwd_workspace(a);
-    l.total = o + l.fwd_bytes;
+    l.total = o;
     return l;
 }
 
 }  // namespace
 
-size_t scan_2d_workspace(const ScanArgs &a, bool has_z) { return scan2d_layout(a, has_z).total; }
+size_t scan_2d_workspace(const ScanArgs &a, bool has_z, int direction, int64_t height, int64_t width) {
+    return scan2d_layout(a, has_z, visits_in_place(a, effective_direction(direction, height, width))).total;
+}
 
 hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int direction, hipStream_t s) {
     if (a.batch == 0 || a.dim == 0) return hipSuccess;
-    const Scan2dLayout l = scan2d_layout(a, a.z != nullptr);
+    direction = effective_direction(direction, height, width);
+    const bool in_place = visits_in_place(a, direction);
+    const Scan2dLayout l = scan2d_layout(a, a.z != nullptr, in_place);
     char *ws = static_cast<char *>(a.workspace);
-    // a grid of one row or one column is visited column-major in row-major order
-    if (direction >= 2 && (height == 1 || width == 1)) direction -= 2;
-    const size_t esz = a.bf16 ? 2 : 4;
-    const bool in_place = direction == 0 ||
-                          (a.dstate == 16 && (direction == 1 || (a.seqlen < (int64_t(1) << 23) &&
-                                                                 size_t(a.seqlen) * a.dim * esz < (size_t(1) << 31))));
     if (in_place) {
         // row-major: the sequence as stored, or read backwards; column-major at
         // d_state 16: the kernel computes each step's patch row itself
@@ -112,7 +126,7 @@ hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int 
         f.reverse = direction & 1;
         f.column_major = direction >= 2;
         f.grid_h = height; f.grid_w = width;
-        f.workspace = ws + l.fwd_off; f.workspace_bytes = l.fwd_bytes;
+        f.workspace = ws; f.workspace_bytes = l.fwd_bytes;
         return launch_scan_fwd(f, s);
     }
     const size_t es = a.bf16 ? 2 : 4;
@@ -120,7 +134,7 @@ hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int 
     ScanArgs f = a;
     f.x = ws + l.x_off; f.delta = ws + l.d_off; f.z = a.z ? ws + l.z_off : nullptr;
     f.B = ws + l.b_off; f.C = ws + l.c_off; f.y = ws + l.y_off;
-    f.workspace = ws + l.fwd_off; f.workspace_bytes = l.fwd_bytes;
+    f.workspace = ws; f.workspace_bytes = l.fwd_bytes;
     hipError_t e;
     if ((e = permute(a.x, const_cast<void *>(f.x), a.batch, height, width, direction, rd, false, s))) return e;
     if ((e = permute(a.delta, const_cast<void *>(f.delta), a.batch, height, width, direction, rd, false, s))) return e;

@@ -67,7 +67,7 @@ namespace {
 
 constexpr int kTB = SSM_SCAN_TB;
 constexpr int kTile = 64;                    // channels per workgroup (one per lane)
-constexpr uint32_t kSpinLimit = 1u << 22;    // bounded wait on the previous segment
+constexpr uint32_t kSpinLimit = 1u << 22;    // bounded wait on the previous segment (polls)
 
 template <int N> constexpr int waves_for() {
     return N % 4 == 0 ? 4 : (N % 2 == 0 ? 2 : 1);
@@ -79,6 +79,8 @@ struct Params {
     void *y;
     float *last;
     uint32_t *words;     // [0] ticket, [1] error flag, [64 ..) per-tile progress
+    uint32_t spin_limit; // polls before a wait on the previous segment gives up
+    int publish;         // 0: segments never hand their state on (error-path tests only)
     float *hbuf;         // per tile: d_state x 64 carried states
     float *ckpt;         // row kernel, optional: state entering each 16-step block
     int64_t seqlen, dim, nblk;
@@ -183,7 +185,7 @@ void scan_fwd_kernel(Params p) {
     __shared__ float4 sDX[2][kTB / 2][kTile];   // (Delta, Delta*x) of steps 2i, 2i+1
     __shared__ float4 sP[2][NW][kTB / 4][kTile];// partial readouts of steps 4i .. 4i+3
     __shared__ float sBC[2][2 * N][kBCS];       // [buf][n (B) | N + n (C)][step], fp32
-    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_ticket, s_gaveup;
 
     using raw = typename Io<T>::raw;
     const int64_t seqlen = p.seqlen, dim = p.dim;
@@ -242,12 +244,17 @@ void scan_fwd_kernel(Params p) {
     } else {
         // Poll with relaxed coherent loads (an acquire per poll would
         // invalidate the L2 every time) and acquire once when the flag is seen.
+        // A wait that gives up records it in the workspace's error word and
+        // poisons the state with NaN, so every output that depends on it is
+        // NaN rather than silently wrong.
         if (tid == 0) {
             uint32_t spins = 0;
+            s_gaveup = 0u;
             while (__hip_atomic_load(&progress[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                    static_cast<uint32_t>(seg)) {
-                if (++spins > kSpinLimit) {       // never wait unboundedly
-                    p.words[1] = 1u;
+                if (++spins > p.spin_limit) {     // never wait unboundedly
+                    __hip_atomic_store(&p.words[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_gaveup = 1u;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
@@ -255,8 +262,9 @@ void scan_fwd_kernel(Params p) {
         }
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool gaveup = __builtin_amdgcn_readfirstlane(s_gaveup) != 0u;
 #pragma unroll
-        for (int i = 0; i < NPW; ++i) h[i] = hslot[(n0 + i) * kTile + lane];
+        for (int i = 0; i < NPW; ++i) h[i] = gaveup ? __builtin_nanf("") : hslot[(n0 + i) * kTile + lane];
     }
 
     // ---- prefetch registers.  Loads are issued right after the data they
@@ -471,7 +479,7 @@ void scan_fwd_kernel(Params p) {
         for (int i = 0; i < NPW; ++i) hslot[(n0 + i) * kTile + lane] = h[i];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // every wave's stores, then the flag
         __syncthreads();
-        if (tid == 0)
+        if (tid == 0 && p.publish)
             __hip_atomic_store(&progress[tile], static_cast<uint32_t>(seg + 1), __ATOMIC_RELEASE,
                                __HIP_MEMORY_SCOPE_AGENT);
     } else if (p.last && active) {
@@ -684,15 +692,19 @@ void scan_rows_kernel(Params p) {
             uint64_t *slot = &hslot[(n0 + i) * kTile + tcol];
             uint64_t v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             uint32_t spins = 0;
+            bool gaveup = false;
             while (static_cast<uint32_t>(v >> 32) != static_cast<uint32_t>(seg)) {
-                if (++spins > kSpinLimit) {          // never wait unboundedly
-                    p.words[1] = 1u;
+                if (++spins > p.spin_limit) {        // never wait unboundedly
+                    __hip_atomic_store(&p.words[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    gaveup = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
                 v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            h[i] = __uint_as_float(static_cast<uint32_t>(v));
+            // a give-up is recorded in the error word and poisons the state
+            // (NaN), so no output that depends on it passes for a value
+            h[i] = gaveup ? __builtin_nanf("") : __uint_as_float(static_cast<uint32_t>(v));
         }
     }
 
@@ -861,7 +873,7 @@ void scan_rows_kernel(Params p) {
     if (seg + 1 < p.n_segs) {
 #pragma unroll
         for (int i = 0; i < NPL; ++i)
-            __hip_atomic_store(&hslot[(n0 + i) * kTile + tcol],
+            if (p.publish) __hip_atomic_store(&hslot[(n0 + i) * kTile + tcol],
                                (static_cast<uint64_t>(seg + 1) << 32) | __float_as_uint(h[i]), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     } else if (p.last && active) {
@@ -897,6 +909,8 @@ template <int N, int NW, typename T, int FL> hipError_t launch(const ScanArgs &a
     p.softplus = a.softplus;
     p.ckpt = nullptr;
     p.nblk = 0;
+    p.spin_limit = a.test_spin_limit ? a.test_spin_limit : kSpinLimit;
+    p.publish = a.test_spin_limit ? 0 : 1;
     const int64_t nclear = static_cast<int64_t>(l.hbuf_off / sizeof(uint32_t));   // ticket + progress
     hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((nclear + 255) / 256)), dim3(256), 0, s,
                        p.words, nclear);
@@ -918,6 +932,8 @@ hipError_t launch_rows(const ScanArgs &a, hipStream_t s) {
     p.seqlen = a.seqlen; p.dim = a.dim;
     p.n_dt = l.n_dt; p.n_tiles = l.n_tiles; p.seg_len = l.seg_len; p.n_segs = l.n_segs;
     p.softplus = a.softplus;
+    p.spin_limit = a.test_spin_limit ? a.test_spin_limit : kSpinLimit;
+    p.publish = a.test_spin_limit ? 0 : 1;
     p.ckpt = a.ckpt;
     p.nblk = (a.seqlen + kRowTB - 1) / kRowTB;
     p.grid_h = static_cast<int>(a.grid_h);

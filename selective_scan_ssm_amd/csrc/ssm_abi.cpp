@@ -3,6 +3,7 @@
 // touches the HIP runtime, so every error path returns before anything is
 // enqueued.
 #include "ssm_scan.h"
+#include "ssm_scan_testing.h"
 
 #include <hip/hip_runtime.h>
 
@@ -115,6 +116,7 @@ const char *ssm_status_string(int status) {
     case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported a launch error";
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
+    case SSM_ERR_WAIT: return "SSM_ERR_WAIT: a segment's bounded wait gave up; that call's outputs are invalid";
     default: return "unknown ssm status";
     }
 }
@@ -361,16 +363,16 @@ int ssm_scan_fwd_ckpt(const void *x, const void *delta, const float *delta_bias,
 }
 
 size_t ssm_scan_2d_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t d_inner,
-                                   int64_t d_state, int has_z, int io_dtype) {
+                                   int64_t d_state, int direction, int has_z, int io_dtype) {
     if (check_dtype(io_dtype) || batch < 0 || height < 0 || width < 0 || d_inner < 0 || d_state < 1 ||
-        d_state > SSM_MAX_D_STATE)
+        d_state > SSM_MAX_D_STATE || direction < 0 || direction > 3)
         return static_cast<size_t>(-1);
     const int64_t L = mul3(height, width, 1);
     if (L < 0) return static_cast<size_t>(-1);
     ssm::ScanArgs a = make_args(nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
                                 nullptr, nullptr, nullptr, nullptr, batch, L, d_inner, d_state,
                                 io_dtype, nullptr, 0);
-    return ssm::scan_2d_workspace(a, has_z != 0);
+    return ssm::scan_2d_workspace(a, has_z != 0, direction, height, width);
 }
 
 int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
@@ -389,7 +391,7 @@ int ssm_scan_fwd_2d(const void *x, const void *delta, const float *delta_bias, i
     ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
                                 last_state, batch, L, d_inner, d_state, io_dtype, workspace,
                                 workspace_bytes);
-    const size_t need = ssm::scan_2d_workspace(a, z != nullptr);
+    const size_t need = ssm::scan_2d_workspace(a, z != nullptr, direction, height, width);
     if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
     if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
     return hip_status(ssm::launch_scan_2d(a, height, width, direction, static_cast<hipStream_t>(stream)));
@@ -529,21 +531,37 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
     return hip_status(ssm::launch_ssd_scan(a, static_cast<hipStream_t>(stream)));
 }
 
-int ssm_mb_copy(const void *src, void *dst, size_t bytes, void *stream) {
-    if (bytes == 0) return SSM_OK;
-    if (!src || !dst) return SSM_ERR_NULL;
-    if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return SSM_ERR_ALIGN;
-    if (overlap(range(src, static_cast<int64_t>(bytes), 1), range(dst, static_cast<int64_t>(bytes), 1)))
-        return SSM_ERR_ALIAS;
-    return hip_status(ssm::launch_mb_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+int ssm_scan_status(const void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace) return SSM_ERR_NULL;
+    if (workspace_bytes < 256) return SSM_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    if (hipStreamSynchronize(s) != hipSuccess) return SSM_ERR_HIP;
+    if (hipMemcpy(&word, static_cast<const char *>(workspace) + ssm::kErrorWordOffset, sizeof(word),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return SSM_ERR_HIP;
+    return word ? SSM_ERR_WAIT : SSM_OK;
 }
 
-int ssm_mb_valu(int op, float *out, int64_t blocks, int64_t iters, void *stream) {
-    if (op < 0 || op > 3 || blocks < 0 || iters < 0 || blocks > (int64_t(1) << 31) - 1) return SSM_ERR_SHAPE;
-    if (blocks == 0) return SSM_OK;
-    if (!out) return SSM_ERR_NULL;
-    if (!aligned(out, 4)) return SSM_ERR_ALIGN;
-    return hip_status(ssm::launch_mb_valu(op, out, blocks, iters, static_cast<hipStream_t>(stream)));
+int ssm_testing_scan_fwd_no_handoff(const void *x, const void *delta, const float *delta_bias,
+                                    int delta_softplus, const float *A, const void *B, const void *C,
+                                    const float *D, const void *z, const float *h0, void *y,
+                                    float *last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                    int64_t d_state, int io_dtype, void *workspace, size_t workspace_bytes,
+                                    uint32_t spin_limit, void *stream) {
+    if (spin_limit == 0 || spin_limit > (1u << 16)) return SSM_ERR_SHAPE;
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, seqlen,
+                          d_inner, d_state, io_dtype);
+    if (r) return r;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, seqlen, d_inner, d_state, io_dtype, workspace,
+                                workspace_bytes);
+    a.test_spin_limit = spin_limit;
+    const size_t need = ssm::scan_fwd_workspace(a);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

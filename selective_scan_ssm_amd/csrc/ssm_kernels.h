@@ -32,7 +32,16 @@ struct ScanArgs {
     // with ckpt, seqlen < 2^23 and seqlen * dim * io bytes < 2^31
     int column_major = 0;
     int64_t grid_h = 0, grid_w = 0;
+    // error-path tests only: nonzero makes segments withhold their hand-off
+    // and bounds the successor's wait at this many polls, so every job past
+    // a tile's first segment gives up (and says so in the error word)
+    uint32_t test_spin_limit = 0;
 };
+
+// The first 256 bytes of a forward scan's workspace: word 0 is the job
+// ticket, word 1 the error word (nonzero once a segment's wait gave up),
+// cleared by every call that uses the workspace.
+constexpr size_t kErrorWordOffset = 4;
 
 struct StepArgs {
     float *state;
@@ -80,7 +89,10 @@ hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 hipError_t launch_scan_fwd_ckpt(const ScanArgs &a, hipStream_t s);
 
 // The 2-D scan orders: gather into scan order, the forward scan, scatter y.
-size_t scan_2d_workspace(const ScanArgs &a, bool has_z);
+// The forward's own workspace comes first, so its error word sits where
+// ssm_scan_status reads it; the gathered copies follow only for the orders
+// that are not visited in place.
+size_t scan_2d_workspace(const ScanArgs &a, bool has_z, int direction, int64_t height, int64_t width);
 hipError_t launch_scan_2d(const ScanArgs &a, int64_t height, int64_t width, int direction, hipStream_t s);
 
 struct ConvArgs {
@@ -126,9 +138,5 @@ hipError_t launch_dt_proj(const DtProjArgs &a, hipStream_t s);
 // Causal depthwise conv1d (+ SiLU), whole sequence and one decode token.
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);
-
-// Measurement helpers (copy bandwidth, fp32 VALU issue rate).
-hipError_t launch_mb_copy(const void *src, void *dst, uint64_t bytes, hipStream_t s);
-hipError_t launch_mb_valu(int op, float *out, int64_t blocks, int64_t iters, hipStream_t s);
 
 }  // namespace ssm

@@ -323,7 +323,7 @@ def scan_fwd_2d(x, delta, A, B, C, height, width, direction, D=None, z=None, del
     y = out if out is not None else torch.empty_like(x)
     _dev(y, "out", io, x.shape)
     last = torch.empty((Bt, Dd, N), dtype=torch.float32, device=x.device) if return_last_state else None
-    need = lib.ssm_scan_2d_workspace_bytes(Bt, height, width, Dd, N, int(z is not None), _IO[io])
+    need = lib.ssm_scan_2d_workspace_bytes(Bt, height, width, Dd, N, int(direction), int(z is not None), _IO[io])
     if need == (1 << 64) - 1:
         raise RuntimeError("ssm_scan_2d_workspace_bytes: invalid arguments")
     ws = None
@@ -371,3 +371,20 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
                           _IO[io], _stream(x.device))
     _check(rc, "ssd_scan_fwd")
     return (y, last) if return_last_state else y
+
+
+def scan_status(workspace, stream_device=None):
+    """ssm_scan_status on a workspace tensor (uint8, device) of the last
+    forward scan: 0 (SSM_OK) or SSM_ERR_WAIT when a segment's bounded wait
+    gave up.  Synchronises torch's current stream of the workspace's device."""
+    lib = _lib.load()
+    dev = workspace.device if stream_device is None else stream_device
+    return lib.ssm_scan_status(_ptr(workspace), workspace.numel(), _stream(dev))
+
+
+def scan_workspace_bytes(batch, seqlen, d_inner, d_state, dtype):
+    """ssm_scan_workspace_bytes for io dtype `dtype` (torch.float32 / torch.bfloat16)."""
+    need = _lib.load().ssm_scan_workspace_bytes(batch, seqlen, d_inner, d_state, _IO[dtype])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("ssm_scan_workspace_bytes: invalid arguments")
+    return need

@@ -10,9 +10,10 @@ import pytest
 from selective_scan_ssm_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("ssm_scan.h", "ssm_scan_testing.h")]
+BENCH_HEADER = os.path.join(ROOT, "include", "ssm_bench.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EALIAS, EWAIT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 F32, BF16 = 0, 1
 MB = 1 << 20
 
@@ -25,25 +26,46 @@ def lib():
     return _lib.load()
 
 
-def header_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, re.M)))
+def header_functions(paths=HEADERS):
+    out = set()
+    for path in paths:
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        out |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, re.M))
+    return sorted(out)
 
 
 def test_header_declares_the_boundary():
     fns = header_functions()
     assert set(fns) == set(_lib.EXPORTS), fns
+    assert set(header_functions([BENCH_HEADER])) == set(_lib.BENCH_EXPORTS)
+    # the measurement helpers are not part of the scan library's ABI
+    assert not set(_lib.BENCH_EXPORTS) & set(fns)
 
 
 def test_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.ssm_abi_version() == 1
+    assert lib.ssm_abi_version() == _lib.ABI_VERSION == 2
+    for name in _lib.BENCH_EXPORTS:
+        assert not hasattr(lib, name), name
+
+
+@pytest.fixture(scope="module")
+def bench_lib():
+    if not os.path.exists(_lib.BENCH_LIB_PATH):
+        from selective_scan_ssm_amd import build
+        build.build()
+    return _lib.load_bench()
+
+
+def test_bench_library_exports(bench_lib):
+    for name in header_functions([BENCH_HEADER]):
+        assert hasattr(bench_lib, name), name
 
 
 def test_status_strings(lib):
-    for code in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EALIAS):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EALIAS, EWAIT):
         s = lib.ssm_status_string(code).decode()
         assert s.startswith("SSM_"), s
     assert "unknown" in lib.ssm_status_string(12345).decode()
@@ -308,10 +330,44 @@ def test_scan_2d_validation(lib, over, kw, code):
 
 
 def test_scan_2d_workspace(lib):
-    # a copy of x, delta, z, B, C, y plus the forward's own workspace
-    need = lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 16, 1, BF16)
-    assert need >= 2 * 64 * (4 * 96 + 2 * 16) * 2
-    assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 0, 1, BF16) == (1 << 64) - 1
+    fwd = lib.ssm_scan_workspace_bytes(2, 64, 96, 16, BF16)
+    # d_state 16 visits every order in place: the forward's own workspace only
+    for direction in range(4):
+        assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 16, direction, 1, BF16) == fwd
+    # other widths gather the column-major and reversed orders: a copy of x,
+    # delta, z, B, C, y after the forward's workspace
+    fwd8 = lib.ssm_scan_workspace_bytes(2, 64, 96, 8, BF16)
+    assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 8, 0, 1, BF16) == fwd8
+    for direction in (1, 2, 3):
+        need = lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 8, direction, 1, BF16)
+        assert need >= fwd8 + 2 * 64 * (4 * 96 + 2 * 8) * 2
+    # a one-row grid visited column-major is the row-major order
+    assert lib.ssm_scan_2d_workspace_bytes(2, 1, 64, 96, 8, 2, 1, BF16) == fwd8
+    assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 0, 0, 1, BF16) == (1 << 64) - 1
+    assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 16, 4, 1, BF16) == (1 << 64) - 1
+    assert lib.ssm_scan_2d_workspace_bytes(2, 8, 8, 96, 16, -1, 1, BF16) == (1 << 64) - 1
+
+
+def test_scan_status_validation(lib):
+    # argument checks only (the query itself synchronises a stream)
+    assert lib.ssm_scan_status(None, 4096, None) == ENULL
+    assert lib.ssm_scan_status(FakeDev()(), 16, None) == EWS
+
+
+def call_no_handoff(lib, a, spin):
+    return lib.ssm_testing_scan_fwd_no_handoff(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"],
+                                               a["B"], a["C"], a["D"], a["z"], a["h0"], a["y"], a["last"],
+                                               a["batch"], a["seqlen"], a["dim"], a["dstate"], a["io"],
+                                               a["ws"], a["ws_bytes"], spin, a["stream"])
+
+
+def test_no_handoff_hook_validation(lib):
+    # the test hook validates exactly as ssm_scan_fwd, plus its poll bound
+    assert call_no_handoff(lib, scan_args(dstate=16, ws_bytes=16), 64) == EWS
+    assert call_no_handoff(lib, scan_args(dstate=16, ws_bytes=16), 0) == ESHAPE
+    assert call_no_handoff(lib, scan_args(dstate=16, ws_bytes=16), 1 << 20) == ESHAPE
+    assert call_no_handoff(lib, scan_args(x=None), 64) == ENULL
+    assert call_no_handoff(lib, scan_args(batch=0), 64) == OK
 
 
 # ------------------------------------------------------ Mamba-2 multi-head scan
@@ -365,27 +421,30 @@ def test_ssd_alias_detection(lib):
 
 
 # ------------------------------------------------------ measurement helpers
+MB_ERR_ARG = -1
+
+
 @pytest.mark.parametrize("args,code", [
-    (dict(src=None), ENULL), (dict(bytes_=24), EALIGN), (dict(src=0x7f0000000008), EALIGN),
-    (dict(dst="src+16"), EALIAS), (dict(bytes_=0, src=None, dst=None), OK),
+    (dict(src=None), MB_ERR_ARG), (dict(bytes_=24), MB_ERR_ARG), (dict(src=0x7f0000000008), MB_ERR_ARG),
+    (dict(dst="src+16"), MB_ERR_ARG), (dict(bytes_=0, src=None, dst=None), OK),
 ])
-def test_mb_copy_validation(lib, args, code):
+def test_mb_copy_validation(bench_lib, args, code):
     f = FakeDev()
     src, dst = f(), f()
     a = dict(src=src, dst=dst, bytes_=1 << 20)
     a.update(args)
     if a["dst"] == "src+16":
         a["dst"] = a["src"] + 16
-    assert lib.ssm_mb_copy(a["src"], a["dst"], a["bytes_"], None) == code
+    assert bench_lib.ssm_mb_copy(a["src"], a["dst"], a["bytes_"], None) == code
 
 
 @pytest.mark.parametrize("op,blocks,iters,out,code", [
-    (4, 1, 1, True, ESHAPE), (-1, 1, 1, True, ESHAPE), (0, -1, 1, True, ESHAPE), (0, 1, -1, True, ESHAPE),
-    (0, 1, 1, False, ENULL), (3, 0, 1, False, OK),
+    (4, 1, 1, True, MB_ERR_ARG), (-1, 1, 1, True, MB_ERR_ARG), (0, -1, 1, True, MB_ERR_ARG),
+    (0, 1, -1, True, MB_ERR_ARG), (0, 1, 1, False, MB_ERR_ARG), (3, 0, 1, False, OK),
 ])
-def test_mb_valu_validation(lib, op, blocks, iters, out, code):
+def test_mb_valu_validation(bench_lib, op, blocks, iters, out, code):
     ptr = FakeDev()() if out else None
-    assert lib.ssm_mb_valu(op, ptr, blocks, iters, None) == code
+    assert bench_lib.ssm_mb_valu(op, ptr, blocks, iters, None) == code
 
 
 # ------------------------------------------------------------------ dt_proj
