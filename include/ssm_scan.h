@@ -47,7 +47,8 @@
  *   - Alignment: every pointer must be aligned to its element size (4 bytes
  *     for fp32 tensors, 2 bytes for bf16 tensors), else SSM_ERR_ALIGN.
  *   - Thread safety: the entry points keep no mutable global state and may be
- *     called concurrently on different streams.
+ *     called concurrently on different streams -- except ssm_scan_fwd_noalloc,
+ *     whose calls share one scratch array per GPU (see there).
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -74,7 +75,8 @@ typedef enum {
     SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required         */
     SSM_ERR_HIP = -6,       /* the HIP runtime reported a launch error          */
     SSM_ERR_ALIAS = -7,     /* an output overlaps an input                      */
-    SSM_ERR_WAIT = -8       /* a segment's bounded wait gave up (ssm_scan_status) */
+    SSM_ERR_WAIT = -8,      /* a segment's bounded wait gave up (ssm_scan_status) */
+    SSM_ERR_SCRATCH = -9    /* the shape needs more than SSM_SCRATCH_BYTES (noalloc) */
 } ssm_status_t;
 
 /*
@@ -97,6 +99,32 @@ int ssm_scan_fwd(const void *x, const void *delta, const float *delta_bias, int 
  * (size_t)-1 for invalid arguments. */
 size_t ssm_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                                 int io_dtype);
+
+/*
+ * ssm_scan_fwd_noalloc -- ssm_scan_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments as ssm_scan_fwd without the
+ * workspace, same outputs (the same kernels run).  The scratch the scan needs
+ * (ssm_scan_workspace_bytes for the shape) is taken from a static device array
+ * of SSM_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends; nothing is allocated or freed by the call.
+ *   A shape whose scratch exceeds SSM_SCRATCH_BYTES: SSM_ERR_SCRATCH, nothing
+ *   enqueued.  The scratch grows with batch x ceil(d_inner / 64) x d_state
+ *   (512 bytes per state of a 64-channel tile): 16 MiB covers up to 2046 tiles
+ *   at d_state 16, e.g. batch 16 at d_inner 8192.
+ *   Every call on one GPU uses that GPU's array and leaves its contents
+ *   behind; each call clears what must start at zero itself.  Calls that
+ *   overlap on one GPU (different streams, or different host threads without
+ *   ordering) race on the array and must not be issued.  ssm_scan_status does
+ *   not apply (there is no caller workspace); a segment wait that gives up
+ *   still poisons the affected outputs with NaN.  The first call on a device
+ *   resolves the array's address there (once, under a lock).
+ */
+#define SSM_SCRATCH_BYTES (16u << 20)
+int ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                         const float *A, const void *B, const void *C, const float *D, const void *z,
+                         const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                         int64_t d_inner, int64_t d_state, int io_dtype, void *stream);
 
 /*
  * sm1_scan_fwd -- the d_state = 1 scan ("Windows SM1 (Scalar Mamba1)" page,

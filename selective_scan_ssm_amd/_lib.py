@@ -20,12 +20,14 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan
            "ssm_state_update", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_scan_ckpt_bytes",
            "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd",
-           "ssm_dt_proj", "ssm_scan_status", "ssm_testing_scan_fwd_no_handoff",
+           "ssm_dt_proj", "ssm_scan_status", "ssm_testing_scan_fwd_no_handoff", "ssm_scan_fwd_noalloc",
            "ssm_status_string", "ssm_abi_version")
 BENCH_LIB_PATH = os.path.join(PKG, "libssmbench.so")
 BENCH_EXPORTS = ("ssm_mb_copy", "ssm_mb_valu")
 ABI_VERSION = 2
 SSM_ERR_WAIT = -8
+SSM_ERR_SCRATCH = -9
+SSM_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 _lock = threading.Lock()
@@ -84,6 +86,9 @@ def _bind(lib):
     lib.ssd_scan_fwd.restype = _int
     lib.ssm_dt_proj.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _vp]
     lib.ssm_dt_proj.restype = _int
+    lib.ssm_scan_fwd_noalloc.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _i64, _i64, _i64, _i64, _int, _vp]
+    lib.ssm_scan_fwd_noalloc.restype = _int
     lib.ssm_scan_status.argtypes = [_vp, _sz, _vp]
     lib.ssm_scan_status.restype = _int
     lib.ssm_testing_scan_fwd_no_handoff.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

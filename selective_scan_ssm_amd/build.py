@@ -25,7 +25,7 @@ BENCH_LIB = os.path.join(PKG, "libssmbench.so")
 ARCH = "gfx950"
 
 SOURCES = ["scan_fwd.hip", "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip",
-           "ssd_scan.hip", "dt_proj.hip", "ssm_abi.cpp"]
+           "ssd_scan.hip", "dt_proj.hip", "scan_noalloc.hip", "ssm_abi.cpp"]
 BENCH_SOURCES = ["microbench.hip"]
 
 # Packed fp32 VALU forms are switched off (plain fp32 VALU only); code object

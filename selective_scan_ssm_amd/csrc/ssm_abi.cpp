@@ -117,6 +117,7 @@ const char *ssm_status_string(int status) {
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported a launch error";
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output overlaps an input";
     case SSM_ERR_WAIT: return "SSM_ERR_WAIT: a segment's bounded wait gave up; that call's outputs are invalid";
+    case SSM_ERR_SCRATCH: return "SSM_ERR_SCRATCH: the shape needs more scratch than SSM_SCRATCH_BYTES (ssm_scan_fwd_noalloc)";
     default: return "unknown ssm status";
     }
 }
@@ -147,6 +148,27 @@ int ssm_scan_fwd(const void *x, const void *delta, const float *delta_bias, int 
     const size_t need = ssm::scan_fwd_workspace(a);
     if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
     if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *delta_bias, int delta_softplus,
+                         const float *A, const void *B, const void *C, const float *D, const void *z,
+                         const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
+                         int64_t d_inner, int64_t d_state, int io_dtype, void *stream) {
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, seqlen,
+                          d_inner, d_state, io_dtype);
+    if (r) return r;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, seqlen, d_inner, d_state, io_dtype, nullptr, 0);
+    const size_t need = ssm::scan_fwd_workspace(a);
+    if (need > SSM_SCRATCH_BYTES) return SSM_ERR_SCRATCH;
+    if (need) {
+        void *ptr = nullptr;             // this device's static scratch array
+        if (ssm::noalloc_scratch(&ptr) != hipSuccess) return SSM_ERR_HIP;
+        a.workspace = ptr;
+        a.workspace_bytes = SSM_SCRATCH_BYTES;
+    }
     return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -57,6 +57,10 @@ struct StepArgs {
 size_t scan_fwd_workspace(const ScanArgs &a);
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t s);
 
+// The device address of this device's static scratch array (SSM_SCRATCH_BYTES,
+// 256-byte aligned), resolved once per device: ssm_scan_fwd_noalloc's workspace.
+hipError_t noalloc_scratch(void **out);
+
 // d_state = 1 time-chunked scan.
 size_t sm1_workspace(int64_t batch, int64_t seqlen, int64_t dim, int bf16);
 hipError_t launch_sm1_scan(const ScanArgs &a, hipStream_t s);

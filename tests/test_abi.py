@@ -531,3 +531,36 @@ def test_bwd_ckpt_validation(lib):
     assert call_bwd_ckpt(lib, a, ck + 4) == EALIGN
     assert call_bwd_ckpt(lib, a, a["dx"]) == EALIAS      # an output over the checkpoints
     assert call_bwd_ckpt(lib, a, a["dh0"]) == EALIAS
+
+
+# ------------------------------------------------- the allocation-free forward
+def call_noalloc(lib, a):
+    return lib.ssm_scan_fwd_noalloc(a["x"], a["delta"], a["delta_bias"], a["softplus"], a["A"], a["B"],
+                                    a["C"], a["D"], a["z"], a["h0"], a["y"], a["last"], a["batch"],
+                                    a["seqlen"], a["dim"], a["dstate"], a["io"], a["stream"])
+
+
+def test_noalloc_scratch_limit(lib):
+    # 512 bytes per state of a 64-channel tile, after a 256-byte header and the
+    # tiles' progress words: 2046 tiles at d_state 16 fit in 16 MiB, 2048 do not
+    fits = lib.ssm_scan_workspace_bytes(2, 4096, 2046 * 32, 16, BF16)
+    assert 0 < fits <= _lib.SSM_SCRATCH_BYTES
+    assert lib.ssm_scan_workspace_bytes(32, 4096, 4096, 16, BF16) > _lib.SSM_SCRATCH_BYTES
+    f = FakeDev()
+    big = dict((k, f(1 << 32)) for k in ("x", "delta", "delta_bias", "A", "B", "C", "D", "z", "h0", "y", "last"))
+    assert call_noalloc(lib, scan_args(batch=32, seqlen=4096, dim=4096, dstate=16, io=BF16, **big)) == -9
+    assert "SCRATCH" in lib.ssm_status_string(-9).decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), ENULL), (dict(dstate=0), ESHAPE), (dict(io=7), EDTYPE), (dict(A=0x7f0000000002), EALIGN),
+    (dict(batch=0), OK), (dict(dim=0), OK),
+])
+def test_noalloc_validation(lib, over, code):
+    assert call_noalloc(lib, scan_args(**over)) == code
+
+
+def test_noalloc_alias_detection(lib):
+    a = scan_args()
+    a["y"] = a["x"]
+    assert call_noalloc(lib, a) == EALIAS
