@@ -78,11 +78,14 @@ SLOTS_PER_ELEM = 3 + (5 + EXP2 + LOG2) + 1 + (3 + EXP2 + RCP) + 3
 #  3 rounding converts
 BWD_SLOTS_PER_ITEM = (4 + EXP2) + 9 + 2
 BWD_SLOTS_PER_ELEM = 4 + (5 + EXP2 + LOG2) + 1 + (8 + EXP2 + RCP) + (2 + EXP2 + RCP) + 2 + 2 + 1 + 2 + 3
+# The block's prologue fused into the scan (ssm_conv_scan_fwd), per element:
+# three more widened rows, four taps (fma), SiLU (scale, exp2, add, rcp, mul).
+CONV_SLOTS_PER_ELEM = 3 + 4 + (3 + EXP2 + RCP)
 COPY_CAL_BYTES = 1 << 30
 
 SOURCES = {
-    "scan": ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
-    "rows": ["selective_scan_ssm_amd/csrc/scan_fwd.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "scan": ["selective_scan_ssm_amd/csrc/scan_fwd_kernels.h", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "rows": ["selective_scan_ssm_amd/csrc/scan_fwd_kernels.h", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "sm1": ["selective_scan_ssm_amd/csrc/sm1_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "conv": ["selective_scan_ssm_amd/csrc/conv1d.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
@@ -199,6 +202,50 @@ def traffic_from_profile(kind, wname):
     return int(float(rec["bytes_per_launch"]))
 
 
+def host_record():
+    """The host the oracle runs on: CPU model, logical CPUs, the CPUs this
+    process may use (affinity, and the cgroup's CPU quota where one is set)
+    and the ROCm version.  No child process is started."""
+    rec = {"cpu_model": "", "logical_cpus": os.cpu_count() or 0}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    rec["cpu_model"] = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    granted = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    rec["affinity_cpus"] = granted
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            rec["cgroup_cpu_quota"] = round(int(quota) / int(period), 2)
+            granted = min(granted, max(1, int(int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    rec["cpus_granted"] = granted
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rec["rocm"] = f.read().strip()
+            break
+        except OSError:
+            continue
+    return rec
+
+
+# The oracle's threads: every CPU this process is granted, at most 16 -- the
+# CPU share one GPU's job has on the GPU hosts this runs on, whatever the
+# machine's own core count.
+ORACLE_THREAD_CAP = 16
+
+
+def oracle_threads():
+    return max(1, min(ORACLE_THREAD_CAP, host_record()["cpus_granted"]))
+
+
 def cpu_baseline(inp, w, seconds_target):
     """The fp64 oracle on a bounded sample of the workload: all batches over
     the full sequence and the first `nd` channels (decode: one layer)."""
@@ -206,8 +253,7 @@ def cpu_baseline(inp, w, seconds_target):
     import oracle
     from selective_scan_ssm_amd import inputs as gen
     io = inp["io"]
-    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    threads = max(1, min(16, threads))
+    threads = oracle_threads()
     # about 7e6 elements/s per core at d_state 16: size the sample to about
     # `seconds_target` core-seconds
     per_core = 7e6 * 16 / max(1, w.d_state)
@@ -434,8 +480,7 @@ def cpu_baseline_bwd(inp, dout, w, seconds_target):
     import oracle
     from selective_scan_ssm_amd import inputs as gen
     io = inp["io"]
-    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    threads = max(1, min(16, threads))
+    threads = oracle_threads()
     per_core = 2.5e6 * 16 / max(1, w.d_state)         # the forward's rate / ~3
     nd = int(min(w.d_inner, max(64, seconds_target * per_core / (w.batch * w.seqlen))))
     sl = lambda a: None if a is None else np.ascontiguousarray(gen.to_f64(a[:, :, :nd], io))
@@ -646,7 +691,7 @@ def bench_dtproj(args, dev):
                      "unit": "TFLOP/s", "flops_per_launch": flops}}
     cpu = None
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        threads = oracle_threads()
         # about 3e9 multiply-adds per core-second (measured): size the sample to
         # about `cpu_seconds` core-seconds
         nr = int(min(rows, max(64, args.cpu_seconds * 3e9 / (rank * dim))))
@@ -724,7 +769,7 @@ def bench_conv(args, dev):
             "algorithmic_bytes_per_launch": alg}
     cpu = None
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        threads = oracle_threads()
         nd = int(min(w.d_inner, max(64, args.cpu_seconds * 4e7 / (w.batch * w.seqlen))))
         xs64 = np.ascontiguousarray(gen.to_f64(inp["x"][:, :, :nd], io))
         t1 = time.perf_counter()
@@ -744,6 +789,112 @@ def bench_conv(args, dev):
             "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16" if io == gen.BF16 else "f32", "data": "synthetic",
             "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
+def bench_conv_scan(args, dev):
+    """ssm_conv_scan_fwd on a d_state-16 scan workload: the causal conv1d
+    (width 4) + SiLU run inside the scan kernel, one launch.  Timed beside
+    the same work as two launches (ssm_causal_conv1d_fwd into a buffer, then
+    ssm_scan_fwd), with HIP events on the stream both launch on."""
+    import numpy as np
+    import torch
+    from selective_scan_ssm_amd import _lib, ops
+    from selective_scan_ssm_amd import inputs as gen
+    import oracle
+    _lib.load()
+    w = gen.WORKLOADS[args.workload]
+    if kind_of(w) != "rows":
+        raise SystemExit("--conv-scan needs a d_state-16 scan workload (2 or 3)")
+    io, K = w.io, 4
+    io_b = 2 if io == gen.BF16 else 4
+    log(f"[bench] conv1d + scan, workload {args.workload} ({w.name}): generating inputs")
+    inp = gen.workload_inputs(args.workload)
+    cp = gen.make_conv_params(w.batch, w.d_inner, K, io=io, seed=31)
+    alg = algorithmic_bytes(w, io_b) + w.d_inner * (K + 1) * 4
+    nset = max(1, math.ceil(600e6 / alg)) if args.rotate is None else args.rotate
+    sets = [device_set(inp, dev) for _ in range(nset)]
+    wd, bd = upload(cp["conv_w"], gen.F32, dev), upload(cp["conv_b"], gen.F32, dev)
+    N = w.d_state
+    for st in sets:
+        st["last"] = torch.empty((w.batch, w.d_inner, N), dtype=torch.float32, device=dev)
+    need = ops.scan_workspace_bytes(w.batch, w.seqlen, w.d_inner, N, sets[0]["x"].dtype)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    xc = torch.empty_like(sets[0]["x"])          # the two-launch path's filtered x
+    stream = torch.cuda.current_stream(dev)
+    cur = [0]
+
+    def fused():
+        st = sets[cur[0] % nset]
+        cur[0] += 1
+        ops.conv_scan_fwd(st["x"], wd, st["delta"], st["A"], st["B"], st["C"], conv_bias=bd, D=st["D"],
+                          z=st["z"], delta_bias=st["delta_bias"], out=st["y"], workspace=ws)
+
+    def two_launches():
+        st = sets[cur[0] % nset]
+        cur[0] += 1
+        ops.causal_conv1d(st["x"], wd, bd, silu=True, out=xc)
+        ops.scan_fwd(xc, st["delta"], st["A"], st["B"], st["C"], D=st["D"], z=st["z"],
+                     delta_bias=st["delta_bias"], return_last_state=True, out=st["y"],
+                     last_state_out=st["last"], workspace=ws)
+
+    def timed(fn, steps, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in ev]
+
+    log(f"[bench] two launches: warmup {args.warmup}, {args.steps} steps")
+    two_ms, two_ev = timed(two_launches, args.steps, args.warmup)
+    log(f"[bench] fused: warmup {args.warmup}, {args.steps} steps")
+    ms_per_step, step_ms = timed(fused, args.steps, args.warmup)
+    call_ms = float(np.mean(step_ms))
+    slots = valu_slots(w) + w.batch * w.seqlen * w.d_inner * CONV_SLOTS_PER_ELEM
+    ach = slots / (call_ms * 1e-3) / 1e12
+    hbm = alg / (call_ms * 1e-3) / 1e9
+    roof = {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+            "unit": "T fp32 fma-equivalent lane-slots/s", "frac": round(ach / VALU_PEAK_TSLOTS, 4),
+            "traffic": None, "kernel": "ssm_conv_scan_fwd (scan_rows_kernel with the conv prologue)",
+            "algorithmic_slots_per_launch": slots, "hbm_achieved_GBs": round(hbm, 1),
+            "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
+            "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
+            "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
+            "algorithmic_bytes_per_launch": alg,
+            "two_launches_ms_mean": round(float(np.mean(two_ev)), 5),
+            "two_launches_ms_per_step": round(two_ms, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle conv1d + scan on a sample)")
+        threads = oracle_threads()
+        nd = int(min(w.d_inner, max(64, args.cpu_seconds * 7e6 / (w.batch * w.seqlen))))
+        sl = lambda a: None if a is None else np.ascontiguousarray(gen.to_f64(a[:, :, :nd], io))
+        t1 = time.perf_counter()
+        xo, _ = oracle.causal_conv1d(sl(inp["x"]), cp["conv_w"][:nd], cp["conv_b"][:nd], None, silu=True,
+                                     threads=threads)
+        oracle.selective_scan(xo, sl(inp["delta"]), np.ascontiguousarray(inp["A"][:nd]),
+                              gen.to_f64(inp["B"], io), gen.to_f64(inp["C"], io), D=inp["D"][:nd],
+                              z=sl(inp["z"]), delta_bias=inp["delta_bias"][:nd], threads=threads)
+        dt = time.perf_counter() - t1
+        el = w.batch * w.seqlen * nd
+        cpu = {"value": el / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+               "sample": f"conv1d + scan, all {w.batch} batches x {w.seqlen} steps x first {nd} of "
+                         f"{w.d_inner} channels ({el} elements, width 4, d_state 16), fp64, {dt:.2f} s wall"}
+    elems = w.batch * w.seqlen * w.d_inner
+    cfg = {"workload": w.name + "-conv-scan", "batch": w.batch, "seqlen": w.seqlen, "d_inner": w.d_inner,
+           "d_state": N, "width": K, "io": io, "state": "fp32", "seed": args.workload}
+    if nset > 1:
+        cfg["rotated_input_sets"] = nset
+    return {"metric": "conv1d + SiLU + selective-scan fwd elements/s (B*T*D)",
+            "value": elems / (ms_per_step * 1e-3), "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if io == gen.BF16 else "f32",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
 
 
 def ssd_algorithmic_bytes(w, io_bytes):
@@ -810,7 +961,7 @@ def bench_ssd(args, dev):
     if not args.no_cpu_baseline:
         # the oracle on every batch row and head, the first nc channels of each
         # head (about 5e8 state updates -- one channel, step and n -- per core-second)
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        threads = oracle_threads()
         nc = int(min(w.headdim, max(1, args.cpu_seconds * 5e8 / (w.batch * w.seqlen * w.n_heads * w.d_state))))
         f64 = lambda a: np.ascontiguousarray(gen.to_f64(a, io))
         xs = np.ascontiguousarray(f64(inp["x"])[:, :, :, :nc])
@@ -1024,6 +1175,9 @@ def main():
                     help="with --direction: the sequence as an H x W patch grid (default 1 x seqlen)")
     ap.add_argument("--direction", type=int, default=None,
                     help="scan order through ssm_scan_fwd_2d (height 1): 0 forward, 1 reversed")
+    ap.add_argument("--conv-scan", action="store_true",
+                    help="time ssm_conv_scan_fwd (conv1d + SiLU fused into the d_state-16 scan) on a scan "
+                         "workload, beside the two separate launches")
     ap.add_argument("--conv", action="store_true",
                     help="time ssm_causal_conv1d_fwd (width 4, SiLU) on a scan workload's x instead")
     ap.add_argument("--dt-proj", action="store_true",
@@ -1082,11 +1236,14 @@ def main():
         return
     from selective_scan_ssm_amd import _lib
     _lib.load()
-    fn = (bench_backward if args.backward else bench_conv if args.conv else bench_dtproj if args.dt_proj else
+    fn = (bench_backward if args.backward else bench_conv if args.conv else
+          bench_conv_scan if args.conv_scan else bench_dtproj if args.dt_proj else
           bench_ssd if args.ssd is not None else bench_micro if args.microbench else bench_workload)
     rec = fn(args, torch.device("cuda:0"))
     # the GPU's name, CUs and clocks, read after the timed region
     rec.setdefault("device", device_record())
+    if isinstance(rec.get("cpu_baseline"), dict):
+        rec["cpu_baseline"]["host"] = host_record()
     print(json.dumps(rec), flush=True)
 
 

@@ -127,6 +127,49 @@ int ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *delta_bi
                          int64_t d_inner, int64_t d_state, int io_dtype, void *stream);
 
 /*
+ * ssm_conv_scan_fwd -- the Mamba block's prologue and the scan in one call
+ * (youngju.dev guide, section 5, "complete Mamba implementation": the x
+ * branch runs the causal depthwise conv1d, then SiLU, then the selective
+ * scan).  The scan of ssm_scan_fwd runs on
+ *     xc[b,t,d] = SiLU(conv_bias[d] + sum_{k<W} conv_weight[d,k] * x[b, t-(W-1)+k, d])
+ * (W = conv_width; the inputs before step 0 come from conv_state_in, oldest
+ * first, or are zeros): xc replaces x in Delta*B*x and in the D skip.  xc is
+ * computed in fp32 and never rounded or stored; the result equals
+ * ssm_causal_conv1d_fwd (apply_silu = 1) followed by ssm_scan_fwd up to that
+ * intermediate rounding.
+ *   x              : (batch, seqlen, d_inner) io dtype, the conv's input
+ *   conv_weight    : (d_inner, conv_width) fp32, required; conv_width in [1, 4]
+ *   conv_bias      : (d_inner) fp32, optional
+ *   conv_state_in  : (batch, d_inner, conv_width - 1) io dtype, optional
+ *   conv_state_out : same shape, optional output -- the last conv_width - 1
+ *                    inputs of (conv_state_in, x), where a following call or
+ *                    ssm_causal_conv1d_update continues
+ *   every other argument as ssm_scan_fwd.  Workspace:
+ *   ssm_conv_scan_workspace_bytes (at d_state 16 the scan's own: the filter
+ *   runs inside the scan kernel; at other widths it adds room for xc in fp32,
+ *   which the conv kernel writes there first and the scan then reads, so xc
+ *   is not rounded to the io dtype on that path either).
+ *   Errors as ssm_scan_fwd, plus conv_width outside [1, 4] (SSM_ERR_SHAPE),
+ *   at d_state below 16 seqlen * d_inner * 4 bytes of 2 GiB or more
+ *   (SSM_ERR_SHAPE),
+ *   conv_weight NULL (SSM_ERR_NULL) and conv_state_out overlapping any input
+ *   or output (SSM_ERR_ALIAS).  seqlen == 0 writes last_state = h0 and
+ *   conv_state_out = conv_state_in (or zeros).
+ */
+int ssm_conv_scan_fwd(const void *x, const float *conv_weight, const float *conv_bias,
+                      const void *conv_state_in, void *conv_state_out, int64_t conv_width,
+                      const void *delta, const float *delta_bias, int delta_softplus, const float *A,
+                      const void *B, const void *C, const float *D, const void *z, const float *h0,
+                      void *y, float *last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
+                      int64_t d_state, int io_dtype, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Workspace bytes ssm_conv_scan_fwd needs (0 = none); (size_t)-1 for invalid
+ * arguments. */
+size_t ssm_conv_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                     int io_dtype);
+
+/*
  * sm1_scan_fwd -- the d_state = 1 scan ("Windows SM1 (Scalar Mamba1)" page,
  * detailed sections: the scalar-state recurrence whose closed form is a
  * cumulative product and a cumulative sum).  Same definition as ssm_scan_fwd
@@ -372,8 +415,8 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
  *   SSM_ERR_NULL / SSM_ERR_WORKSPACE  workspace NULL or under 256 bytes;
  *   SSM_ERR_HIP   the synchronisation or the copy failed (for example a
  *                 fault of an earlier kernel on the stream).
- * `workspace` is the workspace of the last ssm_scan_fwd, ssm_scan_fwd_ckpt or
- * ssm_scan_fwd_2d call on `stream` (or of an sm1_scan_fwd call whose
+ * `workspace` is the workspace of the last ssm_scan_fwd, ssm_scan_fwd_ckpt,
+ * ssm_conv_scan_fwd or ssm_scan_fwd_2d call on `stream` (or of an sm1_scan_fwd call whose
  * sm1_scan_workspace_bytes was nonzero), not yet reused.  The error word is
  * cleared at the start of every such call.  Not capturable in a HIP graph
  * (it synchronises); call it outside a capture.

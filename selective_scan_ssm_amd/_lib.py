@@ -21,6 +21,7 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan
            "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd",
            "ssm_dt_proj", "ssm_scan_status", "ssm_testing_scan_fwd_no_handoff", "ssm_scan_fwd_noalloc",
+           "ssm_conv_scan_fwd", "ssm_conv_scan_workspace_bytes",
            "ssm_status_string", "ssm_abi_version")
 BENCH_LIB_PATH = os.path.join(PKG, "libssmbench.so")
 BENCH_EXPORTS = ("ssm_mb_copy", "ssm_mb_valu")
@@ -89,6 +90,11 @@ def _bind(lib):
     lib.ssm_scan_fwd_noalloc.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _i64, _i64, _i64, _i64, _int, _vp]
     lib.ssm_scan_fwd_noalloc.restype = _int
+    lib.ssm_conv_scan_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]
+    lib.ssm_conv_scan_fwd.restype = _int
+    lib.ssm_conv_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _int]
+    lib.ssm_conv_scan_workspace_bytes.restype = _sz
     lib.ssm_scan_status.argtypes = [_vp, _sz, _vp]
     lib.ssm_scan_status.restype = _int
     lib.ssm_testing_scan_fwd_no_handoff.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -24,7 +24,9 @@ LIB = os.path.join(PKG, "libssmscan.so")
 BENCH_LIB = os.path.join(PKG, "libssmbench.so")
 ARCH = "gfx950"
 
-SOURCES = ["scan_fwd.hip", "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip",
+SOURCES = ["scan_fwd.hip", "scan_rows_bf16.hip", "scan_rows_f32.hip", "scan_rows_2d_bf16.hip",
+           "scan_rows_2d_f32.hip", "scan_general_bf16.hip", "scan_general_bf16_xf32.hip", "scan_general_f32.hip",
+           "sm1_scan.hip", "state_update.hip", "scan_bwd.hip", "conv1d.hip", "scan_2d.hip",
            "ssd_scan.hip", "dt_proj.hip", "scan_noalloc.hip", "ssm_abi.cpp"]
 BENCH_SOURCES = ["microbench.hip"]
 
@@ -65,7 +67,7 @@ def _link(objs, lib: str, verbose: bool) -> None:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + BENCH_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     _link(objs[:len(SOURCES)], LIB, verbose)
     _link(objs[len(SOURCES):], BENCH_LIB, verbose)

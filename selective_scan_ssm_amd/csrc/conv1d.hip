@@ -17,6 +17,8 @@
 // channels of one time chunk of kChunk steps; the K - 1 inputs before the
 // chunk are read again (3 of 128 rows at K = 4).  Rows are loaded eight steps
 // ahead of their use.
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_kernels.h"
 
@@ -86,7 +88,9 @@ template <> __device__ __forceinline__ void store_row<bf16_t, 4>(const float (&v
     __builtin_amdgcn_raw_buffer_store_b64(q, rs, off, 0, kStream);
 }
 
-template <typename T, int K, int VEC>
+// TO: the type of out -- T, or float for an fp32 intermediate that the scan
+// reads next (the fused prologue at d_state below 16).
+template <typename T, int K, int VEC, typename TO = T>
 __global__ __launch_bounds__(kConvWaves * 64) void conv1d_kernel(ConvParams p) {
     using RW = Row<T, VEC>;
     using raw = typename RW::raw;
@@ -113,9 +117,14 @@ __global__ __launch_bounds__(kConvWaves * 64) void conv1d_kernel(ConvParams p) {
     const int64_t base = static_cast<int64_t>(b) * T_ * dim * es;
     const uint32_t bytes = static_cast<uint32_t>(T_ * dim * es);
     const rsrc_t rx = make_rsrc(static_cast<const char *>(p.x) + base, bytes);
-    const rsrc_t ro = make_rsrc(static_cast<char *>(p.out) + base, bytes);
+    constexpr uint32_t eo = sizeof(TO);
+    const rsrc_t ro = make_rsrc(static_cast<char *>(p.out) + static_cast<int64_t>(b) * T_ * dim * eo,
+                                static_cast<uint32_t>(T_ * dim * eo));
     auto row_off = [&](int64_t t) -> uint32_t {
         return (active && t >= 0 && t < T_) ? static_cast<uint32_t>((t * dim + c0) * es) : kOffNone;
+    };
+    auto out_off = [&](int64_t t) -> uint32_t {
+        return (active && t >= 0 && t < T_) ? static_cast<uint32_t>((t * dim + c0) * eo) : kOffNone;
     };
 
     // the K - 1 inputs before the chunk: from x, or from the state before the sequence
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(kConvWaves * 64) void conv1d_kernel(ConvParams p) {
                 for (int j = 0; j + 1 < H; ++j) hist[v][j] = hist[v][j + 1];
                 if (H > 0) hist[v][H > 0 ? H - 1 : 0] = xv;
             }
-            store_row<T, VEC>(o, ro, row_off(ts + i));   // rows past the sequence are dropped
+            store_row<TO, VEC>(o, ro, out_off(ts + i));  // rows past the sequence are dropped
         }
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) cur[i][0] = nxt[i][0];
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(256) void conv_update_kernel(void *state, const voi
     if (H > 0) st[H > 0 ? H - 1 : 0] = xr;
 }
 
-template <typename T, int K, int VEC> hipError_t launch_conv_t(const ConvArgs &a, hipStream_t s) {
+template <typename T, int K, int VEC, typename TO = T> hipError_t launch_conv_t(const ConvArgs &a, hipStream_t s) {
     ConvParams p;
     p.x = a.x; p.w = a.weight; p.bias = a.bias; p.state_in = a.state_in; p.out = a.out;
     p.seqlen = a.seqlen; p.dim = a.dim; p.silu = a.silu;
@@ -222,7 +231,7 @@ template <typename T, int K, int VEC> hipError_t launch_conv_t(const ConvArgs &a
         const dim3 grid(static_cast<unsigned>((a.dim + 64 * VEC - 1) / (64 * VEC)),
                         static_cast<unsigned>((chunks + kConvWaves - 1) / kConvWaves),
                         static_cast<unsigned>(a.batch));
-        hipLaunchKernelGGL((conv1d_kernel<T, K, VEC>), grid, dim3(kConvWaves * 64), 0, s, p);
+        hipLaunchKernelGGL((conv1d_kernel<T, K, VEC, TO>), grid, dim3(kConvWaves * 64), 0, s, p);
     }
     if (a.state_out && K > 1) {
         const int64_t n = a.batch * a.dim * (K - 1);
@@ -234,8 +243,11 @@ template <typename T, int K, int VEC> hipError_t launch_conv_t(const ConvArgs &a
 
 template <typename T, int K> hipError_t launch_conv_k(const ConvArgs &a, hipStream_t s) {
     const size_t vec_bytes = 4 * sizeof(T);
+    const size_t out_bytes = 4 * (a.out_f32 ? sizeof(float) : sizeof(T));
     const bool vec = a.dim % 4 == 0 && reinterpret_cast<uintptr_t>(a.x) % vec_bytes == 0 &&
-                     reinterpret_cast<uintptr_t>(a.out) % vec_bytes == 0;
+                     reinterpret_cast<uintptr_t>(a.out) % out_bytes == 0;
+    if (a.out_f32 && !std::is_same<T, float>::value)
+        return vec ? launch_conv_t<T, K, 4, float>(a, s) : launch_conv_t<T, K, 1, float>(a, s);
     return vec ? launch_conv_t<T, K, 4>(a, s) : launch_conv_t<T, K, 1>(a, s);
 }
 
@@ -263,6 +275,19 @@ template <typename T> hipError_t launch_update_dt(const ConvUpdateArgs &a, hipSt
 
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s) {
     return a.bf16 ? launch_conv_dt<bf16_t>(a, s) : launch_conv_dt<float>(a, s);
+}
+
+hipError_t launch_conv_state_out(const ConvArgs &a, hipStream_t s) {
+    if (!a.state_out || a.width <= 1 || a.batch == 0 || a.dim == 0) return hipSuccess;
+    ConvParams p{};
+    p.x = a.x; p.state_in = a.state_in; p.seqlen = a.seqlen; p.dim = a.dim;
+    const int64_t n = a.batch * a.dim * (a.width - 1);
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+    if (a.bf16)
+        hipLaunchKernelGGL(conv_state_out_kernel<bf16_t>, grid, dim3(256), 0, s, p, a.state_out, a.width - 1, a.batch);
+    else
+        hipLaunchKernelGGL(conv_state_out_kernel<float>, grid, dim3(256), 0, s, p, a.state_out, a.width - 1, a.batch);
+    return hipGetLastError();
 }
 
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s) {

@@ -172,6 +172,63 @@ int ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *delta_bi
     return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t ssm_conv_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                     int io_dtype) {
+    if (check_dtype(io_dtype) || batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 ||
+        d_state > SSM_MAX_D_STATE || mul3(batch, seqlen, d_inner) < 0)
+        return static_cast<size_t>(-1);
+    ssm::ScanArgs a = make_args(nullptr, nullptr, nullptr, 1, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr, batch, seqlen, d_inner,
+                                d_state, io_dtype, nullptr, 0);
+    return ssm::conv_scan_workspace(a);
+}
+
+int ssm_conv_scan_fwd(const void *x, const float *conv_weight, const float *conv_bias,
+                      const void *conv_state_in, void *conv_state_out, int64_t conv_width,
+                      const void *delta, const float *delta_bias, int delta_softplus, const float *A,
+                      const void *B, const void *C, const float *D, const void *z, const float *h0,
+                      void *y, float *last_state, int64_t batch, int64_t seqlen, int64_t d_inner,
+                      int64_t d_state, int io_dtype, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    int r = validate_scan(x, delta, delta_bias, A, B, C, D, z, h0, y, last_state, batch, seqlen,
+                          d_inner, d_state, io_dtype);
+    if (r) return r;
+    if (conv_width < 1 || conv_width > SSM_MAX_CONV_WIDTH) return SSM_ERR_SHAPE;
+    const int64_t n_win = mul3(batch, d_inner, conv_width - 1);
+    if (n_win < 0) return SSM_ERR_SHAPE;
+    // below d_state 16 the filtered x of one batch row (fp32) is addressed
+    // with 32-bit byte offsets
+    if (d_state != 16 && mul3(seqlen, d_inner, 4) > (int64_t(1) << 31) - 1) return SSM_ERR_SHAPE;
+    if (batch == 0 || d_inner == 0) return SSM_OK;
+    if (!conv_weight) return SSM_ERR_NULL;
+    const size_t es = io_size(io_dtype);
+    if (!aligned(conv_weight, 4) || (conv_bias && !aligned(conv_bias, 4))) return SSM_ERR_ALIGN;
+    if ((conv_state_in && !aligned(conv_state_in, es)) || (conv_state_out && !aligned(conv_state_out, es)))
+        return SSM_ERR_ALIGN;
+    const int64_t n_btd = mul3(batch, seqlen, d_inner), n_btn = mul3(batch, seqlen, d_state);
+    const int64_t n_bdn = mul3(batch, d_inner, d_state);
+    const Range win_out = range(conv_state_out, n_win, es);
+    const Range ins[] = {range(x, n_btd, es),         range(delta, n_btd, es),
+                         range(z, n_btd, es),         range(B, n_btn, es),
+                         range(C, n_btn, es),         range(A, d_inner * d_state, 4),
+                         range(D, d_inner, 4),        range(delta_bias, d_inner, 4),
+                         range(h0, n_bdn, 4),         range(conv_weight, d_inner * conv_width, 4),
+                         range(conv_bias, d_inner, 4), range(conv_state_in, n_win, es)};
+    const Range outs[] = {range(y, seqlen > 0 ? n_btd : 0, es), range(last_state, n_bdn, 4), win_out};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlap(o, i)) return SSM_ERR_ALIAS;
+    if (overlap(outs[0], win_out) || overlap(outs[1], win_out)) return SSM_ERR_ALIAS;
+    ssm::ScanArgs a = make_args(x, delta, delta_bias, delta_softplus, A, B, C, D, z, h0, y,
+                                last_state, batch, seqlen, d_inner, d_state, io_dtype, workspace,
+                                workspace_bytes);
+    a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state_in; a.conv_k = conv_width;
+    const size_t need = ssm::conv_scan_workspace(a);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    return hip_status(ssm::launch_conv_scan_fwd(a, conv_state_out, static_cast<hipStream_t>(stream)));
+}
+
 size_t sm1_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int io_dtype) {
     if (check_dtype(io_dtype) || batch < 0 || seqlen < 0 || d_inner < 0)
         return static_cast<size_t>(-1);

@@ -36,6 +36,15 @@ struct ScanArgs {
     // and bounds the successor's wait at this many polls, so every job past
     // a tile's first segment gives up (and says so in the error word)
     uint32_t test_spin_limit = 0;
+    // the block's prologue fused into the d_state-16 scan (launch_conv_scan_fwd):
+    // x is the conv input; conv_w (dim, conv_k) fp32, conv_b (dim) optional,
+    // conv_state (batch, dim, conv_k - 1) io dtype optional
+    const float *conv_w = nullptr, *conv_b = nullptr;
+    const void *conv_state = nullptr;
+    int64_t conv_k = 0;
+    // 1: x is fp32 while the other io tensors are bf16 (an internal fp32
+    // intermediate, d_state below 16 only)
+    int x_f32 = 0;
 };
 
 // The first 256 bytes of a forward scan's workspace: word 0 is the job
@@ -106,6 +115,7 @@ struct ConvArgs {
     void *out, *state_out;
     int64_t batch, seqlen, dim;
     int width, silu, bf16;
+    int out_f32 = 0;                      // 1: out is written in fp32 whatever the io dtype
 };
 struct ConvUpdateArgs {
     void *state;                          // io dtype (batch, dim, width - 1), in place
@@ -141,6 +151,16 @@ hipError_t launch_dt_proj(const DtProjArgs &a, hipStream_t s);
 
 // Causal depthwise conv1d (+ SiLU), whole sequence and one decode token.
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
+// The window after a sequence alone: state_out = the last width - 1 inputs
+// of (state_in, x) (a.out is not used).
+hipError_t launch_conv_state_out(const ConvArgs &a, hipStream_t s);
+
+// conv1d + SiLU feeding the forward scan: at d_state 16 one fused launch
+// (the convolved x stays in registers); at other widths the filtered x goes
+// to the workspace (after the scan's own) and the scan reads it.  The window
+// after the sequence goes to conv_state_out when given.
+size_t conv_scan_workspace(const ScanArgs &a);
+hipError_t launch_conv_scan_fwd(const ScanArgs &a, void *conv_state_out, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t s);
 
 }  // namespace ssm

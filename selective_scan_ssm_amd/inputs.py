@@ -28,7 +28,8 @@ F32 = "f32"
 BF16 = "bf16"
 
 # tensor ids inside one seed
-_TID = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "bias": 6, "A": 7, "D": 8, "h0": 9, "x_dbl": 10, "W_dt": 11}
+_TID = {"x": 1, "delta": 2, "z": 3, "B": 4, "C": 5, "bias": 6, "A": 7, "D": 8, "h0": 9, "x_dbl": 10, "W_dt": 11,
+        "conv_w": 12, "conv_b": 13, "conv_state": 14}
 
 
 def bf16_from_f32(a: np.ndarray) -> np.ndarray:
@@ -142,6 +143,21 @@ def workload_inputs(cfg: int, seed: Optional[int] = None, layer: int = 0, **over
               a_kind=w.a_kind, h0_kind=w.h0_kind, seed=cfg if seed is None else seed, layer=layer)
     kw.update(over)
     return make_inputs(**kw)
+
+
+# ------------------------------------------------------- the block's conv1d
+# The causal depthwise conv1d in front of the scan (the guide's MambaBlock:
+# nn.Conv1d(d_inner, d_inner, kernel_size=d_conv, groups=d_inner,
+# padding=d_conv - 1)), with PyTorch's default initialisation of such a layer:
+# weight and bias ~ U(-1/sqrt(K), 1/sqrt(K)) (fan-in K per channel).  The
+# window before the sequence (for continuation) ~ N(0, 1) in the io dtype.
+def make_conv_params(batch: int, d_inner: int, width: int, io: str = F32, seed: int = 0,
+                     with_bias: bool = True, with_state: bool = False) -> dict:
+    bound = 1.0 / np.sqrt(width)
+    w = _rng(seed, "conv_w").uniform(-bound, bound, size=(d_inner, width)).astype(np.float32)
+    b = _rng(seed, "conv_b").uniform(-bound, bound, size=d_inner).astype(np.float32) if with_bias else None
+    st = _store(_normal(seed, "conv_state", (batch, d_inner, width - 1)), io) if with_state else None
+    return {"conv_w": w, "conv_b": b, "conv_state": st}
 
 
 # ------------------------------------------------------------- Mamba-2 (SSD)

@@ -388,3 +388,54 @@ def scan_workspace_bytes(batch, seqlen, d_inner, d_state, dtype):
     if need == (1 << 64) - 1:
         raise RuntimeError("ssm_scan_workspace_bytes: invalid arguments")
     return need
+
+
+def conv_scan_fwd(x, conv_weight, delta, A, B, C, conv_bias=None, conv_state=None, D=None, z=None,
+                  delta_bias=None, delta_softplus=True, h0=None, return_last_state=False,
+                  return_conv_state=False, out=None, workspace=None):
+    """The block's prologue and the scan in one call (ssm_conv_scan_fwd): the
+    scan of scan_fwd on SiLU(causal_conv1d(x)).  x: (batch, seqlen, d_inner)
+    conv input; conv_weight: (d_inner, width) fp32; conv_bias: (d_inner,)
+    fp32; conv_state: (batch, d_inner, width - 1) in x's dtype.  Returns y,
+    plus last_state and/or the conv window after the sequence when asked."""
+    lib = _lib.load()
+    if x.dtype not in _IO:
+        raise ValueError("x must be float32 or bfloat16")
+    io = x.dtype
+    Bt, T, Dd = x.shape
+    N = A.shape[-1]
+    K = conv_weight.shape[-1]
+    _dev(x, "x", io)
+    _dev(conv_weight, "conv_weight", torch.float32, (Dd, K))
+    _dev(conv_bias, "conv_bias", torch.float32, (Dd,))
+    _dev(conv_state, "conv_state", io, (Bt, Dd, K - 1))
+    _dev(delta, "delta", io, x.shape)
+    _dev(z, "z", io, x.shape)
+    _dev(B, "B", io, (Bt, T, N))
+    _dev(C, "C", io, (Bt, T, N))
+    _dev(A, "A", torch.float32, (Dd, N))
+    _dev(D, "D", torch.float32, (Dd,))
+    _dev(delta_bias, "delta_bias", torch.float32, (Dd,))
+    _dev(h0, "h0", torch.float32, (Bt, Dd, N))
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, "out", io, x.shape)
+    last = torch.empty((Bt, Dd, N), dtype=torch.float32, device=x.device) if return_last_state else None
+    win = torch.empty((Bt, Dd, K - 1), dtype=io, device=x.device) if return_conv_state else None
+    need = lib.ssm_conv_scan_workspace_bytes(Bt, T, Dd, N, _IO[io])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("ssm_conv_scan_workspace_bytes: invalid arguments")
+    ws = None
+    if need:
+        ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
+            need, dtype=torch.uint8, device=x.device)
+    rc = lib.ssm_conv_scan_fwd(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(win), K,
+                               _ptr(delta), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last), Bt, T, Dd, N, _IO[io],
+                               _ptr(ws), need, _stream(x.device))
+    _check(rc, "ssm_conv_scan_fwd")
+    res = (y,)
+    if return_last_state:
+        res += (last,)
+    if return_conv_state:
+        res += (win,)
+    return res if len(res) > 1 else y
