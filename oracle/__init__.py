@@ -22,6 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
 _BUILD_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD_DIR, "libssm_oracle.so")
+# a sanitized build (build_sanitized) is loaded instead when this names it
+_LIB_OVERRIDE = os.environ.get("SSM_ORACLE_LIB")
 _lib = None
 _lock = threading.Lock()
 
@@ -35,6 +37,16 @@ def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
     tmp = out + ".tmp%d" % os.getpid()
     subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, out)
+    return out
+
+
+def build_sanitized(out: str, cc: str = "clang") -> str:
+    """The same source and fp flags under AddressSanitizer and
+    UndefinedBehaviorSanitizer (any report aborts), for the CPU check that
+    runs the oracle's pins against it."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    subprocess.run([cc, *CFLAGS, "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-shared-libasan", _SRC, "-o", out, "-lm"], check=True)
     return out
 
 
@@ -74,6 +86,8 @@ def load(path: Optional[str] = None):
     with _lock:
         if path is not None:
             return _bind(ctypes.CDLL(path))
+        if _lib is None and _LIB_OVERRIDE:
+            _lib = _bind(ctypes.CDLL(_LIB_OVERRIDE))
         if _lib is None:
             if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
                 build()

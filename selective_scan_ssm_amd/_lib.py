@@ -13,7 +13,9 @@ import sys
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libssmscan.so")
+# SSM_SCAN_LIB names another build of the same library (the host-sanitized
+# one the CPU sanitizer check loads); default: the in-tree build
+LIB_PATH = os.environ.get("SSM_SCAN_LIB") or os.path.join(PKG, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan_workspace_bytes",

@@ -74,6 +74,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """libssmscan.so with its host-side C ABI (argument validation, aliasing
+    and size arithmetic, ssm_abi.cpp) compiled under AddressSanitizer and
+    UndefinedBehaviorSanitizer; the kernels' objects are the regular ones
+    (GPU code is not sanitized: -fsanitize goes to the host pass only)."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.basename(src) + ".o") for src in SOURCES if src != "ssm_abi.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    abi_obj = os.path.join(BUILD, "ssm_abi.cpp.asan.o")
+    cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, *san, "-c", os.path.join(CSRC, "ssm_abi.cpp"), "-o", abi_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized ssm_abi.cpp:\n{r.stdout}\n{r.stderr}")
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-shared-libasan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", *objs, abi_obj,
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the sanitized library failed:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
