@@ -607,6 +607,418 @@ __global__ __launch_bounds__(64 * waves_for<PT>()) void ssd_chunk_kernel(SsdPara
     }
 }
 
+// ===========================================================================
+// ---- helpers of ssd_line_kernel
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 values as a packed bf16 pair, rounded to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+// eight computed values as an MFMA operand of two bf16 terms: hi = bf16(v),
+// lo = bf16(v - hi) (16 significant bits together)
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t &hi, bf16x8_t &lo) {
+    u32x4_t h, l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float r0 = v[2 * q] - __uint_as_float(h[q] << 16);
+        const float r1 = v[2 * q + 1] - __uint_as_float(h[q] & 0xffff0000u);
+        l[q] = pack_bf16(r0, r1);
+    }
+    hi = __builtin_bit_cast(bf16x8_t, h);
+    lo = __builtin_bit_cast(bf16x8_t, l);
+}
+// the eight values of an accumulator tile pair in the K order of PermK
+__device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = a[e];
+        v[4 + e] = b[e];
+    }
+}
+
+// ssd_line_kernel: bf16 io, head sizes that are multiples of 64, d_state 32
+// or 64.
+//
+// A workgroup owns (b, h, 64 channels): whole 128-byte lines of x, z and y,
+// so no line is shared with another workgroup.  Its 8 waves pair up on
+// 16-channel blocks (cb = wave % 4); the two waves of a pair (half = wave /
+// 4) split the chunk's four 16-step output blocks ({0, 3} and {1, 2}: equal
+// triangular work) and the state's n-tiles (each keeps half of the block's
+// N x 16 state, fp32, in MFMA accumulators; nothing is duplicated).
+//
+// Global memory is touched in whole rows only: each thread moves one
+// 16-byte piece of x, z (and B, C) per chunk, and of y, so every wave
+// instruction covers eight full 128-byte lines.  LDS redistributes: x and z
+// as stored (rows = steps), B and C as stored, B^T (rows = n), y as produced
+// -- all double buffered, one barrier per chunk -- plus each wave's half of
+// the carried state as ready-made MFMA operands (hi and lo bf16 fragments in
+// lane order) for its partner's readout.  A chunk's y leaves at the top of
+// the next chunk.  Loads go out a chunk ahead; the chunk body has no branch.
+//
+// Per chunk and wave, with s_t the chunk prefix of Delta A (log2 units):
+//   G^T = B C^T for the five lower tiles of its output blocks (K = n),
+//   M^T = G^T masked, times Delta_s exp(s_t - s_s): on the diagonal tiles
+//     element by element, below them as u_s r_t with u_s = Delta_s
+//     exp(e_i - s_s), r_t = exp(s_t - e_i), e_i the end of s-block i (every
+//     factor <= 1 whatever the decay);
+//   Y^T = X^T M^T + (S_in C^T) diag(exp(s_t)); D skip, gate (x^T gathered
+//     from the staged rows into the K order of M^T's accumulator tiles);
+//   its state half  S^T <- exp(s_Q) S^T + B^T (w x),  w_s = u_s exp(s_Q - e_i).
+// M, S_in and w x enter the products as hi + lo bf16 terms.
+template <int N, bool GATE>
+__global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
+    using MM = Mma<bf16_t>;
+    using PK = PermK<bf16_t>;
+    using E = uint16_t;
+    using EL = Elem<bf16_t>;
+    using ST = Steps<FastMath>;
+    using QD = Quad<bf16_t>;
+    using frag = bf16x8_t;
+    constexpr uint32_t es = 2;
+    constexpr int kWaves = 8, kThreads = 64 * kWaves;
+    constexpr int PT = 64;                       // channels per workgroup
+    constexpr int NNT = N / 16;                  // 16-row state tiles of a channel block
+    constexpr int NH = NNT / 2;                  // ... kept by each wave of the pair
+    constexpr int NKN = N / 32;                  // 32-wide K steps over n
+    constexpr int PAD = 8;                       // 16 bytes of row padding
+    constexpr int LN = N + PAD;                  // rows with n contiguous
+    constexpr int LQ = kQ + PAD;                 // rows with s contiguous
+    constexpr int LP = PT + PAD;                 // rows with channels contiguous
+    constexpr int PBB = piece_bytes(N * es, kThreads);
+    constexpr int VB = PBB / es;
+    constexpr int UBT = (kQ / 2) * (N / VB) / kThreads;
+    static_assert(UBT >= 1 && (kQ / 2) * (N / VB) == UBT * kThreads, "whole B / C pieces per thread");
+    static_assert(N % 32 == 0 && NH >= 1, "n tiles in pairs");
+    static_assert(kQ * PT * es == kThreads * 16, "one 16-byte piece of x, z, y per thread and chunk");
+    using VBt = typename Vec<PBB>::t;
+
+    __shared__ __attribute__((aligned(16))) E sB[2][kQ][LN];    // B[s][n]
+    __shared__ __attribute__((aligned(16))) E sC[2][kQ][LN];    // C[t][n]
+    __shared__ __attribute__((aligned(16))) E sBt[2][N][LQ];    // B[s][n] at [n][s]
+    __shared__ __attribute__((aligned(16))) E sX[2][kQ][LP];    // x[s][p] of the tile
+    __shared__ __attribute__((aligned(16))) E sZ[2][kQ][LP];    // z[t][p]
+    __shared__ __attribute__((aligned(16))) E sY[2][kQ][LP];    // y[t][p]
+    __shared__ __attribute__((aligned(16))) float sCum[kWaves][kQ];   // per wave: prefix s_t
+    __shared__ __attribute__((aligned(16))) float sDl[kWaves][kQ];    // per wave: Delta_t
+    // per wave: its S_in tiles as readout operands, [buffer][wave][fragment][term][lane]
+    constexpr int NSP = (NH + 1) / 2;
+    __shared__ __attribute__((aligned(16))) u32x4_t sS[2][kWaves][NSP][2][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cb = w & 3, half = w >> 2;         // channel block, and which half of the pair
+    const int partner = w ^ 4;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    // block -> (b, h, channel tile), consecutive logical blocks on one XCD
+    const int64_t H = p.nheads, P = p.headdim, L = p.seqlen;
+    const int64_t npb = P / PT;
+    const int64_t total = static_cast<int64_t>(gridDim.x);
+    int64_t lin = blockIdx.x;
+    if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+    const int64_t pt = lin % npb;
+    const int64_t h = (lin / npb) % H;
+    const int64_t b = lin / (npb * H);
+    const int64_t p0 = pt * PT;
+
+    const uint32_t rowX = static_cast<uint32_t>(H * P * es);
+    const uint32_t rowN = static_cast<uint32_t>(N * es);
+    const uint32_t rowH = static_cast<uint32_t>(H * es);
+    const int64_t tile0 = (h * P + p0) * es;                   // the tile inside a step
+    const char *xb = static_cast<const char *>(p.x) + b * L * H * P * es + tile0;
+    const char *zb = static_cast<const char *>(GATE ? p.z : p.x) + b * L * H * P * es + tile0;
+    char *yb = static_cast<char *>(p.y) + b * L * H * P * es + tile0;
+    const char *dtb = static_cast<const char *>(p.dt) + b * L * H * es;
+    const char *Bb = static_cast<const char *>(p.B) + b * L * N * es;
+    const char *Cb = static_cast<const char *>(p.C) + b * L * N * es;
+    // descriptors of the steps from t0 on (t0 < L or past it): rows past the
+    // sequence fall outside the range and read 0 (stores to them are dropped)
+    auto rows_from = [&](const void *base, int64_t t0, uint32_t row) __attribute__((always_inline)) {
+        const int64_t left = L - t0 > 0 ? L - t0 : 0;
+        return make_rsrc(static_cast<const char *>(base) + t0 * row, static_cast<uint32_t>(left) * row);
+    };
+
+    const float Ah = p.A[h] * ST::kScale;
+    const float bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
+    const float Dh = p.D ? p.D[h] : 0.0f;
+    const bool sp_on = p.softplus != 0;
+
+    // B / C staging pieces of this thread (two steps, VB elements of n)
+    const int sp = 2 * (tid % 32);
+    int nB0[UBT];
+    uint32_t oB[UBT];
+#pragma unroll
+    for (int i = 0; i < UBT; ++i) {
+        nB0[i] = ((tid + i * kThreads) / 32) * VB;
+        oB[i] = sp * rowN + nB0[i] * es;
+    }
+    // the thread's 16-byte piece of x, z, y: step pr, channels 8 pc .. 8 pc + 7
+    const int pr = tid / 8, pc = tid % 8;
+    const uint32_t oPiece = static_cast<uint32_t>(pr) * rowX + static_cast<uint32_t>(16 * pc);
+    const uint32_t oDt = static_cast<uint32_t>(lane) * rowH + static_cast<uint32_t>(h) * es;
+    // this wave's two output blocks
+    const int jb0 = half ? 1 : 0, jb1 = half ? 2 : 3;
+
+    // ---- one chunk's registers (fetched a chunk ahead, consumed at its top)
+    uint32_t rdt;
+    u32x4_t rxp, rzp;
+    VBt rbv[UBT][2], rcv[UBT][2];
+    auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+        rdt = __builtin_amdgcn_raw_buffer_load_b16(rows_from(dtb, t0, rowH), oDt, 0, kStream);
+        const rsrc_t rB = rows_from(Bb, t0, rowN), rC = rows_from(Cb, t0, rowN);
+#pragma unroll
+        for (int i = 0; i < UBT; ++i) {
+            rbv[i][0] = Vec<PBB>::template load<kCached>(rB, oB[i]);
+            rbv[i][1] = Vec<PBB>::template load<kCached>(rB, oB[i] + rowN);
+            rcv[i][0] = Vec<PBB>::template load<kCached>(rC, oB[i]);
+            rcv[i][1] = Vec<PBB>::template load<kCached>(rC, oB[i] + rowN);
+        }
+        rxp = __builtin_amdgcn_raw_buffer_load_b128(rows_from(xb, t0, rowX), oPiece, 0, kStream);
+        // no z: an empty descriptor, zeros
+        rzp = __builtin_amdgcn_raw_buffer_load_b128(GATE ? rows_from(zb, t0, rowX) : make_rsrc(p.x, 0u), oPiece, 0,
+                                                    kStream);
+    };
+    // y of chunk cy (staged in sY[cy % 2]) to global memory; cy < 0: nothing (dropped)
+    auto store_y = [&](int64_t cy) __attribute__((always_inline)) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&sY[static_cast<int>(cy & 1)][pr][8 * pc]);
+        const rsrc_t rY = cy >= 0 ? rows_from(yb, cy * kQ, rowX) : make_rsrc(yb, 0u);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rY, oPiece, 0, kStream);
+    };
+
+    // ---- this wave's half of the block's state: tiles S^T[16 (NH half + k) ..][16 cb ..]
+    // (lane: n = 16 (NH half + k) + 4 g + v, p = l16)
+    f32x4_t acc_s[NH];
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+        acc_s[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.h0)
+            acc_s[k] = *reinterpret_cast<const f32x4_t *>(p.h0 + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
+                                                                  16 * (NH * half + k) + 4 * g));
+    }
+
+    auto chunk = [&](int64_t c) __attribute__((always_inline)) {
+        const int64_t t0 = c * kQ;
+        const int buf = static_cast<int>(c & 1);
+
+        // ---- per-step quantities (lane = step), each wave its own copy
+        const float vmask = t0 + lane < L ? 1.0f : 0.0f;
+        const float v = __uint_as_float(rdt << 16) + bias;
+        const float delta = (sp_on ? FastMath::softplus(v) : v) * vmask;
+        const float cum = ST::prefix(delta * Ah, lane);
+        const float cend = ST::lane_value(cum, 63);
+        sCum[w][lane] = cum;
+        sDl[w][lane] = delta;
+
+        // ---- S_in of this wave's half as readout operands (hi, lo) for both
+        // waves of the pair: NH == 1 holds one n-tile (its partner the other),
+        // NH >= 2 whole tile pairs
+        if constexpr (NH == 1) {
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[e] = acc_s[0][e];
+#pragma unroll
+            for (int e = 4; e < 8; ++e) sv[e] = 0.0f;
+            frag fh, fl;
+            split8(sv, fh, fl);
+            sS[buf][w][0][0][lane] = __builtin_bit_cast(u32x4_t, fh);
+            sS[buf][w][0][1][lane] = __builtin_bit_cast(u32x4_t, fl);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NH / 2; ++k) {
+                float sv[8];
+                tile_pair(acc_s[2 * k], acc_s[2 * k + 1], sv);
+                frag fh, fl;
+                split8(sv, fh, fl);
+                sS[buf][w][k][0][lane] = __builtin_bit_cast(u32x4_t, fh);
+                sS[buf][w][k][1][lane] = __builtin_bit_cast(u32x4_t, fl);
+            }
+        }
+
+        // ---- stage this chunk (buffer c % 2; the previous readers of that
+        // buffer, chunk c - 2, finished before the last barrier)
+        *reinterpret_cast<u32x4_t *>(&sX[buf][pr][8 * pc]) = rxp;
+        *reinterpret_cast<u32x4_t *>(&sZ[buf][pr][8 * pc]) = rzp;
+#pragma unroll
+        for (int i = 0; i < UBT; ++i) {
+            const int n0 = nB0[i];
+            *reinterpret_cast<VBt *>(&sB[buf][sp][n0]) = rbv[i][0];
+            *reinterpret_cast<VBt *>(&sB[buf][sp + 1][n0]) = rbv[i][1];
+            *reinterpret_cast<VBt *>(&sC[buf][sp][n0]) = rcv[i][0];
+            *reinterpret_cast<VBt *>(&sC[buf][sp + 1][n0]) = rcv[i][1];
+#pragma unroll
+            for (int e = 0; e < VB; ++e) MM::put2(&sBt[buf][n0 + e][sp], EL::raw(rbv[i][0], e), EL::raw(rbv[i][1], e));
+        }
+        fetch(t0 + kQ);                        // the next chunk (past the end: empty reads)
+        __syncthreads();
+        store_y(c - 1);                        // the previous chunk's y, complete now
+
+        // ---- x^T operand: lane (channel 16 cb + l16, group g) takes steps
+        // 16 i + 4 g + v (i < 4, v < 4): K slots 8 g .. 8 g + 7 of the two
+        // 32-step K ranges in the order M^T's accumulator tiles give them
+        frag xt[2];
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            u32x4_t u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 16 * (2 * kp + q / 2) + 4 * g + 2 * (q % 2);
+                u[q] = static_cast<uint32_t>(sX[buf][s0][16 * cb + l16]) |
+                       (static_cast<uint32_t>(sX[buf][s0 + 1][16 * cb + l16]) << 16);
+            }
+            xt[kp] = __builtin_bit_cast(frag, u);
+        }
+
+        // ---- per-step values at the lane's K slots (steps 16 i + 4 g + v) and
+        // columns (steps 16 j + l16): u_s = Delta_s exp(e_i - s_s) with e_i
+        // the prefix at the end of s-block i
+        f32x4_t cs[4], ds[4], us[4];
+        float ct[4], eb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cs[i] = *reinterpret_cast<const f32x4_t *>(&sCum[w][16 * i + 4 * g]);
+            ds[i] = *reinterpret_cast<const f32x4_t *>(&sDl[w][16 * i + 4 * g]);
+            ct[i] = sCum[w][16 * i + l16];
+            eb[i] = sCum[w][16 * i + 15];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) us[i][e] = ds[i][e] * ST::ex(eb[i] - cs[i][e]);
+        }
+
+        // ---- the readout operand over all N: this wave's S_in half and the partner's
+        frag fs[NKN][2];
+        if constexpr (NH == 1) {
+            // K slots 0..3 from half 0, 4..7 from half 1
+            const u32x4_t a0 = sS[buf][half ? partner : w][0][0][lane], b0 = sS[buf][half ? w : partner][0][0][lane];
+            const u32x4_t a1 = sS[buf][half ? partner : w][0][1][lane], b1 = sS[buf][half ? w : partner][0][1][lane];
+            fs[0][0] = __builtin_bit_cast(frag, u32x4_t{a0[0], a0[1], b0[0], b0[1]});
+            fs[0][1] = __builtin_bit_cast(frag, u32x4_t{a1[0], a1[1], b1[0], b1[1]});
+        } else {
+#pragma unroll
+            for (int kn = 0; kn < NKN; ++kn) {
+                const int owner = (kn < NKN / 2) == (half == 0) ? w : partner;
+                const int k = kn % (NKN / 2);
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) fs[kn][q2] = __builtin_bit_cast(frag, sS[buf][owner][k][q2][lane]);
+            }
+        }
+
+        // ---- the wave's two output blocks
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int j = r ? jb1 : jb0;         // 0..3, uniform
+            // C rows of t-block j (B operand, K = n): for G^T and for the readout
+            frag fc[NKN];
+#pragma unroll
+            for (int kn = 0; kn < NKN; ++kn) fc[kn] = PK::from_lds(&sC[buf][16 * j + l16][32 * kn], g, 0);
+            // M^T tiles (s-block i <= j, t-block j)
+            f32x4_t m[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                m[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                if (i <= j) {
+                    f32x4_t gt = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kn = 0; kn < NKN; ++kn)
+                        gt = MM::mma(PK::from_lds(&sB[buf][16 * i + l16][32 * kn], g, 0), fc[kn], gt);
+                    if (i < j) {
+                        const float rt = ST::ex(ct[j] - eb[i]);   // t after block i's end: <= 1
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) m[i][e] = gt[e] * (us[i][e] * rt);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            // on the diagonal: s <= t when 4 g + e <= l16; the exponent
+                            // is clamped so a masked entry never overflows
+                            const float f = ds[i][e] * ST::ex(fminf(ct[j] - cs[i][e], 0.0f));
+                            m[i][e] = 4 * g + e <= l16 ? gt[e] * f : 0.0f;
+                        }
+                    }
+                }
+            }
+            // Y^T block: the state's readout, scaled by exp(s_t) ...
+            f32x4_t yo = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kn = 0; kn < NKN; ++kn)
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) yo = MM::mma(fs[kn][q2], fc[kn], yo);
+            f32x4_t acc = yo * ST::ex(ct[j]);
+            // ... plus X^T M^T over the s-blocks up to j
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp)
+                if (2 * kp <= j) {
+                    float mv[8];
+                    tile_pair(m[2 * kp], m[2 * kp + 1], mv);
+                    frag mh, ml;
+                    split8(mv, mh, ml);
+                    acc = MM::mma(xt[kp], mh, acc);
+                    acc = MM::mma(xt[kp], ml, acc);
+                }
+            // D skip, gate (lane: channels 16 cb + 4 g + e, step 16 j + l16), into sY
+            const int trow = 16 * j + l16, pcol = 16 * cb + 4 * g;
+            const u32x2_t xq = *reinterpret_cast<const u32x2_t *>(&sX[buf][trow][pcol]);
+            const u32x2_t zq = *reinterpret_cast<const u32x2_t *>(&sZ[buf][trow][pcol]);
+            float yv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float o = fmaf(Dh, QD::get(xq, e), acc[e]);
+                if constexpr (GATE) o *= silu(QD::get(zq, e));
+                yv[e] = o;
+            }
+            *reinterpret_cast<u32x2_t *>(&sY[buf][trow][pcol]) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
+        }
+
+        // ---- state half: S^T <- exp(s_Q) S^T + B^T (w x), K = s in the x^T slot
+        // order, w_s = u_s exp(s_Q - e_i)
+        frag fwx[2][2];
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            const u32x4_t u = __builtin_bit_cast(u32x4_t, xt[kp]);
+            const float q0 = ST::ex(cend - eb[2 * kp]), q1 = ST::ex(cend - eb[2 * kp + 1]);
+            float wv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = 2 * kp + q / 4, e = q % 4;
+                const float xv = __uint_as_float(q % 2 ? (u[q / 2] & 0xffff0000u) : (u[q / 2] << 16));
+                wv[q] = xv * (us[i][e] * (q < 4 ? q0 : q1));
+            }
+            split8(wv, fwx[kp][0], fwx[kp][1]);
+        }
+        const float dec = ST::ex(cend);
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+            const int ni = NH * half + k;
+            f32x4_t a = acc_s[k] * dec;
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+                const frag fbt = PK::from_lds(&sBt[buf][16 * ni + l16][32 * kp], g, 0);
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) a = MM::mma(fbt, fwx[kp][q2], a);
+            }
+            acc_s[k] = a;
+        }
+    };
+
+    const int64_t nchunks = (L + kQ - 1) / kQ;
+    fetch(0);
+    // a (dropped) store after the first fetch, as every chunk issues one after
+    // its fetch: every path into the loop has the same memory history, so a
+    // chunk's top waits for its own registers only
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, make_rsrc(yb, 0u), oPiece, 0, kStream);
+    for (int64_t c = 0; c < nchunks; ++c) chunk(c);
+    __syncthreads();
+    store_y(nchunks - 1);
+
+    if (p.last) {
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+            *reinterpret_cast<f32x4_t *>(p.last + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
+                                                   16 * (NH * half + k) + 4 * g)) = acc_s[k];
+    }
+}
+
 template <typename T, int N, int PT>
 hipError_t launch(const SsdParams &p, int64_t blocks, hipStream_t s) {
     hipLaunchKernelGGL((ssd_chunk_kernel<T, N, PT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * waves_for<PT>()),
@@ -614,9 +1026,20 @@ hipError_t launch(const SsdParams &p, int64_t blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-// 32-channel tiles when the head size allows
+// bf16 with head sizes that are multiples of 64: whole-line tiles
+// (ssd_line_kernel); otherwise 32- or 16-channel tiles of ssd_chunk_kernel
 template <typename T, int N>
 hipError_t launch_pt(const SsdParams &p, int64_t batch, hipStream_t s) {
+    if constexpr (std::is_same<T, bf16_t>::value && N <= 64) {
+        if (p.headdim % 64 == 0) {
+            const dim3 grid(static_cast<unsigned>(batch * p.nheads * (p.headdim / 64)));
+            if (p.z)
+                hipLaunchKernelGGL((ssd_line_kernel<N, true>), grid, dim3(512), 0, s, p);
+            else
+                hipLaunchKernelGGL((ssd_line_kernel<N, false>), grid, dim3(512), 0, s, p);
+            return hipGetLastError();
+        }
+    }
     if (p.headdim % 32 == 0) return launch<T, N, 32>(p, batch * p.nheads * (p.headdim / 32), s);
     return launch<T, N, 16>(p, batch * p.nheads * (p.headdim / 16), s);
 }

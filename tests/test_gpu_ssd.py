@@ -100,6 +100,31 @@ def test_ssd_bf16(N, P, T):
     check(inp, tag=f"bf16-N{N}-P{P}")
 
 
+# the whole-line kernel (bf16, head sizes that are multiples of 64): every
+# d_state, one and two 64-channel tiles per head, ragged and short sequences
+@pytest.mark.parametrize("N,P,T", [(64, 64, 300), (64, 128, 129), (32, 64, 65), (128, 128, 200), (32, 192, 1),
+                                   (64, 320, 64), (128, 64, 3)])
+def test_ssd_bf16_whole_line_tiles(N, P, T):
+    inp = gen.make_ssd_inputs(2, T, 3, P, N, io=gen.BF16, h0_kind="normal", seed=750 + N + P + T)
+    check(inp, tag=f"bf16-line-N{N}-P{P}-T{T}")
+
+
+def test_ssd_bf16_whole_line_options_off():
+    # no z, D, bias, softplus or h0
+    inp = gen.make_ssd_inputs(2, 190, 2, 64, 64, io=gen.BF16, h0_kind="none", seed=760, with_z=False,
+                              with_D=False, with_bias=False)
+    inp["dt"] = gen.bf16_from_f32(np.abs(gen.f32_from_bf16(inp["dt"])) * np.float32(0.2))
+    check(inp, softplus=False, tag="bf16-line-plain")
+
+
+def test_ssd_bf16_whole_line_fast_decay():
+    # heads with |A| up to e^4: decays underflow inside a chunk
+    inp = gen.make_ssd_inputs(1, 200, 4, 64, 64, io=gen.BF16, h0_kind="normal", seed=761)
+    inp["A"] = (-np.exp(np.array([-4.0, 0.0, 2.5, 4.0]))).astype(np.float32)
+    inp["dt_bias"] = np.full(4, 0.5, np.float32)
+    check(inp, tag="bf16-line-fast-decay")
+
+
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 def test_ssd_more_workgroups_than_cus(io):
     # 4 x 72 heads x one 32-channel tile = 288 workgroups, more than the CUs:
@@ -140,6 +165,19 @@ def test_ssd_deterministic_and_continuation():
 
 
 # -------------------------------------------------- the layer shapes, full size
+@pytest.mark.parametrize("name", ["mamba2-130m-ssd-layer-bf16", "mamba2-2.7b-ssd-layer-bf16"])
+def test_ssd_layer_every_output(name):
+    """One launch at the full layer shape; every output and final state
+    against the oracle."""
+    inp = gen.ssd_workload_inputs(name, seed=741)
+    G.say(f"[ssd] {name} full size, every output")
+    y, last = run_gpu(inp)
+    yo, lo = run_oracle(inp)
+    ey, el = G.err(y, yo), G.err(last, lo)
+    G.say(f"[ssd] {name} all err_y={ey:.2e} err_last={el:.2e}")
+    assert ey <= 2e-2 and el <= 2e-2
+
+
 @pytest.mark.parametrize("name", ["mamba2-130m-ssd-layer-bf16", "mamba2-2.7b-ssd-layer-bf16"])
 def test_ssd_layer_full_sampled(name):
     """One launch at the full layer shape; sampled heads x channels (every
