@@ -7,10 +7,11 @@
 // with the inputs before step 0 taken from the caller's state (or 0).
 //
 // HBM-bound: every input is read once from HBM and every output written
-// once.  It is a kernel of its own rather than a prologue fused into the
-// scan: the scan at d_state 16 is bound by VALU issue with HBM 80% idle, so
-// fusing the filter and SiLU into it would lengthen its bottleneck to save
-// bandwidth it does not lack.
+// once.  This is the stand-alone form (its output is the scan's input); the
+// same filter also runs inside the d_state-16 scan kernel when the caller
+// asks for both at once (ssm_conv_scan_fwd), where the filtered x never
+// leaves the registers.  Below d_state 16 that call runs this kernel with an
+// fp32 output in its workspace, which the scan then reads.
 //
 // conv1d_kernel: a lane owns VEC consecutive channels (VEC = 4 when d_inner
 // and the pointers allow 8- or 16-byte accesses, else 1) and a wave 64*VEC
