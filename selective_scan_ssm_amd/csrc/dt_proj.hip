@@ -25,7 +25,11 @@
 //   * Wave w computes a 64 x 64 sub-tile as 4 x 4 MFMA tiles.  W supplies the
 //     A operand (rows = channels) and xdt the B operand (columns = rows of
 //     delta), so each lane's four accumulator values are four consecutive
-//     channels of one row of delta: one 8-byte (bf16) or 16-byte (fp32) store.
+//     channels of one row of delta.
+//   * The finished tile goes back through LDS (the K staging space, reused)
+//     and leaves in whole rows: 16-byte pieces, eight lanes per 128-byte line,
+//     so a store instruction covers full lines instead of 32-byte pieces of 16
+//     rows (which HBM serves at a fraction of the rate).
 #include "ssm_device.h"
 #include "ssm_kernels.h"
 
@@ -80,8 +84,13 @@ __global__ __launch_bounds__(256) void dt_proj_kernel(DtProjArgs a) {
     constexpr int PE = 16 / es;               // elements per 16-byte piece
     constexpr int KC = 128 / es;              // K elements per LDS chunk (128 bytes per row)
     constexpr int RS = KC + PE;               // LDS row stride: 16 bytes of padding
-    __shared__ __attribute__((aligned(16))) E sW[kTD * RS];
-    __shared__ __attribute__((aligned(16))) E sX[kTM * RS];
+    // K staging (sW, sX), reused for the output tile once the products are done
+    constexpr int OS = kTD + 32 / es;         // output row stride: 32 bytes of padding
+    constexpr int kStageBytes = (kTD + kTM) * RS * es, kOutBytes = kTM * OS * es;
+    __shared__ __attribute__((aligned(16))) char smem[kStageBytes > kOutBytes ? kStageBytes : kOutBytes];
+    E *sW = reinterpret_cast<E *>(smem);
+    E *sX = sW + kTD * RS;
+    E *sO = reinterpret_cast<E *>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,15 +156,33 @@ __global__ __launch_bounds__(256) void dt_proj_kernel(DtProjArgs a) {
         __syncthreads();
     }
 
-    // lane: channels d .. d + 3 of row m of each 16 x 16 tile
-    char *out = static_cast<char *>(a.out);
+    // lane: channels d .. d + 3 of row m of each 16 x 16 tile, into the tile
+    // in LDS (the loop's last barrier freed the staging space)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t d = d0 + wd * 64 + i * 16 + kq * 4;
+        const int dl = wd * 64 + i * 16 + kq * 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t m = m0 + wm * 64 + j * 16 + l16;
-            if (m < M && d < D) O::store4(out + (m * D + d) * static_cast<int64_t>(es), acc[i][j]);
+        for (int j = 0; j < 4; ++j) O::store4(&sO[(wm * 64 + j * 16 + l16) * OS + dl], acc[i][j]);
+    }
+    __syncthreads();
+    // whole rows out: piece q (16 bytes) is row q / PR, PE channels at (q % PR) PE
+    constexpr int PR = kTD / PE;              // pieces per tile row
+    char *out = static_cast<char *>(a.out);
+    // rows start 16-byte aligned when d_inner is a multiple of a piece; else
+    // (bf16, d_inner % 8 == 4) 8-byte aligned, and pieces go out in halves
+    const bool whole = D % PE == 0;
+#pragma unroll
+    for (int q = tid; q < kTM * PR; q += 256) {
+        const int row = q / PR, c = (q % PR) * PE;
+        const int64_t m = m0 + row, d = d0 + c;
+        if (m >= M || d >= D) continue;
+        char *dst = out + (m * D + d) * static_cast<int64_t>(es);
+        if (whole) {
+            *reinterpret_cast<u32x4_t *>(dst) = *reinterpret_cast<const u32x4_t *>(&sO[row * OS + c]);
+        } else {
+            // 8-byte halves; d_inner % 4 == 0, so a half is whole or past the end
+            for (int hh = 0; hh < PE && d + hh < D; hh += 8 / es)
+                *reinterpret_cast<u32x2_t *>(dst + hh * es) = *reinterpret_cast<const u32x2_t *>(&sO[row * OS + c + hh]);
         }
     }
 }
