@@ -46,9 +46,11 @@
  *     seqlen == 0 writes last_state := h0 (or zeros) and leaves y untouched.
  *   - Alignment: every pointer must be aligned to its element size (4 bytes
  *     for fp32 tensors, 2 bytes for bf16 tensors), else SSM_ERR_ALIGN.
- *   - Thread safety: the entry points keep no mutable global state and may be
- *     called concurrently on different streams -- except ssm_scan_fwd_noalloc,
- *     whose calls share one scratch array per GPU (see there).
+ *   - Thread safety: the entry points may be called concurrently on different
+ *     streams -- except ssm_scan_fwd_noalloc, whose calls share one scratch
+ *     array per GPU (see there).  Their only global state is created once
+ *     and guarded by locks: that scratch array's address, and the side stream
+ *     of ssm_scan_bwd (see there).
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -223,10 +225,20 @@ int ssm_state_update(float *state, const void *x, const void *delta, const float
  *                      when h0 is NULL: it is dL/d(initial state))
  *   The gradient of delta is taken through softplus when delta_softplus is set.
  *   Workspace: ssm_scan_bwd_workspace_bytes() (state checkpoints every 16
- *   steps and per-tile partial sums; 256-byte aligned).  Sums over channels
- *   and over the batch are added in a fixed order: results are deterministic.
- *   Limits: seqlen * d_inner and seqlen * d_state elements of one batch row
- *   must span less than 2 GiB, else SSM_ERR_SHAPE.
+ *   steps, per-tile partial sums and the carries of the time segments the
+ *   reverse sweep is cut into; 256-byte aligned).  Sums over channels, over
+ *   the batch and over segments are added in a fixed order, and the segments
+ *   depend on the shape alone: results are deterministic.
+ *   Limits: seqlen * d_inner and seqlen * d_state elements of one batch row,
+ *   and d_inner * d_state fp32 checkpoints of one 16-step block, must span
+ *   less than 2 GiB, else SSM_ERR_SHAPE.
+ *   Streams: part of the work (the segment carries, which do not depend on the
+ *   checkpoints) runs beside the checkpoint pass on a stream the library
+ *   creates once per device (default priority, never destroyed), forked from
+ *   `stream` and joined back into it by events; every kernel of the call is
+ *   ordered after the work enqueued on `stream` before it, and the work
+ *   enqueued on `stream` after it waits for all of them, also under graph
+ *   capture of `stream`.  ssm_scan_bwd_ckpt runs on `stream` alone.
  *   Edge cases: seqlen == 0 gives dh0 = dlast (or 0) and zero dA, dD,
  *   ddelta_bias; batch == 0 gives zero dA, dD, ddelta_bias; d_inner == 0
  *   gives zero dB, dC.

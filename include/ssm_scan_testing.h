@@ -30,6 +30,17 @@ int ssm_testing_scan_fwd_no_handoff(const void *x, const void *delta, const floa
                                     int64_t d_state, int io_dtype, void *workspace,
                                     size_t workspace_bytes, uint32_t spin_limit, void *stream);
 
+/*
+ * ssm_testing_bwd_segments -- how ssm_scan_bwd / ssm_scan_bwd_ckpt cut each
+ * (channel tile, batch row) sequence in time for the given shape: the number
+ * of segments (*segments, >= 1) and the 16-step blocks per segment
+ * (*blocks_per_segment; the last segment may be shorter).  A pure function of
+ * the shape and io dtype.  Same argument rules as
+ * ssm_scan_bwd_workspace_bytes; SSM_ERR_NULL for a null output pointer.
+ */
+int ssm_testing_bwd_segments(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                             int io_dtype, int *segments, int *blocks_per_segment);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan
            "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt", "ssm_causal_conv1d_fwd",
            "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd",
            "ssm_dt_proj", "ssm_scan_status", "ssm_testing_scan_fwd_no_handoff", "ssm_scan_fwd_noalloc",
-           "ssm_conv_scan_fwd", "ssm_conv_scan_workspace_bytes",
+           "ssm_conv_scan_fwd", "ssm_conv_scan_workspace_bytes", "ssm_testing_bwd_segments",
            "ssm_status_string", "ssm_abi_version")
 BENCH_LIB_PATH = os.path.join(PKG, "libssmbench.so")
 BENCH_EXPORTS = ("ssm_mb_copy", "ssm_mb_valu")
@@ -103,6 +103,9 @@ def _bind(lib):
                                                     _vp, _i64, _i64, _i64, _i64, _int, _vp, _sz,
                                                     ctypes.c_uint32, _vp]
     lib.ssm_testing_scan_fwd_no_handoff.restype = _int
+    lib.ssm_testing_bwd_segments.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_int),
+                                             ctypes.POINTER(_int)]
+    lib.ssm_testing_bwd_segments.restype = _int
     lib.ssm_status_string.argtypes = [_int]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_abi_version.argtypes = []

@@ -7,16 +7,32 @@
 // autograd) but print no backward: the kernels compute the exact reverse-mode
 // derivative of the forward definition, statement by statement.
 //
-// Three launches:
+// Four launches:
 //   1. checkpoints   -- the forward recurrence again, writing the state that
 //                       enters every block of kBT steps and no output: the
 //                       forward row kernel at d_state 16, ckpt_kernel else.
-//   2. bwd_kernel    -- walks the blocks from last to first.  For a block it
-//                       recomputes the kBT states from the checkpoint (kept in
-//                       registers), then runs the adjoint g = dL/dh backwards
-//                       through them:  g += dy C ;  contributions ;  g *= a.
-//   3. bwd_reduce    -- sums the per-tile partials of dB, dC (over channel
-//                       tiles) and of dA, dD, dbias (over the batch).
+//   2. bwd_carry     -- the sequence of every (channel tile, batch row) is cut
+//                       into S time segments.  For each segment but the first
+//                       this pass runs the adjoint alone (no contributions)
+//                       from zero at the segment's end to its start, and sums
+//                       Delta over the segment.  The adjoint is linear, so the
+//                       adjoint entering segment s from later times follows
+//                       from these in a fixed order:
+//                         carry_{S-1} = dL/dlast,
+//                         carry_{s-1} = glocal_s + exp(A sum_s Delta) carry_s.
+//   3. bwd_kernel    -- one workgroup per (tile, batch row, segment) walks the
+//                       segment's blocks from last to first, starting from its
+//                       carry.  For a block it recomputes the kBT states from
+//                       the checkpoint (kept in registers), then runs the
+//                       adjoint g = dL/dh backwards through them:
+//                       g += dy C ;  contributions ;  g *= a.
+//   4. bwd_reduce    -- sums the per-tile partials of dB, dC (over channel
+//                       tiles) and of dA, dD, dbias (over batch rows and
+//                       segments).
+// The segments exist for the chip's sake: a sweep is sequential in time, and
+// one workgroup per (tile, batch row) leaves most of the 256 CUs idle or
+// alone (a lone workgroup issues at about two thirds of the rate of a pair).
+// S is a function of the shape only, so results do not depend on the device.
 //
 // Work split of 1 and 2 (the forward general kernel's split): a workgroup of
 // four waves owns 64 channels of one batch row (lane = channel) for the whole
@@ -27,6 +43,8 @@
 // i.e. over the 64 lanes: a butterfly reduce-scatter (v_permlane32_swap,
 // v_permlane16_swap, then DPP row rotations and mirrors) leaves each lane one
 // channel-sum, written as a per-tile partial.  Results are deterministic.
+#include <mutex>
+
 #include "ssm_device.h"
 #include "ssm_kernels.h"
 
@@ -47,8 +65,11 @@ struct BwdParams {
     float *dAp;         // (batch, dim, N)
     float *dDp, *dbp;   // (batch, dim)
     float *dh0;         // (batch, dim, N) or null
+    float *glocal;      // (batch, S, dim, N): segment adjoints from zero (segments 1..S-1)
+    float *sdelta;      // (batch, S, dim): sum of Delta over each segment
     int64_t seqlen, dim;
     int n_dt, nblk, N, softplus;
+    int S, sblk;        // segments per sequence, blocks per segment (the last may be shorter)
 };
 
 __device__ __forceinline__ float sigmoid_f(float v) { return fast_rcp(1.0f + fast_exp2(-v * kLog2e)); }
@@ -224,21 +245,158 @@ __global__ __launch_bounds__(kBThreads) void ckpt_kernel(BwdParams p) {
 }
 
 // ===========================================================================
-// 2. the reverse sweep
+// 2. segment carries: the adjoint of each segment from zero at its end
 //
-// Two waves per SIMD (two workgroups per CU: 68 KB of LDS each) where the
-// registers allow it; the fp32 sweep over 16 states needs more than 256
-// registers per lane with the accurate expm1 and runs one wave per SIMD.
-template <typename IO, int NPW> struct BwdWaves { static constexpr int v = 2; };
-template <> struct BwdWaves<float, 4> { static constexpr int v = 1; };
+// One workgroup per (tile, batch row, segment s >= 1), the sweep's work split:
+// wave w owns states [w NPW, w NPW + NPW) of 64 channels (lane = channel) and
+// discretises steps 4w .. 4w+3 of each block (Delta and dL/d(pre-gate y),
+// shared through LDS, double buffered: one barrier per block).  Per step,
+// latest first:  g += dy' C ;  g *= exp(Delta A)  -- the sweep's own adjoint
+// without its contributions.
+template <typename IO, int NPW, bool GATE>
+__global__ __launch_bounds__(kBThreads) void bwd_carry_kernel(BwdParams p) {
+    using M = typename MathFor<IO>::type;
+    using R = typename Io<IO>::raw;
+    constexpr uint32_t es = sizeof(IO);
+    __shared__ float2 sG[2][kBT][kBTile];             // (Delta, dy')
+    __shared__ float sC[2][kBT][16];
+    __shared__ float sS[kBWaves][kBTile];
 
-template <typename IO, int NPW>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWaves<IO, NPW>::v, 2))) void bwd_kernel(BwdParams p) {
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int b = blockIdx.y;
+    const int seg = blockIdx.z + 1;
+    const int64_t T = p.seqlen, dim = p.dim;
+    const int N = p.N;
+    constexpr bool gate = GATE;
+    const int64_t ch = static_cast<int64_t>(blockIdx.x) * kBTile + lane;
+    const bool active = ch < dim;
+    const int64_t chc = active ? ch : dim - 1;
+    const int blk_lo = seg * p.sblk;
+    const int blk_hi = min(p.nblk, blk_lo + p.sblk);   // exclusive, > blk_lo
+
+    float A2[NPW], g[NPW];
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+        const int n = w * NPW + i;
+        A2[i] = n < N ? M::prep_A(p.A[chc * N + n]) : 0.0f;
+        g[i] = 0.0f;
+    }
+    const float bias = p.bias ? p.bias[chc] : 0.0f;
+
+    const int64_t row0 = static_cast<int64_t>(b) * T;
+    const uint32_t io_bytes = static_cast<uint32_t>(T * dim * es);
+    const int64_t ebase = row0 * dim * es;
+    const rsrc_t rd = make_rsrc(static_cast<const char *>(p.delta) + ebase, io_bytes);
+    const rsrc_t rz = make_rsrc(static_cast<const char *>(gate ? p.z : p.delta) + ebase, io_bytes);
+    const rsrc_t rg = make_rsrc(static_cast<const char *>(p.dout) + ebase, io_bytes);
+    const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * es, static_cast<uint32_t>(T * N * es));
+
+    struct Raw {
+        R d[4], z[4], g[4];
+        R c;
+    };
+    auto load_raw = [&](Raw &r, int blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t t = static_cast<int64_t>(blk) * kBT + 4 * w + k;
+            const uint32_t vo = (active && t < T) ? static_cast<uint32_t>((t * dim + ch) * es) : kOffNone;
+            r.d[k] = Io<IO>::load(rd, vo, 0);
+            r.z[k] = gate ? Io<IO>::load(rz, vo, 0) : R(0);
+            r.g[k] = Io<IO>::load(rg, vo, 0);
+        }
+        const int k = tid / 16, n = tid % 16;
+        const int64_t t = static_cast<int64_t>(blk) * kBT + k;
+        const uint32_t co = (n < N && t < T) ? static_cast<uint32_t>((t * N + n) * es) : kOffNone;
+        r.c = Io<IO>::load(rC, co, 0);
+    };
+    float dsum = 0.0f;                               // Delta over this wave's steps
+    auto produce = [&](const Raw &r, int blk, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kk = 4 * w + k;
+            const int64_t t = static_cast<int64_t>(blk) * kBT + kk;
+            const bool in = active && t < T;
+            const float v = Io<IO>::f32(r.d[k]) + bias;
+            float dt = p.softplus ? M::softplus(v) : v;
+            float dy = Io<IO>::f32(r.g[k]);
+            if (gate) {
+                const float zv = Io<IO>::f32(r.z[k]);
+                dy *= zv * sigmoid_f(zv);
+            }
+            dt = in ? dt : 0.0f;
+            dy = in ? dy : 0.0f;
+            dsum += dt;
+            sG[buf][kk][lane] = make_float2(dt, dy);
+        }
+        sC[buf][tid / 16][tid % 16] = Io<IO>::f32(r.c);
+    };
+
+    // A block's sweep is short next to a load's latency, so the raw inputs
+    // are loaded two blocks ahead, alternately into ra and rb: entering the
+    // sweep of block blk, r holds block blk - 1 (converted into LDS after the
+    // sweep) and the other set block blk - 2.
+    auto iteration = [&](int blk, Raw &r) __attribute__((always_inline)) {
+        const int cur = (blk_hi - 1 - blk) & 1;
+#pragma unroll
+        for (int k = kBT - 1; k >= 0; --k) {
+            const float2 q = sG[cur][k][lane];
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) {
+                g[i] = fmaf(q.y, sC[cur][k][w * NPW + i], g[i]);
+                g[i] = M::apply(M::factor(q.x * A2[i]), g[i], 0.0f);
+            }
+        }
+        if (blk > blk_lo) {
+            produce(r, blk - 1, cur ^ 1);
+            if (blk - 3 >= blk_lo) load_raw(r, blk - 3);
+        }
+        __syncthreads();
+    };
+    Raw ra, rb;
+    load_raw(ra, blk_hi - 1);
+    produce(ra, blk_hi - 1, 0);
+    if (blk_hi - 2 >= blk_lo) load_raw(ra, blk_hi - 2);
+    if (blk_hi - 3 >= blk_lo) load_raw(rb, blk_hi - 3);
+    __syncthreads();
+    for (int blk = blk_hi - 1; blk >= blk_lo; blk -= 2) {
+        iteration(blk, ra);
+        if (blk - 1 >= blk_lo) iteration(blk - 1, rb);
+    }
+
+    const int64_t row = static_cast<int64_t>(b) * p.S + seg;
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            const int n = w * NPW + i;
+            if (n < N) p.glocal[(row * dim + ch) * N + n] = g[i];
+        }
+    }
+    sS[w][lane] = dsum;
+    __syncthreads();
+    if (w == 0 && active) {
+        float t = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kBWaves; ++u) t += sS[u][lane];
+        p.sdelta[row * dim + ch] = t;
+    }
+}
+
+// ===========================================================================
+// 3. the reverse sweep
+//
+// Two waves per SIMD: two workgroups per CU (76 KB of LDS each), at most 256
+// registers per lane.
+constexpr int kBwdPerCU = 2;
+
+template <typename IO, int NPW, bool GATE>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(kBwdPerCU, kBwdPerCU))) void bwd_kernel(BwdParams p) {
     using M = typename MathFor<IO>::type;
     using R = typename Io<IO>::raw;
     constexpr uint32_t es = sizeof(IO);
     constexpr int V = PowV<NPW>::v;                   // dB / dC values per 4-step chunk, padded
     __shared__ float4 sP[kBT][kBTile];                // (Delta, Delta x, dL/d(pre-gate y), x)
+    __shared__ float2 sE[kBT][kBTile];                // (dDelta/d(delta), dL/dz per unit pre-gate y)
     __shared__ float sB[kBT][16], sC[kBT][16];
     __shared__ float2 sQ[kBWaves][kBT][kBTile];       // per-wave (dL/dDelta, dx) partials
     __shared__ float sY[kBWaves][kBT][kBTile];        // per-wave readout partials (for dz)
@@ -249,10 +407,14 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
     const int b = blockIdx.y;
     const int64_t T = p.seqlen, dim = p.dim;
     const int N = p.N;
-    const bool gate = p.z != nullptr;
+    constexpr bool gate = GATE;
     const int64_t ch = static_cast<int64_t>(blockIdx.x) * kBTile + lane;
     const bool active = ch < dim;
     const int64_t chc = active ? ch : dim - 1;
+
+    const int seg = blockIdx.z;
+    const int blk_lo = seg * p.sblk;
+    const int blk_hi = min(p.nblk, blk_lo + p.sblk);     // exclusive
 
     float A2[NPW], Ar[NPW], g[NPW], dA[NPW];
 #pragma unroll
@@ -263,6 +425,17 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
         A2[i] = M::prep_A(Ar[i]);
         g[i] = (vn && active && p.dlast) ? p.dlast[(b * dim + chc) * N + n] : 0.0f;
         dA[i] = 0.0f;
+    }
+    // the adjoint entering this segment from later times, later segments first
+    for (int j = p.S - 1; j > seg; --j) {
+        const int64_t row = static_cast<int64_t>(b) * p.S + j;
+        const float sd = p.sdelta[row * dim + chc];
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) {
+            const int n = w * NPW + i;
+            const float gl = n < N ? p.glocal[(row * dim + chc) * N + n] : 0.0f;
+            g[i] = M::apply(M::factor(sd * A2[i]), g[i], gl);
+        }
     }
     const float bias = p.bias ? p.bias[chc] : 0.0f;
     const float Dd = p.D ? p.D[chc] : 0.0f;
@@ -280,7 +453,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
     const uint32_t bc_bytes = static_cast<uint32_t>(T * N * es);
     const rsrc_t rB = make_rsrc(static_cast<const char *>(p.B) + row0 * N * es, bc_bytes);
     const rsrc_t rC = make_rsrc(static_cast<const char *>(p.C) + row0 * N * es, bc_bytes);
-    const float *ckb = p.ckpt + (static_cast<int64_t>(b) * p.nblk * dim + chc) * N;
+    // checkpoints of batch row b; one block's (dim x N fp32, < 2 GiB) are read
+    // through a descriptor of their own, lane offsets out of range for
+    // inactive lanes (loads return 0, no branch)
+    const float *ckrow = p.ckpt + static_cast<int64_t>(b) * p.nblk * dim * N;
+    const uint32_t ck_bytes = static_cast<uint32_t>(dim * N * 4);
+    const uint32_t ck_off = active ? static_cast<uint32_t>((ch * N + w * NPW) * 4) : kOffNone;
 
     // raw inputs of wave w's four steps of a block, B / C of (step tid/16,
     // state tid%16), and the checkpoint of the block
@@ -307,9 +485,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
         const uint32_t bo = (n < N && t < T) ? static_cast<uint32_t>((t * N + n) * es) : kOffNone;
         r.b = Io<IO>::load(rB, bo, 0);
         r.c = Io<IO>::load(rC, bo, 0);
+        const rsrc_t rck = make_rsrc(ckrow + static_cast<int64_t>(blk) * dim * N, ck_bytes);
 #pragma unroll
-        for (int i = 0; i < NPW; ++i)
-            r.ck[i] = (w * NPW + i < N && active) ? ckb[static_cast<int64_t>(blk) * dim * N + w * NPW + i] : 0.0f;
+        for (int i = 0; i < NPW; ++i) {
+            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rck, ck_off + 4 * i, 0, 0));
+            r.ck[i] = w * NPW + i < N ? v : 0.0f;
+        }
     };
     // per-(t, d) discretisation of wave w's steps, and B / C staging
     auto produce = [&](const Raw &r, int blk) __attribute__((always_inline)) {
@@ -321,14 +502,21 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
             const float xv = Io<IO>::f32(r.x[k]);
             const float v = Io<IO>::f32(r.d[k]) + bias;
             float dt = p.softplus ? M::softplus(v) : v;
-            float dy = Io<IO>::f32(r.g[k]);
+            const float dsp = p.softplus ? sigmoid_f(v) : 1.0f;     // dDelta / d(delta)
+            const float dout = Io<IO>::f32(r.g[k]);
+            float dy = dout, ez = 0.0f;
             if (gate) {
+                // y = y_pre SiLU(z): dL/dy_pre = dout SiLU(z), and
+                // dL/dz = dout y_pre s (1 + z (1 - s)), s = sigmoid(z)
                 const float zv = Io<IO>::f32(r.z[k]);
-                dy *= zv * sigmoid_f(zv);
+                const float sz = sigmoid_f(zv);
+                dy *= zv * sz;
+                ez = dout * sz * fmaf(zv, 1.0f - sz, 1.0f);
             }
             dt = in ? dt : 0.0f;
             dy = in ? dy : 0.0f;
             sP[kk][lane] = make_float4(dt, dt * xv, dy, xv);
+            sE[kk][lane] = make_float2(dsp, ez);
         }
         sB[tid / 16][tid % 16] = Io<IO>::f32(r.b);
         sC[tid / 16][tid % 16] = Io<IO>::f32(r.c);
@@ -383,14 +571,15 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
                 for (int i = 0; i < NPW; ++i) {
                     const float bk = sB[st][w * NPW + i], ck = sC[st][w * NPW + i];
                     g[i] = fmaf(q.z, ck, g[i]);                      // dL/dh_t
-                    const float ah = M::apply(fk[k][i], hs[k][i], 0.0f);   // a_t h_{t-1}
-                    const float qa = g[i] * ah;
-                    ddt = fmaf(qa, Ar[i], ddt);
-                    dA[i] = fmaf(qa, q.x, dA[i]);
                     sgb = fmaf(g[i], bk, sgb);
                     vB[kk * NPW + i] = g[i] * q.y;
                     vC[kk * NPW + i] = q.z * hs[k + 1][i];
-                    g[i] = M::apply(fk[k][i], g[i], 0.0f);           // dL/dh_{t-1}
+                    g[i] = M::apply(fk[k][i], g[i], 0.0f);           // dL/dh_{t-1} = a_t dL/dh_t
+                    // dL/d(Delta A) of this step: g a_t h_{t-1}, i.e. the
+                    // decayed adjoint times the previous state
+                    const float qa = g[i] * hs[k][i];
+                    ddt = fmaf(qa, Ar[i], ddt);
+                    dA[i] = fmaf(qa, q.x, dA[i]);
                 }
                 sQ[w][st][lane] = make_float2(fmaf(sgb, q.w, ddt), sgb * q.x);
             }
@@ -399,14 +588,20 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
         }
     };
 
-    Raw cur, nxt;
-    if (p.nblk > 0) {
-        load_raw(cur, p.nblk - 1);
-        produce(cur, p.nblk - 1);
+    // one set of raw inputs: those of the next block (earlier in time) are in
+    // flight during a block's sweep and converted into LDS after it; what the
+    // per-step finish needs was staged by produce, the checkpoint kept apart
+    Raw raw;
+    float ck[NPW];
+    if (blk_hi > blk_lo) {
+        load_raw(raw, blk_hi - 1);
+        produce(raw, blk_hi - 1);
     }
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) ck[i] = raw.ck[i];
     __syncthreads();
-    for (int blk = p.nblk - 1; blk >= 0; --blk) {
-        if (blk > 0) load_raw(nxt, blk - 1);     // in flight during the sweep
+    for (int blk = blk_hi - 1; blk >= blk_lo; --blk) {
+        if (blk > blk_lo) load_raw(raw, blk - 1);   // in flight during the sweep
 
         // ---- the block in two halves of kBT / 2 steps, the later half first:
         // the state entering the later half is recomputed (not kept) from the
@@ -414,7 +609,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
         // registers while the adjoint runs back through it
         float hmid[NPW];
 #pragma unroll
-        for (int i = 0; i < NPW; ++i) hmid[i] = cur.ck[i];
+        for (int i = 0; i < NPW; ++i) hmid[i] = ck[i];
 #pragma unroll
         for (int k = 0; k < kBT / 2; ++k) {
             const float4 q = sP[k][lane];
@@ -422,7 +617,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
             for (int i = 0; i < NPW; ++i) hmid[i] = M::step(q.x * A2[i], hmid[i], q.y * sB[k][w * NPW + i]);
         }
         sweep_half(kBT / 2, hmid, blk);
-        sweep_half(0, cur.ck, blk);
+        sweep_half(0, ck, blk);
         __syncthreads();
 
         // ---- finish wave w's steps: sum the four waves' partials in order
@@ -432,6 +627,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
             const int64_t t = static_cast<int64_t>(blk) * kBT + kk;
             const bool in = active && t < T;
             const float4 q = sP[kk][lane];
+            const float2 e = sE[kk][lane];
             float ddt = 0.0f, dxs = 0.0f, yv = 0.0f;
 #pragma unroll
             for (int u = 0; u < kBWaves; ++u) {
@@ -440,39 +636,35 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
                 dxs += s.y;
                 if (gate) yv += sY[u][kk][lane];
             }
-            const float v = Io<IO>::f32(cur.d[k]) + bias;
-            const float dv = p.softplus ? ddt * sigmoid_f(v) : ddt;
+            const float dv = ddt * e.x;
             const float dxv = fmaf(q.z, Dd, dxs);
             const uint32_t vo = step_off(blk, k);
             Io<IO>::store(dxv, rdx, vo, 0);
             Io<IO>::store(dv, rdd, vo, 0);
-            if (gate) {
-                const float zv = Io<IO>::f32(cur.z[k]);
-                const float s = sigmoid_f(zv);
-                const float yfull = fmaf(Dd, q.w, yv);
-                const float dzv = Io<IO>::f32(cur.g[k]) * yfull * s * fmaf(zv, 1.0f - s, 1.0f);
-                Io<IO>::store(dzv, rdz, vo, 0);
-            }
+            if (gate) Io<IO>::store(e.y * fmaf(Dd, q.w, yv), rdz, vo, 0);   // dL/dz
             if (in) {
                 dD_acc = fmaf(q.z, q.w, dD_acc);
                 db_acc += dv;
             }
         }
-        if (blk > 0) {
-            produce(nxt, blk - 1);
-            cur = nxt;
+        if (blk > blk_lo) {
+            produce(raw, blk - 1);
+#pragma unroll
+            for (int i = 0; i < NPW; ++i) ck[i] = raw.ck[i];
         }
         __syncthreads();
     }
 
-    // ---- per-chain and per-(b, d) results
+    // ---- per-chain and per-(b, d) results: partials of this segment; the
+    // first segment's final adjoint is dL/dh0
+    const int64_t prow = static_cast<int64_t>(b) * p.S + seg;
     if (active) {
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
             const int n = w * NPW + i;
             if (n < N) {
-                p.dAp[(b * dim + ch) * N + n] = dA[i];
-                if (p.dh0) p.dh0[(b * dim + ch) * N + n] = g[i];
+                p.dAp[(prow * dim + ch) * N + n] = dA[i];
+                if (p.dh0 && seg == 0) p.dh0[(b * dim + ch) * N + n] = g[i];
             }
         }
     }
@@ -485,19 +677,20 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(BwdWa
             sd += sAcc[u][lane].x;
             sb += sAcc[u][lane].y;
         }
-        p.dDp[b * dim + ch] = sd;
-        p.dbp[b * dim + ch] = sb;
+        p.dDp[prow * dim + ch] = sd;
+        p.dbp[prow * dim + ch] = sb;
     }
 }
 
 // ===========================================================================
-// 3. reductions: dB, dC over the channel tiles; dA, dD, dbias over the batch
+// 4. reductions: dB, dC over the channel tiles; dA, dD, dbias over the rows
+// of partials (batch row x segment)
 struct ReduceParams {
     const float *dBp, *dCp, *dAp, *dDp, *dbp;
     void *dB, *dC;
     float *dA, *dD, *dbias;
     int64_t n_btn, n_dn, dim;
-    int n_dt, batch;
+    int n_dt, rows;          // rows of dA / dD / dbias partials: batch x segments
 };
 
 template <typename T>
@@ -514,12 +707,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ReduceParams r) {
     }
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < r.n_dn; e += stride) {
         float s = 0.0f;
-        for (int bb = 0; bb < r.batch; ++bb) s += r.dAp[bb * r.n_dn + e];
+        for (int bb = 0; bb < r.rows; ++bb) s += r.dAp[bb * r.n_dn + e];
         r.dA[e] = s;
     }
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < r.dim; e += stride) {
         float sd = 0.0f, sb = 0.0f;
-        for (int bb = 0; bb < r.batch; ++bb) {
+        for (int bb = 0; bb < r.rows; ++bb) {
             sd += r.dDp[bb * r.dim + e];
             sb += r.dbp[bb * r.dim + e];
         }
@@ -528,10 +721,94 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(ReduceParams r) {
     }
 }
 
+// ---- segments
+// Cost model of a segmentation, in units of one block swept by one of a pair
+// of workgroups sharing a CU: rounds of kBwdCUs x per_cu workgroups, a lone
+// workgroup on a CU at 1.58 / 2 of a pair's time (measured: one workgroup per
+// CU runs 1.58x slower per unit of work than two), a prologue of about a
+// quarter block plus the carry combination, and the carry pass at about a
+// fifth of the sweep per block it covers.  S depends on the shape only.
+constexpr int kBwdCUs = 256;
+constexpr int kBwdMaxSeg = 64;
+struct BwdPlan {
+    int S, sblk;
+};
+BwdPlan bwd_plan(int64_t units0, int64_t nblk, int per_cu) {
+    BwdPlan best{1, static_cast<int>(nblk)};
+    if (nblk <= 1 || units0 <= 0) return best;
+    const int64_t slots = static_cast<int64_t>(kBwdCUs) * per_cu;
+    double best_cost = 0.0;
+    const int64_t smax = nblk < kBwdMaxSeg ? nblk : kBwdMaxSeg;
+    for (int64_t S = 1; S <= smax; ++S) {
+        const int64_t sblk = (nblk + S - 1) / S;
+        if ((nblk + sblk - 1) / sblk != S) continue;   // the same split as a smaller S
+        const int64_t units = units0 * S;
+        const int64_t full = units / slots, rem = units % slots;
+        const double rounds = static_cast<double>(full) +
+                              (rem == 0 ? 0.0 : ((per_cu == 2 && rem <= kBwdCUs) ? 0.79 : 1.0));
+        const double cost = rounds * (static_cast<double>(sblk) + 0.25 + 0.02 * static_cast<double>(S)) +
+                            0.2 * static_cast<double>(units0) * static_cast<double>(nblk - sblk) /
+                                static_cast<double>(slots);
+        if (S == 1 || cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = BwdPlan{static_cast<int>(S), static_cast<int>(sblk)};
+        }
+    }
+    return best;
+}
+
+// ---- the side stream
+// When the backward computes its own checkpoints, the carry pass (which reads
+// delta, z, dL/dy and C) does not depend on them and runs beside the
+// checkpoint pass on a library-owned stream of each device, at the default
+// priority.  The checkpoint pass is one persistent workgroup per CU (116
+// registers, 21 KB of LDS), so up to two carry workgroups share each CU with it
+// and use issue slots a lone wave per SIMD leaves idle.  The fork and the join
+// are events recorded on the caller's stream and on the side stream; the whole
+// enqueue sequence of one call runs under a lock, so concurrent calls from
+// several host threads cannot interleave their fork and join records.
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// the current device's side stream and events, created on first use unless
+// `create` is false (then *out is null when they do not exist yet); the
+// caller holds g_side_mu
+hipError_t side_stream(SideStream **out, bool create) {
+    *out = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    if (!ss.stream) {
+        if (!create) return hipSuccess;
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+            if (f) (void)hipEventDestroy(f);
+            (void)hipStreamDestroy(st);
+            return e;
+        }
+        ss.stream = st;
+        ss.fork = f;
+        ss.join = j;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
 // ---- workspace
 struct BwdLayout {
     int64_t nblk, n_dt;
-    size_t fwd_off, fwd_bytes, ckpt_off, dBp_off, dCp_off, dAp_off, dDp_off, dbp_off, total;
+    BwdPlan plan;
+    size_t fwd_off, fwd_bytes, ckpt_off, dBp_off, dCp_off, dAp_off, dDp_off, dbp_off, gl_off, sd_off, total;
 };
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // At d_state 16 the checkpoints come from the forward row kernel (run with no
@@ -546,6 +823,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int 
     BwdLayout l;
     l.nblk = (seqlen + kBT - 1) / kBT;
     l.n_dt = (dim + kBTile - 1) / kBTile;
+    l.plan = bwd_plan(l.n_dt * batch, l.nblk, kBwdPerCU);
+    const size_t rows = size_t(batch) * l.plan.S;
     size_t o = 0;
     l.fwd_off = 0;
     l.fwd_bytes = (ckpt_by_forward(N) && batch > 0 && dim > 0 && seqlen > 0)
@@ -554,9 +833,12 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int64_t N, int 
     l.ckpt_off = o; o = align256(o + sizeof(float) * size_t(batch) * l.nblk * dim * N);
     l.dBp_off = o;  o = align256(o + sizeof(float) * size_t(l.n_dt) * batch * seqlen * N);
     l.dCp_off = o;  o = align256(o + sizeof(float) * size_t(l.n_dt) * batch * seqlen * N);
-    l.dAp_off = o;  o = align256(o + sizeof(float) * size_t(batch) * dim * N);
-    l.dDp_off = o;  o = align256(o + sizeof(float) * size_t(batch) * dim);
-    l.dbp_off = o;  o = align256(o + sizeof(float) * size_t(batch) * dim);
+    l.dAp_off = o;  o = align256(o + sizeof(float) * rows * dim * N);
+    l.dDp_off = o;  o = align256(o + sizeof(float) * rows * dim);
+    l.dbp_off = o;  o = align256(o + sizeof(float) * rows * dim);
+    const size_t grows = l.plan.S > 1 ? rows : 0;
+    l.gl_off = o;   o = align256(o + sizeof(float) * grows * dim * N);
+    l.sd_off = o;   o = align256(o + sizeof(float) * grows * dim);
     l.total = o;
     return l;
 }
@@ -578,11 +860,60 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
     p.dDp = reinterpret_cast<float *>(ws + l.dDp_off);
     p.dbp = reinterpret_cast<float *>(ws + l.dbp_off);
     p.dh0 = a.dh0;
+    p.glocal = reinterpret_cast<float *>(ws + l.gl_off);
+    p.sdelta = reinterpret_cast<float *>(ws + l.sd_off);
     p.seqlen = a.seqlen; p.dim = a.dim;
     p.n_dt = static_cast<int>(l.n_dt); p.nblk = static_cast<int>(l.nblk);
     p.N = static_cast<int>(a.dstate); p.softplus = a.softplus;
+    p.S = l.plan.S; p.sblk = l.plan.sblk;
     if (l.n_dt > 0 && a.batch > 0) {
         const dim3 grid(static_cast<unsigned>(l.n_dt), static_cast<unsigned>(a.batch));
+        const dim3 cgrid(static_cast<unsigned>(l.n_dt), static_cast<unsigned>(a.batch),
+                         static_cast<unsigned>(p.S - 1));
+        auto launch_carry = [&](hipStream_t st) {
+            if (a.z) hipLaunchKernelGGL((bwd_carry_kernel<T, NPW, true>), cgrid, dim3(kBThreads), 0, st, p);
+            else hipLaunchKernelGGL((bwd_carry_kernel<T, NPW, false>), cgrid, dim3(kBThreads), 0, st, p);
+            return hipGetLastError();
+        };
+        // the carry pass beside the checkpoint pass (side stream), or before
+        // the sweep on the caller's stream when the checkpoints are given
+        std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+        SideStream *side = nullptr;
+        bool beside = p.S > 1 && !a.ckpt_in;
+        // once the carry pass is on the side stream, the caller's stream waits
+        // for it on every way out, errors included (the caller may free the
+        // buffers it reads as soon as its stream says so)
+        bool forked = false;
+        auto join = [&]() -> hipError_t {
+            if (!forked) return hipSuccess;
+            forked = false;
+            const hipError_t e = hipStreamWaitEvent(s, side->join, 0);
+            side_lock.unlock();
+            return e;
+        };
+        if (beside) {
+            // creating a stream or an event may be refused while `s` is being
+            // captured into a graph: a capture before any uncaptured call on
+            // this device runs the carry pass on `s` instead
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            hipError_t e = hipStreamIsCapturing(s, &cs);
+            if (e != hipSuccess) return e;
+            side_lock.lock();
+            e = side_stream(&side, cs == hipStreamCaptureStatusNone);
+            if (e != hipSuccess) return e;
+            beside = side != nullptr;
+        }
+        if (beside) {
+            hipError_t e = hipEventRecord(side->fork, s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+            if (e == hipSuccess) e = launch_carry(side->stream);
+            if (e == hipSuccess) {
+                e = hipEventRecord(side->join, side->stream);
+                if (e != hipSuccess) (void)hipStreamSynchronize(side->stream);
+            }
+            if (e != hipSuccess) return e;
+            forked = true;
+        }
         if (a.ckpt_in) {
             // nothing to do: the forward recorded them
         } else if (ckpt_by_forward(a.dstate)) {
@@ -595,12 +926,26 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
             f.ckpt = p.ckpt;
             if (a.seqlen > 0) {
                 const hipError_t e = launch_scan_fwd(f, s);
-                if (e != hipSuccess) return e;
+                if (e != hipSuccess) {
+                    (void)join();
+                    return e;
+                }
             }
         } else {
             hipLaunchKernelGGL((ckpt_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
         }
-        hipLaunchKernelGGL((bwd_kernel<T, NPW>), grid, dim3(kBThreads), 0, s, p);
+        if (beside) {
+            const hipError_t e = join();
+            if (e != hipSuccess) return e;
+        } else if (p.S > 1) {
+            if (side_lock.owns_lock()) side_lock.unlock();
+            const hipError_t e = launch_carry(s);
+            if (e != hipSuccess) return e;
+        }
+        const dim3 sgrid(static_cast<unsigned>(l.n_dt), static_cast<unsigned>(a.batch),
+                         static_cast<unsigned>(p.S));
+        if (a.z) hipLaunchKernelGGL((bwd_kernel<T, NPW, true>), sgrid, dim3(kBThreads), 0, s, p);
+        else hipLaunchKernelGGL((bwd_kernel<T, NPW, false>), sgrid, dim3(kBThreads), 0, s, p);
     }
     ReduceParams r;
     r.dBp = p.dBp; r.dCp = p.dCp; r.dAp = p.dAp; r.dDp = p.dDp; r.dbp = p.dbp;
@@ -609,7 +954,7 @@ template <typename T, int NPW> hipError_t launch_bwd_t(const BwdArgs &a, hipStre
     r.n_dn = a.dim * a.dstate;
     r.dim = a.dim;
     r.n_dt = static_cast<int>(l.n_dt);
-    r.batch = static_cast<int>(a.batch);
+    r.rows = static_cast<int>(a.batch * l.plan.S);
     const int64_t most = r.n_btn > r.n_dn ? r.n_btn : r.n_dn;
     const int64_t blocks = (most + 255) / 256;
     hipLaunchKernelGGL(bwd_reduce_kernel<T>, dim3(static_cast<unsigned>(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096)),
@@ -655,6 +1000,13 @@ template <typename T> hipError_t launch_bwd_npw(const BwdArgs &a, hipStream_t s)
 
 size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16) {
     return bwd_layout(batch, seqlen, dim, dstate, bf16).total;
+}
+
+void scan_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16, int *segments,
+                   int *blocks_per_segment) {
+    const BwdLayout l = bwd_layout(batch, seqlen, dim, dstate, bf16);
+    *segments = l.plan.S;
+    *blocks_per_segment = l.plan.sblk;
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {

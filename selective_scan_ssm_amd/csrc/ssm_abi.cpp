@@ -324,6 +324,8 @@ int scan_bwd_impl(const void *x, const void *delta, const float *delta_bias, int
     if (mul3(seqlen, d_inner, static_cast<int64_t>(es)) > lim ||
         mul3(seqlen, d_state, static_cast<int64_t>(es)) > lim)
         return SSM_ERR_SHAPE;
+    // and the checkpoints of one block (d_inner x d_state fp32)
+    if (mul3(d_inner, d_state, 4) > lim) return SSM_ERR_SHAPE;
     // required pointers, for whatever this shape reads or writes
     if (n_dn > 0 && (!A || !dA)) return SSM_ERR_NULL;
     if (n_btd > 0 && (!x || !delta || !dout || !dx || !ddelta)) return SSM_ERR_NULL;
@@ -641,6 +643,16 @@ int ssm_testing_scan_fwd_no_handoff(const void *x, const void *delta, const floa
     if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
     if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
     return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_testing_bwd_segments(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                             int io_dtype, int *segments, int *blocks_per_segment) {
+    if (!segments || !blocks_per_segment) return SSM_ERR_NULL;
+    if (check_dtype(io_dtype)) return SSM_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > SSM_MAX_D_STATE)
+        return SSM_ERR_SHAPE;
+    ssm::scan_bwd_plan(batch, seqlen, d_inner, d_state, io_dtype == SSM_BF16, segments, blocks_per_segment);
+    return SSM_OK;
 }
 
 }  // extern "C"

@@ -94,6 +94,9 @@ struct BwdArgs {
 
 // Backward of the forward scan, 1 <= dstate <= 16.
 size_t scan_bwd_workspace(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16);
+// the time segments of the backward's sweep for a shape (segments, blocks each)
+void scan_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int bf16, int *segments,
+                   int *blocks_per_segment);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 // The forward that also records the state entering every 16-step block in
 // a.ckpt, (batch, ceil(seqlen / 16), dim, dstate) fp32, the layout the

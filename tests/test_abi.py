@@ -248,14 +248,44 @@ def test_bwd_alias_detection(lib):
 
 
 def test_bwd_workspace_sizes(lib):
-    # checkpoints every 16 steps + per-tile partials of dB, dC + per-row sums
+    # checkpoints every 16 steps + per-tile partials of dB, dC + per-(row,
+    # segment) partials of dA, dD, dbias and the segment carries (glocal,
+    # sum of Delta): the sweep cuts each sequence into 8 segments at this shape
     need = lib.ssm_scan_bwd_workspace_bytes(4, 8192, 5120, 16, BF16)
     ckpt = 4 * 512 * 5120 * 16 * 4
     parts = 2 * 80 * 4 * 8192 * 16 * 4
-    assert ckpt + parts <= need < ckpt + parts + (4 << 20)
+    segs = 4 * 8 * 5120 * (2 * 16 + 3) * 4
+    assert ckpt + parts + segs <= need < ckpt + parts + segs + (4 << 20)
     assert lib.ssm_scan_bwd_workspace_bytes(2, 16, 8, 0, F32) == (1 << 64) - 1
     assert lib.ssm_scan_bwd_workspace_bytes(2, 16, 8, 4, 9) == (1 << 64) - 1
     assert lib.ssm_scan_bwd_workspace_bytes(0, 0, 0, 4, F32) == 0
+
+
+def bwd_segments(lib, batch, seqlen, dim, N, io):
+    S, sblk = ctypes.c_int(-1), ctypes.c_int(-1)
+    r = lib.ssm_testing_bwd_segments(batch, seqlen, dim, N, io, ctypes.byref(S), ctypes.byref(sblk))
+    return r, S.value, sblk.value
+
+
+def test_bwd_segments(lib):
+    # the layer shapes: 80 x 4 and 24 x 8 (tile, batch row) sequences, 8
+    # segments each (2560 and 1536 workgroups: whole rounds of 2 per CU)
+    assert bwd_segments(lib, 4, 8192, 5120, 16, BF16) == (OK, 8, 64)
+    assert bwd_segments(lib, 8, 2048, 1536, 16, BF16) == (OK, 8, 16)
+    # one block, or nothing: one segment
+    assert bwd_segments(lib, 2, 16, 70, 16, F32)[:2] == (OK, 1)
+    assert bwd_segments(lib, 2, 0, 70, 16, F32)[:2] == (OK, 1)
+    assert bwd_segments(lib, 0, 100, 70, 16, F32)[:2] == (OK, 1)
+    # every split covers the blocks exactly once, at most 64 segments
+    for shape in [(2, 100, 130, 4, F32), (1, 200_000, 5120, 16, BF16), (3, 1000, 96, 1, F32),
+                  (2, 300, 200, 16, BF16), (1, 77, 70, 16, F32), (64, 4096, 5120, 16, BF16),
+                  (1, 33, 1, 16, F32)]:
+        r, S, sblk = bwd_segments(lib, *shape)
+        nblk = (shape[1] + 15) // 16
+        assert r == OK and 1 <= S <= 64 and (S - 1) * sblk < nblk <= S * sblk, (shape, S, sblk)
+    assert bwd_segments(lib, 2, 16, 8, 0, F32)[0] == ESHAPE
+    assert bwd_segments(lib, 2, 16, 8, 4, 7)[0] == EDTYPE
+    assert lib.ssm_testing_bwd_segments(2, 16, 8, 4, F32, None, None) == ENULL
 
 
 # ------------------------------------------------------- causal conv1d

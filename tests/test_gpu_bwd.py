@@ -101,9 +101,20 @@ def compare(g, o, io, keys, tag):
         assert e <= tol_for(io, k), (tag, k, e)
 
 
+def segments(inp):
+    """(segments, blocks per segment) of the backward's time split for inp's shape."""
+    import ctypes
+    from selective_scan_ssm_amd import _lib
+    S, sblk = ctypes.c_int(0), ctypes.c_int(0)
+    io = _lib.SSM_BF16 if inp["io"] == gen.BF16 else _lib.SSM_F32
+    assert _lib.load().ssm_testing_bwd_segments(inp["batch"], inp["seqlen"], inp["d_inner"], inp["d_state"],
+                                                io, ctypes.byref(S), ctypes.byref(sblk)) == 0
+    return S.value, sblk.value
+
+
 def check_bwd(inp, softplus=True, with_dlast=True, seed=0, tag=""):
     G.say(f"[bwd] {tag} B={inp['batch']} T={inp['seqlen']} D={inp['d_inner']} N={inp['d_state']} "
-          f"io={inp['io']}")
+          f"io={inp['io']} segments={segments(inp)}")
     dout, dlast = grads_inputs(inp, seed, with_dlast)
     g = run_bwd_gpu(inp, dout, dlast, softplus)
     o = run_bwd_oracle(inp, dout, dlast, softplus)
@@ -135,6 +146,26 @@ def test_bwd_sm1_shape_long():
     # d_state 1 over a long sequence (the SM1 distributions: fast decays, h0 ~ N(0,1))
     inp = gen.make_inputs(2, 1000, 96, 1, io=gen.F32, a_kind="sm1", h0_kind="normal", seed=413)
     check_bwd(inp, seed=13, tag="f32-sm1-long")
+
+
+@pytest.mark.parametrize("T,io", [(16, gen.F32), (9, gen.BF16)])
+def test_bwd_one_segment(T, io):
+    # a sequence of one block is swept by one segment (no carry pass)
+    inp = gen.make_inputs(2, T, 130, 16, io=io, h0_kind="normal", seed=416 + T)
+    assert segments(inp)[0] == 1
+    check_bwd(inp, seed=16 + T, tag=f"one-segment-T{T}")
+
+
+@pytest.mark.parametrize("T,io,N", [(1000, gen.F32, 16), (4000, gen.BF16, 16), (1500, gen.F32, 5)])
+def test_bwd_many_segments(T, io, N):
+    # long rows of few tiles: many segments, the last one ragged, so every
+    # segment's incoming adjoint comes through the carry pass; A = -(n+1)
+    # and the SM1 draw A = -exp(U(-4, 1)) (decays as slow as 0.018 per unit Delta)
+    inp = gen.make_inputs(1, T, 70, N, io=io, a_kind="sm1" if N != 16 else "hippo", h0_kind="normal",
+                          seed=430 + N)
+    S, sblk = segments(inp)
+    assert S > 8 and S * sblk * 16 > T, (S, sblk)
+    check_bwd(inp, seed=30 + N, tag=f"segments-{S}x{sblk}")
 
 
 def test_bwd_empty_sequence():

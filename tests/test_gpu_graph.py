@@ -105,3 +105,24 @@ def test_graph_backward_with_checkpoints():
         t["dout"].copy_(torch.randn(t["dout"].shape, device="cuda").to(torch.bfloat16))
         t["x"].copy_(torch.randn(t["x"].shape, device="cuda").to(torch.bfloat16))
     replay_matches_eager(st, fn, refill)
+
+
+def test_graph_backward_self_contained():
+    """ssm_scan_bwd computing its own checkpoints: its carry pass runs on the
+    library's side stream, forked from and joined back into the captured
+    stream; the captured call replays equal to eager calls."""
+    from selective_scan_ssm_amd import ops
+    inp = gen.make_inputs(2, 200, 128, 16, io=gen.BF16, h0_kind="normal", seed=64)
+    st = G.device_inputs(inp)
+    st["dout"] = torch.randn(st["x"].shape, device="cuda").to(torch.bfloat16)
+    st["dlast"] = torch.randn(st["h0"].shape, device="cuda")
+
+    def fn(t):
+        g = ops.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], t["dout"], D=t["D"], z=t["z"],
+                         delta_bias=t["delta_bias"], h0=t["h0"], dlast=t["dlast"])
+        return [v for v in g.values() if v is not None]
+
+    def refill(t, r):
+        t["dout"].copy_(torch.randn(t["dout"].shape, device="cuda").to(torch.bfloat16))
+        t["delta"].copy_(torch.randn(t["delta"].shape, device="cuda").to(torch.bfloat16))
+    replay_matches_eager(st, fn, refill)
