@@ -147,7 +147,12 @@ template <int K> __device__ __forceinline__ float row_bcast(float v) {
 
 // acc += (lane K of each row of c) * h as a single v_fmac_f32 with a DPP
 // source (the compiler folds DPP into v_mul but not into v_fmac).  c must
-// come from a load, not from a VALU write just before (DPP read hazard).
+// come from a load, not from a VALU write just before: on gfx9 a VALU write
+// needs two wait states before a DPP read of the same VGPR, and the compiler's
+// hazard recognizer does not see inside inline assembly.  Every caller passes
+// a value read from LDS; tests/test_dpp_hazards.py disassembles the built
+// library and fails if any DPP source is written by a VALU within two wait
+// states (an s_nop 1 here would cost two wait states per broadcast fma).
 template <int K> __device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
     asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
         : "+v"(acc) : "v"(c), "v"(h), "n"(K));
