@@ -90,12 +90,21 @@ SOURCES = {
     "decode": ["selective_scan_ssm_amd/csrc/state_update.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "conv": ["selective_scan_ssm_amd/csrc/conv1d.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "ssd": ["selective_scan_ssm_amd/csrc/ssd_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "ssdline": ["selective_scan_ssm_amd/csrc/ssd_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "dtproj": ["selective_scan_ssm_amd/csrc/dt_proj.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
 # the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
                  "decode": "state_update_rows_kernel", "conv": "conv1d_kernel", "ssd": "ssd_chunk_kernel",
-                 "dtproj": "dt_proj_kernel"}
+                 "ssdline": "ssd_line_kernel", "dtproj": "dt_proj_kernel"}
+
+
+def ssd_kind(w):
+    """The kernel ssd_scan_fwd runs on an SSD workload: the whole-line kernel
+    for bf16 io, head sizes that are multiples of 64 and d_state up to 64,
+    the chunk kernel otherwise."""
+    from selective_scan_ssm_amd import inputs as gen
+    return "ssdline" if (w.io == gen.BF16 and w.headdim % 64 == 0 and w.d_state <= 64) else "ssd"
 
 
 def grid_of(spec, seqlen):
@@ -952,8 +961,8 @@ def bench_ssd(args, dev):
     call_ms = float(np.mean(step_ms))
     hbm = alg / (call_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("ssd", w.name),
-            "kernel": "ssd_scan_fwd (ssd_chunk_kernel)",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(ssd_kind(w), w.name),
+            "kernel": f"ssd_scan_fwd ({KERNEL_PREFIX[ssd_kind(w)]})",
             "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
             "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
             "algorithmic_bytes_per_launch": alg}
@@ -1200,7 +1209,7 @@ def main():
         wl, fd, wd, cfd, cwd, kcmd, ccmd = args.summarize_traffic
         if wl.startswith("ssd:"):      # "ssd:NAME": the Mamba-2 scan on that layer shape
             w = gen.SSD_WORKLOADS[wl[4:]]
-            kind, wname = "ssd", w.name
+            kind, wname = ssd_kind(w), w.name
             alg = ssd_algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
         elif wl.startswith("dtproj"):  # "dtproj3": dt_proj of workload 3's layer
             w = gen.WORKLOADS[int(wl[6:])]
