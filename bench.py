@@ -92,11 +92,20 @@ SOURCES = {
     "ssd": ["selective_scan_ssm_amd/csrc/ssd_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "ssdline": ["selective_scan_ssm_amd/csrc/ssd_scan.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
     "dtproj": ["selective_scan_ssm_amd/csrc/dt_proj.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
+    "dtprojrows": ["selective_scan_ssm_amd/csrc/dt_proj.hip", "selective_scan_ssm_amd/csrc/ssm_device.h"],
 }
 # the forward scan runs scan_rows_kernel at d_state 16 and scan_fwd_kernel otherwise
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
                  "decode": "state_update_rows_kernel", "conv": "conv1d_kernel", "ssd": "ssd_chunk_kernel",
-                 "ssdline": "ssd_line_kernel", "dtproj": "dt_proj_kernel"}
+                 "ssdline": "ssd_line_kernel", "dtproj": "dt_proj_kernel", "dtprojrows": "dt_proj_rows_kernel"}
+
+
+def dtproj_kind(w):
+    """The kernel ssm_dt_proj runs on a workload's layer: the persistent
+    W-resident kernel for bf16 io and dt_rank <= 160, the tiled one otherwise."""
+    from selective_scan_ssm_amd import inputs as gen
+    _, rank, _, _ = dtproj_shape(w)
+    return "dtprojrows" if (w.io == gen.BF16 and rank <= 160) else "dtproj"
 
 
 def ssd_kind(w):
@@ -691,8 +700,8 @@ def bench_dtproj(args, dev):
     name = w.name + "-dt_proj"
     mfma_peak = 2500.0 if io == gen.BF16 else 157.3
     roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("dtproj", name),
-            "kernel": "ssm_dt_proj (dt_proj_kernel)",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(dtproj_kind(w), name),
+            "kernel": f"ssm_dt_proj ({KERNEL_PREFIX[dtproj_kind(w)]})",
             "launch_ms_mean": round(call_ms, 5), "launch_ms_min": round(min(step_ms), 5),
             "launch_ms_median": round(float(np.median(step_ms)), 5), "launch_ms_max": round(max(step_ms), 5),
             "algorithmic_bytes_per_launch": alg,
@@ -1213,7 +1222,7 @@ def main():
             alg = ssd_algorithmic_bytes(w, 2 if w.io == gen.BF16 else 4)
         elif wl.startswith("dtproj"):  # "dtproj3": dt_proj of workload 3's layer
             w = gen.WORKLOADS[int(wl[6:])]
-            kind, wname = "dtproj", w.name + "-dt_proj"
+            kind, wname = dtproj_kind(w), w.name + "-dt_proj"
             rows, rank, dim, _ = dtproj_shape(w)
             alg = dtproj_algorithmic_bytes(rows, rank, dim, 2 if w.io == gen.BF16 else 4)
         elif wl.startswith("conv"):    # "conv3": the conv1d over workload 3's x

@@ -96,3 +96,46 @@ def test_dt_proj_mamba2p8b_layer_sampled():
     e = G.err(got[pick], expect(inp, rows=pick))
     G.say(f"[dt_proj] 2.8b layer sampled err={e:.2e}")
     assert e <= 2e-2, e
+
+
+@pytest.mark.parametrize("rank", [48, 104])
+def test_dt_proj_bf16_reads_only_the_rank_columns(rank):
+    # bf16 runs the persistent kernel, whose xdt fragments are 8 columns wide
+    # and whose last K step reaches past the rank: those columns (B and C of
+    # the x_proj row) hold NaN here, and nothing of them may show
+    inp = gen.make_dtproj_inputs(300, rank, 264, rank + 32, io=gen.BF16, seed=960 + rank)
+    inp["x_dbl"][:, rank:] = gen.bf16_from_f32(np.full((300, 32), np.nan, np.float32))
+    got = run(inp)
+    assert np.all(np.isfinite(got))
+    assert G.err(got, expect(inp)) <= 2e-2
+
+
+def test_dt_proj_bf16_many_slabs_per_workgroup():
+    """600 and a part 128-row slabs over 21 channel tiles: each persistent
+    workgroup walks about 25 slabs, the last one ragged, and d_inner % 8 == 4
+    sends rows out in 8-byte halves; sampled rows against the oracle."""
+    rows, rank, dim, ldx = 128 * 600 + 37, 160, 2564, 192
+    inp = gen.make_dtproj_inputs(rows, rank, dim, ldx, io=gen.BF16, seed=970)
+    got = run(inp)
+    assert np.all(np.isfinite(got))
+    pick = np.r_[0:40, 128 * 317 - 20:128 * 317 + 20, rows - 45:rows]
+    e = G.err(got[pick], expect(inp, rows=pick))
+    G.say(f"[dt_proj] many slabs err={e:.2e}")
+    assert e <= 2e-2, e
+
+
+def test_dt_proj_bf16_rank_above_the_persistent_kernel():
+    # rank 168 > 160: the tiled kernel with K staged through LDS
+    inp = gen.make_dtproj_inputs(200, 168, 136, 200, io=gen.BF16, seed=971)
+    assert G.err(run(inp), expect(inp)) <= 2e-2
+
+
+def test_dt_proj_mamba130m_layer_sampled():
+    """The 130m layer's dt_proj at full size (8 x 2048 rows, rank 48, x_proj
+    rows of 48 + 2 x 16, d_inner 1536); sampled rows against the oracle."""
+    rows, rank, dim, ldx = 8 * 2048, 48, 1536, 80
+    inp = gen.make_dtproj_inputs(rows, rank, dim, ldx, io=gen.BF16, seed=972)
+    got = run(inp)
+    assert np.all(np.isfinite(got))
+    pick = np.r_[0:64, rows - 64:rows]
+    assert G.err(got[pick], expect(inp, rows=pick)) <= 2e-2
