@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 #define SSM_MAX_D_STATE 16
 #define SSM_MAX_CONV_WIDTH 4
 
@@ -402,11 +402,24 @@ int ssm_dt_proj(const void *xdt, int64_t ldx, const void *W, void *delta, int64_
  * (SSM_ERR_ALIGN); one batch row of x (plus 128 steps) must span less than
  * 2 GiB (SSM_ERR_SHAPE).  Outputs may not overlap inputs (SSM_ERR_ALIAS).
  * All pointers are device memory, owned by the caller; nothing is allocated.
+ *   workspace: ssd_scan_workspace_bytes() bytes, 256-byte aligned (may be
+ *   NULL when that is 0): at few (batch, head, 64-channel) units the sequence
+ *   is cut into time segments (bf16, headdim a multiple of 64, dstate <= 64),
+ *   and the workspace holds each segment's final state from zero and its
+ *   decay.  The segments depend on the shape alone: results are deterministic.
+ *   Too small or NULL when needed: SSM_ERR_WORKSPACE.  It may not overlap any
+ *   input or output (SSM_ERR_ALIAS).
  */
 int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_softplus,
                  const float *A, const void *B, const void *C, const float *D, const void *z,
                  const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
-                 int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *stream);
+                 int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ssd_scan_fwd needs for a shape (0: none); SIZE_MAX for
+ * arguments it would reject as SSM_ERR_SHAPE or SSM_ERR_DTYPE. */
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                int64_t dstate, int io_dtype);
 
 /*
  * ssm_scan_status -- whether the last forward scan that used `workspace`

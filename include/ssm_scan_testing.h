@@ -41,6 +41,17 @@ int ssm_testing_scan_fwd_no_handoff(const void *x, const void *delta, const floa
 int ssm_testing_bwd_segments(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                              int io_dtype, int *segments, int *blocks_per_segment);
 
+/*
+ * ssm_testing_ssd_segments -- how ssd_scan_fwd cuts each (batch, head,
+ * 64-channel) sequence in time for the given shape: the number of segments
+ * (*segments, >= 1) and the 64-step chunks per segment (*chunks_per_segment;
+ * the last segment may be shorter).  A pure function of the shape and io
+ * dtype.  Same argument rules as ssd_scan_workspace_bytes; SSM_ERR_NULL for a
+ * null output pointer.
+ */
+int ssm_testing_ssd_segments(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t dstate, int io_dtype, int *segments, int *chunks_per_segment);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,10 +24,11 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_workspace_bytes", "sm1_scan_fwd", "sm1_scan
            "ssm_causal_conv1d_update", "ssm_scan_fwd_2d", "ssm_scan_2d_workspace_bytes", "ssd_scan_fwd",
            "ssm_dt_proj", "ssm_scan_status", "ssm_testing_scan_fwd_no_handoff", "ssm_scan_fwd_noalloc",
            "ssm_conv_scan_fwd", "ssm_conv_scan_workspace_bytes", "ssm_testing_bwd_segments",
+           "ssd_scan_workspace_bytes", "ssm_testing_ssd_segments",
            "ssm_status_string", "ssm_abi_version")
 BENCH_LIB_PATH = os.path.join(PKG, "libssmbench.so")
 BENCH_EXPORTS = ("ssm_mb_copy", "ssm_mb_valu")
-ABI_VERSION = 2
+ABI_VERSION = 3
 SSM_ERR_WAIT = -8
 SSM_ERR_SCRATCH = -9
 SSM_SCRATCH_BYTES = 16 << 20
@@ -85,8 +86,13 @@ def _bind(lib):
     lib.ssm_scan_2d_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _int, _int, _int]
     lib.ssm_scan_2d_workspace_bytes.restype = _sz
     lib.ssd_scan_fwd.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                 _i64, _i64, _i64, _i64, _i64, _int, _vp]
+                                 _i64, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]
     lib.ssd_scan_fwd.restype = _int
+    lib.ssd_scan_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64, _int]
+    lib.ssd_scan_workspace_bytes.restype = _sz
+    lib.ssm_testing_ssd_segments.argtypes = [_i64, _i64, _i64, _i64, _i64, _int, ctypes.POINTER(_int),
+                                             ctypes.POINTER(_int)]
+    lib.ssm_testing_ssd_segments.restype = _int
     lib.ssm_dt_proj.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _vp]
     lib.ssm_dt_proj.restype = _int
     lib.ssm_scan_fwd_noalloc.argtypes = [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -201,6 +201,10 @@ struct SsdParams {
     float *last;
     int64_t seqlen, nheads, headdim;
     int softplus;
+    // time segments of the whole-line kernel (nseg = 1: none)
+    int nseg, cps;          // segments per sequence, 64-step chunks per segment
+    float *seg_state;       // per (unit, segment < nseg - 1): the segment's final state from zero
+    float *seg_sum;         // per (unit, segment): the segment's sum of Delta A (log2 units)
 };
 
 // Vectors of 4, 8 or 16 bytes (buffer loads, LDS stores) and their io elements.
@@ -668,8 +672,17 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 //     from the staged rows into the K order of M^T's accumulator tiles);
 //   its state half  S^T <- exp(s_Q) S^T + B^T (w x),  w_s = u_s exp(s_Q - e_i).
 // M, S_in and w x enter the products as hi + lo bf16 terms.
-template <int N, bool GATE>
+//
+// Time segments.  At few (b, h, 64 channels) units (160 at the 2.7b layer) one
+// sweep per unit leaves CUs idle, so the sequence is cut into nseg segments of
+// cps chunks.  MODE 1 (the state pass) runs the state recurrence alone over
+// each segment but the last, from zero, and records its final state and its
+// sum of Delta A; MODE 0 (the output pass) sweeps one segment per workgroup,
+// starting from h0 carried through the earlier segments in order:
+//   S_0 = h0,  S_{j+1} = exp(sum_j) S_j + local_j.
+template <int N, bool GATE, int MODE>
 __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
+    constexpr bool OUT = MODE == 0;
     using MM = Mma<bf16_t>;
     using PK = PermK<bf16_t>;
     using E = uint16_t;
@@ -695,17 +708,19 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
     static_assert(kQ * PT * es == kThreads * 16, "one 16-byte piece of x, z, y per thread and chunk");
     using VBt = typename Vec<PBB>::t;
 
-    __shared__ __attribute__((aligned(16))) E sB[2][kQ][LN];    // B[s][n]
-    __shared__ __attribute__((aligned(16))) E sC[2][kQ][LN];    // C[t][n]
+    // (the state pass uses B^T, x and the per-step values only)
+    constexpr int BO = OUT ? 2 : 1, QO = OUT ? kQ : 1;
+    __shared__ __attribute__((aligned(16))) E sB[BO][QO][LN];   // B[s][n]
+    __shared__ __attribute__((aligned(16))) E sC[BO][QO][LN];   // C[t][n]
     __shared__ __attribute__((aligned(16))) E sBt[2][N][LQ];    // B[s][n] at [n][s]
     __shared__ __attribute__((aligned(16))) E sX[2][kQ][LP];    // x[s][p] of the tile
-    __shared__ __attribute__((aligned(16))) E sZ[2][kQ][LP];    // z[t][p]
-    __shared__ __attribute__((aligned(16))) E sY[2][kQ][LP];    // y[t][p]
+    __shared__ __attribute__((aligned(16))) E sZ[BO][QO][LP];   // z[t][p]
+    __shared__ __attribute__((aligned(16))) E sY[BO][QO][LP];   // y[t][p]
     __shared__ __attribute__((aligned(16))) float sCum[kWaves][kQ];   // per wave: prefix s_t
     __shared__ __attribute__((aligned(16))) float sDl[kWaves][kQ];    // per wave: Delta_t
     // per wave: its S_in tiles as readout operands, [buffer][wave][fragment][term][lane]
     constexpr int NSP = (NH + 1) / 2;
-    __shared__ __attribute__((aligned(16))) u32x4_t sS[2][kWaves][NSP][2][64];
+    __shared__ __attribute__((aligned(16))) u32x4_t sS[BO][OUT ? kWaves : 1][NSP][2][OUT ? 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -714,16 +729,23 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
     const int partner = w ^ 4;
     const int l16 = lane & 15, g = lane >> 4;
 
-    // block -> (b, h, channel tile), consecutive logical blocks on one XCD
+    // block -> (segment, b, h, channel tile), consecutive logical blocks on one
+    // XCD (which then share B, C and dt of one segment of one batch row)
     const int64_t H = p.nheads, P = p.headdim, L = p.seqlen;
     const int64_t npb = P / PT;
     const int64_t total = static_cast<int64_t>(gridDim.x);
+    const int64_t nunit = total / (OUT ? p.nseg : p.nseg - 1);
     int64_t lin = blockIdx.x;
     if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
-    const int64_t pt = lin % npb;
-    const int64_t h = (lin / npb) % H;
-    const int64_t b = lin / (npb * H);
+    const int seg = static_cast<int>(lin / nunit);
+    const int64_t unit = lin % nunit;
+    const int64_t pt = unit % npb;
+    const int64_t h = (unit / npb) % H;
+    const int64_t b = unit / (npb * H);
     const int64_t p0 = pt * PT;
+    const int64_t nchunks = (L + kQ - 1) / kQ;
+    const int64_t c_lo = static_cast<int64_t>(seg) * p.cps;
+    const int64_t c_hi = c_lo + p.cps < nchunks ? c_lo + p.cps : nchunks;
 
     const uint32_t rowX = static_cast<uint32_t>(H * P * es);
     const uint32_t rowN = static_cast<uint32_t>(N * es);
@@ -774,31 +796,50 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
         for (int i = 0; i < UBT; ++i) {
             rbv[i][0] = Vec<PBB>::template load<kCached>(rB, oB[i]);
             rbv[i][1] = Vec<PBB>::template load<kCached>(rB, oB[i] + rowN);
-            rcv[i][0] = Vec<PBB>::template load<kCached>(rC, oB[i]);
-            rcv[i][1] = Vec<PBB>::template load<kCached>(rC, oB[i] + rowN);
+            if constexpr (OUT) {
+                rcv[i][0] = Vec<PBB>::template load<kCached>(rC, oB[i]);
+                rcv[i][1] = Vec<PBB>::template load<kCached>(rC, oB[i] + rowN);
+            }
         }
-        rxp = __builtin_amdgcn_raw_buffer_load_b128(rows_from(xb, t0, rowX), oPiece, 0, kStream);
+        // x is read again by the output pass: the state pass keeps it cached
+        rxp = __builtin_amdgcn_raw_buffer_load_b128(rows_from(xb, t0, rowX), oPiece, 0, OUT ? kStream : kCached);
         // no z: an empty descriptor, zeros
-        rzp = __builtin_amdgcn_raw_buffer_load_b128(GATE ? rows_from(zb, t0, rowX) : make_rsrc(p.x, 0u), oPiece, 0,
-                                                    kStream);
+        if constexpr (OUT)
+            rzp = __builtin_amdgcn_raw_buffer_load_b128(GATE ? rows_from(zb, t0, rowX) : make_rsrc(p.x, 0u), oPiece,
+                                                        0, kStream);
     };
-    // y of chunk cy (staged in sY[cy % 2]) to global memory; cy < 0: nothing (dropped)
+    // y of chunk cy (staged in sY[cy % 2]) to global memory; cy before this
+    // segment: nothing (dropped)
     auto store_y = [&](int64_t cy) __attribute__((always_inline)) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&sY[static_cast<int>(cy & 1)][pr][8 * pc]);
-        const rsrc_t rY = cy >= 0 ? rows_from(yb, cy * kQ, rowX) : make_rsrc(yb, 0u);
+        const rsrc_t rY = cy >= c_lo ? rows_from(yb, cy * kQ, rowX) : make_rsrc(yb, 0u);
         __builtin_amdgcn_raw_buffer_store_b128(v, rY, oPiece, 0, kStream);
     };
 
     // ---- this wave's half of the block's state: tiles S^T[16 (NH half + k) ..][16 cb ..]
     // (lane: n = 16 (NH half + k) + 4 g + v, p = l16)
+    // (the recorded segment states use the accumulators' own lane order)
+    auto seg_slot = [&](int j, int k) __attribute__((always_inline)) {
+        return p.seg_state + (((unit * (p.nseg - 1) + j) * kWaves + w) * NH + k) * 256 + 4 * lane;
+    };
     f32x4_t acc_s[NH];
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
         acc_s[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.h0)
+        if (OUT && p.h0)
             acc_s[k] = *reinterpret_cast<const f32x4_t *>(p.h0 + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
                                                                   16 * (NH * half + k) + 4 * g));
     }
+    if constexpr (OUT) {
+        // the state entering this segment: h0 through the earlier segments, in order
+        for (int j = 0; j < seg; ++j) {
+            const float dec = ST::ex(p.seg_sum[unit * p.nseg + j]);
+#pragma unroll
+            for (int k = 0; k < NH; ++k)
+                acc_s[k] = acc_s[k] * dec + *reinterpret_cast<const f32x4_t *>(seg_slot(j, k));
+        }
+    }
+    float seg_acc = 0.0f;                        // the state pass: sum of Delta A over the segment
 
     auto chunk = [&](int64_t c) __attribute__((always_inline)) {
         const int64_t t0 = c * kQ;
@@ -812,11 +853,13 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
         const float cend = ST::lane_value(cum, 63);
         sCum[w][lane] = cum;
         sDl[w][lane] = delta;
+        if constexpr (!OUT) seg_acc += cend;
 
         // ---- S_in of this wave's half as readout operands (hi, lo) for both
         // waves of the pair: NH == 1 holds one n-tile (its partner the other),
         // NH >= 2 whole tile pairs
-        if constexpr (NH == 1) {
+        if constexpr (!OUT) {
+        } else if constexpr (NH == 1) {
             float sv[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sv[e] = acc_s[0][e];
@@ -841,20 +884,22 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
         // ---- stage this chunk (buffer c % 2; the previous readers of that
         // buffer, chunk c - 2, finished before the last barrier)
         *reinterpret_cast<u32x4_t *>(&sX[buf][pr][8 * pc]) = rxp;
-        *reinterpret_cast<u32x4_t *>(&sZ[buf][pr][8 * pc]) = rzp;
+        if constexpr (OUT) *reinterpret_cast<u32x4_t *>(&sZ[buf][pr][8 * pc]) = rzp;
 #pragma unroll
         for (int i = 0; i < UBT; ++i) {
             const int n0 = nB0[i];
-            *reinterpret_cast<VBt *>(&sB[buf][sp][n0]) = rbv[i][0];
-            *reinterpret_cast<VBt *>(&sB[buf][sp + 1][n0]) = rbv[i][1];
-            *reinterpret_cast<VBt *>(&sC[buf][sp][n0]) = rcv[i][0];
-            *reinterpret_cast<VBt *>(&sC[buf][sp + 1][n0]) = rcv[i][1];
+            if constexpr (OUT) {
+                *reinterpret_cast<VBt *>(&sB[buf][sp][n0]) = rbv[i][0];
+                *reinterpret_cast<VBt *>(&sB[buf][sp + 1][n0]) = rbv[i][1];
+                *reinterpret_cast<VBt *>(&sC[buf][sp][n0]) = rcv[i][0];
+                *reinterpret_cast<VBt *>(&sC[buf][sp + 1][n0]) = rcv[i][1];
+            }
 #pragma unroll
             for (int e = 0; e < VB; ++e) MM::put2(&sBt[buf][n0 + e][sp], EL::raw(rbv[i][0], e), EL::raw(rbv[i][1], e));
         }
         fetch(t0 + kQ);                        // the next chunk (past the end: empty reads)
         __syncthreads();
-        store_y(c - 1);                        // the previous chunk's y, complete now
+        if constexpr (OUT) store_y(c - 1);     // the previous chunk's y, complete now
 
         // ---- x^T operand: lane (channel 16 cb + l16, group g) takes steps
         // 16 i + 4 g + v (i < 4, v < 4): K slots 8 g .. 8 g + 7 of the two
@@ -889,7 +934,8 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
 
         // ---- the readout operand over all N: this wave's S_in half and the partner's
         frag fs[NKN][2];
-        if constexpr (NH == 1) {
+        if constexpr (!OUT) {
+        } else if constexpr (NH == 1) {
             // K slots 0..3 from half 0, 4..7 from half 1
             const u32x4_t a0 = sS[buf][half ? partner : w][0][0][lane], b0 = sS[buf][half ? w : partner][0][0][lane];
             const u32x4_t a1 = sS[buf][half ? partner : w][0][1][lane], b1 = sS[buf][half ? w : partner][0][1][lane];
@@ -907,7 +953,7 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
 
         // ---- the wave's two output blocks
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < (OUT ? 2 : 0); ++r) {
             const int j = r ? jb1 : jb0;         // 0..3, uniform
             // C rows of t-block j (B operand, K = n): for G^T and for the readout
             frag fc[NKN];
@@ -1001,21 +1047,28 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
         }
     };
 
-    const int64_t nchunks = (L + kQ - 1) / kQ;
-    fetch(0);
+    fetch(c_lo * kQ);
     // a (dropped) store after the first fetch, as every chunk issues one after
     // its fetch: every path into the loop has the same memory history, so a
     // chunk's top waits for its own registers only
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, make_rsrc(yb, 0u), oPiece, 0, kStream);
-    for (int64_t c = 0; c < nchunks; ++c) chunk(c);
-    __syncthreads();
-    store_y(nchunks - 1);
+    if constexpr (OUT)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, make_rsrc(yb, 0u), oPiece, 0, kStream);
+    for (int64_t c = c_lo; c < c_hi; ++c) chunk(c);
 
-    if (p.last) {
+    if constexpr (OUT) {
+        __syncthreads();
+        store_y(c_hi - 1);
+        if (p.last && seg == p.nseg - 1) {
 #pragma unroll
-        for (int k = 0; k < NH; ++k)
-            *reinterpret_cast<f32x4_t *>(p.last + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
-                                                   16 * (NH * half + k) + 4 * g)) = acc_s[k];
+            for (int k = 0; k < NH; ++k)
+                *reinterpret_cast<f32x4_t *>(p.last + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
+                                                       16 * (NH * half + k) + 4 * g)) = acc_s[k];
+        }
+    } else {
+        // this segment's final state from zero, and its sum of Delta A
+#pragma unroll
+        for (int k = 0; k < NH; ++k) *reinterpret_cast<f32x4_t *>(seg_slot(seg, k)) = acc_s[k];
+        if (tid == 0) p.seg_sum[unit * p.nseg + seg] = seg_acc;
     }
 }
 
@@ -1026,17 +1079,75 @@ hipError_t launch(const SsdParams &p, int64_t blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---- time segments of the whole-line kernel
+// Cost model in units of one chunk swept by a workgroup: the output pass runs
+// one workgroup per CU (its LDS), in rounds of kSsdCUs, each unit paying about
+// half a chunk of prologue; the state pass costs about 0.36 of a chunk per
+// chunk it covers and fits three workgroups per CU.  A function of the shape
+// alone, so results do not depend on the device.
+constexpr int kSsdCUs = 256;
+constexpr int kSsdMaxSeg = 64;
+struct SsdPlan {
+    int S, cps;
+};
+bool line_kernel_shape(int64_t headdim, int64_t dstate, int bf16) {
+    return bf16 && dstate <= 64 && headdim % 64 == 0;
+}
+SsdPlan ssd_plan_of(int64_t units0, int64_t nchunks) {
+    SsdPlan best{1, static_cast<int>(nchunks)};
+    if (nchunks <= 1 || units0 <= 0) return best;
+    double best_cost = 0.0;
+    const int64_t smax = nchunks < kSsdMaxSeg ? nchunks : kSsdMaxSeg;
+    for (int64_t S = 1; S <= smax; ++S) {
+        const int64_t cps = (nchunks + S - 1) / S;
+        if ((nchunks + cps - 1) / cps != S) continue;   // the same split as a smaller S
+        const int64_t rounds = (units0 * S + kSsdCUs - 1) / kSsdCUs;
+        const double cost = static_cast<double>(rounds) * (static_cast<double>(cps) + 0.5) +
+                            0.36 * static_cast<double>(units0 * (S - 1) * cps) / (3.0 * kSsdCUs);
+        if (S == 1 || cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = SsdPlan{static_cast<int>(S), static_cast<int>(cps)};
+        }
+    }
+    return best;
+}
+struct SsdLayout {
+    SsdPlan plan;
+    int64_t units0;
+    size_t state_bytes, sum_off, total;
+};
+SsdLayout ssd_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int bf16) {
+    SsdLayout l{};
+    l.plan = SsdPlan{1, static_cast<int>((seqlen + kQ - 1) / kQ)};
+    if (!line_kernel_shape(headdim, dstate, bf16) || batch == 0 || nheads == 0) return l;
+    l.units0 = batch * nheads * (headdim / 64);
+    l.plan = ssd_plan_of(l.units0, (seqlen + kQ - 1) / kQ);
+    if (l.plan.S == 1) return l;
+    // per (unit, segment but the last): 8 waves x (dstate / 32) tiles x 64 lanes x 4 fp32
+    l.state_bytes = sizeof(float) * static_cast<size_t>(l.units0) * (l.plan.S - 1) * 8 * (dstate / 32) * 256;
+    l.sum_off = (l.state_bytes + 255) & ~size_t(255);
+    l.total = l.sum_off + ((sizeof(float) * static_cast<size_t>(l.units0) * l.plan.S + 255) & ~size_t(255));
+    return l;
+}
+
 // bf16 with head sizes that are multiples of 64: whole-line tiles
-// (ssd_line_kernel); otherwise 32- or 16-channel tiles of ssd_chunk_kernel
+// (ssd_line_kernel, cut into time segments when there are few of them);
+// otherwise 32- or 16-channel tiles of ssd_chunk_kernel
 template <typename T, int N>
 hipError_t launch_pt(const SsdParams &p, int64_t batch, hipStream_t s) {
     if constexpr (std::is_same<T, bf16_t>::value && N <= 64) {
         if (p.headdim % 64 == 0) {
-            const dim3 grid(static_cast<unsigned>(batch * p.nheads * (p.headdim / 64)));
+            const int64_t units = batch * p.nheads * (p.headdim / 64);
+            if (p.nseg > 1) {
+                const dim3 sgrid(static_cast<unsigned>(units * (p.nseg - 1)));
+                if (p.z) hipLaunchKernelGGL((ssd_line_kernel<N, true, 1>), sgrid, dim3(512), 0, s, p);
+                else hipLaunchKernelGGL((ssd_line_kernel<N, false, 1>), sgrid, dim3(512), 0, s, p);
+            }
+            const dim3 grid(static_cast<unsigned>(units * p.nseg));
             if (p.z)
-                hipLaunchKernelGGL((ssd_line_kernel<N, true>), grid, dim3(512), 0, s, p);
+                hipLaunchKernelGGL((ssd_line_kernel<N, true, 0>), grid, dim3(512), 0, s, p);
             else
-                hipLaunchKernelGGL((ssd_line_kernel<N, false>), grid, dim3(512), 0, s, p);
+                hipLaunchKernelGGL((ssd_line_kernel<N, false, 0>), grid, dim3(512), 0, s, p);
             return hipGetLastError();
         }
     }
@@ -1052,6 +1163,17 @@ bool ssd_supported(int64_t headdim, int64_t dstate, int bf16) {
     return bf16 && dstate == 128;
 }
 
+size_t ssd_workspace(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int bf16) {
+    return ssd_layout(batch, seqlen, nheads, headdim, dstate, bf16).total;
+}
+
+void ssd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int bf16,
+              int *segments, int *chunks_per_segment) {
+    const SsdLayout l = ssd_layout(batch, seqlen, nheads, headdim, dstate, bf16);
+    *segments = l.plan.S;
+    *chunks_per_segment = l.plan.cps;
+}
+
 hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t s) {
     if (a.batch == 0 || a.nheads == 0) return hipSuccess;
     SsdParams p;
@@ -1060,6 +1182,11 @@ hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t s) {
     p.y = a.y; p.last = a.last_state;
     p.seqlen = a.seqlen; p.nheads = a.nheads; p.headdim = a.headdim;
     p.softplus = a.softplus;
+    const SsdLayout l = ssd_layout(a.batch, a.seqlen, a.nheads, a.headdim, a.dstate, a.bf16);
+    p.nseg = l.plan.S;
+    p.cps = l.plan.cps;
+    p.seg_state = l.total ? static_cast<float *>(a.workspace) : nullptr;
+    p.seg_sum = l.total ? reinterpret_cast<float *>(static_cast<char *>(a.workspace) + l.sum_off) : nullptr;
     if (a.bf16) {
         switch (a.dstate) {
         case 32: return launch_pt<bf16_t, 32>(p, a.batch, s);

@@ -564,10 +564,36 @@ int ssm_causal_conv1d_update(void *conv_state, const void *x, const float *weigh
     return hip_status(ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// the shape checks of ssd_scan_fwd (and its workspace and plan queries)
+int check_ssd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                    int io_dtype) {
+    if (int r = check_dtype(io_dtype)) return r;
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0) return SSM_ERR_SHAPE;
+    if (!ssm::ssd_supported(headdim, dstate, io_dtype == SSM_BF16)) return SSM_ERR_SHAPE;
+    const size_t es = io_size(io_dtype);
+    const int64_t hp = mul3(nheads, headdim, 1);
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    if (hp < 0 || mul3(batch, seqlen, hp) < 0 || mul3(batch, hp, dstate) < 0) return SSM_ERR_SHAPE;
+    if (mul3(seqlen + 128, hp, es) > lim || mul3(seqlen + 128, dstate, es) > lim ||
+        mul3(seqlen + 128, nheads, es) > lim)
+        return SSM_ERR_SHAPE;
+    if (mul3(batch, hp / 16, 1) > lim) return SSM_ERR_SHAPE;
+    return SSM_OK;
+}
+}  // namespace
+
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                int64_t dstate, int io_dtype) {
+    if (check_ssd_shape(batch, seqlen, nheads, headdim, dstate, io_dtype)) return static_cast<size_t>(-1);
+    return ssm::ssd_workspace(batch, seqlen, nheads, headdim, dstate, io_dtype == SSM_BF16);
+}
+
 int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_softplus,
                  const float *A, const void *B, const void *C, const float *D, const void *z,
                  const float *h0, void *y, float *last_state, int64_t batch, int64_t seqlen,
-                 int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *stream) {
+                 int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype, void *workspace,
+                 size_t workspace_bytes, void *stream) {
     if (int r = check_dtype(io_dtype)) return r;
     if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0) return SSM_ERR_SHAPE;
     if (!ssm::ssd_supported(headdim, dstate, io_dtype == SSM_BF16)) return SSM_ERR_SHAPE;
@@ -602,6 +628,16 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
         for (const Range &i : ins)
             if (overlap(o, i)) return SSM_ERR_ALIAS;
     if (overlap(outs[0], outs[1])) return SSM_ERR_ALIAS;
+    const size_t need = ssm::ssd_workspace(batch, seqlen, nheads, headdim, dstate, io_dtype == SSM_BF16);
+    if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
+    if (need) {
+        const Range wsr = range(workspace, static_cast<int64_t>(need), 1);
+        for (const Range &o : outs)
+            if (overlap(o, wsr)) return SSM_ERR_ALIAS;
+        for (const Range &i : ins)
+            if (overlap(i, wsr)) return SSM_ERR_ALIAS;
+    }
     ssm::SsdArgs a;
     a.x = x; a.dt = dt; a.z = z; a.B = B; a.C = C;
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.h0 = h0;
@@ -609,6 +645,8 @@ int ssd_scan_fwd(const void *x, const void *dt, const float *dt_bias, int dt_sof
     a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.headdim = headdim; a.dstate = dstate;
     a.softplus = dt_softplus ? 1 : 0;
     a.bf16 = io_dtype == SSM_BF16 ? 1 : 0;
+    a.workspace = need ? workspace : nullptr;
+    a.workspace_bytes = need ? workspace_bytes : 0;
     return hip_status(ssm::launch_ssd_scan(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -643,6 +681,14 @@ int ssm_testing_scan_fwd_no_handoff(const void *x, const void *delta, const floa
     if (need && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
     if (need && !aligned(workspace, 256)) return SSM_ERR_ALIGN;
     return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int ssm_testing_ssd_segments(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                             int64_t dstate, int io_dtype, int *segments, int *chunks_per_segment) {
+    if (!segments || !chunks_per_segment) return SSM_ERR_NULL;
+    if (int r = check_ssd_shape(batch, seqlen, nheads, headdim, dstate, io_dtype)) return r;
+    ssm::ssd_plan(batch, seqlen, nheads, headdim, dstate, io_dtype == SSM_BF16, segments, chunks_per_segment);
+    return SSM_OK;
 }
 
 int ssm_testing_bwd_segments(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,

@@ -136,10 +136,17 @@ struct SsdArgs {
     float *last_state;
     int64_t batch, seqlen, nheads, headdim, dstate;
     int softplus, bf16;
+    void *workspace = nullptr;            // ssd_workspace() bytes, 256-byte aligned
+    size_t workspace_bytes = 0;
 };
 
 // Mamba-2 multi-head scan (chunked, MFMA).
 bool ssd_supported(int64_t headdim, int64_t dstate, int bf16);
+// workspace of the time segments of the whole-line kernel (0: none needed)
+size_t ssd_workspace(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int bf16);
+// the time segments of a shape: (segments, 64-step chunks per segment)
+void ssd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int bf16,
+              int *segments, int *chunks_per_segment);
 hipError_t launch_ssd_scan(const SsdArgs &a, hipStream_t s);
 
 // dt_proj: delta (rows, dim) = xdt[:, :rank] (row stride ldx) x W^T, W (dim, rank);

@@ -339,7 +339,7 @@ def scan_fwd_2d(x, delta, A, B, C, height, width, direction, D=None, z=None, del
 
 
 def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
-                 return_last_state=False, out=None, last_state_out=None):
+                 return_last_state=False, out=None, last_state_out=None, workspace=None):
     """Mamba-2 multi-head scan.  x, z: (batch, seqlen, nheads, headdim) fp32 or
     bf16; dt: (batch, seqlen, nheads); B, C: (batch, seqlen, dstate) same dtype;
     A, D, dt_bias: (nheads,) fp32; h0: (batch, nheads, headdim, dstate) fp32.
@@ -366,9 +366,16 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
         last = last_state_out if last_state_out is not None else torch.empty(
             (Bt, H, P, N), dtype=torch.float32, device=x.device)
         _dev(last, "last_state_out", torch.float32, (Bt, H, P, N))
+    need = lib.ssd_scan_workspace_bytes(Bt, T, H, P, N, _IO[io])
+    if need == (1 << 64) - 1:
+        raise RuntimeError("ssd_scan_workspace_bytes: invalid arguments")
+    ws = None
+    if need:
+        ws = workspace if workspace is not None and workspace.numel() >= need else torch.empty(
+            need, dtype=torch.uint8, device=x.device)
     rc = lib.ssd_scan_fwd(_ptr(x), _ptr(dt), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(A), _ptr(B),
                           _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(last), Bt, T, H, P, N,
-                          _IO[io], _stream(x.device))
+                          _IO[io], _ptr(ws), need, _stream(x.device))
     _check(rc, "ssd_scan_fwd")
     return (y, last) if return_last_state else y
 

@@ -46,7 +46,7 @@ def test_header_declares_the_boundary():
 def test_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.ssm_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.ssm_abi_version() == _lib.ABI_VERSION == 3
     for name in _lib.BENCH_EXPORTS:
         assert not hasattr(lib, name), name
 
@@ -405,7 +405,7 @@ def ssd_args(batch=2, seqlen=16, nheads=3, headdim=32, dstate=64, io=F32, **over
     f = FakeDev()
     a = dict(x=f(), dt=f(), dt_bias=f(), softplus=1, A=f(), B=f(), C=f(), D=f(), z=f(), h0=f(), y=f(),
              last=f(), batch=batch, seqlen=seqlen, nheads=nheads, headdim=headdim, dstate=dstate, io=io,
-             stream=None)
+             ws=f(), ws_bytes=64 * MB, stream=None)
     a.update(over)
     return a
 
@@ -413,7 +413,7 @@ def ssd_args(batch=2, seqlen=16, nheads=3, headdim=32, dstate=64, io=F32, **over
 def call_ssd(lib, a):
     return lib.ssd_scan_fwd(a["x"], a["dt"], a["dt_bias"], a["softplus"], a["A"], a["B"], a["C"], a["D"],
                             a["z"], a["h0"], a["y"], a["last"], a["batch"], a["seqlen"], a["nheads"],
-                            a["headdim"], a["dstate"], a["io"], a["stream"])
+                            a["headdim"], a["dstate"], a["io"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -430,6 +430,57 @@ def call_ssd(lib, a):
 ])
 def test_ssd_validation(lib, over, code):
     assert call_ssd(lib, ssd_args(**over)) == code
+
+
+def ssd_segments(lib, batch, seqlen, nheads, headdim, dstate, io):
+    S, cps = ctypes.c_int(-1), ctypes.c_int(-1)
+    r = lib.ssm_testing_ssd_segments(batch, seqlen, nheads, headdim, dstate, io, ctypes.byref(S),
+                                     ctypes.byref(cps))
+    return r, S.value, cps.value
+
+
+def test_ssd_segments_and_workspace(lib):
+    # the 2.7b layer (4 x 8 heads x 5 line tiles = 160 units, 128 chunks):
+    # 8 segments of 16 chunks, 1280 workgroups (five rounds on 256 CUs); the
+    # workspace holds 7 segment states per unit (8 waves x 2 tiles x 1 KB)
+    # and 8 decay sums per unit
+    assert ssd_segments(lib, 4, 8192, 8, 320, 64, BF16) == (OK, 8, 16)
+    need = lib.ssd_scan_workspace_bytes(4, 8192, 8, 320, 64, BF16)
+    state = 160 * 7 * 8 * 2 * 256 * 4
+    assert need == state + ((160 * 8 * 4 + 255) & ~255)
+    # the chunk kernel's shapes (fp32, or head size not a multiple of 64): no segments
+    assert ssd_segments(lib, 8, 2048, 24, 96, 64, BF16)[:2] == (OK, 1)
+    assert lib.ssd_scan_workspace_bytes(8, 2048, 24, 96, 64, BF16) == 0
+    assert lib.ssd_scan_workspace_bytes(2, 300, 3, 64, 32, F32) == 0
+    # plenty of units: one segment
+    assert ssd_segments(lib, 64, 4096, 8, 320, 64, BF16)[:2] == (OK, 1)
+    # every split covers the chunks once
+    for shape in [(1, 1000, 2, 64, 32), (1, 4096, 1, 128, 64), (2, 65, 1, 64, 64), (1, 64, 1, 64, 32)]:
+        r, S, cps = ssd_segments(lib, *shape, BF16)
+        nch = (shape[1] + 63) // 64
+        assert r == OK and 1 <= S <= 64 and (S - 1) * cps < nch <= S * cps, (shape, S, cps)
+    assert lib.ssd_scan_workspace_bytes(2, 16, 3, 24, 64, F32) == (1 << 64) - 1
+    assert lib.ssd_scan_workspace_bytes(2, 16, 3, 32, 64, 9) == (1 << 64) - 1
+    assert ssd_segments(lib, 2, 16, 3, 24, 64, F32)[0] == ESHAPE
+    assert lib.ssm_testing_ssd_segments(2, 16, 3, 32, 64, F32, None, None) == ENULL
+
+
+def test_ssd_workspace_validation(lib):
+    # a segmented shape: the workspace is required, 256-byte aligned and apart
+    # from every tensor
+    shape = dict(batch=1, seqlen=4096, nheads=1, headdim=128, dstate=64, io=BF16)
+    need = lib.ssd_scan_workspace_bytes(1, 4096, 1, 128, 64, BF16)
+    assert need > 0
+    assert call_ssd(lib, ssd_args(**shape, ws=None, ws_bytes=0)) == EWS
+    assert call_ssd(lib, ssd_args(**shape, ws_bytes=need - 1)) == EWS
+    a = ssd_args(**shape)
+    a["ws"] += 128
+    assert call_ssd(lib, a) == EALIGN
+    a = ssd_args(**shape)
+    a["ws"] = a["x"]
+    assert call_ssd(lib, a) == EALIAS
+    # no workspace needed: NULL is fine
+    assert call_ssd(lib, ssd_args(io=F32, ws=None, ws_bytes=0, batch=0)) == OK
 
 
 def test_ssd_supported_shapes_pass_validation_rules(lib):

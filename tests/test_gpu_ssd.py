@@ -164,13 +164,49 @@ def test_ssd_deterministic_and_continuation():
     assert ey <= 1e-5 and el <= 1e-5
 
 
+def ssd_segments(inp):
+    """(segments, chunks per segment) of ssd_scan_fwd's time split for inp's shape."""
+    import ctypes
+    from selective_scan_ssm_amd import _lib
+    S, cps = ctypes.c_int(0), ctypes.c_int(0)
+    io = _lib.SSM_BF16 if inp["io"] == gen.BF16 else _lib.SSM_F32
+    assert _lib.load().ssm_testing_ssd_segments(inp["batch"], inp["seqlen"], inp["nheads"], inp["headdim"],
+                                                inp["d_state"], io, ctypes.byref(S), ctypes.byref(cps)) == 0
+    return S.value, cps.value
+
+
+@pytest.mark.parametrize("N,T,gate", [(32, 4000, True), (64, 2500, False)])
+def test_ssd_bf16_time_segments(N, T, gate):
+    """The whole-line kernel cut into time segments of several chunks: the
+    state pass's segment states and decays carry h0 into every later segment;
+    the last segment and the last chunk are ragged."""
+    inp = gen.make_ssd_inputs(2, T, 4, 128, N, io=gen.BF16, h0_kind="normal", seed=780 + N, with_z=gate)
+    S, cps = ssd_segments(inp)
+    assert S > 1 and cps > 1 and (T + 63) // 64 < S * cps, (S, cps)
+    check(inp, tag=f"bf16-segments-{S}x{cps}")
+
+
+def test_ssd_bf16_time_segments_fast_decay_deterministic():
+    # |A| up to e^4 (segment decays underflow to 0) and two calls bit for bit
+    inp = gen.make_ssd_inputs(1, 3000, 4, 64, 64, io=gen.BF16, h0_kind="normal", seed=790)
+    inp["A"] = (-np.exp(np.array([-4.0, 0.0, 2.5, 4.0]))).astype(np.float32)
+    inp["dt_bias"] = np.full(4, 0.5, np.float32)
+    assert ssd_segments(inp)[0] > 1
+    check(inp, tag="bf16-segments-fast-decay")
+    y1, l1 = run_gpu(inp)
+    y2, l2 = run_gpu(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
+
+
 # -------------------------------------------------- the layer shapes, full size
 @pytest.mark.parametrize("name", ["mamba2-130m-ssd-layer-bf16", "mamba2-2.7b-ssd-layer-bf16"])
 def test_ssd_layer_every_output(name):
     """One launch at the full layer shape; every output and final state
     against the oracle."""
     inp = gen.ssd_workload_inputs(name, seed=741)
-    G.say(f"[ssd] {name} full size, every output")
+    if name == "mamba2-2.7b-ssd-layer-bf16":
+        assert ssd_segments(inp) == (8, 16)           # the launch the bench times
+    G.say(f"[ssd] {name} full size, every output, segments {ssd_segments(inp)}")
     y, last = run_gpu(inp)
     yo, lo = run_oracle(inp)
     ey, el = G.err(y, yo), G.err(last, lo)
