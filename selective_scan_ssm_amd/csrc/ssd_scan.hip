@@ -677,11 +677,13 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 // sweep per unit leaves CUs idle, so the sequence is cut into nseg segments of
 // cps chunks.  MODE 1 (the state pass) runs the state recurrence alone over
 // each segment but the last, from zero, and records its final state and its
-// sum of Delta A; MODE 0 (the output pass) sweeps one segment per workgroup,
-// starting from h0 carried through the earlier segments in order:
-//   S_0 = h0,  S_{j+1} = exp(sum_j) S_j + local_j.
+// sum of Delta A; ssd_carry_kernel turns those, in place, into the state
+// entering each segment, in order:
+//   S_0 = h0,  S_{j+1} = exp(sum_j) S_j + local_j;
+// MODE 0 (the output pass) then sweeps one segment per workgroup from S_seg.
+// The state pass fits three workgroups per CU (40 KB of LDS, <= 85 registers).
 template <int N, bool GATE, int MODE>
-__global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ? 6 : 1))) void ssd_line_kernel(SsdParams p) {
     constexpr bool OUT = MODE == 0;
     using MM = Mma<bf16_t>;
     using PK = PermK<bf16_t>;
@@ -822,22 +824,18 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
     auto seg_slot = [&](int j, int k) __attribute__((always_inline)) {
         return p.seg_state + (((unit * (p.nseg - 1) + j) * kWaves + w) * NH + k) * 256 + 4 * lane;
     };
+    // the state entering the segment: h0 for the first, else the carry
+    // ssd_carry_kernel left in the previous segment's slot (the state pass
+    // starts from zero)
     f32x4_t acc_s[NH];
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
         acc_s[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (OUT && p.h0)
+        if (OUT && seg > 0)
+            acc_s[k] = *reinterpret_cast<const f32x4_t *>(seg_slot(seg - 1, k));
+        else if (OUT && p.h0)
             acc_s[k] = *reinterpret_cast<const f32x4_t *>(p.h0 + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
                                                                   16 * (NH * half + k) + 4 * g));
-    }
-    if constexpr (OUT) {
-        // the state entering this segment: h0 through the earlier segments, in order
-        for (int j = 0; j < seg; ++j) {
-            const float dec = ST::ex(p.seg_sum[unit * p.nseg + j]);
-#pragma unroll
-            for (int k = 0; k < NH; ++k)
-                acc_s[k] = acc_s[k] * dec + *reinterpret_cast<const f32x4_t *>(seg_slot(j, k));
-        }
     }
     float seg_acc = 0.0f;                        // the state pass: sum of Delta A over the segment
 
@@ -1072,6 +1070,44 @@ __global__ __launch_bounds__(512) void ssd_line_kernel(SsdParams p) {
     }
 }
 
+// Between the state pass and the output pass: for every unit, in place,
+// slot j := S_{j+1} = exp(sum_j) S_j + local_j with S_0 = h0 (or 0).  One
+// workgroup per unit with the output pass's thread -> state mapping (thread
+// (wave w, lane) holds the same elements as there), so every load and store
+// is one 16-byte piece per thread.
+template <int N>
+__global__ __launch_bounds__(512) void ssd_carry_kernel(SsdParams p) {
+    using ST = Steps<FastMath>;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NH = N / 32, kWaves = 8;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cb = w & 3, half = w >> 2, l16 = lane & 15, g = lane >> 4;
+    const int64_t H = p.nheads, P = p.headdim;
+    const int64_t npb = P / 64;
+    const int64_t unit = blockIdx.x;
+    const int64_t pt = unit % npb, h = (unit / npb) % H, b = unit / (npb * H);
+    const int64_t p0 = pt * 64;
+    f32x4 acc[NH];
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+        acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.h0)
+            acc[k] = *reinterpret_cast<const f32x4 *>(p.h0 + (((b * H + h) * P + p0 + 16 * cb + l16) * N +
+                                                               16 * (NH * half + k) + 4 * g));
+    }
+    for (int j = 0; j + 1 < p.nseg; ++j) {
+        const float dec = ST::ex(p.seg_sum[unit * p.nseg + j]);
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+            f32x4 *slot = reinterpret_cast<f32x4 *>(p.seg_state +
+                                                    (((unit * (p.nseg - 1) + j) * kWaves + w) * NH + k) * 256 +
+                                                    4 * lane);
+            acc[k] = acc[k] * dec + *slot;
+            *slot = acc[k];
+        }
+    }
+}
+
 template <typename T, int N, int PT>
 hipError_t launch(const SsdParams &p, int64_t blocks, hipStream_t s) {
     hipLaunchKernelGGL((ssd_chunk_kernel<T, N, PT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * waves_for<PT>()),
@@ -1142,6 +1178,7 @@ hipError_t launch_pt(const SsdParams &p, int64_t batch, hipStream_t s) {
                 const dim3 sgrid(static_cast<unsigned>(units * (p.nseg - 1)));
                 if (p.z) hipLaunchKernelGGL((ssd_line_kernel<N, true, 1>), sgrid, dim3(512), 0, s, p);
                 else hipLaunchKernelGGL((ssd_line_kernel<N, false, 1>), sgrid, dim3(512), 0, s, p);
+                hipLaunchKernelGGL((ssd_carry_kernel<N>), dim3(static_cast<unsigned>(units)), dim3(512), 0, s, p);
             }
             const dim3 grid(static_cast<unsigned>(units * p.nseg));
             if (p.z)
