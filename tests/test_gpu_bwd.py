@@ -288,3 +288,46 @@ def test_bwd_with_forward_checkpoints(io, N, T):
         e = G.err(c[:, j], lo)
         G.say(f"[bwd] checkpoint block {j} ({io}, N={N}) err={e:.2e}")
         assert e <= (1e-5 if io == gen.F32 else 2e-2), (j, e)
+
+
+def test_bwd_concurrent_host_threads():
+    """Self-contained backward calls from four host threads, each on a stream
+    of its own, at once: they share the library's side stream per device (the
+    carry pass beside the checkpoint pass), whose fork and join are enqueued
+    under a lock.  Every call's gradients equal those of a call made alone,
+    bit for bit."""
+    import threading
+    from selective_scan_ssm_amd import ops
+    inputs = [gen.make_inputs(2, 700, 260, 16, io=gen.BF16, h0_kind="normal", seed=480 + i) for i in range(4)]
+    assert all(segments(inp)[0] > 1 for inp in inputs)
+    dev = [G.device_inputs(inp) for inp in inputs]
+    douts = [G.to_torch(grads_inputs(inp, 80 + i)[0], inp["io"]) for i, inp in enumerate(inputs)]
+    call = lambda t, d: ops.scan_bwd(t["x"], t["delta"], t["A"], t["B"], t["C"], d, D=t["D"], z=t["z"],
+                                     delta_bias=t["delta_bias"], h0=t["h0"])
+    alone = []
+    for t, d in zip(dev, douts):
+        alone.append(call(t, d))
+        torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    results[i] = call(dev[i], douts[i])
+            s.synchronize()
+        except Exception as e:          # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(4):
+        for k, v in alone[i].items():
+            if v is not None:
+                assert torch.equal(v, results[i][k]), (i, k)
