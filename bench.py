@@ -40,6 +40,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -98,6 +99,13 @@ SOURCES = {
 KERNEL_PREFIX = {"scan": "scan_fwd_kernel", "rows": "scan_rows_kernel", "sm1": "sm1_scan_kernel",
                  "decode": "state_update_rows_kernel", "conv": "conv1d_kernel", "ssd": "ssd_chunk_kernel",
                  "ssdline": "ssd_line_kernel", "dtproj": "dt_proj_kernel", "dtprojrows": "dt_proj_rows_kernel"}
+# kinds whose one launch runs several kernels: (a pattern every kernel of the
+# launch matches, a pattern of the kernel that ends each launch); the others
+# run their one kernel per launch
+LAUNCH_KERNELS = {
+    # the state pass and the carry (time segments only), then the output pass
+    "ssdline": (r"ssd_line_kernel<|ssd_carry_kernel<", r"ssd_line_kernel<\d+, \w+, 0>"),
+}
 
 
 def dtproj_kind(w):
@@ -1128,6 +1136,30 @@ def summarize_stats(d, command):
     return "\n".join(lines) + "\n"
 
 
+def _counter_per_launch(d, counter, kind):
+    """Median over launches of the counter summed over every kernel of a
+    launch (dispatches taken in order, a launch closed by its last kernel),
+    and the number of launches."""
+    every, last = LAUNCH_KERNELS.get(kind, (re.escape(KERNEL_PREFIX[kind]),) * 2)
+    per = {}
+    for r in _rows(d, "*counter_collection.csv"):
+        if r["Counter_Name"] != counter or not re.search(every, r["Kernel_Name"]):
+            continue
+        k = int(r["Dispatch_Id"])
+        per[k] = (r["Kernel_Name"], per.get(k, ("", 0.0))[1] + float(r["Counter_Value"]))
+    launches, acc = [], 0.0
+    for k in sorted(per):
+        name, v = per[k]
+        acc += v
+        if re.search(last, name):
+            launches.append(acc)
+            acc = 0.0
+    if not launches:
+        raise SystemExit(f"no {counter} rows for {kind} launches in {d}")
+    v = sorted(launches)
+    return v[len(v) // 2], len(v)
+
+
 def _counter_per_dispatch(d, counter, kernel_prefix):
     vals = {}
     for r in _rows(d, "*counter_collection.csv"):
@@ -1151,12 +1183,14 @@ def summarize_traffic(kind, wname, fetch_dir, write_dir, copy_fetch_dir, copy_wr
     cw, _ = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     kib = COPY_CAL_BYTES / 1024
     f_fac, w_fac = kib / cf, kib / cw
-    kf, nf = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", pre)
-    kw, nw = _counter_per_dispatch(write_dir, "WRITE_SIZE", pre)
+    kf, nf = _counter_per_launch(fetch_dir, "FETCH_SIZE", kind)
+    kw, nw = _counter_per_launch(write_dir, "WRITE_SIZE", kind)
     fb, wb = kf * f_fac * 1024, kw * w_fac * 1024
     total = fb + wb
+    every = LAUNCH_KERNELS.get(kind, (pre,))[0].replace("\\", "").replace("<", "").replace("|", ", ")
     lines = [
-        f"# HBM traffic of {pre} on {wname}, from rocprofv3 --pmc (median over dispatches)",
+        f"# HBM traffic of {pre} on {wname}, from rocprofv3 --pmc (median over launches; "
+        f"a launch counts every kernel it runs: {every})",
         *[f"# command: {c}" for c in commands],
         f"kernel: {pre}",
         f"workload: {wname}",
@@ -1166,8 +1200,8 @@ def summarize_traffic(kind, wname, fetch_dir, write_dir, copy_fetch_dir, copy_wr
         f"copy_WRITE_SIZE_KiB: {cw:.1f}",
         f"fetch_scale: {f_fac:.4f}",
         f"write_scale: {w_fac:.4f}",
-        f"kernel_FETCH_SIZE_KiB: {kf:.1f}  ({nf} dispatches)",
-        f"kernel_WRITE_SIZE_KiB: {kw:.1f}  ({nw} dispatches)",
+        f"kernel_FETCH_SIZE_KiB: {kf:.1f}  (per launch, {nf} launches)",
+        f"kernel_WRITE_SIZE_KiB: {kw:.1f}  (per launch, {nw} launches)",
         f"fetch_bytes: {fb:.0f}",
         f"write_bytes: {wb:.0f}",
         f"bytes_per_launch: {total:.0f}",

@@ -634,6 +634,18 @@ __device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t &hi, bf16x8
     hi = __builtin_bit_cast(bf16x8_t, h);
     lo = __builtin_bit_cast(bf16x8_t, l);
 }
+// four computed values (one accumulator tile's lane) as the hi and lo halves
+// of an MFMA operand: the same terms as split8 gives them
+__device__ __forceinline__ void split4(const float (&v)[4], u32x2_t &hi, u32x2_t &lo) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) hi[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const float r0 = v[2 * q] - __uint_as_float(hi[q] << 16);
+        const float r1 = v[2 * q + 1] - __uint_as_float(hi[q] & 0xffff0000u);
+        lo[q] = pack_bf16(r0, r1);
+    }
+}
 // the eight values of an accumulator tile pair in the K order of PermK
 __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, float (&v)[8]) {
 #pragma unroll
@@ -653,25 +665,38 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 // triangular work) and the state's n-tiles (each keeps half of the block's
 // N x 16 state, fp32, in MFMA accumulators; nothing is duplicated).
 //
-// Global memory is touched in whole rows only: each thread moves one
-// 16-byte piece of x, z (and B, C) per chunk, and of y, so every wave
-// instruction covers eight full 128-byte lines.  LDS redistributes: x and z
-// as stored (rows = steps), B and C as stored, B^T (rows = n), y as produced
-// -- all double buffered, one barrier per chunk -- plus each wave's half of
-// the carried state as ready-made MFMA operands (hi and lo bf16 fragments in
-// lane order) for its partner's readout.  A chunk's y leaves at the top of
-// the next chunk.  Loads go out a chunk ahead; the chunk body has no branch.
+// Global memory: x, B, C and y move in whole rows (one 16-byte piece of x,
+// B, C and y per thread and chunk, every wave instruction covering full
+// 128-byte lines); z goes straight to the lanes that use it (8 bytes each),
+// dt to the lane of its step.  LDS redistributes: x, B and C as stored (rows
+// = steps), y as produced, each wave's half of the carried state as ready
+// MFMA operands (hi and lo bf16 fragments in lane order) for its partner's
+// readout, and the operands the workgroup shares (M^T, B^T diag(w), the
+// per-step values).  Two barriers per chunk: the first after staging, the
+// second once the shared operands are made; every read of staged data comes
+// before the second, every write of the next chunk's after it, so one buffer
+// of each suffices (79 KB at d_state 64: two workgroups per CU).  A chunk's
+// y leaves at the top of the next chunk.  Loads go out a chunk ahead; no
+// global memory operation in the chunk body sits behind a branch (the waves'
+// different shares of the shared operands are uniform branches over LDS and
+// arithmetic only).
 //
-// Per chunk and wave, with s_t the chunk prefix of Delta A (log2 units):
-//   G^T = B C^T for the five lower tiles of its output blocks (K = n),
-//   M^T = G^T masked, times Delta_s exp(s_t - s_s): on the diagonal tiles
-//     element by element, below them as u_s r_t with u_s = Delta_s
-//     exp(e_i - s_s), r_t = exp(s_t - e_i), e_i the end of s-block i (every
-//     factor <= 1 whatever the decay);
-//   Y^T = X^T M^T + (S_in C^T) diag(exp(s_t)); D skip, gate (x^T gathered
-//     from the staged rows into the K order of M^T's accumulator tiles);
-//   its state half  S^T <- exp(s_Q) S^T + B^T (w x),  w_s = u_s exp(s_Q - e_i).
-// M, S_in and w x enter the products as hi + lo bf16 terms.
+// Per chunk, with s_t the chunk prefix of Delta A (log2 units):
+//   one wave: the per-step values (Delta_t, s_t, u_s and w_s below);
+//   the workgroup's ten lower 16 x 16 tiles of M^T, each made once (G^T =
+//     B C^T over K = n, masked, times Delta_s exp(s_t - s_s): on the diagonal
+//     tiles element by element, below them as u_s r_t with u_s = Delta_s
+//     exp(e_i - s_s), r_t = exp(s_t - e_i), e_i the end of s-block i; every
+//     factor <= 1 whatever the decay): waves 0..3 the diagonal tiles, waves
+//     4..7 the six below;
+//   B^T diag(w), w_s = Delta_s exp(s_Q - s_s), one (n-tile, 32 steps) per wave;
+//   (M and B^T diag(w) do not depend on the channel: the four channel blocks
+//   share them)
+//   per wave, its blocks' readouts (S_in C^T) diag(exp(s_t));
+//   the second barrier; then per wave its state half  S^T <- exp(s_Q) S^T +
+//     (B^T diag(w)) x^T, and Y^T = X^T M^T + the readout, D skip, gate (x^T
+//     gathered from the staged rows into the K order of M^T's tiles).
+// M, S_in and B^T diag(w) enter the products as hi + lo bf16 terms.
 //
 // Time segments.  At few (b, h, 64 channels) units (160 at the 2.7b layer) one
 // sweep per unit leaves CUs idle, so the sequence is cut into nseg segments of
@@ -681,14 +706,13 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 // entering each segment, in order:
 //   S_0 = h0,  S_{j+1} = exp(sum_j) S_j + local_j;
 // MODE 0 (the output pass) then sweeps one segment per workgroup from S_seg.
-// The state pass fits three workgroups per CU (40 KB of LDS, <= 85 registers).
+// The state pass fits three workgroups per CU (35 KB of LDS, <= 85 registers).
 template <int N, bool GATE, int MODE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ? 6 : 1))) void ssd_line_kernel(SsdParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ? 6 : 4))) void ssd_line_kernel(SsdParams p) {
     constexpr bool OUT = MODE == 0;
     using MM = Mma<bf16_t>;
     using PK = PermK<bf16_t>;
     using E = uint16_t;
-    using EL = Elem<bf16_t>;
     using ST = Steps<FastMath>;
     using QD = Quad<bf16_t>;
     using frag = bf16x8_t;
@@ -700,7 +724,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
     constexpr int NKN = N / 32;                  // 32-wide K steps over n
     constexpr int PAD = 8;                       // 16 bytes of row padding
     constexpr int LN = N + PAD;                  // rows with n contiguous
-    constexpr int LQ = kQ + PAD;                 // rows with s contiguous
     constexpr int LP = PT + PAD;                 // rows with channels contiguous
     constexpr int PBB = piece_bytes(N * es, kThreads);
     constexpr int VB = PBB / es;
@@ -710,19 +733,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
     static_assert(kQ * PT * es == kThreads * 16, "one 16-byte piece of x, z, y per thread and chunk");
     using VBt = typename Vec<PBB>::t;
 
-    // (the state pass uses B^T, x and the per-step values only)
-    constexpr int BO = OUT ? 2 : 1, QO = OUT ? kQ : 1;
-    __shared__ __attribute__((aligned(16))) E sB[BO][QO][LN];   // B[s][n]
-    __shared__ __attribute__((aligned(16))) E sC[BO][QO][LN];   // C[t][n]
-    __shared__ __attribute__((aligned(16))) E sBt[2][N][LQ];    // B[s][n] at [n][s]
-    __shared__ __attribute__((aligned(16))) E sX[2][kQ][LP];    // x[s][p] of the tile
-    __shared__ __attribute__((aligned(16))) E sZ[BO][QO][LP];   // z[t][p]
-    __shared__ __attribute__((aligned(16))) E sY[BO][QO][LP];   // y[t][p]
-    __shared__ __attribute__((aligned(16))) float sCum[kWaves][kQ];   // per wave: prefix s_t
-    __shared__ __attribute__((aligned(16))) float sDl[kWaves][kQ];    // per wave: Delta_t
-    // per wave: its S_in tiles as readout operands, [buffer][wave][fragment][term][lane]
+    // Single buffers: every read of a chunk's staged rows, of the per-step
+    // values, of sS and of sY comes before the chunk's second barrier, every
+    // write of the next chunk's after it.  (The state pass uses B, x and the
+    // per-step values only.)
+    constexpr int QO = OUT ? kQ : 1;
+    __shared__ __attribute__((aligned(16))) E sB[kQ][LN];       // B[s][n]
+    __shared__ __attribute__((aligned(16))) E sC[QO][LN];       // C[t][n]
+    __shared__ __attribute__((aligned(16))) E sX[kQ][LP];       // x[s][p] of the tile
+    __shared__ __attribute__((aligned(16))) E sY[QO][LP];       // y[t][p] of the previous chunk
+    // per-step values (index = step), written by one wave
+    __shared__ __attribute__((aligned(16))) float sCum[kQ];     // prefix s_t
+    __shared__ __attribute__((aligned(16))) float sDl[kQ];      // Delta_t
+    __shared__ __attribute__((aligned(16))) float sUs[kQ];      // u_s (below)
+    __shared__ __attribute__((aligned(16))) float sWs[kQ];      // w_s (below)
+    constexpr int kStepWave = 7;
+    // per wave: its S_in tiles as readout operands, [wave][fragment][term][lane]
     constexpr int NSP = (NH + 1) / 2;
-    __shared__ __attribute__((aligned(16))) u32x4_t sS[BO][OUT ? kWaves : 1][NSP][2][OUT ? 64 : 1];
+    __shared__ __attribute__((aligned(16))) u32x4_t sS[OUT ? kWaves : 1][NSP][2][OUT ? 64 : 1];
+    // the chunk's B^T diag(w) as MFMA A operands, [n-tile][K range][term][lane]
+    __shared__ __attribute__((aligned(16))) u32x4_t sBW[NNT][2][2][64];
+    // the chunk's ten lower M^T tiles as halves of MFMA B operands,
+    // [tile][term][lane], tile (t-block j, s-block i <= j) at j (j + 1) / 2 + i;
+    // the operand of (j, s-blocks 2 kp, 2 kp + 1) is tile 2 kp then tile 2 kp + 1
+    constexpr int kMTiles = 10;
+    __shared__ __attribute__((aligned(16))) u32x2_t sM[OUT ? kMTiles : 1][2][OUT ? 64 : 1];
+    auto m_tile = [](int j, int i) __attribute__((always_inline)) { return j * (j + 1) / 2 + i; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -780,16 +816,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
         nB0[i] = ((tid + i * kThreads) / 32) * VB;
         oB[i] = sp * rowN + nB0[i] * es;
     }
-    // the thread's 16-byte piece of x, z, y: step pr, channels 8 pc .. 8 pc + 7
+    // the thread's 16-byte piece of x and y: step pr, channels 8 pc .. 8 pc + 7
     const int pr = tid / 8, pc = tid % 8;
     const uint32_t oPiece = static_cast<uint32_t>(pr) * rowX + static_cast<uint32_t>(16 * pc);
     const uint32_t oDt = static_cast<uint32_t>(lane) * rowH + static_cast<uint32_t>(h) * es;
-    // this wave's two output blocks
+    // this wave's two output blocks, and the lane's z there (steps 16 j +
+    // l16, channels 16 cb + 4 g .. + 3)
     const int jb0 = half ? 1 : 0, jb1 = half ? 2 : 3;
+    uint32_t oZ[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        oZ[r] = static_cast<uint32_t>(16 * (r ? jb1 : jb0) + l16) * rowX + static_cast<uint32_t>(16 * cb + 4 * g) * es;
 
     // ---- one chunk's registers (fetched a chunk ahead, consumed at its top)
     uint32_t rdt;
-    u32x4_t rxp, rzp;
+    u32x4_t rxp;
+    u32x2_t rz[2];
     VBt rbv[UBT][2], rcv[UBT][2];
     auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
         rdt = __builtin_amdgcn_raw_buffer_load_b16(rows_from(dtb, t0, rowH), oDt, 0, kStream);
@@ -805,15 +847,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
         }
         // x is read again by the output pass: the state pass keeps it cached
         rxp = __builtin_amdgcn_raw_buffer_load_b128(rows_from(xb, t0, rowX), oPiece, 0, OUT ? kStream : kCached);
-        // no z: an empty descriptor, zeros
-        if constexpr (OUT)
-            rzp = __builtin_amdgcn_raw_buffer_load_b128(GATE ? rows_from(zb, t0, rowX) : make_rsrc(p.x, 0u), oPiece,
-                                                        0, kStream);
+        // z straight to the lanes that use it (no z: an empty descriptor, zeros)
+        if constexpr (OUT) {
+            const rsrc_t rZ = GATE ? rows_from(zb, t0, rowX) : make_rsrc(p.x, 0u);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) rz[r] = __builtin_amdgcn_raw_buffer_load_b64(rZ, oZ[r], 0, kStream);
+        }
     };
-    // y of chunk cy (staged in sY[cy % 2]) to global memory; cy before this
-    // segment: nothing (dropped)
+
+    // y of chunk cy (staged in sY) to global memory; cy before this segment:
+    // nothing (dropped)
     auto store_y = [&](int64_t cy) __attribute__((always_inline)) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&sY[static_cast<int>(cy & 1)][pr][8 * pc]);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(&sY[pr][8 * pc]);
         const rsrc_t rY = cy >= c_lo ? rows_from(yb, cy * kQ, rowX) : make_rsrc(yb, 0u);
         __builtin_amdgcn_raw_buffer_store_b128(v, rY, oPiece, 0, kStream);
     };
@@ -841,17 +886,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
 
     auto chunk = [&](int64_t c) __attribute__((always_inline)) {
         const int64_t t0 = c * kQ;
-        const int buf = static_cast<int>(c & 1);
 
-        // ---- per-step quantities (lane = step), each wave its own copy
-        const float vmask = t0 + lane < L ? 1.0f : 0.0f;
-        const float v = __uint_as_float(rdt << 16) + bias;
-        const float delta = (sp_on ? FastMath::softplus(v) : v) * vmask;
-        const float cum = ST::prefix(delta * Ah, lane);
-        const float cend = ST::lane_value(cum, 63);
-        sCum[w][lane] = cum;
-        sDl[w][lane] = delta;
-        if constexpr (!OUT) seg_acc += cend;
+        // ---- per-step quantities (lane = step), by one wave for all
+        if (w == kStepWave) {
+            const float vmask = t0 + lane < L ? 1.0f : 0.0f;
+            const float v = __uint_as_float(rdt << 16) + bias;
+            const float delta = (sp_on ? FastMath::softplus(v) : v) * vmask;
+            const float cum = ST::prefix(delta * Ah, lane);
+            const float send = ST::lane_value(cum, 63);
+            sCum[lane] = cum;
+            sDl[lane] = delta;
+            // u_s = Delta_s exp(e_i - s_s), e_i the prefix at the end of the
+            // s-block (lane 15 of the step's 16-lane row)
+            const float eblk = __builtin_bit_cast(
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, cum), 0x15F, 0xF, 0xF, true));   // row_newbcast:15
+            sUs[lane] = delta * ST::ex(eblk - cum);
+            // w_s = Delta_s exp(s_Q - s_s), the weight of step s in the chunk's state
+            sWs[lane] = delta * ST::ex(send - cum);
+        }
+        // this chunk's z (the fetch below refills rz)
+        u32x2_t zq[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) zq[r] = OUT ? rz[r] : u32x2_t{0u, 0u};
 
         // ---- S_in of this wave's half as readout operands (hi, lo) for both
         // waves of the pair: NH == 1 holds one n-tile (its partner the other),
@@ -865,8 +921,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
             for (int e = 4; e < 8; ++e) sv[e] = 0.0f;
             frag fh, fl;
             split8(sv, fh, fl);
-            sS[buf][w][0][0][lane] = __builtin_bit_cast(u32x4_t, fh);
-            sS[buf][w][0][1][lane] = __builtin_bit_cast(u32x4_t, fl);
+            sS[w][0][0][lane] = __builtin_bit_cast(u32x4_t, fh);
+            sS[w][0][1][lane] = __builtin_bit_cast(u32x4_t, fl);
         } else {
 #pragma unroll
             for (int k = 0; k < NH / 2; ++k) {
@@ -874,30 +930,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
                 tile_pair(acc_s[2 * k], acc_s[2 * k + 1], sv);
                 frag fh, fl;
                 split8(sv, fh, fl);
-                sS[buf][w][k][0][lane] = __builtin_bit_cast(u32x4_t, fh);
-                sS[buf][w][k][1][lane] = __builtin_bit_cast(u32x4_t, fl);
+                sS[w][k][0][lane] = __builtin_bit_cast(u32x4_t, fh);
+                sS[w][k][1][lane] = __builtin_bit_cast(u32x4_t, fl);
             }
         }
 
-        // ---- stage this chunk (buffer c % 2; the previous readers of that
-        // buffer, chunk c - 2, finished before the last barrier)
-        *reinterpret_cast<u32x4_t *>(&sX[buf][pr][8 * pc]) = rxp;
-        if constexpr (OUT) *reinterpret_cast<u32x4_t *>(&sZ[buf][pr][8 * pc]) = rzp;
+        // ---- stage this chunk (the readers of the last one finished before
+        // its second barrier)
+        *reinterpret_cast<u32x4_t *>(&sX[pr][8 * pc]) = rxp;
 #pragma unroll
         for (int i = 0; i < UBT; ++i) {
             const int n0 = nB0[i];
+            *reinterpret_cast<VBt *>(&sB[sp][n0]) = rbv[i][0];
+            *reinterpret_cast<VBt *>(&sB[sp + 1][n0]) = rbv[i][1];
             if constexpr (OUT) {
-                *reinterpret_cast<VBt *>(&sB[buf][sp][n0]) = rbv[i][0];
-                *reinterpret_cast<VBt *>(&sB[buf][sp + 1][n0]) = rbv[i][1];
-                *reinterpret_cast<VBt *>(&sC[buf][sp][n0]) = rcv[i][0];
-                *reinterpret_cast<VBt *>(&sC[buf][sp + 1][n0]) = rcv[i][1];
+                *reinterpret_cast<VBt *>(&sC[sp][n0]) = rcv[i][0];
+                *reinterpret_cast<VBt *>(&sC[sp + 1][n0]) = rcv[i][1];
             }
-#pragma unroll
-            for (int e = 0; e < VB; ++e) MM::put2(&sBt[buf][n0 + e][sp], EL::raw(rbv[i][0], e), EL::raw(rbv[i][1], e));
         }
         fetch(t0 + kQ);                        // the next chunk (past the end: empty reads)
         __syncthreads();
         if constexpr (OUT) store_y(c - 1);     // the previous chunk's y, complete now
+        const float cend = sCum[kQ - 1];       // s_Q
+        if constexpr (!OUT) seg_acc += cend;
 
         // ---- x^T operand: lane (channel 16 cb + l16, group g) takes steps
         // 16 i + 4 g + v (i < 4, v < 4): K slots 8 g .. 8 g + 7 of the two
@@ -909,25 +964,93 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int s0 = 16 * (2 * kp + q / 2) + 4 * g + 2 * (q % 2);
-                u[q] = static_cast<uint32_t>(sX[buf][s0][16 * cb + l16]) |
-                       (static_cast<uint32_t>(sX[buf][s0 + 1][16 * cb + l16]) << 16);
+                u[q] = static_cast<uint32_t>(sX[s0][16 * cb + l16]) |
+                       (static_cast<uint32_t>(sX[s0 + 1][16 * cb + l16]) << 16);
             }
             xt[kp] = __builtin_bit_cast(frag, u);
         }
 
-        // ---- per-step values at the lane's K slots (steps 16 i + 4 g + v) and
-        // columns (steps 16 j + l16): u_s = Delta_s exp(e_i - s_s) with e_i
-        // the prefix at the end of s-block i
-        f32x4_t cs[4], ds[4], us[4];
-        float ct[4], eb[4];
+        // ---- M^T tile (s-block i, t-block j) of this chunk into sM: G^T over
+        // K = n, then the decay weights (lane: s = 16 i + 4 g + e, t = 16 j + l16)
+        auto g_tile = [&](int j, int i) __attribute__((always_inline)) {
+            f32x4_t gt = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            cs[i] = *reinterpret_cast<const f32x4_t *>(&sCum[w][16 * i + 4 * g]);
-            ds[i] = *reinterpret_cast<const f32x4_t *>(&sDl[w][16 * i + 4 * g]);
-            ct[i] = sCum[w][16 * i + l16];
-            eb[i] = sCum[w][16 * i + 15];
+            for (int kn = 0; kn < NKN; ++kn)
+                gt = MM::mma(PK::from_lds(&sB[16 * i + l16][32 * kn], g, 0),
+                             PK::from_lds(&sC[16 * j + l16][32 * kn], g, 0), gt);
+            return gt;
+        };
+        auto put_m = [&](int j, int i, const float (&mv)[4]) __attribute__((always_inline)) {
+            u32x2_t mh, ml;
+            split4(mv, mh, ml);
+            sM[m_tile(j, i)][0][lane] = mh;
+            sM[m_tile(j, i)][1][lane] = ml;
+        };
+        // below the diagonal (i < j): every t after block i's end, so r_t =
+        // exp(s_t - e_i) <= 1
+        auto m_below = [&](int j, int i) __attribute__((always_inline)) {
+            const f32x4_t gt = g_tile(j, i);
+            const f32x4_t ui = *reinterpret_cast<const f32x4_t *>(&sUs[16 * i + 4 * g]);
+            const float rt = ST::ex(sCum[16 * j + l16] - sCum[16 * i + 15]);
+            float mv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) us[i][e] = ds[i][e] * ST::ex(eb[i] - cs[i][e]);
+            for (int e = 0; e < 4; ++e) mv[e] = gt[e] * (ui[e] * rt);
+            put_m(j, i, mv);
+        };
+        // on the diagonal: s <= t when 4 g + e <= l16; the exponent is clamped
+        // so a masked entry never overflows
+        auto m_diag = [&](int j) __attribute__((always_inline)) {
+            const f32x4_t gt = g_tile(j, j);
+            const f32x4_t cs = *reinterpret_cast<const f32x4_t *>(&sCum[16 * j + 4 * g]);
+            const f32x4_t dl = *reinterpret_cast<const f32x4_t *>(&sDl[16 * j + 4 * g]);
+            const float ct = sCum[16 * j + l16];
+            float mv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = dl[e] * ST::ex(fminf(ct - cs[e], 0.0f));
+                mv[e] = 4 * g + e <= l16 ? gt[e] * f : 0.0f;
+            }
+            put_m(j, j, mv);
+        };
+        if constexpr (OUT) {
+            if (w < 4) {
+                m_diag(w);
+            } else {
+                // waves 4..7: (1, 0) (2, 0) | (2, 1) (3, 0) | (3, 1) | (3, 2)
+                const int k = w - 4;
+                m_below((0x3321 >> (4 * k)) & 15, (0x2110 >> (4 * k)) & 15);
+                if (k < 2) m_below(2 + k, 0);
+            }
+        }
+
+        // ---- B^T diag(w) into sBW as MFMA A operands (rows n, K = s in the
+        // x^T slot order): one (n-tile, K range) per wave, shared by the
+        // channel blocks (d_state 32: waves 4..7)
+        {
+            const int u = w ^ 4;
+            if (u < 2 * NNT) {
+                const int ni = u >> 1, kp = u & 1;
+                // B[s][n] at n = 16 ni + l16, s = 32 kp + 4 g + 0..3 and 32 kp + 16 + 4 g + 0..3
+                u32x4_t bt;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int s0 = 32 * kp + 16 * (q / 2) + 4 * g + 2 * (q % 2);
+                    bt[q] = static_cast<uint32_t>(sB[s0][16 * ni + l16]) |
+                            (static_cast<uint32_t>(sB[s0 + 1][16 * ni + l16]) << 16);
+                }
+                const f32x4_t w0 = *reinterpret_cast<const f32x4_t *>(&sWs[32 * kp + 4 * g]);
+                const f32x4_t w1 = *reinterpret_cast<const f32x4_t *>(&sWs[32 * kp + 16 + 4 * g]);
+                float bw[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float bv = __uint_as_float(q % 2 ? (bt[q / 2] & 0xffff0000u) : (bt[q / 2] << 16));
+                    bw[q] = bv * (q < 4 ? w0[q] : w1[q - 4]);
+                }
+                frag fh, fl;
+                split8(bw, fh, fl);
+                sBW[ni][kp][0][lane] = __builtin_bit_cast(u32x4_t, fh);
+                sBW[ni][kp][1][lane] = __builtin_bit_cast(u32x4_t, fl);
+            }
         }
 
         // ---- the readout operand over all N: this wave's S_in half and the partner's
@@ -935,8 +1058,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
         if constexpr (!OUT) {
         } else if constexpr (NH == 1) {
             // K slots 0..3 from half 0, 4..7 from half 1
-            const u32x4_t a0 = sS[buf][half ? partner : w][0][0][lane], b0 = sS[buf][half ? w : partner][0][0][lane];
-            const u32x4_t a1 = sS[buf][half ? partner : w][0][1][lane], b1 = sS[buf][half ? w : partner][0][1][lane];
+            const u32x4_t a0 = sS[half ? partner : w][0][0][lane], b0 = sS[half ? w : partner][0][0][lane];
+            const u32x4_t a1 = sS[half ? partner : w][0][1][lane], b1 = sS[half ? w : partner][0][1][lane];
             fs[0][0] = __builtin_bit_cast(frag, u32x4_t{a0[0], a0[1], b0[0], b0[1]});
             fs[0][1] = __builtin_bit_cast(frag, u32x4_t{a1[0], a1[1], b1[0], b1[1]});
         } else {
@@ -945,103 +1068,84 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
                 const int owner = (kn < NKN / 2) == (half == 0) ? w : partner;
                 const int k = kn % (NKN / 2);
 #pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) fs[kn][q2] = __builtin_bit_cast(frag, sS[buf][owner][k][q2][lane]);
+                for (int q2 = 0; q2 < 2; ++q2) fs[kn][q2] = __builtin_bit_cast(frag, sS[owner][k][q2][lane]);
             }
         }
 
-        // ---- the wave's two output blocks
+        // ---- the readouts of the wave's two output blocks: (S_in C^T) exp(s_t)
+        f32x4_t acc[2];
 #pragma unroll
         for (int r = 0; r < (OUT ? 2 : 0); ++r) {
             const int j = r ? jb1 : jb0;         // 0..3, uniform
-            // C rows of t-block j (B operand, K = n): for G^T and for the readout
-            frag fc[NKN];
-#pragma unroll
-            for (int kn = 0; kn < NKN; ++kn) fc[kn] = PK::from_lds(&sC[buf][16 * j + l16][32 * kn], g, 0);
-            // M^T tiles (s-block i <= j, t-block j)
-            f32x4_t m[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                m[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                if (i <= j) {
-                    f32x4_t gt = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int kn = 0; kn < NKN; ++kn)
-                        gt = MM::mma(PK::from_lds(&sB[buf][16 * i + l16][32 * kn], g, 0), fc[kn], gt);
-                    if (i < j) {
-                        const float rt = ST::ex(ct[j] - eb[i]);   // t after block i's end: <= 1
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) m[i][e] = gt[e] * (us[i][e] * rt);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            // on the diagonal: s <= t when 4 g + e <= l16; the exponent
-                            // is clamped so a masked entry never overflows
-                            const float f = ds[i][e] * ST::ex(fminf(ct[j] - cs[i][e], 0.0f));
-                            m[i][e] = 4 * g + e <= l16 ? gt[e] * f : 0.0f;
-                        }
-                    }
-                }
-            }
-            // Y^T block: the state's readout, scaled by exp(s_t) ...
             f32x4_t yo = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kn = 0; kn < NKN; ++kn)
+            for (int kn = 0; kn < NKN; ++kn) {
+                const frag fc = PK::from_lds(&sC[16 * j + l16][32 * kn], g, 0);
 #pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) yo = MM::mma(fs[kn][q2], fc[kn], yo);
-            f32x4_t acc = yo * ST::ex(ct[j]);
-            // ... plus X^T M^T over the s-blocks up to j
-#pragma unroll
-            for (int kp = 0; kp < 2; ++kp)
-                if (2 * kp <= j) {
-                    float mv[8];
-                    tile_pair(m[2 * kp], m[2 * kp + 1], mv);
-                    frag mh, ml;
-                    split8(mv, mh, ml);
-                    acc = MM::mma(xt[kp], mh, acc);
-                    acc = MM::mma(xt[kp], ml, acc);
-                }
-            // D skip, gate (lane: channels 16 cb + 4 g + e, step 16 j + l16), into sY
-            const int trow = 16 * j + l16, pcol = 16 * cb + 4 * g;
-            const u32x2_t xq = *reinterpret_cast<const u32x2_t *>(&sX[buf][trow][pcol]);
-            const u32x2_t zq = *reinterpret_cast<const u32x2_t *>(&sZ[buf][trow][pcol]);
-            float yv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float o = fmaf(Dh, QD::get(xq, e), acc[e]);
-                if constexpr (GATE) o *= silu(QD::get(zq, e));
-                yv[e] = o;
+                for (int q2 = 0; q2 < 2; ++q2) yo = MM::mma(fs[kn][q2], fc, yo);
             }
-            *reinterpret_cast<u32x2_t *>(&sY[buf][trow][pcol]) = u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
+            acc[r] = yo * ST::ex(sCum[16 * j + l16]);
         }
 
-        // ---- state half: S^T <- exp(s_Q) S^T + B^T (w x), K = s in the x^T slot
-        // order, w_s = u_s exp(s_Q - e_i)
-        frag fwx[2][2];
+        // x at the lanes' outputs (channels 16 cb + 4 g + e, steps 16 j + l16)
+        u32x2_t xq[2];
+        if constexpr (OUT) {
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-            const u32x4_t u = __builtin_bit_cast(u32x4_t, xt[kp]);
-            const float q0 = ST::ex(cend - eb[2 * kp]), q1 = ST::ex(cend - eb[2 * kp + 1]);
-            float wv[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int i = 2 * kp + q / 4, e = q % 4;
-                const float xv = __uint_as_float(q % 2 ? (u[q / 2] & 0xffff0000u) : (u[q / 2] << 16));
-                wv[q] = xv * (us[i][e] * (q < 4 ? q0 : q1));
+            for (int r = 0; r < 2; ++r) {
+                const int trow = 16 * (r ? jb1 : jb0) + l16, pcol = 16 * cb + 4 * g;
+                xq[r] = *reinterpret_cast<const u32x2_t *>(&sX[trow][pcol]);
             }
-            split8(wv, fwx[kp][0], fwx[kp][1]);
         }
+        __syncthreads();                         // sM and sBW complete; staged rows read
+
+        // ---- state half: S^T <- exp(s_Q) S^T + (B^T diag(w)) x^T
         const float dec = ST::ex(cend);
 #pragma unroll
         for (int k = 0; k < NH; ++k) {
             const int ni = NH * half + k;
             f32x4_t a = acc_s[k] * dec;
 #pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-                const frag fbt = PK::from_lds(&sBt[buf][16 * ni + l16][32 * kp], g, 0);
+            for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) a = MM::mma(fbt, fwx[kp][q2], a);
-            }
+                for (int q2 = 0; q2 < 2; ++q2) a = MM::mma(__builtin_bit_cast(frag, sBW[ni][kp][q2][lane]), xt[kp], a);
             acc_s[k] = a;
+        }
+
+        if constexpr (OUT) {
+            // ---- the wave's two output blocks: + X^T M^T over the s-blocks up to j,
+            // D skip, gate, into sY (whole rows leave from there: the four
+            // channel blocks' 32-byte pieces stored one by one would reach
+            // HBM as partial lines)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int j = r ? jb1 : jb0;
+                f32x4_t a = acc[r];
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+                    if (2 * kp <= j) {
+                        // s-block 2 kp + 1 past j: zeros (its slot holds another tile)
+                        const bool two = 2 * kp + 1 <= j;
+                        frag mt[2];
+#pragma unroll
+                        for (int q2 = 0; q2 < 2; ++q2) {
+                            const u32x2_t lo = sM[m_tile(j, 2 * kp)][q2][lane];
+                            const u32x2_t hi = two ? sM[m_tile(j, 2 * kp) + 1][q2][lane] : u32x2_t{0u, 0u};
+                            mt[q2] = __builtin_bit_cast(frag, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+                        }
+                        a = MM::mma(xt[kp], mt[0], a);
+                        a = MM::mma(xt[kp], mt[1], a);
+                    }
+                const int trow = 16 * j + l16, pcol = 16 * cb + 4 * g;
+                float yv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float o = fmaf(Dh, QD::get(xq[r], e), a[e]);
+                    if constexpr (GATE) o *= silu(QD::get(zq[r], e));
+                    yv[e] = o;
+                }
+                *reinterpret_cast<u32x2_t *>(&sY[trow][pcol]) =
+                    u32x2_t{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3])};
+            }
         }
     };
 
