@@ -669,17 +669,17 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 // B, C and y per thread and chunk, every wave instruction covering full
 // 128-byte lines); z goes straight to the lanes that use it (8 bytes each),
 // dt to the lane of its step.  LDS redistributes: x, B and C as stored (rows
-// = steps), y as produced, each wave's half of the carried state as ready
-// MFMA operands (hi and lo bf16 fragments in lane order) for its partner's
-// readout, and the operands the workgroup shares (M^T, B^T diag(w), the
-// per-step values).  Two barriers per chunk: the first after staging, the
-// second once the shared operands are made; every read of staged data comes
-// before the second, every write of the next chunk's after it, so one buffer
-// of each suffices (79 KB at d_state 64: two workgroups per CU).  A chunk's
-// y leaves at the top of the next chunk.  Loads go out a chunk ahead; no
-// global memory operation in the chunk body sits behind a branch (the waves'
-// different shares of the shared operands are uniform branches over LDS and
-// arithmetic only).
+// = steps), B^T (rows = n), y as produced, each wave's half of the carried
+// state as ready MFMA operands (hi and lo bf16 fragments in lane order) for
+// its partner's readout, the per-step values and the M^T tiles the
+// workgroup shares.  Two barriers per chunk: the first after staging, the
+// second once the M^T tiles are made; every read of staged data comes before
+// the second, every write of the next chunk's after it, so one buffer of
+// each suffices (72 KB at d_state 64: two workgroups per CU).  A chunk's y
+// leaves at the top of the next chunk.  Loads go out a chunk ahead; no global
+// memory operation in the chunk body sits behind a branch (the waves'
+// different M^T tiles and the per-step wave are uniform branches over LDS
+// and arithmetic only).
 //
 // Per chunk, with s_t the chunk prefix of Delta A (log2 units):
 //   one wave: the per-step values (Delta_t, s_t, u_s and w_s below);
@@ -688,15 +688,13 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 //     tiles element by element, below them as u_s r_t with u_s = Delta_s
 //     exp(e_i - s_s), r_t = exp(s_t - e_i), e_i the end of s-block i; every
 //     factor <= 1 whatever the decay): waves 0..3 the diagonal tiles, waves
-//     4..7 the six below;
-//   B^T diag(w), w_s = Delta_s exp(s_Q - s_s), one (n-tile, 32 steps) per wave;
-//   (M and B^T diag(w) do not depend on the channel: the four channel blocks
-//   share them)
-//   per wave, its blocks' readouts (S_in C^T) diag(exp(s_t));
-//   the second barrier; then per wave its state half  S^T <- exp(s_Q) S^T +
-//     (B^T diag(w)) x^T, and Y^T = X^T M^T + the readout, D skip, gate (x^T
+//     4..7 the six below (M does not depend on the channel: the four channel
+//     blocks share it);
+//   per wave, its state half  S^T <- exp(s_Q) S^T + B^T (w x), w_s = Delta_s
+//     exp(s_Q - s_s), and its blocks' readouts (S_in C^T) diag(exp(s_t));
+//   the second barrier; then Y^T = X^T M^T + the readout, D skip, gate (x^T
 //     gathered from the staged rows into the K order of M^T's tiles).
-// M, S_in and B^T diag(w) enter the products as hi + lo bf16 terms.
+// M, S_in and w x enter the products as hi + lo bf16 terms.
 //
 // Time segments.  At few (b, h, 64 channels) units (160 at the 2.7b layer) one
 // sweep per unit leaves CUs idle, so the sequence is cut into nseg segments of
@@ -706,13 +704,14 @@ __device__ __forceinline__ void tile_pair(const f32x4_t &a, const f32x4_t &b, fl
 // entering each segment, in order:
 //   S_0 = h0,  S_{j+1} = exp(sum_j) S_j + local_j;
 // MODE 0 (the output pass) then sweeps one segment per workgroup from S_seg.
-// The state pass fits three workgroups per CU (35 KB of LDS, <= 85 registers).
+// The state pass fits three workgroups per CU (19 KB of LDS, <= 85 registers).
 template <int N, bool GATE, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ? 6 : 4))) void ssd_line_kernel(SsdParams p) {
     constexpr bool OUT = MODE == 0;
     using MM = Mma<bf16_t>;
     using PK = PermK<bf16_t>;
     using E = uint16_t;
+    using EL = Elem<bf16_t>;
     using ST = Steps<FastMath>;
     using QD = Quad<bf16_t>;
     using frag = bf16x8_t;
@@ -724,6 +723,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
     constexpr int NKN = N / 32;                  // 32-wide K steps over n
     constexpr int PAD = 8;                       // 16 bytes of row padding
     constexpr int LN = N + PAD;                  // rows with n contiguous
+    constexpr int LQ = kQ + PAD;                 // rows with s contiguous
     constexpr int LP = PT + PAD;                 // rows with channels contiguous
     constexpr int PBB = piece_bytes(N * es, kThreads);
     constexpr int VB = PBB / es;
@@ -735,10 +735,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
 
     // Single buffers: every read of a chunk's staged rows, of the per-step
     // values, of sS and of sY comes before the chunk's second barrier, every
-    // write of the next chunk's after it.  (The state pass uses B, x and the
+    // write of the next chunk's after it.  (The state pass uses B^T, x and the
     // per-step values only.)
     constexpr int QO = OUT ? kQ : 1;
-    __shared__ __attribute__((aligned(16))) E sB[kQ][LN];       // B[s][n]
+    __shared__ __attribute__((aligned(16))) E sB[QO][LN];       // B[s][n]
+    __shared__ __attribute__((aligned(16))) E sBt[N][LQ];       // B[s][n] at [n][s]
     __shared__ __attribute__((aligned(16))) E sC[QO][LN];       // C[t][n]
     __shared__ __attribute__((aligned(16))) E sX[kQ][LP];       // x[s][p] of the tile
     __shared__ __attribute__((aligned(16))) E sY[QO][LP];       // y[t][p] of the previous chunk
@@ -751,8 +752,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
     // per wave: its S_in tiles as readout operands, [wave][fragment][term][lane]
     constexpr int NSP = (NH + 1) / 2;
     __shared__ __attribute__((aligned(16))) u32x4_t sS[OUT ? kWaves : 1][NSP][2][OUT ? 64 : 1];
-    // the chunk's B^T diag(w) as MFMA A operands, [n-tile][K range][term][lane]
-    __shared__ __attribute__((aligned(16))) u32x4_t sBW[NNT][2][2][64];
     // the chunk's ten lower M^T tiles as halves of MFMA B operands,
     // [tile][term][lane], tile (t-block j, s-block i <= j) at j (j + 1) / 2 + i;
     // the operand of (j, s-blocks 2 kp, 2 kp + 1) is tile 2 kp then tile 2 kp + 1
@@ -941,12 +940,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
 #pragma unroll
         for (int i = 0; i < UBT; ++i) {
             const int n0 = nB0[i];
-            *reinterpret_cast<VBt *>(&sB[sp][n0]) = rbv[i][0];
-            *reinterpret_cast<VBt *>(&sB[sp + 1][n0]) = rbv[i][1];
             if constexpr (OUT) {
+                *reinterpret_cast<VBt *>(&sB[sp][n0]) = rbv[i][0];
+                *reinterpret_cast<VBt *>(&sB[sp + 1][n0]) = rbv[i][1];
                 *reinterpret_cast<VBt *>(&sC[sp][n0]) = rcv[i][0];
                 *reinterpret_cast<VBt *>(&sC[sp + 1][n0]) = rcv[i][1];
             }
+#pragma unroll
+            for (int e = 0; e < VB; ++e) MM::put2(&sBt[n0 + e][sp], EL::raw(rbv[i][0], e), EL::raw(rbv[i][1], e));
         }
         fetch(t0 + kQ);                        // the next chunk (past the end: empty reads)
         __syncthreads();
@@ -1023,34 +1024,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
             }
         }
 
-        // ---- B^T diag(w) into sBW as MFMA A operands (rows n, K = s in the
-        // x^T slot order): one (n-tile, K range) per wave, shared by the
-        // channel blocks (d_state 32: waves 4..7)
-        {
-            const int u = w ^ 4;
-            if (u < 2 * NNT) {
-                const int ni = u >> 1, kp = u & 1;
-                // B[s][n] at n = 16 ni + l16, s = 32 kp + 4 g + 0..3 and 32 kp + 16 + 4 g + 0..3
-                u32x4_t bt;
+        // ---- state half: S^T <- exp(s_Q) S^T + B^T (w x), K = s in the x^T slot
+        // order, w_s = Delta_s exp(s_Q - s_s) (w x as hi + lo terms)
+        frag fwx[2][2];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int s0 = 32 * kp + 16 * (q / 2) + 4 * g + 2 * (q % 2);
-                    bt[q] = static_cast<uint32_t>(sB[s0][16 * ni + l16]) |
-                            (static_cast<uint32_t>(sB[s0 + 1][16 * ni + l16]) << 16);
-                }
-                const f32x4_t w0 = *reinterpret_cast<const f32x4_t *>(&sWs[32 * kp + 4 * g]);
-                const f32x4_t w1 = *reinterpret_cast<const f32x4_t *>(&sWs[32 * kp + 16 + 4 * g]);
-                float bw[8];
+        for (int kp = 0; kp < 2; ++kp) {
+            const u32x4_t u = __builtin_bit_cast(u32x4_t, xt[kp]);
+            const f32x4_t w0 = *reinterpret_cast<const f32x4_t *>(&sWs[32 * kp + 4 * g]);
+            const f32x4_t w1 = *reinterpret_cast<const f32x4_t *>(&sWs[32 * kp + 16 + 4 * g]);
+            float wv[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float bv = __uint_as_float(q % 2 ? (bt[q / 2] & 0xffff0000u) : (bt[q / 2] << 16));
-                    bw[q] = bv * (q < 4 ? w0[q] : w1[q - 4]);
-                }
-                frag fh, fl;
-                split8(bw, fh, fl);
-                sBW[ni][kp][0][lane] = __builtin_bit_cast(u32x4_t, fh);
-                sBW[ni][kp][1][lane] = __builtin_bit_cast(u32x4_t, fl);
+            for (int q = 0; q < 8; ++q) {
+                const float xv = __uint_as_float(q % 2 ? (u[q / 2] & 0xffff0000u) : (u[q / 2] << 16));
+                wv[q] = xv * (q < 4 ? w0[q] : w1[q - 4]);
             }
+            split8(wv, fwx[kp][0], fwx[kp][1]);
+        }
+        const float dec = ST::ex(cend);
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+            const int ni = NH * half + k;
+            f32x4_t a = acc_s[k] * dec;
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+                const frag fbt = PK::from_lds(&sBt[16 * ni + l16][32 * kp], g, 0);
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) a = MM::mma(fbt, fwx[kp][q2], a);
+            }
+            acc_s[k] = a;
         }
 
         // ---- the readout operand over all N: this wave's S_in half and the partner's
@@ -1096,20 +1097,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
                 xq[r] = *reinterpret_cast<const u32x2_t *>(&sX[trow][pcol]);
             }
         }
-        __syncthreads();                         // sM and sBW complete; staged rows read
-
-        // ---- state half: S^T <- exp(s_Q) S^T + (B^T diag(w)) x^T
-        const float dec = ST::ex(cend);
-#pragma unroll
-        for (int k = 0; k < NH; ++k) {
-            const int ni = NH * half + k;
-            f32x4_t a = acc_s[k] * dec;
-#pragma unroll
-            for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) a = MM::mma(__builtin_bit_cast(frag, sBW[ni][kp][q2][lane]), xt[kp], a);
-            acc_s[k] = a;
-        }
+        __syncthreads();                         // sM complete; staged rows read
 
         if constexpr (OUT) {
             // ---- the wave's two output blocks: + X^T M^T over the s-blocks up to j,
