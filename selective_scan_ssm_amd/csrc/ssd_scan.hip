@@ -52,6 +52,12 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 values as a packed bf16 pair, rounded to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 
 // MFMA operand policy per io dtype: LDS element, K per instruction, K
 // elements held per lane, fragment load and the instruction.
@@ -263,11 +269,16 @@ template <typename T> struct PermK;
 template <> struct PermK<bf16_t> {
     using frag = bf16x8_t;
     static constexpr int kSteps = 1;              // MFMAs per 32-wide K range
+    // term q2 of the eight values (Mma's hi / lo), converted in pairs
     static __device__ __forceinline__ frag from_tiles(const f32x4_t &a, const f32x4_t &b, int, int q2) {
-        using MM = Mma<bf16_t>;
-        const u16x8_t u = {MM::enc(MM::term(a[0], q2)), MM::enc(MM::term(a[1], q2)), MM::enc(MM::term(a[2], q2)),
-                           MM::enc(MM::term(a[3], q2)), MM::enc(MM::term(b[0], q2)), MM::enc(MM::term(b[1], q2)),
-                           MM::enc(MM::term(b[2], q2)), MM::enc(MM::term(b[3], q2))};
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        u32x4_t u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t h = pack_bf16(v[2 * q], v[2 * q + 1]);
+            u[q] = q2 == 0 ? h
+                           : pack_bf16(v[2 * q] - __uint_as_float(h << 16), v[2 * q + 1] - __uint_as_float(h & 0xffff0000u));
+        }
         return __builtin_bit_cast(frag, u);
     }
     // row points at K = 0 of the 32-wide range
@@ -613,12 +624,6 @@ __global__ __launch_bounds__(64 * waves_for<PT>()) void ssd_chunk_kernel(SsdPara
 
 // ===========================================================================
 // ---- helpers of ssd_line_kernel
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// two fp32 values as a packed bf16 pair, rounded to nearest even (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
 // eight computed values as an MFMA operand of two bf16 terms: hi = bf16(v),
 // lo = bf16(v - hi) (16 significant bits together)
 __device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t &hi, bf16x8_t &lo) {
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MODE == 1 ?
     constexpr int UBT = (kQ / 2) * (N / VB) / kThreads;
     static_assert(UBT >= 1 && (kQ / 2) * (N / VB) == UBT * kThreads, "whole B / C pieces per thread");
     static_assert(N % 32 == 0 && NH >= 1, "n tiles in pairs");
-    static_assert(kQ * PT * es == kThreads * 16, "one 16-byte piece of x, z, y per thread and chunk");
+    static_assert(kQ * PT * es == kThreads * 16, "one 16-byte piece of x and of y per thread and chunk");
     using VBt = typename Vec<PBB>::t;
 
     // Single buffers: every read of a chunk's staged rows, of the per-step
