@@ -518,16 +518,18 @@ void scan_fwd_kernel(Params p) {
 // states [4r, 4r + 4) of channel c, so a 16-lane DPP row is one state group
 // and a lane column is one channel.  Waves share nothing and never wait on
 // each other; within a wave, the per-(t, d) work and the readout sum over
-// states cross the four rows with the gfx950 lane-swap instructions
-// (v_permlane16_swap / v_permlane32_swap), not with LDS:
+// states cross the four rows:
 //   * per group of 4 steps, row r discretises step kRowStep[r] of the group
-//     (softplus of delta + bias, Delta*x) and an all-gather of the four rows
-//     gives every lane the four steps (3 swaps per value);
+//     (softplus of delta + bias, Delta*x), two groups ahead, and the wave's
+//     LDS slot gives every lane the four steps (an all-gather by the gfx950
+//     lane swaps took 6 VALU swaps per group: 3% slower at the 2.8b layer);
 //   * B and C of the block, staged in this wave's own LDS slice, reach the
 //     arithmetic through DPP row broadcasts (lane q < 4 of row r holds
 //     B[4r + q], lanes 4..7 hold C[4r + q - 4]);
 //   * the four steps' partial readouts are summed across rows by a
-//     reduce-scatter (3 swaps, 3 adds) that leaves the total of step
+//     reduce-scatter with the lane swaps v_permlane16_swap /
+//     v_permlane32_swap (3 swaps, 3 adds; through LDS, with the output a
+//     group later, it measured 3% slower) that leaves the total of step
 //     kRowStep[r] in row r, which then applies the D skip and the gate and
 //     stores it.
 // x, delta and z of a group are loaded two blocks ahead.  Long sequences are
@@ -621,6 +623,10 @@ void scan_rows_kernel(Params p) {
     constexpr int N = 16, NPL = 4, NG = kRowTB / 4;
     constexpr uint32_t es = sizeof(T);
     __shared__ __attribute__((aligned(16))) float sBC[4][2][kRowBCWords];   // per wave, double-buffered B / C
+    // per wave: one group's (Delta, Delta x) of 16 channels x 4 steps,
+    // [channel (stride 6: every channel in banks of its own)][step]
+    constexpr int kXGS = 6;
+    __shared__ __attribute__((aligned(16))) float2 sXG[4][16 * kXGS];
     __shared__ uint32_t s_ticket;
 
     const int64_t seqlen = p.seqlen, dim = p.dim;
@@ -847,7 +853,61 @@ void scan_rows_kernel(Params p) {
     // the next group's (the first of block j + 1 comes from the other buffer,
     // stashed at the start of block j) so the LDS latency is covered by a
     // whole group of arithmetic.
-    auto block = [&](Pre &pr, BCRaw &bcn, float4 &bcq, int j, auto full) __attribute__((always_inline)) {
+    auto widen = [](uint32_t wd) __attribute__((always_inline)) {
+        return sizeof(raw) == 4 ? __uint_as_float(wd) : __uint_as_float(wd << 16);
+    };
+    // ---- the per-(t, d) values of a group, two groups ahead: lane (r, c)
+    // discretises step kRowStep[r] of channel c (Delta, Delta x, and its own
+    // x for the D skip), writes (Delta, Delta x) to its wave's LDS slot at
+    // [c][step] and reads its channel's four steps straight back into the
+    // register set of the group's parity.  A wave's LDS operations run in
+    // order, so no barrier is needed, and the round trip runs under a whole
+    // group of arithmetic (a lane-swap all-gather took six VALU swaps per
+    // group).
+    float2 *xg = &sXG[w][0];
+    float4 xg01[2], xg23[2];                         // (Delta, Delta x) of steps 0, 1 / 2, 3, per group parity
+    float xvg[2];                                    // this lane's x (filtered by the prologue), per group parity
+    // (win: the group may hold the sequence's first steps, whose conv window
+    // comes from the caller; false in whole blocks, which never do)
+    auto prepare = [&](const Pre &q, int jj, int gg, auto win) __attribute__((always_inline)) {
+        // pin the first use of the group's raw inputs here: otherwise the
+        // scheduler hoists their widening next to the loads two blocks ahead
+        // and the wave waits for memory it does not need yet.  The pinned
+        // words are widened straight from 32 bits (a bf16 load zero-extends,
+        // and the shift drops the upper half anyway).
+        uint32_t dw = q.d[gg], xw = q.x[gg];
+        asm volatile("" : "+v"(dw), "+v"(xw));
+        const int sl = jj * kRowTB + 4 * gg + rstep;
+        const float v = widen(dw) + bias;
+        float dt = softplus_on ? M::softplus(v) : v;
+        dt = sl < steps ? dt : 0.0f;                 // past the end: identity step
+        float xv = widen(xw);
+        if constexpr (CONV) {
+            uint32_t h1 = q.xh[0][gg], h2 = q.xh[1][gg], h3 = q.xh[2][gg];
+            asm volatile("" : "+v"(h1), "+v"(h2), "+v"(h3));
+            float x1 = widen(h1), x2 = widen(h2), x3 = widen(h3);   // x at s - 1, s - 2, s - 3
+            if (decltype(win)::value && t_begin == 0 && jj == 0) {   // steps before 0: the caller's window
+                x1 = sl >= 1 ? x1 : cwin[2];
+                x2 = sl >= 2 ? x2 : (sl == 1 ? cwin[2] : cwin[1]);
+                x3 = sl >= 3 ? x3 : (sl == 2 ? cwin[2] : (sl == 1 ? cwin[1] : cwin[0]));
+            }
+            xv = silu(fmaf(cw[3], xv, fmaf(cw[2], x1, fmaf(cw[1], x2, fmaf(cw[0], x3, cbias)))));
+        }
+        xg[c * kXGS + rstep] = make_float2(dt, dt * xv);
+        __builtin_amdgcn_wave_barrier();
+        xg01[gg & 1] = *reinterpret_cast<const float4 *>(&xg[c * kXGS]);
+        xg23[gg & 1] = *reinterpret_cast<const float4 *>(&xg[c * kXGS + 2]);
+        xvg[gg & 1] = xv;
+    };
+
+    // one block: four groups; the raw inputs of block j + 2 are loaded into
+    // the same registers right after each group consumed its own (nx holds
+    // block j + 1's, whose first two groups are prepared in this block's last two)
+    // bcq holds the staged B / C of the group about to run: each group reads
+    // the next group's (the first of block j + 1 comes from the other buffer,
+    // stashed at the start of block j) so the LDS latency is covered by a
+    // whole group of arithmetic.
+    auto block = [&](Pre &pr, const Pre &nx, BCRaw &bcn, float4 &bcq, int j, auto full) __attribute__((always_inline)) {
         constexpr bool F = decltype(full)::value;
         if (CK && active) {                         // the state entering this block
             const int64_t blk = t_begin / kRowTB + j;
@@ -862,21 +922,38 @@ void scan_rows_kernel(Params p) {
         for (int g = 0; g < NG; ++g) {
             const float4 bc4 = bcq;
             bcq = *reinterpret_cast<const float4 *>(g + 1 < NG ? buf + 4 * (g + 1) : nbuf);
-            // pin the first use of this group's raw inputs here: otherwise the
-            // scheduler hoists their widening next to the loads two blocks
-            // ahead and the wave waits for memory it does not need yet.  The
-            // pinned words are widened straight from 32 bits (a bf16 load
-            // zero-extends, and the shift drops the upper half anyway).
-            uint32_t dw = pr.d[g], xw = pr.x[g], zw = pr.z[g];   // (raw words)
-            asm volatile("" : "+v"(dw), "+v"(xw), "+v"(zw));
-            auto widen = [](uint32_t wd) { return sizeof(raw) == 4 ? __uint_as_float(wd) : __uint_as_float(wd << 16); };
             const int sl = j * kRowTB + 4 * g + rstep;
-            const bool valid = F || sl < steps;
-            const float v = widen(dw) + bias;
-            float dt = softplus_on ? M::softplus(v) : v;
-            dt = valid ? dt : 0.0f;                  // past the end: identity step
-            float xv = widen(xw);
-            if constexpr (CONV) {
+            const float bcs[4] = {bc4.x, bc4.y, bc4.z, bc4.w};
+            float part[4];
+            float xv;
+            uint32_t zw;
+            if constexpr (!CONV) {
+                zw = pr.z[g];                        // (raw word, pinned as above)
+                asm volatile("" : "+v"(zw));
+                // this group's values, prepared two groups ago
+                const float4 e01 = xg01[g & 1], e23 = xg23[g & 1];
+                const float dts[4] = {e01.x, e01.z, e23.x, e23.z};
+                const float dtxs[4] = {e01.y, e01.w, e23.y, e23.w};
+                xv = xvg[g & 1];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    part[k] = scan_step<M, NPL, NPL>(std::make_integer_sequence<int, NPL>{}, h, A2, dts[k],
+                                                     dtxs[k], bcs[k], bcs[k]);
+                // the group after next: in this block, or among the next block's first two
+                if (g + 2 < NG)
+                    prepare(pr, j, g + 2, std::integral_constant<bool, !F>{});
+                else
+                    prepare(nx, j + 1, g + 2 - NG, std::integral_constant<bool, !F>{});
+            } else {
+                // with the conv prologue (registers already tight) the group is
+                // discretised here and all-gathered by lane swaps: the LDS form
+                // two groups ahead measured 4% slower in this instantiation
+                uint32_t dw = pr.d[g], xw = pr.x[g];
+                zw = pr.z[g];
+                asm volatile("" : "+v"(dw), "+v"(xw), "+v"(zw));
+                const float v = widen(dw) + bias;
+                float dt = softplus_on ? M::softplus(v) : v;
+                dt = (F || sl < steps) ? dt : 0.0f;  // past the end: identity step
                 uint32_t h1 = pr.xh[0][g], h2 = pr.xh[1][g], h3 = pr.xh[2][g];
                 asm volatile("" : "+v"(h1), "+v"(h2), "+v"(h3));
                 float x1 = widen(h1), x2 = widen(h2), x3 = widen(h3);   // x at s - 1, s - 2, s - 3
@@ -885,19 +962,17 @@ void scan_rows_kernel(Params p) {
                     x2 = sl >= 2 ? x2 : (sl == 1 ? cwin[2] : cwin[1]);
                     x3 = sl >= 3 ? x3 : (sl == 2 ? cwin[2] : (sl == 1 ? cwin[1] : cwin[0]));
                 }
-                xv = silu(fmaf(cw[3], xv, fmaf(cw[2], x1, fmaf(cw[1], x2, fmaf(cw[0], x3, cbias)))));
-            }
-            float dts[4], dtxs[4];
-            row_allgather(dt, dts);
-            row_allgather(dt * xv, dtxs);
-            const float bcs[4] = {bc4.x, bc4.y, bc4.z, bc4.w};
-            // group step k lives in row kRowStep^-1(k): 0 -> 0, 1 -> 2, 2 -> 1, 3 -> 3
-            constexpr int src_row[4] = {0, 2, 1, 3};
-            float part[4];
+                xv = silu(fmaf(cw[3], widen(xw), fmaf(cw[2], x1, fmaf(cw[1], x2, fmaf(cw[0], x3, cbias)))));
+                float dts[4], dtxs[4];
+                row_allgather(dt, dts);
+                row_allgather(dt * xv, dtxs);
+                // group step k lives in row kRowStep^-1(k): 0 -> 0, 1 -> 2, 2 -> 1, 3 -> 3
+                constexpr int src_row[4] = {0, 2, 1, 3};
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                part[k] = scan_step<M, NPL, NPL>(std::make_integer_sequence<int, NPL>{}, h, A2,
-                                                 dts[src_row[k]], dtxs[src_row[k]], bcs[k], bcs[k]);
+                for (int k = 0; k < 4; ++k)
+                    part[k] = scan_step<M, NPL, NPL>(std::make_integer_sequence<int, NPL>{}, h, A2,
+                                                     dts[src_row[k]], dtxs[src_row[k]], bcs[k], bcs[k]);
+            }
             float out = fmaf(Dd, xv, row_reduce_scatter(part));
             if (has_z) out *= silu(widen(zw));
             if constexpr (COL) {
@@ -937,24 +1012,28 @@ void scan_rows_kernel(Params p) {
         stash_bc(bca, 0);
     }
     float4 bcq = *reinterpret_cast<const float4 *>(bc_lds + bc_row);   // block 0, group 0
+    if constexpr (!CONV) {
+        prepare(p0, 0, 0, std::true_type{});
+        prepare(p0, 0, 1, std::true_type{});
+    }
     // bcb carries block j + 1 into block j (stashed there), then block j + 2
     int j = 0;
     if (CONV && t_begin == 0) {
         // the first two blocks of a sequence read the conv window before
         // step 0: they take the path with per-lane row checks
-        block(p0, bcb, bcq, 0, std::false_type{});
-        if (nb > 1) block(p1, bcb, bcq, 1, std::false_type{});
+        block(p0, p1, bcb, bcq, 0, std::false_type{});
+        if (nb > 1) block(p1, p0, bcb, bcq, 1, std::false_type{});
         j = 2;
     }
     for (; j + 1 < nb && j + 3 < nfull; j += 2) {
-        block(p0, bcb, bcq, j, std::true_type{});
-        block(p1, bcb, bcq, j + 1, std::true_type{});
+        block(p0, p1, bcb, bcq, j, std::true_type{});
+        block(p1, p0, bcb, bcq, j + 1, std::true_type{});
     }
     for (; j + 1 < nb; j += 2) {
-        block(p0, bcb, bcq, j, std::false_type{});
-        block(p1, bcb, bcq, j + 1, std::false_type{});
+        block(p0, p1, bcb, bcq, j, std::false_type{});
+        block(p1, p0, bcb, bcq, j + 1, std::false_type{});
     }
-    if (j < nb) block(p0, bcb, bcq, j, std::false_type{});
+    if (j < nb) block(p0, p1, bcb, bcq, j, std::false_type{});
 
     if (seg + 1 < p.n_segs) {
 #pragma unroll
