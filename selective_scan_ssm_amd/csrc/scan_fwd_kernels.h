@@ -867,8 +867,10 @@ void scan_rows_kernel(Params p) {
     float2 *xg = &sXG[w][0];
     float4 xg01[2], xg23[2];                         // (Delta, Delta x) of steps 0, 1 / 2, 3, per group parity
     float xvg[2];                                    // this lane's x (filtered by the prologue), per group parity
-    // (win: the group may hold the sequence's first steps, whose conv window
-    // comes from the caller; false in whole blocks, which never do)
+    // (win: the group may lie outside whole blocks, so it may hold the
+    // sequence's first steps, whose conv window comes from the caller, or
+    // steps past the segment's end; false when it lies in a whole block,
+    // which holds neither)
     auto prepare = [&](const Pre &q, int jj, int gg, auto win) __attribute__((always_inline)) {
         // pin the first use of the group's raw inputs here: otherwise the
         // scheduler hoists their widening next to the loads two blocks ahead
@@ -880,7 +882,8 @@ void scan_rows_kernel(Params p) {
         const int sl = jj * kRowTB + 4 * gg + rstep;
         const float v = widen(dw) + bias;
         float dt = softplus_on ? M::softplus(v) : v;
-        dt = sl < steps ? dt : 0.0f;                 // past the end: identity step
+        if constexpr (decltype(win)::value)
+            dt = sl < steps ? dt : 0.0f;             // past the end: identity step
         float xv = widen(xw);
         if constexpr (CONV) {
             uint32_t h1 = q.xh[0][gg], h2 = q.xh[1][gg], h3 = q.xh[2][gg];
