@@ -9,7 +9,13 @@ must come from a load.  This test disassembles every gfx950 code object of
 libssmscan.so (code built here from this repository's sources) and checks
 every DPP instruction: no VALU write of its source register within the two
 wait states before it.  A planted listing checks that the checker finds such a
-write."""
+write.
+
+The same holds for an MFMA's A and B operands: a VALU write needs two wait
+states before an MFMA reads the VGPR (the compiler inserts s_nop 1 for its
+own code; an operand last written inside inline assembly would get none).
+Every MFMA of the library (the SSD and dt_proj kernels) is checked for that
+hazard too."""
 import os
 import re
 import shutil
@@ -77,6 +83,39 @@ def dpp_hazards(insts):
     return n_dpp, found
 
 
+def mfma_src_hazards(insts):
+    """MFMA instructions whose A or B operand register a VALU wrote less
+    than two wait states before (counted as in dpp_hazards)."""
+    found, n_mfma = [], 0
+    for i, (op, args) in enumerate(insts):
+        if not op.startswith("v_mfma"):
+            continue
+        n_mfma += 1
+        ops = [a.strip() for a in args.split(",")]
+        if len(ops) < 3:
+            continue
+        srcs = set()
+        for a in ops[1:3]:
+            m = re.match(r"v\[(\d+):(\d+)\]", a)
+            if m:
+                srcs |= {f"v{k}" for k in range(int(m.group(1)), int(m.group(2)) + 1)}
+            elif re.match(r"^v\d+$", a):
+                srcs.add(a)
+        waits, j = 0, i - 1
+        while j >= 0 and waits < 2:
+            pop, pargs = insts[j]
+            if pop == "LABEL":
+                break
+            if pop == "s_nop":
+                waits += int(pargs.split()[0], 0) + 1
+            else:
+                if pop.startswith("v_") and not pop.startswith("v_mfma") and srcs & written_vgprs(pargs):
+                    found.append((insts[j], insts[i]))
+                waits += 1
+            j -= 1
+    return n_mfma, found
+
+
 def code_objects(lib_path, tmp):
     """The gfx950 code objects of the library's .hip_fatbin (one bundle per
     translation unit)."""
@@ -116,6 +155,42 @@ def test_checker_finds_a_planted_hazard():
     n, found = dpp_hazards(parse(listing))
     assert n == 4
     assert [f[1][1].split(",")[1].strip() for f in found] == ["v5", "v11"]
+
+
+def test_checker_finds_a_planted_mfma_source_hazard():
+    listing = """0000000000002000 <k>:
+    v_fmac_f32_dpp v20, v23, v17 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1
+    v_mul_f32_e64 v5, |v4|, s96
+    v_mfma_f32_16x16x4_f32 a[0:3], v57, v20, a[0:3]
+    v_fmac_f32_dpp v21, v23, v17 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1
+    s_nop 1
+    v_mfma_f32_16x16x4_f32 a[0:3], v57, v21, a[0:3]
+    v_mov_b32_e32 v[30:31], 0
+    v_mfma_f32_16x16x32_bf16 v[0:3], v[28:31], v[40:43], v[0:3]
+    ds_read_b128 v[44:47], v1
+    v_mfma_f32_16x16x32_bf16 v[0:3], v[44:47], v[40:43], v[0:3]
+"""
+    n, found = mfma_src_hazards(parse(listing))
+    assert n == 4
+    assert [f[0][1].split(",")[0].strip() for f in found] == ["v20", "v[30:31]"]
+
+
+@pytest.mark.skipif(not (os.path.exists(OBJDUMP) and shutil.which("objcopy")), reason="no llvm-objdump / objcopy")
+def test_no_mfma_source_hazard_in_the_built_library(tmp_path):
+    if not os.path.exists(_lib.LIB_PATH):
+        from selective_scan_ssm_amd import build
+        build.build()
+    paths = code_objects(_lib.LIB_PATH, str(tmp_path))
+    assert paths, "no gfx950 code object in the library"
+    total, hazards = 0, []
+    for path in paths:
+        dis = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", path], capture_output=True, text=True,
+                             check=True).stdout
+        n, found = mfma_src_hazards(parse(dis))
+        total += n
+        hazards += found
+    assert total > 100, total               # the SSD and dt_proj kernels' MFMAs are there
+    assert not hazards, hazards[:5]
 
 
 @pytest.mark.skipif(not (os.path.exists(OBJDUMP) and shutil.which("objcopy")), reason="no llvm-objdump / objcopy")
