@@ -89,14 +89,19 @@ constexpr int kDppRor8 = 0x128;        // row_ror:8   (lane i <-> i ^ 8 within a
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror (i <-> 7 - i within 8 lanes)
 constexpr int kDppQuad2301 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppQuad1032 = 0xB1;     // quad_perm [1,0,3,2]
+// (every pattern used here pairs lanes inside a row, so no source lane is out
+// of bounds; bound_ctrl on lets the compiler fold the move into the add that
+// consumes it, v_add_f32_dpp)
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // One butterfly stage inside a 16-lane row: lanes whose `bit` is 0 keep the
 // lower half of the R values, the others the upper half, and each adds the
 // matching half of its partner (the lane the DPP pattern pairs it with, which
-// differs in `bit`).  With one value left the stage sums both lanes.
+// differs in `bit`).  Both pair sums are formed in every lane (own + partner,
+// one DPP add each) and the lane keeps its half's: one select per kept value.
+// With one value left the stage sums both lanes.
 template <int R, int CTRL>
 __device__ __forceinline__ void dpp_stage(float (&v)[R], float (&out)[R > 1 ? R / 2 : 1], bool upper) {
     if constexpr (R == 1) {
@@ -104,9 +109,9 @@ __device__ __forceinline__ void dpp_stage(float (&v)[R], float (&out)[R > 1 ? R 
     } else {
 #pragma unroll
         for (int m = 0; m < R / 2; ++m) {
-            const float keep = upper ? v[m + R / 2] : v[m];
-            const float send = upper ? v[m] : v[m + R / 2];
-            out[m] = keep + dpp<CTRL>(send);
+            const float lo = v[m] + dpp<CTRL>(v[m]);
+            const float hi = v[m + R / 2] + dpp<CTRL>(v[m + R / 2]);
+            out[m] = upper ? hi : lo;
         }
     }
 }
